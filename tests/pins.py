@@ -1,0 +1,533 @@
+"""Pins of the CPU oracle: checks against what the pages and mathematics fix.
+
+Each ``pin_*`` function takes an oracle instance (``oracle.oracle.Oracle``)
+and raises AssertionError on failure.  ``test_oracle_pins.py`` runs them on
+the oracle; ``test_oracle_mutants.py`` runs them on copies of the oracle with
+planted mistakes and requires every mistake to be caught.
+
+Independent routes used here (none re-types the oracle's own arithmetic):
+  * E4M3 decoding comes from PyTorch's float8_e4m3fn dtype (a library);
+  * nearest-with-ties-to-even is decided by comparing against grid midpoints
+    in float64, where every quantity involved is exact;
+  * BF16 rounding is cross-checked against PyTorch's CPU cast;
+  * the MXFP8 exponent is checked against a closed form read off the bits;
+  * block formats are checked on inputs built to be exactly representable,
+    where the whole round trip must be the identity and every scale is a
+    known power of two (a different power per tile/block, so that tile and
+    block indexing is exercised), on hand-worked examples whose values were
+    derived from the printed formulas, and on invariants (QDQ equals
+    dequantize-of-quantize, idempotence, sibling sharing, nearest-code).
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# --------------------------------------------------------------------------- helpers
+
+def f32_bits(x) -> np.ndarray:
+    return np.asarray(x, np.float32).view(np.uint32)
+
+
+def bf16_f32(w) -> np.ndarray:
+    return (np.asarray(w, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def f32_to_bf16_torch(x) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def all_finite_bf16() -> np.ndarray:
+    """The 65,280 finite BF16 bit patterns (both zeros, subnormals included)."""
+    u = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f = bf16_f32(u)
+    return u[np.isfinite(f)]
+
+
+def e4m3_table():
+    """Decoded value of every E4M3 code, from PyTorch's float8_e4m3fn."""
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    return codes.view(torch.float8_e4m3fn).to(torch.float32).numpy()
+
+
+def e4m3_positive_grid():
+    vals = e4m3_table()[:0x7F]          # codes 0x00..0x7E: 0 .. 448, increasing
+    return vals.astype(np.float64), np.arange(0x7F, dtype=np.int64)
+
+
+def read_grid_file() -> np.ndarray:
+    vals = []
+    with open(os.path.join(GOLDEN, "e2m1_grid.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                vals.append(float(line))
+    return np.array(vals, np.float64)
+
+
+def read_constants() -> dict:
+    out = {}
+    with open(os.path.join(GOLDEN, "format_constants.txt")) as f:
+        for line in f:
+            line = line.split("--")[0].split("#")[0].strip()
+            if line:
+                k, v = line.split()[:2]
+                out[k] = float(v)
+    return out
+
+
+def nearest_even_codes(v, grid, codes) -> np.ndarray:
+    """Code of the grid point nearest to |v| (ties to the even code, saturating at
+    the top of the grid), with the sign bit supplied by the caller.  float64
+    comparisons against midpoints of neighbouring grid points are exact here."""
+    a = np.abs(np.asarray(v, np.float64))
+    hi = np.searchsorted(grid, a, side="left")           # first grid point >= a
+    hi = np.minimum(hi, len(grid) - 1)
+    lo = np.maximum(hi - 1, 0)
+    exact = grid[hi] == a
+    mid = (grid[lo] + grid[hi]) / 2.0
+    pick_lo = a < mid
+    pick_hi = a > mid
+    tie_lo = (codes[lo] % 2) == 0
+    out = np.where(pick_lo, codes[lo], np.where(pick_hi, codes[hi], np.where(tie_lo, codes[lo], codes[hi])))
+    out = np.where(exact, codes[hi], out)
+    out = np.where(a >= grid[-1], codes[-1], out)
+    return out
+
+
+def midpoint_probes(grid) -> np.ndarray:
+    """float32 values at, and one float32 ulp either side of, each grid midpoint."""
+    mids = ((grid[1:] + grid[:-1]) / 2.0).astype(np.float32)
+    up = np.nextafter(mids, np.float32(np.inf))
+    dn = np.nextafter(mids, np.float32(0))
+    return np.concatenate([mids, up, dn])
+
+
+def random_f32(n, seed, lo_exp=-140, hi_exp=12) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    m = rng.integers(0, 1 << 23, n, dtype=np.uint32)
+    e = rng.integers(max(lo_exp + 127, 0), min(hi_exp + 127, 254), n, dtype=np.uint32)
+    s = rng.integers(0, 2, n, dtype=np.uint32)
+    return ((s << 31) | (e << 23) | m).view(np.float32)
+
+
+def sign_bit(v) -> np.ndarray:
+    return (f32_bits(np.asarray(v, np.float32)) >> 31).astype(np.int64)
+
+
+# --------------------------------------------------------------------------- scalar pins
+
+def pin_constants(O):
+    """The pages' constants: E4M3 max 448, E2M1 max 6, 6 * 448 = 2688."""
+    c = read_constants()
+    assert c["E4M3_MAX"] == 448.0 and c["E2M1_MAX"] == 6.0
+    assert c["NVFP4_GLOBAL_DIVISOR"] == c["E2M1_MAX"] * c["E4M3_MAX"]
+    assert O.e4m3_decode(0x7E) == c["E4M3_MAX"] and O.e4m3_decode(0xFE) == -c["E4M3_MAX"]
+    assert O.e2m1_decode(7) == c["E2M1_MAX"] and O.e2m1_decode(15) == -c["E2M1_MAX"]
+    # global scale of an amax equal to the divisor is exactly one
+    assert O.nvfp4_global_scale(c["NVFP4_GLOBAL_DIVISOR"]) == 1.0
+
+
+def pin_e4m3_decode_library(O):
+    """Every non-NaN E4M3 code decodes to PyTorch's float8_e4m3fn value (sign of zero too)."""
+    tab = e4m3_table()
+    for c in range(256):
+        if c in (0x7F, 0xFF):
+            continue
+        v = O.e4m3_decode(c)
+        assert f32_bits(np.float32(v)) == f32_bits(tab[c]), (c, v, tab[c])
+
+
+def pin_e4m3_encode_exact(O):
+    """E4M3 encode == nearest E4M3 value, ties to even code, saturating, sign kept:
+    on all finite BF16 values, FP32 probes around every midpoint, and random FP32."""
+    grid, codes = e4m3_positive_grid()
+    v = np.concatenate([bf16_f32(all_finite_bf16()), midpoint_probes(grid), -midpoint_probes(grid),
+                        random_f32(200000, 1), np.float32([448.0, 464.0, 479.9, 480.0, 1e30, -1e30, np.inf, -np.inf])])
+    want = nearest_even_codes(v, grid, codes) | (sign_bit(v) << 7)
+    got = O.e4m3_encode(v).astype(np.int64)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{bad.size} mismatches, first {v[bad[:5]]} got {got[bad[:5]]} want {want[bad[:5]]}"
+
+
+def pin_e4m3_encode_library(O):
+    """E4M3 encode == PyTorch's round-to-nearest cast after clamping to +-448."""
+    v = np.concatenate([random_f32(400000, 2, -20, 10), bf16_f32(all_finite_bf16())])
+    t = torch.from_numpy(v).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = O.e4m3_encode(v)
+    assert np.array_equal(got, t)
+
+
+def pin_e2m1_table(O):
+    """The pages' E2M1 ladder: code k decodes to the k-th grid value, each grid
+    value encodes back to its code, anything above 6 saturates to code 7."""
+    grid = read_grid_file()
+    assert len(grid) == 8 and grid[-1] == read_constants()["E2M1_MAX"]
+    for c in range(16):
+        want = grid[c & 7] * (-1.0 if c & 8 else 1.0)
+        got = O.e2m1_decode(c)
+        assert got == want and (np.signbit(got) == bool(c & 8)), (c, got, want)
+    assert list(O.e2m1_encode(grid)) == list(range(8))
+    assert list(O.e2m1_encode(-grid)) == [8 + k for k in range(8)]
+    assert list(O.e2m1_encode([6.0001, 7.0, 100.0, 1e30, -7.0])) == [7, 7, 7, 7, 15]
+
+
+def pin_e2m1_encode_exact(O):
+    """E2M1 encode == nearest grid value, ties to even code, on all finite BF16 values,
+    FP32 probes around every midpoint and random FP32."""
+    grid = read_grid_file()
+    codes = np.arange(8, dtype=np.int64)
+    v = np.concatenate([bf16_f32(all_finite_bf16()), midpoint_probes(grid), -midpoint_probes(grid),
+                        random_f32(200000, 3, -10, 5)])
+    want = nearest_even_codes(v, grid, codes) | (sign_bit(v) << 3)
+    got = O.e2m1_encode(v).astype(np.int64)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{bad.size} mismatches, first {v[bad[:5]]} got {got[bad[:5]]} want {want[bad[:5]]}"
+
+
+def pin_bf16_library(O):
+    """FP32 -> BF16 equals PyTorch's CPU cast (nearest even, overflow to Inf)."""
+    rng = np.random.default_rng(4)
+    u = rng.integers(0, 1 << 32, 400000, dtype=np.uint64).astype(np.uint32)
+    v = u.view(np.float32)
+    v = v[~np.isnan(v)]
+    ties = ((rng.integers(0, 1 << 16, 1000, dtype=np.uint32) << 16) | 0x8000).view(np.float32)
+    ties = ties[np.isfinite(ties)]
+    edge = np.float32([3.3895314e38, 3.3961775e38, 3.4028235e38, -3.4028235e38, 0.0, -0.0, 1e-45, -1e-45])
+    v = np.concatenate([v, ties, edge])
+    assert np.array_equal(O.f32_to_bf16(v), f32_to_bf16_torch(v))
+
+
+def pin_mxfp8_byte_closed_form(O):
+    """On all 32,640 non-negative finite BF16 amax values: the shared exponent e is the
+    smallest integer with amax <= 448 * 2^e (or -127), and equals the closed form read
+    off the bits, e + 127 = max(0, Eb - 8 + [m7 > 96]) (448 = 1.75 * 2^8, 0.75 = 96/128)."""
+    u = all_finite_bf16()
+    u = u[u < 0x8000]
+    amax = bf16_f32(u)
+    got = O.mxfp8_scale_byte(amax).astype(np.int64)
+    Eb = (u.astype(np.int64) >> 7) & 0xFF
+    m7 = u.astype(np.int64) & 0x7F
+    closed = np.maximum(0, Eb - 8 + (m7 > 96))
+    assert np.array_equal(got, closed)
+    e = got - 127
+    a = amax.astype(np.float64)
+    assert np.all(a <= np.ldexp(448.0, e))
+    assert np.all((e == -127) | (a > np.ldexp(448.0, e - 1)))
+    assert got.max() <= 254
+
+
+# --------------------------------------------------------------------------- worked examples
+
+def _read_examples():
+    ex = {}
+    with open(os.path.join(GOLDEN, "worked_examples.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            fmt, key, *vals = line.split()
+            ex.setdefault(fmt, {})[key] = vals
+    return ex
+
+
+def _num(v):
+    return [int(x, 0) if x.startswith("0x") or x.isdigit() else float(x) for x in v]
+
+
+def _to_bf16(vals) -> np.ndarray:
+    return f32_to_bf16_torch(np.float32(vals))
+
+
+def pin_worked_examples(O):
+    ex = _read_examples()
+    # NVFP4: the block, in a group with an anchor tensor of amax A
+    nv = ex["nvfp4"]
+    x = _to_bf16(_num(nv["x"])).reshape(1, 16)
+    anchor = _to_bf16([float(nv["A"][0])] + [0.0] * 15).reshape(1, 16)
+    A, g, outs = O.nvfp4_quantize_group([x, anchor])
+    assert A == float(nv["A"][0]) and g == float(nv["g"][0])
+    p, s = outs[0]
+    assert int(s[0, 0]) == int(nv["block_scale_code"][0], 0)
+    assert O.nvfp4_effective_scale(int(s[0, 0]), g) == float(nv["S"][0])
+    codes = _num(nv["codes"])
+    want_p = np.array([codes[2 * j] | (codes[2 * j + 1] << 4) for j in range(8)], np.uint8)
+    assert np.array_equal(p[0], want_p), (p[0], want_p)
+    y = O.nvfp4_dequantize(p, s, g)
+    assert np.array_equal(y[0], _to_bf16(_num(nv["y"])))
+    assert np.array_equal(O.nvfp4_qdq(x, g)[0], _to_bf16(_num(nv["y"])))
+    # MXFP8: one 1x32 block
+    mx = ex["mxfp8"]
+    xs = _num(mx["x"])
+    x = _to_bf16(xs + [0.0] * (32 - len(xs))).reshape(1, 32)
+    q, e = O.mxfp8_quantize(x)
+    assert int(e[0, 0]) == int(mx["byte"][0])
+    assert list(q[0, :len(xs)]) == _num(mx["codes"]) and not q[0, len(xs):].any()
+    y = O.mxfp8_dequantize(q, e)
+    assert np.array_equal(y[0, :len(xs)], _to_bf16(_num(mx["y"])))
+    # block-wise FP8: one tile (a 1 x 5 tensor is a single clipped tile)
+    fb = ex["fp8blk"]
+    x = _to_bf16(_num(fb["x"])).reshape(1, -1)
+    q, s = O.fp8blk_quantize(x)
+    assert float(s[0, 0]) == float(fb["s"][0])
+    assert list(q[0]) == _num(fb["codes"])
+    assert np.array_equal(O.fp8blk_dequantize(q, s)[0], _to_bf16(_num(fb["y"])))
+
+
+# --------------------------------------------------------------------------- exact round trips
+
+def _e4m3_values(rng, n, normal_only=False):
+    tab = e4m3_table()
+    pool = np.array([c for c in range(256) if c not in (0x7F, 0xFF) and (not normal_only or (c & 0x78))])
+    return tab[rng.choice(pool, n)].astype(np.float64)
+
+
+def pin_round_trip_fp8blk(O):
+    """Tiles built from E4M3 values times 2^k_tile, each holding +-448 * 2^k_tile:
+    s == 2^k_tile, the codes are those values, and dequantize returns the input.
+    Ragged 300 x 200 tensor (2 x 3 ... partial tiles), a different k per tile."""
+    rng = np.random.default_rng(10)
+    M, N = 300, 200
+    tm, tn = (M + 127) // 128, (N + 127) // 128
+    k = rng.integers(-30, 20, (tm, tn))
+    vals = _e4m3_values(rng, M * N).reshape(M, N)
+    kk = np.repeat(np.repeat(k, 128, 0), 128, 1)[:M, :N]
+    for i in range(tm):
+        for j in range(tn):
+            r, c = 128 * i + int(rng.integers(0, min(128, M - 128 * i))), 128 * j + int(rng.integers(0, min(128, N - 128 * j)))
+            vals[r, c] = 448.0 * (1 if rng.integers(0, 2) else -1)
+    x = np.ldexp(vals, kk).astype(np.float32)
+    w = f32_to_bf16_torch(x).reshape(M, N)
+    assert np.array_equal(bf16_f32(w), x), "construction must be BF16-exact"
+    q, s = O.fp8blk_quantize(w)
+    assert np.array_equal(s, np.ldexp(1.0, k).astype(np.float32))
+    want_codes = O.e4m3_encode(vals.astype(np.float32)).reshape(M, N)
+    assert np.array_equal(q, want_codes)
+    assert np.array_equal(e4m3_table()[q].astype(np.float64), vals)
+    assert np.array_equal(O.fp8blk_dequantize(q, s), w)
+
+
+def pin_round_trip_mxfp8(O):
+    """Blocks of E4M3 values times 2^k_block holding +-448 * 2^k_block: byte == 127 + k,
+    codes are those values, dequantize returns the input (a different k per block)."""
+    rng = np.random.default_rng(11)
+    M, N = 37, 256
+    nb = N // 32
+    k = rng.integers(-100, 100, (M, nb))
+    vals = _e4m3_values(rng, M * N).reshape(M, N)
+    for r in range(M):
+        for b in range(nb):
+            vals[r, 32 * b + int(rng.integers(0, 32))] = 448.0 * (1 if rng.integers(0, 2) else -1)
+    x = np.ldexp(vals, np.repeat(k, 32, 1)).astype(np.float32)
+    w = f32_to_bf16_torch(x).reshape(M, N)
+    assert np.array_equal(bf16_f32(w), x)
+    q, e = O.mxfp8_quantize(w)
+    assert np.array_equal(e.astype(np.int64), 127 + k)
+    assert np.array_equal(e4m3_table()[q].astype(np.float64), vals)
+    assert np.array_equal(O.mxfp8_dequantize(q, e), w)
+
+
+def pin_round_trip_nvfp4(O):
+    """Group amax A = 2688 * 2^k, so g = 2^k; each block holds E2M1 grid values times
+    s_b * 2^k with one +-6 * s_b * 2^k (s_b a normal E4M3 value): the block-scale code
+    is s_b's, the element codes are the grid codes, dequantize returns the input."""
+    rng = np.random.default_rng(12)
+    grid = read_grid_file()
+    for k in (-20, 0, 7):
+        M, N = 24, 64
+        nb = N // 16
+        sb = _e4m3_values(rng, M * nb, normal_only=True).reshape(M, nb)
+        sb = np.abs(sb)
+        gc = rng.integers(0, 16, (M, N))
+        gv = grid[gc & 7] * np.where(gc & 8, -1.0, 1.0)
+        for r in range(M):
+            for b in range(nb):
+                gc[r, 16 * b + int(rng.integers(0, 16))] = 7 | (8 if rng.integers(0, 2) else 0)
+        gv = grid[gc & 7] * np.where(gc & 8, -1.0, 1.0)
+        x = np.ldexp(gv * np.repeat(sb, 16, 1), k).astype(np.float32)
+        w1 = f32_to_bf16_torch(x).reshape(M, N)
+        assert np.array_equal(bf16_f32(w1), x)
+        anchor = np.zeros((2, 32), np.float32)
+        anchor[1, 5] = np.ldexp(2688.0, k)
+        w2 = f32_to_bf16_torch(anchor).reshape(2, 32)
+        A, g, outs = O.nvfp4_quantize_group([w1, w2])
+        assert g == np.ldexp(1.0, k)
+        p, s = outs[0]
+        assert np.array_equal(e4m3_table()[s].astype(np.float64), sb)
+        codes = np.empty((M, N), np.int64)
+        codes[:, 0::2] = p & 15
+        codes[:, 1::2] = p >> 4
+        mag_ok = (codes & 7) == (gc & 7)
+        sign_ok = ((codes & 8) == (gc & 8)) | ((gc & 7) == 0)
+        assert np.all(mag_ok & sign_ok)
+        assert np.array_equal(O.nvfp4_dequantize(p, s, g), w1)
+
+
+# --------------------------------------------------------------------------- invariants on random data
+
+def _moe_like(rng, M, N, scale=0.02, p_out=0.01, factor=50.0):
+    z = rng.standard_normal((M, N)) * scale * np.exp(0.5 * rng.standard_normal((M, 1)))
+    z = z * np.where(rng.random((M, N)) < p_out, factor, 1.0)
+    return f32_to_bf16_torch(z.astype(np.float32)).reshape(M, N)
+
+
+def pin_nearest_fp8blk(O):
+    """Every code is the E4M3 value nearest to x / s (up to the FP32 rounding of the
+    quotient), the tile max lands on +-448, and s is a multiple of its tile's
+    amax by 1/448 within one FP32 rounding."""
+    rng = np.random.default_rng(13)
+    M, N = 200, 300
+    w = _moe_like(rng, M, N)
+    q, s = O.fp8blk_quantize(w)
+    x = bf16_f32(w).astype(np.float64)
+    tab = e4m3_table().astype(np.float64)
+    sf = np.repeat(np.repeat(s.astype(np.float64), 128, 0), 128, 1)[:M, :N]
+    qq = x / sf
+    grid, _ = e4m3_positive_grid()
+    d_chosen = np.abs(tab[q] - qq)
+    d_best = np.min(np.abs(np.abs(qq)[..., None] - grid[None, None, :]), axis=-1)
+    assert np.all(d_chosen <= d_best + 2.0 ** -22 * np.abs(qq))
+    assert np.all(np.sign(tab[q]) * np.sign(qq) >= 0)
+    pad = np.zeros((256, 384))
+    pad[:M, :N] = np.abs(x)
+    tmax = pad.reshape(2, 128, 3, 128).max(axis=(1, 3))
+    assert np.all(np.abs(s.astype(np.float64) * 448.0 / tmax - 1.0) <= 2.0 ** -23)
+
+
+def pin_nearest_mxfp8(O):
+    """Every code is the E4M3 value nearest to x * 2^-e, and no element saturates."""
+    rng = np.random.default_rng(14)
+    M, N = 64, 512
+    w = _moe_like(rng, M, N)
+    q, e = O.mxfp8_quantize(w)
+    x = bf16_f32(w).astype(np.float64)
+    qq = x * np.ldexp(1.0, 127 - np.repeat(e.astype(np.int64), 32, 1))
+    assert np.all(np.abs(qq) <= 448.0)
+    tab = e4m3_table().astype(np.float64)
+    grid, _ = e4m3_positive_grid()
+    d_chosen = np.abs(tab[q] - qq)
+    d_best = np.min(np.abs(np.abs(qq)[..., None] - grid[None, None, :]), axis=-1)
+    assert np.all(d_chosen <= d_best)
+
+
+def pin_nearest_nvfp4(O):
+    """Every element code is the E2M1 value nearest to x / S; each block's largest
+    element lands within the E4M3 rounding of the block scale of 6 (normal scales)."""
+    rng = np.random.default_rng(15)
+    M, N = 64, 256
+    w = _moe_like(rng, M, N)
+    A, g, [(p, s)] = O.nvfp4_quantize_group([w])
+    grid = read_grid_file()
+    x = bf16_f32(w).astype(np.float64)
+    S = np.array([[O.nvfp4_effective_scale(int(c), g) for c in row] for row in s])
+    Sf = np.repeat(S, 16, 1)
+    codes = np.empty((M, N), np.int64)
+    codes[:, 0::2] = p & 15
+    codes[:, 1::2] = p >> 4
+    val = grid[codes & 7] * np.where(codes & 8, -1.0, 1.0)
+    nz = Sf > 0
+    qq = np.where(nz, x / np.where(nz, Sf, 1.0), 0.0)
+    d_best = np.min(np.abs(np.abs(qq)[..., None] - grid[None, None, :]), axis=-1)
+    assert np.all(np.abs(val - qq) <= d_best + 2.0 ** -22 * np.abs(qq))
+    tab = e4m3_table()
+    normal = (s & 0x78) != 0
+    bmax = np.abs(x).reshape(M, N // 16, 16).max(-1)
+    ratio = bmax[normal] / S[normal]
+    assert np.all((ratio >= 6.0 / (1 + 2.0 ** -4) * (1 - 2.0 ** -20)) & (ratio <= 6.0 / (1 - 2.0 ** -4) * (1 + 2.0 ** -20)))
+    assert A == np.abs(x).max()
+    assert np.all(tab[s] >= 0)
+
+
+def pin_sibling_sharing(O):
+    """Members of a sibling group share one global scale, the largest of the members'
+    own scales (fl(. / 2688) is monotone), and the group amax is the members' max."""
+    rng = np.random.default_rng(16)
+    q = _moe_like(rng, 64, 128, 0.02, 0.0)
+    k = _moe_like(rng, 16, 128, 0.05, 0.0)
+    v = _moe_like(rng, 16, 128, 0.01, 0.0)
+    members = [q, k, v]
+    A, g, outs = O.nvfp4_quantize_group(members)
+    solo = [O.nvfp4_group_scale([m])[1] for m in members]
+    assert g == max(solo)
+    assert A == max(float(np.abs(bf16_f32(m)).max()) for m in members)
+    for m, (p, s) in zip(members, outs):
+        p2, s2 = O.nvfp4_quantize(m, g)
+        assert np.array_equal(p, p2) and np.array_equal(s, s2)
+
+
+def pin_qdq_equals_dequant_quant(O):
+    """Fake quantization equals dequantize(quantize(x)) bit for bit."""
+    rng = np.random.default_rng(17)
+    for M, N, sc in ((32, 128, 0.02), (8, 2048, 1.0), (16, 64, 1e-30)):
+        x = _moe_like(rng, M, N, sc)
+        _, g = O.nvfp4_group_scale([x])
+        p, s = O.nvfp4_quantize(x, g)
+        assert np.array_equal(O.nvfp4_qdq(x, g), O.nvfp4_dequantize(p, s, g))
+
+
+def pin_idempotence(O):
+    """QDQ(QDQ(x)) == QDQ(x) on blocks whose E4M3 scale is zero or normal;
+    FP8 block: quantize(dequantize(quantize(x))) == quantize(x);
+    MXFP8: dequantize(quantize(.)) is idempotent on values."""
+    rng = np.random.default_rng(18)
+    x = _moe_like(rng, 64, 256)
+    _, g = O.nvfp4_group_scale([x])
+    y = O.nvfp4_qdq(x, g)
+    _, g2 = O.nvfp4_group_scale([y])
+    z = O.nvfp4_qdq(y, g2)
+    _, s = O.nvfp4_quantize(x, g)
+    ok = np.repeat((s == 0) | ((s & 0x78) != 0), 16, 1)
+    assert np.array_equal(z[ok], y[ok])
+    q, sc = O.fp8blk_quantize(x)
+    q2, sc2 = O.fp8blk_quantize(O.fp8blk_dequantize(q, sc))
+    assert np.array_equal(q, q2) and np.array_equal(sc, sc2)
+    qm, em = O.mxfp8_quantize(x)
+    y1 = O.mxfp8_dequantize(qm, em)
+    y2 = O.mxfp8_dequantize(*O.mxfp8_quantize(y1))
+    assert np.array_equal(y1, y2)
+
+
+def pin_zero_and_sign(O):
+    """All-zero tiles/blocks/groups and negative zeros round-trip exactly, with the sign
+    of zero kept in codes and outputs; a zero global scale zeroes every block scale."""
+    w = np.zeros((128, 128), np.uint16)
+    w[::3, ::5] = 0x8000                              # -0
+    q, s = O.fp8blk_quantize(w)
+    assert s[0, 0] == 0.0 and np.array_equal(q, np.where(w == 0x8000, 0x80, 0).astype(np.uint8))
+    assert np.array_equal(O.fp8blk_dequantize(q, s), w)
+    q, e = O.mxfp8_quantize(w)
+    assert not e.any() and np.array_equal(q, np.where(w == 0x8000, 0x80, 0).astype(np.uint8))
+    assert np.array_equal(O.mxfp8_dequantize(q, e), w)
+    A, g, [(p, s)] = O.nvfp4_quantize_group([w])
+    assert A == 0.0 and g == 0.0 and not s.any()
+    assert np.array_equal(O.nvfp4_dequantize(p, s, g), w)
+    assert np.array_equal(O.nvfp4_qdq(w, g), w)
+    # negative values whose code rounds to zero keep the sign bit
+    x = f32_to_bf16_torch(np.float32([-1e-4] + [0.0] * 14 + [448.0])).reshape(1, 16)
+    q, s = O.fp8blk_quantize(x)
+    assert q[0, 0] == 0x80
+    anchor = f32_to_bf16_torch(np.float32([2688.0] + [0.0] * 15)).reshape(1, 16)
+    _, g, [(p, s), _] = O.nvfp4_quantize_group([x, anchor])
+    assert (p[0, 0] & 15) == 8
+
+
+def pin_config1_layout(O):
+    """The parity weight of the single-Linear workload: its zero tile has scale 0 and
+    zero codes in every format."""
+    from synth import synth
+    w = synth.single_linear()
+    q, s = O.fp8blk_quantize(w)
+    assert s[1, 1] == 0.0 and not q[128:256, 128:256].any() and (s[0, 0] > 0) and (s[1, 2] > 0)
+    q, e = O.mxfp8_quantize(w)
+    assert not e[128:, 4:8].any() and not q[128:, 128:256].any()
+    _, g, [(p, s)] = O.nvfp4_quantize_group([w])
+    assert not s[128:, 8:16].any() and not p[128:, 64:128].any()
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,101 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and require the
+pins to catch every one: evidence that the pins constrain each step."""
+import os
+
+import pytest
+
+from oracle import oracle as O
+from tests import pins
+
+MUTANTS = [
+    ("e4m3 ties away from zero",
+     "if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) keep += 1u;",
+     "if (rest >= 0x80000u) keep += 1u;"),
+    ("e4m3 subnormal ties up",
+     "if (frac > 0.5f || (frac == 0.5f && (ki & 1u))) ki += 1u;",
+     "if (frac >= 0.5f) ki += 1u;"),
+    ("e4m3 no saturation",
+     "if (mag >= 448.0f) return (uint8_t)(sign | 0x7e);",
+     "if (mag >= 480.0f) return (uint8_t)(sign | 0x7f);"),
+    ("e4m3 drops sign of zero",
+     "uint8_t sign = (uint8_t)((u >> 24) & 0x80u);",
+     "uint8_t sign = (uint8_t)((v < 0.0f) ? 0x80u : 0u);"),
+    ("e2m1 tie at 0.25 goes up",
+     "if (a <= 0.25f) c = 0;",
+     "if (a < 0.25f) c = 0;"),
+    ("e2m1 tie at 2.5 goes up",
+     "else if (a <= 2.5f) c = 4;",
+     "else if (a < 2.5f) c = 4;"),
+    ("bf16 truncates",
+     "if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u))) keep += 1u;",
+     ""),
+    ("fp8blk scale divisor 256",
+     "float scale = amax / 448.0f;",
+     "float scale = amax / 256.0f;"),
+    ("fp8blk tile index transposed",
+     "s[ti * tiles_n + tj] = scale;",
+     "s[tj * tiles_m + ti] = scale;"),
+    ("fp8blk amax without abs",
+     "float a = fabsf(oc_bf16_to_f32(w[r * N + c]));\n                    if (a > amax) amax = a;",
+     "float a = oc_bf16_to_f32(w[r * N + c]);\n                    if (a > amax) amax = a;"),
+    ("fp8blk dequant divides",
+     "y[r * N + c] = oc_f32_to_bf16(oc_e4m3_decode(q[r * N + c]) * scale);",
+     "y[r * N + c] = oc_f32_to_bf16(oc_e4m3_decode(q[r * N + c]) / scale);"),
+    ("fp8blk ragged tile clipped wrong",
+     "int64_t r0 = ti * T, r1 = (r0 + T < M) ? r0 + T : M;",
+     "int64_t r0 = ti * T, r1 = (r0 + T < M) ? r0 + T - 1 : M;"),
+    ("mxfp8 floor exponent rule",
+     "while (a > ldexp(448.0, e)) e++;",
+     "while (a >= ldexp(512.0, e)) e++;"),
+    ("mxfp8 scale index transposed",
+     "e[r * nb + b] = byte;",
+     "e[b * M + r] = byte;"),
+    ("mxfp8 dequant block width 16",
+     "float X = oc_ue8m0_decode(e[r * nb + c / 32]);",
+     "float X = oc_ue8m0_decode(e[r * nb + (c / 16) % nb]);"),
+    ("nvfp4 global divisor 448",
+     "OC_API float oc_nvfp4_global_scale(float A) { return A / (6.0f * 448.0f); }",
+     "OC_API float oc_nvfp4_global_scale(float A) { return A / 448.0f; }"),
+    ("nvfp4 block scale drops /6",
+     "float t = b / 6.0f;",
+     "float t = b;"),
+    ("nvfp4 effective scale drops g",
+     "return oc_e4m3_decode(scode) * g;",
+     "return oc_e4m3_decode(scode);"),
+    ("nvfp4 nibbles swapped",
+     "p[(r * N + b * 16 + k) / 2] = (uint8_t)(lo | (hi << 4));",
+     "p[(r * N + b * 16 + k) / 2] = (uint8_t)(hi | (lo << 4));"),
+    ("nvfp4 dequant scale index by 8",
+     "float S = oc_nvfp4_effective_scale(s[r * nb + c / 16], g);",
+     "float S = oc_nvfp4_effective_scale(s[r * nb + (c / 8) % nb], g);"),
+    ("nvfp4 zero scale loses sign",
+     "if (S == 0.0f) return (f2u(x) >> 31) ? 8 : 0;",
+     "if (S == 0.0f) return 0;"),
+    ("nvfp4 qdq block amax over 8 elements",
+     "const uint16_t* blk = x + r * N + b * 16;\n            float bmax = 0.0f;\n            for (int k = 0; k < 16; k++) {",
+     "const uint16_t* blk = x + r * N + b * 16;\n            float bmax = 0.0f;\n            for (int k = 0; k < 8; k++) {"),
+    ("nvfp4 qdq does not multiply back by the global scale",
+     "float S = oc_nvfp4_effective_scale(oc_nvfp4_block_scale(bmax, g), g);",
+     "float S = oc_e4m3_decode(oc_nvfp4_block_scale(bmax, g)) * (g > 0.0f ? 1.0f : 0.0f);"),
+]
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(O.SRC) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, source, name, old, new):
+    assert source.count(old) == 1, f"mutation site not found exactly once: {name}"
+    path = O.build_variant(source.replace(old, new), str(tmp_path / "mutant.so"))
+    mutant = O.Oracle(path)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(mutant)
+        except Exception as exc:  # noqa: BLE001 - any failure of a pin counts as caught
+            caught.append((pin.__name__, type(exc).__name__))
+            break
+    assert caught, f"no pin caught the planted mistake: {name}"
