@@ -1,0 +1,201 @@
+/*
+ * lpq.h -- C ABI of the MI355X (gfx950) low-precision weight codec library
+ * (liblpq.so): BF16 -> block-wise FP8 / MXFP8 / NVFP4 quantizers, their
+ * dequantizers, and the NVFP4 fake-quant (quantize-dequantize, "QDQ").
+ *
+ * What the calls compute (web pages, cited by title and section):
+ *  - "Low Precision RL" (Miles documentation), "Choose a precision" table and
+ *    "Modes": block-wise FP8 = E4M3 codes with one FP32 scale per 128x128
+ *    tile; MXFP8 = E4M3 codes with one UE8M0 (power-of-two, uint8) scale per
+ *    1x32 block; NVFP4 = E2M1 codes in 1x16 blocks with a two-level scale
+ *    (E4M3 per block, FP32 per tensor).  Weights are re-quantized from the BF16
+ *    master copy at every weight-update sync.
+ *  - "verl NVFP4 QAT" article (capital-peak.com), section 2.3: NVFP4 global
+ *    scale = amax / (6 * 448); per-16-element block amax turned into an E4M3
+ *    block scale; values snapped to the nearest of {0,0.5,1,1.5,2,3,4,6} and
+ *    multiplied back (fake quantization).  Section 2.4: q/k/v and gate/up
+ *    siblings share one global scale, taken from the group maximum.  Sections
+ *    2.5 and 3.3: exported tensors are the packed FP4 weight, the E4M3 block
+ *    scales and the FP32 global scale.
+ *  - vime pull request 503 review: exact round-to-nearest numerics.
+ * Every cast rounds to nearest, ties to even; E4M3 and E2M1 casts saturate
+ * (+-448, +-6); zero scales give zero codes that keep the element's sign.
+ * The exact arithmetic of each format is written out where it is declared.
+ *
+ * Conventions (all entry points):
+ *  - Pointers are DEVICE pointers unless stated otherwise.  The caller owns
+ *    every buffer; the library never allocates, frees or synchronizes, keeps
+ *    no state between calls (apart from the thread-local last HIP error) and
+ *    is safe to call from several host threads.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued asynchronously; a kernel fault surfaces at the caller's
+ *    next synchronization.
+ *  - Tensors are row-major and contiguous: M rows (out_features) by N
+ *    columns (in_features); blocks run along N.  BF16 values travel as
+ *    uint16_t bit patterns, E4M3 codes as uint8_t (float8_e4m3fn).
+ *  - Every argument check that can run on the host runs before anything is
+ *    enqueued; on failure nothing is enqueued and the status says why.
+ *  - Alignment (LPQ_ERR_ALIGN otherwise): MXFP8 and NVFP4 BF16 arrays 16
+ *    bytes, MXFP8 code arrays 8 bytes, NVFP4 packed arrays 4 bytes; the
+ *    block-wise FP8 calls accept any 2-byte aligned BF16 and any code array
+ *    (rows that are not 16-byte aligned take a slower path).  FP32 arrays
+ *    (scales, amax, global scales) must be 4-byte aligned; byte scale arrays
+ *    have no requirement.
+ *  - Inputs are finite; NaN and Inf inputs are outside the contract.
+ */
+#ifndef LPQ_H
+#define LPQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lpq_status {
+    LPQ_OK = 0,
+    LPQ_ERR_NULL = 1,   /* a required pointer is NULL                                   */
+    LPQ_ERR_SHAPE = 2,  /* M or N <= 0, N not a multiple of the block (32 MXFP8, 16
+                           NVFP4), or a tensor count <= 0                               */
+    LPQ_ERR_ALIGN = 3,  /* a pointer is not aligned as required (see above)             */
+    LPQ_ERR_GROUP = 4,  /* an NVFP4 sibling-group index is outside [0, n_groups)        */
+    LPQ_ERR_HIP = 5,    /* a HIP launch failed; lpq_last_hip_error() holds the code     */
+    LPQ_ERR_ARG = 6     /* any other invalid argument (reserved field not 0, ...)      */
+} lpq_status;
+
+/* Static, NUL-terminated description of a status code. */
+const char* lpq_status_string(int status);
+
+/* hipError_t of the most recent LPQ_ERR_HIP on the calling thread (0 if none). */
+int lpq_last_hip_error(void);
+
+/* Library version, as MAJOR * 10000 + MINOR * 100 + PATCH. */
+int lpq_version(void);
+
+/* ======================================================================== */
+/* Block-wise FP8 ("DeepSeek-style"): "Low Precision RL", "Choose a precision"
+ * and "2. Unified block-wise FP8" -- 128 x 128 tiles, FP32 (not power-of-two)
+ * scales.
+ *   tile (i, j) = rows [128i, min(128i+128, M)) x cols [128j, min(128j+128, N))
+ *   amax  = max |w| over the tile
+ *   s     = fl(amax / 448)                       stored FP32, the dequant multiplier
+ *   q     = E4M3(fl(w / s))   (s == 0: a zero with w's sign)
+ *   y     = BF16(fl(E4M3value(q) * s))
+ * w: [M, N] BF16.  q: [M, N] codes.  s: [ceil(M/128), ceil(N/128)] FP32. */
+lpq_status lpq_quantize_fp8blk(const uint16_t* w, int64_t M, int64_t N,
+                               uint8_t* q, float* s, void* stream);
+lpq_status lpq_dequantize_fp8blk(const uint8_t* q, const float* s, int64_t M, int64_t N,
+                                 uint16_t* y, void* stream);
+
+/* ======================================================================== */
+/* MXFP8: "Low Precision RL", "3. Unified MXFP8" -- 1 x 32 blocks along a row,
+ * UE8M0 power-of-two scales stored as uint8, E4M3 values.  N % 32 == 0.
+ *   amax  = max |w| over the 32 elements of the block
+ *   e     = the smallest integer with amax <= 448 * 2^e, clamped to e >= -127
+ *           (the power-of-two counterpart of amax / 448: no element saturates)
+ *   byte  = e + 127                               (never 255)
+ *   q     = E4M3(w * 2^-e)                        (exact scaling, one rounding)
+ *   y     = BF16(E4M3value(q) * 2^e)
+ * w: [M, N] BF16.  q: [M, N] codes.  e: [M, N/32] uint8. */
+lpq_status lpq_quantize_mxfp8(const uint16_t* w, int64_t M, int64_t N,
+                              uint8_t* q, uint8_t* e, void* stream);
+lpq_status lpq_dequantize_mxfp8(const uint8_t* q, const uint8_t* e, int64_t M, int64_t N,
+                                uint16_t* y, void* stream);
+
+/* ======================================================================== */
+/* NVFP4: "Low Precision RL", "4. NVFP4"; "verl NVFP4 QAT", sections 2.3-2.5
+ * and 3.3 -- E2M1 values in 1 x 16 blocks, an E4M3 block scale and an FP32
+ * global scale.  N % 16 == 0.
+ *   A     = max |w| over the tensor or its whole sibling group (the amax input)
+ *   g     = fl(A / 2688)                           (2688 = 6 * 448)
+ *   b     = max |w| over the 16-element block
+ *   sb    = (g == 0) ? 0 : E4M3(fl(fl(b / 6) / g)) stored E4M3 block-scale code
+ *   S     = fl(E4M3value(sb) * g)                  effective FP32 block multiplier
+ *   code  = (S == 0) ? a zero with w's sign : E2M1(fl(w / S))
+ *   y     = BF16(fl(E2M1value(code) * S))
+ * Packed layout: element 2j in the low nibble of byte j. */
+
+/* amax pre-pass: *amax = max(*amax, max |w|) when accumulate != 0; when
+ * accumulate == 0 *amax is overwritten with max |w|.  amax: 1 FP32 on the
+ * device.  The result does not depend on the order of the reduction. */
+lpq_status lpq_nvfp4_amax(const uint16_t* w, int64_t M, int64_t N, float* amax,
+                          int accumulate, void* stream);
+
+/* amax: 1 FP32 (device) holding A.  p: [M, N/2] packed codes.  s: [M, N/16]
+ * E4M3 codes.  g: 1 FP32 (device), receives the global scale. */
+lpq_status lpq_quantize_nvfp4(const uint16_t* w, int64_t M, int64_t N, const float* amax,
+                              uint8_t* p, uint8_t* s, float* g, void* stream);
+
+/* g: 1 FP32 (device), the global scale written by the quantizer. */
+lpq_status lpq_dequantize_nvfp4(const uint8_t* p, const uint8_t* s, const float* g,
+                                int64_t M, int64_t N, uint16_t* y, void* stream);
+
+/* Fake quantization ("verl NVFP4 QAT" 2.3, also used on W4A4 activations):
+ * y = dequantize(quantize(x)) bit for bit, without storing codes.
+ * amax: 1 FP32 (device) holding A.  x, y: [M, N] BF16 (may not overlap). */
+lpq_status lpq_nvfp4_qdq(const uint16_t* x, int64_t M, int64_t N, const float* amax,
+                         uint16_t* y, void* stream);
+
+/* ======================================================================== */
+/* Grouped calls: one launch over many tensors (MoE experts, sibling groups).
+ * Each call takes the same n descriptors twice: `host` (host memory, used to
+ * validate every descriptor and size the launch) and `dev` (device memory,
+ * read by the kernels).  The two must hold identical bytes.
+ *
+ *   call                        src            dst               scale
+ *   quantize_fp8blk_grouped     BF16 [M,N]     codes [M,N]       FP32 tiles (out)
+ *   dequantize_fp8blk_grouped   codes [M,N]    BF16 [M,N]        FP32 tiles (in)
+ *   quantize_mxfp8_grouped      BF16           codes             uint8 [M,N/32] (out)
+ *   dequantize_mxfp8_grouped    codes          BF16              uint8 (in)
+ *   nvfp4_amax_grouped          BF16           unused            unused
+ *   quantize_nvfp4_grouped      BF16           packed [M,N/2]    E4M3 [M,N/16] (out)
+ *   dequantize_nvfp4_grouped    packed         BF16              E4M3 (in)
+ *   nvfp4_qdq_grouped           BF16           BF16              unused
+ * `group` is the NVFP4 sibling-group index of the tensor (q/k/v share one,
+ * gate/up share one, a lone tensor has its own); other formats ignore it.
+ */
+typedef struct lpq_tensor {
+    const void* src;
+    void* dst;
+    void* scale;
+    int64_t rows;      /* M */
+    int64_t cols;      /* N */
+    int32_t group;     /* NVFP4 sibling group, 0 <= group < n_groups */
+    int32_t reserved;  /* must be 0 */
+} lpq_tensor;
+
+lpq_status lpq_quantize_fp8blk_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n,
+                                       void* stream);
+lpq_status lpq_dequantize_fp8blk_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n,
+                                         void* stream);
+lpq_status lpq_quantize_mxfp8_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n,
+                                      void* stream);
+lpq_status lpq_dequantize_mxfp8_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n,
+                                        void* stream);
+
+/* group_amax: n_groups FP32 (device).  accumulate == 0: the group slots are
+ * first set to 0, then group_amax[group] = max over the group's members of
+ * max |w|; accumulate != 0: max-accumulated into the existing values. */
+lpq_status lpq_nvfp4_amax_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n,
+                                  float* group_amax, int32_t n_groups, int accumulate, void* stream);
+
+/* group_amax: n_groups FP32 (device, the A of each group, e.g. from
+ * lpq_nvfp4_amax_grouped or a cached value).  group_g: n_groups FP32
+ * (device, out): g of every group that has at least one member. */
+lpq_status lpq_quantize_nvfp4_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n,
+                                      const float* group_amax, int32_t n_groups, float* group_g,
+                                      void* stream);
+
+/* group_g: n_groups FP32 (device), the global scales written by the quantizer. */
+lpq_status lpq_dequantize_nvfp4_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n,
+                                        const float* group_g, int32_t n_groups, void* stream);
+
+/* group_amax: n_groups FP32 (device).  src and dst of a descriptor may not overlap. */
+lpq_status lpq_nvfp4_qdq_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n,
+                                 const float* group_amax, int32_t n_groups, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LPQ_H */

@@ -1,0 +1,270 @@
+"""Python binding of liblpq.so, the gfx950 low-precision weight codec library.
+
+Argument marshalling only: every step of the codecs runs in the HIP kernels
+behind the C ABI (include/lpq.h).  PyTorch supplies device memory and the
+current stream.  The functions carry the C names; each accepts CUDA (HIP)
+tensors, allocates any output that is not passed in, launches on the current
+stream and returns the outputs.  BF16 data is a ``torch.bfloat16`` tensor (or
+its ``int16``/``uint16`` bit view), E4M3 codes come back as
+``torch.float8_e4m3fn``, scale bytes and packed FP4 as ``torch.uint8``.
+
+If the library has not been built the import fails: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblpq.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m precision_weight_quantization_amd.build`")
+
+_L = ctypes.CDLL(LIB_PATH)
+
+LPQ_OK = 0
+STATUS_NAMES = {0: "LPQ_OK", 1: "LPQ_ERR_NULL", 2: "LPQ_ERR_SHAPE", 3: "LPQ_ERR_ALIGN",
+                4: "LPQ_ERR_GROUP", 5: "LPQ_ERR_HIP", 6: "LPQ_ERR_ARG"}
+
+
+class LpqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _L.lpq_status_string(status).decode()
+        if status == 5:
+            msg += f" (hipError {_L.lpq_last_hip_error()})"
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: {msg}")
+
+
+class lpq_tensor(ctypes.Structure):
+    _fields_ = [("src", ctypes.c_void_p), ("dst", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("group", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+assert ctypes.sizeof(lpq_tensor) == 48
+
+_vp, _i64, _i32, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
+_tp = ctypes.POINTER(lpq_tensor)
+_SIG = {
+    "lpq_status_string": (ctypes.c_char_p, [_int]),
+    "lpq_last_hip_error": (_int, []),
+    "lpq_version": (_int, []),
+    "lpq_quantize_fp8blk": (_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
+    "lpq_dequantize_fp8blk": (_int, [_vp, _vp, _i64, _i64, _vp, _vp]),
+    "lpq_quantize_mxfp8": (_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
+    "lpq_dequantize_mxfp8": (_int, [_vp, _vp, _i64, _i64, _vp, _vp]),
+    "lpq_nvfp4_amax": (_int, [_vp, _i64, _i64, _vp, _int, _vp]),
+    "lpq_quantize_nvfp4": (_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
+    "lpq_dequantize_nvfp4": (_int, [_vp, _vp, _vp, _i64, _i64, _vp, _vp]),
+    "lpq_nvfp4_qdq": (_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
+    "lpq_quantize_fp8blk_grouped": (_int, [_tp, _vp, _i32, _vp]),
+    "lpq_dequantize_fp8blk_grouped": (_int, [_tp, _vp, _i32, _vp]),
+    "lpq_quantize_mxfp8_grouped": (_int, [_tp, _vp, _i32, _vp]),
+    "lpq_dequantize_mxfp8_grouped": (_int, [_tp, _vp, _i32, _vp]),
+    "lpq_nvfp4_amax_grouped": (_int, [_tp, _vp, _i32, _vp, _i32, _int, _vp]),
+    "lpq_quantize_nvfp4_grouped": (_int, [_tp, _vp, _i32, _vp, _i32, _vp, _vp]),
+    "lpq_dequantize_nvfp4_grouped": (_int, [_tp, _vp, _i32, _vp, _i32, _vp]),
+    "lpq_nvfp4_qdq_grouped": (_int, [_tp, _vp, _i32, _vp, _i32, _vp]),
+}
+for _name, (_res, _args) in _SIG.items():
+    _fn = getattr(_L, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = sorted(k for k in _SIG)
+
+
+def _check(status: int, where: str) -> None:
+    if status != LPQ_OK:
+        raise LpqError(status, where)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _bf16_in(x: torch.Tensor, name: str) -> torch.Tensor:
+    if x.dim() != 2:
+        raise ValueError(f"{name} must be 2-D [M, N]")
+    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must be bfloat16 (or its 16-bit view), got {x.dtype}")
+    if not x.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return x.contiguous()
+
+
+def _empty(shape, dtype, like: torch.Tensor) -> torch.Tensor:
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+# --------------------------------------------------------------------------- block-wise FP8
+
+def fp8blk_scale_shape(M: int, N: int):
+    return ((M + 127) // 128, (N + 127) // 128)
+
+
+def lpq_quantize_fp8blk(w, q=None, s=None, stream=None):
+    """BF16 [M,N] -> (codes [M,N] float8_e4m3fn, FP32 tile scales [ceil(M/128), ceil(N/128)])."""
+    w = _bf16_in(w, "w")
+    M, N = w.shape
+    q = _empty((M, N), torch.float8_e4m3fn, w) if q is None else q
+    s = _empty(fp8blk_scale_shape(M, N), torch.float32, w) if s is None else s
+    _check(_L.lpq_quantize_fp8blk(w.data_ptr(), M, N, q.data_ptr(), s.data_ptr(), _stream(stream)),
+           "lpq_quantize_fp8blk")
+    return q, s
+
+
+def lpq_dequantize_fp8blk(q, s, y=None, stream=None):
+    M, N = q.shape
+    y = _empty((M, N), torch.bfloat16, q) if y is None else y
+    _check(_L.lpq_dequantize_fp8blk(q.data_ptr(), s.data_ptr(), M, N, y.data_ptr(), _stream(stream)),
+           "lpq_dequantize_fp8blk")
+    return y
+
+
+# --------------------------------------------------------------------------- MXFP8
+
+def lpq_quantize_mxfp8(w, q=None, e=None, stream=None):
+    """BF16 [M,N] (N % 32 == 0) -> (codes [M,N] float8_e4m3fn, UE8M0 bytes [M,N/32] uint8)."""
+    w = _bf16_in(w, "w")
+    M, N = w.shape
+    q = _empty((M, N), torch.float8_e4m3fn, w) if q is None else q
+    e = _empty((M, max(N // 32, 1)), torch.uint8, w) if e is None else e
+    _check(_L.lpq_quantize_mxfp8(w.data_ptr(), M, N, q.data_ptr(), e.data_ptr(), _stream(stream)),
+           "lpq_quantize_mxfp8")
+    return q, e
+
+
+def lpq_dequantize_mxfp8(q, e, y=None, stream=None):
+    M, N = q.shape
+    y = _empty((M, N), torch.bfloat16, q) if y is None else y
+    _check(_L.lpq_dequantize_mxfp8(q.data_ptr(), e.data_ptr(), M, N, y.data_ptr(), _stream(stream)),
+           "lpq_dequantize_mxfp8")
+    return y
+
+
+# --------------------------------------------------------------------------- NVFP4
+
+def lpq_nvfp4_amax(w, amax=None, accumulate=False, stream=None):
+    """max |w| into a 1-element FP32 device tensor (max-accumulated when accumulate)."""
+    w = _bf16_in(w, "w")
+    M, N = w.shape
+    amax = _empty((1,), torch.float32, w) if amax is None else amax
+    _check(_L.lpq_nvfp4_amax(w.data_ptr(), M, N, amax.data_ptr(), int(bool(accumulate)), _stream(stream)),
+           "lpq_nvfp4_amax")
+    return amax
+
+
+def lpq_quantize_nvfp4(w, amax, p=None, s=None, g=None, stream=None):
+    """BF16 [M,N] (N % 16 == 0) with group amax (1-element FP32 device tensor) ->
+    (packed [M,N/2] uint8, E4M3 block scales [M,N/16] float8_e4m3fn, global scale [1] FP32)."""
+    w = _bf16_in(w, "w")
+    M, N = w.shape
+    p = _empty((M, max(N // 2, 1)), torch.uint8, w) if p is None else p
+    s = _empty((M, max(N // 16, 1)), torch.float8_e4m3fn, w) if s is None else s
+    g = _empty((1,), torch.float32, w) if g is None else g
+    _check(_L.lpq_quantize_nvfp4(w.data_ptr(), M, N, amax.data_ptr(), p.data_ptr(), s.data_ptr(), g.data_ptr(),
+                                 _stream(stream)), "lpq_quantize_nvfp4")
+    return p, s, g
+
+
+def lpq_dequantize_nvfp4(p, s, g, y=None, stream=None):
+    M, N = p.shape[0], p.shape[1] * 2
+    y = _empty((M, N), torch.bfloat16, p) if y is None else y
+    _check(_L.lpq_dequantize_nvfp4(p.data_ptr(), s.data_ptr(), g.data_ptr(), M, N, y.data_ptr(), _stream(stream)),
+           "lpq_dequantize_nvfp4")
+    return y
+
+
+def lpq_nvfp4_qdq(x, amax, y=None, stream=None):
+    """NVFP4 fake quantization of BF16 [M,N] under the group amax; returns BF16 [M,N]."""
+    x = _bf16_in(x, "x")
+    M, N = x.shape
+    y = _empty((M, N), torch.bfloat16, x) if y is None else y
+    _check(_L.lpq_nvfp4_qdq(x.data_ptr(), M, N, amax.data_ptr(), y.data_ptr(), _stream(stream)), "lpq_nvfp4_qdq")
+    return y
+
+
+# --------------------------------------------------------------------------- grouped
+
+class TensorTable:
+    """The n descriptors of a grouped call, in host memory and on the device.
+
+    ``entries`` is a list of (src, dst, scale, rows, cols, group): torch tensors
+    (dst / scale may be None where the call ignores them), the logical shape
+    M x N of the BF16 tensor, and the NVFP4 sibling group.  The tensors must
+    stay alive while the table is used."""
+
+    def __init__(self, entries, device=None):
+        n = len(entries)
+        self.host = (lpq_tensor * n)()
+        self.keep = []
+        for i, (src, dst, scale, rows, cols, group) in enumerate(entries):
+            self.host[i].src = _ptr(src)
+            self.host[i].dst = _ptr(dst)
+            self.host[i].scale = _ptr(scale)
+            self.host[i].rows = int(rows)
+            self.host[i].cols = int(cols)
+            self.host[i].group = int(group)
+            self.host[i].reserved = 0
+            self.keep.append((src, dst, scale))
+        raw = torch.frombuffer(bytearray(bytes(self.host)), dtype=torch.uint8)
+        dev = device if device is not None else entries[0][0].device
+        self.dev = raw.to(dev)
+        self.n = n
+
+    def args(self):
+        return self.host, self.dev.data_ptr(), self.n
+
+
+def lpq_quantize_fp8blk_grouped(table: TensorTable, stream=None):
+    _check(_L.lpq_quantize_fp8blk_grouped(*table.args(), _stream(stream)), "lpq_quantize_fp8blk_grouped")
+
+
+def lpq_dequantize_fp8blk_grouped(table: TensorTable, stream=None):
+    _check(_L.lpq_dequantize_fp8blk_grouped(*table.args(), _stream(stream)), "lpq_dequantize_fp8blk_grouped")
+
+
+def lpq_quantize_mxfp8_grouped(table: TensorTable, stream=None):
+    _check(_L.lpq_quantize_mxfp8_grouped(*table.args(), _stream(stream)), "lpq_quantize_mxfp8_grouped")
+
+
+def lpq_dequantize_mxfp8_grouped(table: TensorTable, stream=None):
+    _check(_L.lpq_dequantize_mxfp8_grouped(*table.args(), _stream(stream)), "lpq_dequantize_mxfp8_grouped")
+
+
+def lpq_nvfp4_amax_grouped(table: TensorTable, group_amax, accumulate=False, stream=None):
+    _check(_L.lpq_nvfp4_amax_grouped(*table.args(), group_amax.data_ptr(), group_amax.numel(),
+                                     int(bool(accumulate)), _stream(stream)), "lpq_nvfp4_amax_grouped")
+    return group_amax
+
+
+def lpq_quantize_nvfp4_grouped(table: TensorTable, group_amax, group_g, stream=None):
+    _check(_L.lpq_quantize_nvfp4_grouped(*table.args(), group_amax.data_ptr(), group_amax.numel(),
+                                         group_g.data_ptr(), _stream(stream)), "lpq_quantize_nvfp4_grouped")
+    return group_g
+
+
+def lpq_dequantize_nvfp4_grouped(table: TensorTable, group_g, stream=None):
+    _check(_L.lpq_dequantize_nvfp4_grouped(*table.args(), group_g.data_ptr(), group_g.numel(), _stream(stream)),
+           "lpq_dequantize_nvfp4_grouped")
+
+
+def lpq_nvfp4_qdq_grouped(table: TensorTable, group_amax, stream=None):
+    _check(_L.lpq_nvfp4_qdq_grouped(*table.args(), group_amax.data_ptr(), group_amax.numel(), _stream(stream)),
+           "lpq_nvfp4_qdq_grouped")
+
+
+def raw():
+    """The ctypes handle of liblpq.so (for tests of the C ABI itself)."""
+    return _L

@@ -1,0 +1,45 @@
+"""Build step of the HIP library (liblpq.so) for gfx950.
+
+Run ``python -m precision_weight_quantization_amd.build`` (or
+``__graft_entry__.build()``).  Compiles in-tree with hipcc; no GPU is needed
+to build.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "liblpq.so")
+SOURCES = [os.path.join(CSRC, "lpq_kernels.hip")]
+HEADERS = [os.path.join(ROOT, "include", "lpq.h"), os.path.join(CSRC, "lpq_device.hpp")]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# -ffp-contract=off: every multiply/add written separately stays separately
+# rounded (the kernels spell out each fused multiply-add they want).
+# Packed FP32 instructions are disabled for the whole library.
+HIP_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-ffp-contract=off",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile liblpq.so (always recompiles)."""
+    cmd = [HIPCC, *HIP_FLAGS, "-I" + os.path.join(ROOT, "include"), "-I" + CSRC, "-o", LIB + ".tmp", *SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building liblpq.so")
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,733 @@
+// gfx950 kernels of the low-precision weight codecs and the C ABI that
+// launches them (declared in include/lpq.h).
+//
+// Formats ("Low Precision RL", "Choose a precision"; "verl NVFP4 QAT",
+// sections 2.3-2.5 and 3.3): block-wise FP8 (E4M3, FP32 scale per 128x128
+// tile), MXFP8 (E4M3, UE8M0 byte per 1x32 block) and NVFP4 (E2M1, E4M3 scale
+// per 1x16 block, FP32 global scale amax / 2688 shared by a sibling group),
+// plus the NVFP4 fake-quant.  All of it is streaming work bound by HBM
+// bandwidth: no kernel here is a contraction, so none uses MFMA.
+//
+// Launch shape.  A grouped call covers many tensors in one launch: grid.y is
+// the tensor (its descriptor is read into scalar registers), grid.x the chunk
+// or tile inside it; workgroups past the end of a smaller tensor exit at once.
+//  * MXFP8 / NVFP4 are flat in memory (N is a multiple of the block), so a
+//    workgroup of 256 lanes streams 16-byte BF16 vectors, 8 elements per lane,
+//    UNROLL vectors per lane in flight; a 1x32 block is a quad of lanes and a
+//    1x16 block a pair, reduced with DPP lane permutations.
+//  * Block-wise FP8 gives one 256-lane workgroup a 128x128 tile: 16 lanes per
+//    256-byte row segment, 8 row passes, all 64 values of a lane kept in
+//    registers between the tile-amax reduction (DPP + LDS across the 4
+//    waves) and the encode, so HBM is read once.
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+#include <stdint.h>
+
+#include "lpq.h"
+#include "lpq_device.hpp"
+
+using namespace lpq;
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+constexpr int64_t kFlatChunk = (int64_t)kThreads * 8 * kUnroll;  // elements per workgroup
+constexpr int kAmaxUnroll = 8;
+constexpr int64_t kAmaxChunk = (int64_t)kThreads * 8 * kAmaxUnroll;
+constexpr int kTile = 128;
+
+__device__ __forceinline__ lpq_tensor load_desc(const lpq_tensor* table, const lpq_tensor& one) {
+    return table ? table[blockIdx.y] : one;
+}
+
+// ---------------------------------------------------------------------------
+// MXFP8
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kThreads) void k_mxfp8_quant(const lpq_tensor* table, lpq_tensor one) {
+    const lpq_tensor d = load_desc(table, one);
+    const int64_t total = d.rows * d.cols;
+    const int64_t base = (int64_t)blockIdx.x * kFlatChunk;
+    if (base >= total) return;
+    const uint4* src = reinterpret_cast<const uint4*>(d.src);
+    uint2* dst = reinterpret_cast<uint2*>(d.dst);
+    uint8_t* esc = reinterpret_cast<uint8_t*>(d.scale);
+    const int tid = threadIdx.x;
+
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) {
+        const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+        v[u] = e0 < total ? src[e0 >> 3] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) {
+        const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+        // a quad of lanes is one 32-element block; blocks never straddle the end
+        const uint32_t amax = quad_max(absmax8_bits(v[u]));
+        const uint32_t byte = mx_scale_byte(amax);
+        const float X = ue8m0_operand(byte);
+        short2_t c01 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((short2_t){0, 0}, bf16_lo(v[u].x), bf16_hi(v[u].x), X, false);
+        c01 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c01, bf16_lo(v[u].y), bf16_hi(v[u].y), X, true);
+        short2_t c23 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((short2_t){0, 0}, bf16_lo(v[u].z), bf16_hi(v[u].z), X, false);
+        c23 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c23, bf16_lo(v[u].w), bf16_hi(v[u].w), X, true);
+        if (e0 < total) {
+            dst[e0 >> 3] = make_uint2(__builtin_bit_cast(uint32_t, c01), __builtin_bit_cast(uint32_t, c23));
+            if ((tid & 3) == 0) esc[e0 >> 5] = (uint8_t)byte;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_mxfp8_dequant(const lpq_tensor* table, lpq_tensor one) {
+    const lpq_tensor d = load_desc(table, one);
+    const int64_t total = d.rows * d.cols;
+    const int64_t base = (int64_t)blockIdx.x * kFlatChunk;
+    if (base >= total) return;
+    const uint2* src = reinterpret_cast<const uint2*>(d.src);
+    uint4* dst = reinterpret_cast<uint4*>(d.dst);
+    const uint8_t* esc = reinterpret_cast<const uint8_t*>(d.scale);
+    const int tid = threadIdx.x;
+
+    uint2 c[kUnroll];
+    uint32_t b[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) {
+        const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+        c[u] = e0 < total ? src[e0 >> 3] : make_uint2(0, 0);
+        b[u] = e0 < total ? esc[e0 >> 5] : 127u;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) {
+        const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+        const float X = ue8m0_operand(b[u]);
+        uint4 o;
+        o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[u].x, X, false));
+        o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[u].x, X, true));
+        o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[u].y, X, false));
+        o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[u].y, X, true));
+        if (e0 < total) dst[e0 >> 3] = o;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4
+// ---------------------------------------------------------------------------
+
+// Per-tensor quantities derived from the group amax A: g = fl(A / 2688) and
+// what the block-scale division by g needs.
+struct GlobalScale {
+    float g;       // the global scale
+    float gd;      // divisor used for fl(t / g): g, or g * 2^64 when g is tiny
+    float rg;      // RN(1 / gd)
+    float tpre;    // 1, or 2^64 when g is tiny (applied to t before the division)
+};
+
+__device__ __forceinline__ GlobalScale global_scale(float A) {
+    GlobalScale G;
+    G.g = A / 2688.0f;  // correctly rounded division
+    const bool tiny = G.g < kTinyScale;
+    G.tpre = tiny ? kPreScale : 1.0f;
+    G.gd = tiny ? G.g * kPreScale : G.g;
+    G.rg = G.g > 0.0f ? rcp_rn(G.gd) : 0.0f;
+    return G;
+}
+
+// Block of 16 with amax b (binary32 bits): E4M3 block-scale code, the block
+// multiplier S = fl(E4M3value * g), and the divisor state for the elements.
+struct BlockScale {
+    uint32_t code;
+    float S;       // multiplier for dequantization
+    float Sd;      // divisor for the quotient: S, or S * 2^64 when S is tiny
+    float r;       // RN(1 / Sd), or 0 when S == 0
+    float xpre;    // 1, or 2^64 when S is tiny
+};
+
+__device__ __forceinline__ BlockScale block_scale(uint32_t bmax_bits, const GlobalScale& G) {
+    BlockScale B;
+    const float b = __uint_as_float(bmax_bits);
+    // fl(b / 6): the short sequence is exact while the quotient is normal;
+    // tinier blocks take the full correctly rounded division.
+    float t6 = quot_rn(b, 6.0f, kRcp6);
+    if (b < 0x1p-100f) t6 = b / 6.0f;
+    const float t = t6 * G.tpre;                             // maybe pre-scaled by 2^64
+    const float u = quot_rn(t, G.gd, G.rg);                  // fl(fl(b / 6) / g)
+    B.code = G.g > 0.0f ? (e4m3x2<false>(u, 0.0f, 0u) & 0xffu) : 0u;
+    B.S = e4m3_to_f32(B.code) * G.g;
+    const bool tiny = B.S > 0.0f && B.S < kTinyScale;
+    B.xpre = tiny ? kPreScale : 1.0f;
+    B.Sd = tiny ? B.S * kPreScale : B.S;
+    B.r = B.S > 0.0f ? rcp_rn(B.Sd) : 0.0f;
+    return B;
+}
+
+// 8 BF16 values -> 8 E2M1 codes (one 32-bit word, element 0 in the low nibble).
+__device__ __forceinline__ uint32_t e2m1x8(const uint4& v, const BlockScale& B) {
+    float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                  bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+    if (B.xpre != 1.0f) {
+#pragma unroll
+        for (int k = 0; k < 8; k++) x[k] *= kPreScale;
+    }
+    float q[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) q[k] = quot_rn(x[k], B.Sd, B.r);
+    uint32_t p = 0;
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, q[0], q[1], 1.0f, 0);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, q[2], q[3], 1.0f, 1);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, q[4], q[5], 1.0f, 2);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, q[6], q[7], 1.0f, 3);
+    return p;
+}
+
+// 8 E2M1 codes (one word) times S -> 8 BF16 values.
+__device__ __forceinline__ uint4 e2m1x8_to_bf16(uint32_t p, float S) {
+    float2_t f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 0);
+    float2_t f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 1);
+    float2_t f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 2);
+    float2_t f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 3);
+    uint4 o;
+    o.x = bf16x2(f0[0] * S, f0[1] * S);
+    o.y = bf16x2(f1[0] * S, f1[1] * S);
+    o.z = bf16x2(f2[0] * S, f2[1] * S);
+    o.w = bf16x2(f3[0] * S, f3[1] * S);
+    return o;
+}
+
+__global__ __launch_bounds__(kThreads) void k_fill_f32(float* p, int64_t n, float v) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+// max |w| of each tensor, max-accumulated into its group slot (binary32 bits
+// of non-negative values order like unsigned integers).
+__global__ __launch_bounds__(kThreads) void k_amax(const lpq_tensor* table, lpq_tensor one, float* group_amax) {
+    const lpq_tensor d = load_desc(table, one);
+    const int64_t total = d.rows * d.cols;
+    const int64_t base = (int64_t)blockIdx.x * kAmaxChunk;
+    if (base >= total) return;
+    const uint4* src = reinterpret_cast<const uint4*>(d.src);
+    const int tid = threadIdx.x;
+    uint4 v[kAmaxUnroll];
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; u++) {
+        const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+        v[u] = e0 < total ? src[e0 >> 3] : make_uint4(0, 0, 0, 0);
+    }
+    uint32_t m = 0;
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; u++) m = umax(m, absmax8_bits(v[u]));
+    m = wave_max(m);
+    __shared__ uint32_t part[kThreads / 64];
+    if ((tid & 63) == 0) part[tid >> 6] = m;
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t w = umax(umax(part[0], part[1]), umax(part[2], part[3]));
+        atomicMax(reinterpret_cast<unsigned int*>(group_amax + (table ? d.group : 0)), w);
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_nvfp4_quant(const lpq_tensor* table, lpq_tensor one,
+                                                          const float* group_amax, float* group_g) {
+    const lpq_tensor d = load_desc(table, one);
+    const int64_t total = d.rows * d.cols;
+    const int64_t base = (int64_t)blockIdx.x * kFlatChunk;
+    if (base >= total) return;
+    const int gi = table ? d.group : 0;
+    const GlobalScale G = global_scale(group_amax[gi]);
+    const int tid = threadIdx.x;
+    if (blockIdx.x == 0 && tid == 0) group_g[gi] = G.g;   // same value from every member
+    const uint4* src = reinterpret_cast<const uint4*>(d.src);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(d.dst);
+    uint8_t* ssc = reinterpret_cast<uint8_t*>(d.scale);
+
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) {
+        const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+        v[u] = e0 < total ? src[e0 >> 3] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) {
+        const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+        const BlockScale B = block_scale(pair_max(absmax8_bits(v[u])), G);
+        const uint32_t p = e2m1x8(v[u], B);
+        if (e0 < total) {
+            dst[e0 >> 3] = p;
+            if ((tid & 1) == 0) ssc[e0 >> 4] = (uint8_t)B.code;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_nvfp4_dequant(const lpq_tensor* table, lpq_tensor one,
+                                                            const float* group_g) {
+    const lpq_tensor d = load_desc(table, one);
+    const int64_t total = d.rows * d.cols;
+    const int64_t base = (int64_t)blockIdx.x * kFlatChunk;
+    if (base >= total) return;
+    const float g = group_g[table ? d.group : 0];
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(d.src);
+    const uint8_t* ssc = reinterpret_cast<const uint8_t*>(d.scale);
+    uint4* dst = reinterpret_cast<uint4*>(d.dst);
+    const int tid = threadIdx.x;
+
+    uint32_t p[kUnroll], sb[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) {
+        const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+        p[u] = e0 < total ? src[e0 >> 3] : 0u;
+        sb[u] = e0 < total ? ssc[e0 >> 4] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) {
+        const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+        const float S = e4m3_to_f32(sb[u]) * g;
+        const uint4 o = e2m1x8_to_bf16(p[u], S);
+        if (e0 < total) dst[e0 >> 3] = o;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_nvfp4_qdq(const lpq_tensor* table, lpq_tensor one,
+                                                        const float* group_amax) {
+    const lpq_tensor d = load_desc(table, one);
+    const int64_t total = d.rows * d.cols;
+    const int64_t base = (int64_t)blockIdx.x * kFlatChunk;
+    if (base >= total) return;
+    const GlobalScale G = global_scale(group_amax[table ? d.group : 0]);
+    const uint4* src = reinterpret_cast<const uint4*>(d.src);
+    uint4* dst = reinterpret_cast<uint4*>(d.dst);
+    const int tid = threadIdx.x;
+
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) {
+        const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+        v[u] = e0 < total ? src[e0 >> 3] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) {
+        const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+        const BlockScale B = block_scale(pair_max(absmax8_bits(v[u])), G);
+        const uint4 o = e2m1x8_to_bf16(e2m1x8(v[u], B), B.S);
+        if (e0 < total) dst[e0 >> 3] = o;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Block-wise FP8, one 128 x 128 tile per workgroup
+// ---------------------------------------------------------------------------
+
+// Lane layout inside a tile: lane t covers columns 8*(t%16) .. +8 of rows
+// 16*pass + t/16, pass = 0..7.
+struct TileGeom {
+    int64_t r0, c0, rows, cols;   // tile origin and clipped extent
+    bool fast;                    // full tile and 16-byte aligned rows
+};
+
+__device__ __forceinline__ TileGeom tile_geom(const lpq_tensor& d, int64_t tile) {
+    const int64_t tn = (d.cols + kTile - 1) / kTile;
+    TileGeom T;
+    T.r0 = (tile / tn) * kTile;
+    T.c0 = (tile % tn) * kTile;
+    T.rows = d.rows - T.r0 < kTile ? d.rows - T.r0 : kTile;
+    T.cols = d.cols - T.c0 < kTile ? d.cols - T.c0 : kTile;
+    T.fast = T.rows == kTile && T.cols == kTile && (d.cols & 7) == 0 &&
+             ((reinterpret_cast<uintptr_t>(d.src) | reinterpret_cast<uintptr_t>(d.dst)) & 15) == 0;
+    return T;
+}
+
+__global__ __launch_bounds__(kThreads) void k_fp8blk_quant(const lpq_tensor* table, lpq_tensor one) {
+    const lpq_tensor d = load_desc(table, one);
+    const int64_t tiles = ((d.rows + kTile - 1) / kTile) * ((d.cols + kTile - 1) / kTile);
+    const int64_t tile = blockIdx.x;
+    if (tile >= tiles) return;
+    const TileGeom T = tile_geom(d, tile);
+    const uint16_t* w = reinterpret_cast<const uint16_t*>(d.src);
+    uint8_t* q = reinterpret_cast<uint8_t*>(d.dst);
+    const int tid = threadIdx.x;
+    const int lr = tid >> 4;           // row inside a pass
+    const int lc = (tid & 15) * 8;     // first column of the lane's segment
+
+    uint4 v[8];
+    if (T.fast) {
+#pragma unroll
+        for (int p = 0; p < 8; p++) {
+            const int64_t off = (T.r0 + 16 * p + lr) * d.cols + T.c0 + lc;
+            v[p] = *reinterpret_cast<const uint4*>(w + off);
+        }
+    } else {
+        for (int p = 0; p < 8; p++) {
+            const int64_t r = 16 * p + lr;
+            uint32_t h[8];
+            for (int k = 0; k < 8; k++) {
+                const bool in = r < T.rows && lc + k < T.cols;
+                h[k] = in ? w[(T.r0 + r) * d.cols + T.c0 + lc + k] : 0u;
+            }
+            v[p] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+        }
+    }
+    uint32_t m = 0;
+#pragma unroll
+    for (int p = 0; p < 8; p++) m = umax(m, absmax8_bits(v[p]));
+    m = wave_max(m);
+    __shared__ uint32_t part[kThreads / 64];
+    if ((tid & 63) == 0) part[tid >> 6] = m;
+    __syncthreads();
+    const float amax = __uint_as_float(umax(umax(part[0], part[1]), umax(part[2], part[3])));
+    const float s = amax / kE4M3Max;   // correctly rounded division
+    if (tid == 0) {
+        const int64_t tn = (d.cols + kTile - 1) / kTile;
+        reinterpret_cast<float*>(d.scale)[(T.r0 / kTile) * tn + T.c0 / kTile] = s;
+    }
+    const bool tiny = s > 0.0f && s < kTinyScale;
+    const float sd = tiny ? s * kPreScale : s;
+    const float r = s > 0.0f ? rcp_rn(sd) : 0.0f;
+    const float xpre = tiny ? kPreScale : 1.0f;
+
+#pragma unroll
+    for (int p = 0; p < 8; p++) {
+        float x[8] = {bf16_lo(v[p].x), bf16_hi(v[p].x), bf16_lo(v[p].y), bf16_hi(v[p].y),
+                      bf16_lo(v[p].z), bf16_hi(v[p].z), bf16_lo(v[p].w), bf16_hi(v[p].w)};
+        if (tiny) {
+#pragma unroll
+            for (int k = 0; k < 8; k++) x[k] *= xpre;
+        }
+        float qq[8];
+#pragma unroll
+        for (int k = 0; k < 8; k++) qq[k] = quot_rn(x[k], sd, r);
+        uint32_t lo = e4m3x2<false>(qq[0], qq[1], 0u);
+        lo = e4m3x2<true>(qq[2], qq[3], lo);
+        uint32_t hi = e4m3x2<false>(qq[4], qq[5], 0u);
+        hi = e4m3x2<true>(qq[6], qq[7], hi);
+        const int64_t r = 16 * p + lr;
+        if (T.fast) {
+            *reinterpret_cast<uint2*>(q + (T.r0 + r) * d.cols + T.c0 + lc) = make_uint2(lo, hi);
+        } else if (r < T.rows) {
+            const uint32_t c8[2] = {lo, hi};
+            for (int k = 0; k < 8; k++)
+                if (lc + k < T.cols) q[(T.r0 + r) * d.cols + T.c0 + lc + k] = (uint8_t)(c8[k >> 2] >> (8 * (k & 3)));
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_fp8blk_dequant(const lpq_tensor* table, lpq_tensor one) {
+    const lpq_tensor d = load_desc(table, one);
+    const int64_t tn = (d.cols + kTile - 1) / kTile;
+    const int64_t tiles = ((d.rows + kTile - 1) / kTile) * tn;
+    const int64_t tile = blockIdx.x;
+    if (tile >= tiles) return;
+    const TileGeom T = tile_geom(d, tile);
+    const uint8_t* q = reinterpret_cast<const uint8_t*>(d.src);
+    uint16_t* y = reinterpret_cast<uint16_t*>(d.dst);
+    const float s = reinterpret_cast<const float*>(d.scale)[(T.r0 / kTile) * tn + T.c0 / kTile];
+    const int tid = threadIdx.x;
+    const int lr = tid >> 4;
+    const int lc = (tid & 15) * 8;
+
+    uint2 c[8];
+    if (T.fast) {
+#pragma unroll
+        for (int p = 0; p < 8; p++)
+            c[p] = *reinterpret_cast<const uint2*>(q + (T.r0 + 16 * p + lr) * d.cols + T.c0 + lc);
+    } else {
+        for (int p = 0; p < 8; p++) {
+            const int64_t r = 16 * p + lr;
+            uint32_t b[8];
+            for (int k = 0; k < 8; k++) {
+                const bool in = r < T.rows && lc + k < T.cols;
+                b[k] = in ? q[(T.r0 + r) * d.cols + T.c0 + lc + k] : 0u;
+            }
+            c[p] = make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24), b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < 8; p++) {
+        const float2_t f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[p].x, false);
+        const float2_t f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[p].x, true);
+        const float2_t f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[p].y, false);
+        const float2_t f3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[p].y, true);
+        uint4 o;
+        o.x = bf16x2(f0[0] * s, f0[1] * s);
+        o.y = bf16x2(f1[0] * s, f1[1] * s);
+        o.z = bf16x2(f2[0] * s, f2[1] * s);
+        o.w = bf16x2(f3[0] * s, f3[1] * s);
+        const int64_t r = 16 * p + lr;
+        if (T.fast) {
+            *reinterpret_cast<uint4*>(y + (T.r0 + r) * d.cols + T.c0 + lc) = o;
+        } else if (r < T.rows) {
+            const uint32_t h[4] = {o.x, o.y, o.z, o.w};
+            for (int k = 0; k < 8; k++)
+                if (lc + k < T.cols) y[(T.r0 + r) * d.cols + T.c0 + lc + k] = (uint16_t)(h[k >> 1] >> (16 * (k & 1)));
+        }
+    }
+}
+
+}  // namespace
+
+// ===========================================================================
+// Host side: argument checks and launches
+// ===========================================================================
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kMaxGridY = 65535;
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+inline lpq_status launched() {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return LPQ_ERR_HIP;
+    }
+    return LPQ_OK;
+}
+
+enum Kind { FP8BLK_Q, FP8BLK_DQ, MXFP8_Q, MXFP8_DQ, NV_AMAX, NV_Q, NV_DQ, NV_QDQ };
+
+// Shape and pointer checks of one tensor for one kind of call.
+lpq_status check_tensor(Kind k, const lpq_tensor& t, int32_t n_groups) {
+    if (t.rows <= 0 || t.cols <= 0) return LPQ_ERR_SHAPE;
+    if (t.rows > (int64_t(1) << 40) / t.cols) return LPQ_ERR_SHAPE;   // element count overflow guard
+    if (!t.src) return LPQ_ERR_NULL;
+    if (k != NV_AMAX && !t.dst) return LPQ_ERR_NULL;
+    if (k != NV_AMAX && k != NV_QDQ && !t.scale) return LPQ_ERR_NULL;
+    if (t.reserved != 0) return LPQ_ERR_ARG;
+    switch (k) {
+    case FP8BLK_Q:
+    case FP8BLK_DQ:
+        if (!aligned(k == FP8BLK_Q ? t.src : t.dst, 2) || !aligned(t.scale, 4)) return LPQ_ERR_ALIGN;
+        if ((t.rows + kTile - 1) / kTile * ((t.cols + kTile - 1) / kTile) > INT32_MAX) return LPQ_ERR_SHAPE;
+        break;
+    case MXFP8_Q:
+        if (t.cols % 32) return LPQ_ERR_SHAPE;
+        if (!aligned(t.src, 16) || !aligned(t.dst, 8)) return LPQ_ERR_ALIGN;
+        break;
+    case MXFP8_DQ:
+        if (t.cols % 32) return LPQ_ERR_SHAPE;
+        if (!aligned(t.src, 8) || !aligned(t.dst, 16)) return LPQ_ERR_ALIGN;
+        break;
+    case NV_AMAX:
+    case NV_Q:
+    case NV_DQ:
+    case NV_QDQ:
+        if (t.cols % 16) return LPQ_ERR_SHAPE;
+        if (k == NV_DQ ? !aligned(t.src, 4) : !aligned(t.src, 16)) return LPQ_ERR_ALIGN;
+        if (k == NV_Q && !aligned(t.dst, 4)) return LPQ_ERR_ALIGN;
+        if ((k == NV_DQ || k == NV_QDQ) && !aligned(t.dst, 16)) return LPQ_ERR_ALIGN;
+        if (n_groups > 0 && (t.group < 0 || t.group >= n_groups)) return LPQ_ERR_GROUP;
+        break;
+    }
+    return LPQ_OK;
+}
+
+int64_t grid_x(Kind k, const lpq_tensor& t) {
+    switch (k) {
+    case FP8BLK_Q:
+    case FP8BLK_DQ:
+        return ((t.rows + kTile - 1) / kTile) * ((t.cols + kTile - 1) / kTile);
+    case NV_AMAX:
+        return (t.rows * t.cols + kAmaxChunk - 1) / kAmaxChunk;
+    default:
+        return (t.rows * t.cols + kFlatChunk - 1) / kFlatChunk;
+    }
+}
+
+// One launch of kernel `k` for a single tensor (table == nullptr) or for the
+// tensors dev[0..n) (in slices of at most 65535 along grid.y).
+lpq_status launch(Kind k, const lpq_tensor* host, const lpq_tensor* dev, int32_t n, const lpq_tensor& one,
+                  const float* fa, float* fb, hipStream_t stream) {
+    int64_t gx = 0;
+    if (dev) {
+        for (int32_t i = 0; i < n; i++) {
+            int64_t x = grid_x(k, host[i]);
+            if (x > gx) gx = x;
+        }
+    } else {
+        gx = grid_x(k, one);
+    }
+    if (gx > INT32_MAX) return LPQ_ERR_SHAPE;
+    for (int32_t i0 = 0; i0 < (dev ? n : 1); i0 += kMaxGridY) {
+        const int32_t ny = dev ? (n - i0 < kMaxGridY ? n - i0 : kMaxGridY) : 1;
+        const lpq_tensor* tab = dev ? dev + i0 : nullptr;
+        dim3 grid((unsigned)gx, (unsigned)ny), block(kThreads);
+        switch (k) {
+        case FP8BLK_Q: hipLaunchKernelGGL(k_fp8blk_quant, grid, block, 0, stream, tab, one); break;
+        case FP8BLK_DQ: hipLaunchKernelGGL(k_fp8blk_dequant, grid, block, 0, stream, tab, one); break;
+        case MXFP8_Q: hipLaunchKernelGGL(k_mxfp8_quant, grid, block, 0, stream, tab, one); break;
+        case MXFP8_DQ: hipLaunchKernelGGL(k_mxfp8_dequant, grid, block, 0, stream, tab, one); break;
+        case NV_AMAX: hipLaunchKernelGGL(k_amax, grid, block, 0, stream, tab, one, fb); break;
+        case NV_Q: hipLaunchKernelGGL(k_nvfp4_quant, grid, block, 0, stream, tab, one, fa, fb); break;
+        case NV_DQ: hipLaunchKernelGGL(k_nvfp4_dequant, grid, block, 0, stream, tab, one, fa); break;
+        case NV_QDQ: hipLaunchKernelGGL(k_nvfp4_qdq, grid, block, 0, stream, tab, one, fa); break;
+        }
+        lpq_status st = launched();
+        if (st != LPQ_OK) return st;
+    }
+    return LPQ_OK;
+}
+
+lpq_tensor make_one(const void* src, void* dst, void* scale, int64_t M, int64_t N) {
+    lpq_tensor t;
+    t.src = src;
+    t.dst = dst;
+    t.scale = scale;
+    t.rows = M;
+    t.cols = N;
+    t.group = 0;
+    t.reserved = 0;
+    return t;
+}
+
+lpq_status single(Kind k, const lpq_tensor& one, const float* fa, float* fb, void* stream) {
+    lpq_status st = check_tensor(k, one, 0);
+    if (st != LPQ_OK) return st;
+    return launch(k, nullptr, nullptr, 0, one, fa, fb, (hipStream_t)stream);
+}
+
+lpq_status grouped(Kind k, const lpq_tensor* host, const lpq_tensor* dev, int32_t n, int32_t n_groups,
+                   const float* fa, float* fb, void* stream) {
+    if (!host || !dev) return LPQ_ERR_NULL;
+    if (n <= 0) return LPQ_ERR_SHAPE;
+    if (!aligned(dev, 8)) return LPQ_ERR_ALIGN;
+    for (int32_t i = 0; i < n; i++) {
+        lpq_status st = check_tensor(k, host[i], n_groups);
+        if (st != LPQ_OK) return st;
+    }
+    return launch(k, host, dev, n, make_one(nullptr, nullptr, nullptr, 0, 0), fa, fb, (hipStream_t)stream);
+}
+
+lpq_status fill(float* p, int64_t n, float v, void* stream) {
+    hipLaunchKernelGGL(k_fill_f32, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                       (hipStream_t)stream, p, n, v);
+    return launched();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lpq_status_string(int status) {
+    switch (status) {
+    case LPQ_OK: return "ok";
+    case LPQ_ERR_NULL: return "a required pointer is NULL";
+    case LPQ_ERR_SHAPE: return "invalid shape (M or N <= 0, N not a multiple of the block, or count <= 0)";
+    case LPQ_ERR_ALIGN: return "a pointer is not aligned as required";
+    case LPQ_ERR_GROUP: return "sibling-group index out of range";
+    case LPQ_ERR_HIP: return "HIP launch failed (see lpq_last_hip_error)";
+    case LPQ_ERR_ARG: return "invalid argument";
+    default: return "unknown status";
+    }
+}
+
+int lpq_last_hip_error(void) { return g_last_hip_error; }
+
+int lpq_version(void) { return 10000; }
+
+lpq_status lpq_quantize_fp8blk(const uint16_t* w, int64_t M, int64_t N, uint8_t* q, float* s, void* stream) {
+    return single(FP8BLK_Q, make_one(w, q, s, M, N), nullptr, nullptr, stream);
+}
+
+lpq_status lpq_dequantize_fp8blk(const uint8_t* q, const float* s, int64_t M, int64_t N, uint16_t* y, void* stream) {
+    return single(FP8BLK_DQ, make_one(q, y, const_cast<float*>(s), M, N), nullptr, nullptr, stream);
+}
+
+lpq_status lpq_quantize_mxfp8(const uint16_t* w, int64_t M, int64_t N, uint8_t* q, uint8_t* e, void* stream) {
+    return single(MXFP8_Q, make_one(w, q, e, M, N), nullptr, nullptr, stream);
+}
+
+lpq_status lpq_dequantize_mxfp8(const uint8_t* q, const uint8_t* e, int64_t M, int64_t N, uint16_t* y, void* stream) {
+    return single(MXFP8_DQ, make_one(q, y, const_cast<uint8_t*>(e), M, N), nullptr, nullptr, stream);
+}
+
+lpq_status lpq_nvfp4_amax(const uint16_t* w, int64_t M, int64_t N, float* amax, int accumulate, void* stream) {
+    if (!amax) return LPQ_ERR_NULL;
+    if (!aligned(amax, 4)) return LPQ_ERR_ALIGN;
+    const lpq_tensor one = make_one(w, nullptr, nullptr, M, N);
+    lpq_status st = check_tensor(NV_AMAX, one, 0);
+    if (st != LPQ_OK) return st;
+    if (!accumulate && (st = fill(amax, 1, 0.0f, stream)) != LPQ_OK) return st;
+    return launch(NV_AMAX, nullptr, nullptr, 0, one, nullptr, amax, (hipStream_t)stream);
+}
+
+lpq_status lpq_quantize_nvfp4(const uint16_t* w, int64_t M, int64_t N, const float* amax, uint8_t* p, uint8_t* s,
+                              float* g, void* stream) {
+    if (!amax || !g) return LPQ_ERR_NULL;
+    if (!aligned(amax, 4) || !aligned(g, 4)) return LPQ_ERR_ALIGN;
+    return single(NV_Q, make_one(w, p, s, M, N), amax, g, stream);
+}
+
+lpq_status lpq_dequantize_nvfp4(const uint8_t* p, const uint8_t* s, const float* g, int64_t M, int64_t N, uint16_t* y,
+                                void* stream) {
+    if (!g) return LPQ_ERR_NULL;
+    if (!aligned(g, 4)) return LPQ_ERR_ALIGN;
+    return single(NV_DQ, make_one(p, y, const_cast<uint8_t*>(s), M, N), g, nullptr, stream);
+}
+
+lpq_status lpq_nvfp4_qdq(const uint16_t* x, int64_t M, int64_t N, const float* amax, uint16_t* y, void* stream) {
+    if (!amax) return LPQ_ERR_NULL;
+    if (!aligned(amax, 4)) return LPQ_ERR_ALIGN;
+    return single(NV_QDQ, make_one(x, y, nullptr, M, N), amax, nullptr, stream);
+}
+
+lpq_status lpq_quantize_fp8blk_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, void* stream) {
+    return grouped(FP8BLK_Q, host, dev, n, 0, nullptr, nullptr, stream);
+}
+
+lpq_status lpq_dequantize_fp8blk_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, void* stream) {
+    return grouped(FP8BLK_DQ, host, dev, n, 0, nullptr, nullptr, stream);
+}
+
+lpq_status lpq_quantize_mxfp8_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, void* stream) {
+    return grouped(MXFP8_Q, host, dev, n, 0, nullptr, nullptr, stream);
+}
+
+lpq_status lpq_dequantize_mxfp8_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, void* stream) {
+    return grouped(MXFP8_DQ, host, dev, n, 0, nullptr, nullptr, stream);
+}
+
+lpq_status lpq_nvfp4_amax_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, float* group_amax,
+                                  int32_t n_groups, int accumulate, void* stream) {
+    if (!group_amax) return LPQ_ERR_NULL;
+    if (n_groups <= 0) return LPQ_ERR_SHAPE;
+    if (!aligned(group_amax, 4)) return LPQ_ERR_ALIGN;
+    if (!host || !dev) return LPQ_ERR_NULL;
+    if (n <= 0) return LPQ_ERR_SHAPE;
+    for (int32_t i = 0; i < n; i++) {
+        lpq_status st = check_tensor(NV_AMAX, host[i], n_groups);
+        if (st != LPQ_OK) return st;
+    }
+    if (!accumulate) {
+        lpq_status st = fill(group_amax, n_groups, 0.0f, stream);
+        if (st != LPQ_OK) return st;
+    }
+    return grouped(NV_AMAX, host, dev, n, n_groups, nullptr, group_amax, stream);
+}
+
+lpq_status lpq_quantize_nvfp4_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n,
+                                      const float* group_amax, int32_t n_groups, float* group_g, void* stream) {
+    if (!group_amax || !group_g) return LPQ_ERR_NULL;
+    if (n_groups <= 0) return LPQ_ERR_SHAPE;
+    if (!aligned(group_amax, 4) || !aligned(group_g, 4)) return LPQ_ERR_ALIGN;
+    return grouped(NV_Q, host, dev, n, n_groups, group_amax, group_g, stream);
+}
+
+lpq_status lpq_dequantize_nvfp4_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n,
+                                        const float* group_g, int32_t n_groups, void* stream) {
+    if (!group_g) return LPQ_ERR_NULL;
+    if (n_groups <= 0) return LPQ_ERR_SHAPE;
+    if (!aligned(group_g, 4)) return LPQ_ERR_ALIGN;
+    return grouped(NV_DQ, host, dev, n, n_groups, group_g, nullptr, stream);
+}
+
+lpq_status lpq_nvfp4_qdq_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, const float* group_amax,
+                                 int32_t n_groups, void* stream) {
+    if (!group_amax) return LPQ_ERR_NULL;
+    if (n_groups <= 0) return LPQ_ERR_SHAPE;
+    if (!aligned(group_amax, 4)) return LPQ_ERR_ALIGN;
+    return grouped(NV_QDQ, host, dev, n, n_groups, group_amax, nullptr, stream);
+}
+
+}  // extern "C"

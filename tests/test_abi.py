@@ -1,0 +1,113 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol, and
+rejects invalid arguments on the host before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lpq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lpq_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import precision_weight_quantization_amd as m
+    return m
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 19
+    raw = ctypes.CDLL(lib.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+    assert set(names) == set(lib.EXPORTED)
+
+
+def test_status_strings(lib):
+    L = lib.raw()
+    for code in range(7):
+        assert len(L.lpq_status_string(code)) > 0
+    assert L.lpq_version() == 10000
+    assert L.lpq_last_hip_error() == 0
+
+
+P = 1 << 20          # a fake, suitably aligned address: the checks below must fail before any use of it
+
+
+def test_single_call_validation(lib):
+    L = lib.raw()
+    assert L.lpq_quantize_mxfp8(None, 4, 32, P, P, None) == 1
+    assert L.lpq_quantize_mxfp8(P, 0, 32, P, P, None) == 2
+    assert L.lpq_quantize_mxfp8(P, 4, 48, P, P, None) == 2
+    assert L.lpq_quantize_mxfp8(P, -1, 32, P, P, None) == 2
+    assert L.lpq_quantize_mxfp8(P + 2, 4, 32, P, P, None) == 3
+    assert L.lpq_quantize_mxfp8(P, 4, 32, P + 4, P, None) == 3
+    assert L.lpq_dequantize_mxfp8(P, P, 4, 33, P, None) == 2
+    assert L.lpq_dequantize_mxfp8(P + 4, P, 4, 32, P, None) == 3
+    assert L.lpq_quantize_nvfp4(P, 4, 24, P, P, P, P, None) == 2
+    assert L.lpq_quantize_nvfp4(P, 4, 32, None, P, P, P, None) == 1
+    assert L.lpq_quantize_nvfp4(P, 4, 32, P, P, P, None, None) == 1
+    assert L.lpq_quantize_nvfp4(P, 4, 32, P + 1, P, P, P, None) == 3
+    assert L.lpq_quantize_nvfp4(P + 8, 4, 32, P, P, P, P, None) == 3
+    assert L.lpq_quantize_nvfp4(P, 4, 32, P, P + 2, P, P, None) == 3
+    assert L.lpq_dequantize_nvfp4(P, P, None, 4, 32, P, None) == 1
+    assert L.lpq_dequantize_nvfp4(P, P, P, 4, 32, P + 8, None) == 3
+    assert L.lpq_nvfp4_qdq(P, 4, 32, None, P, None) == 1
+    assert L.lpq_nvfp4_qdq(P, 4, 32, P, None, None) == 1
+    assert L.lpq_nvfp4_amax(P, 4, 32, None, 0, None) == 1
+    assert L.lpq_nvfp4_amax(P, 4, 8, P, 0, None) == 2
+    assert L.lpq_quantize_fp8blk(P, 0, 5, P, P, None) == 2
+    assert L.lpq_quantize_fp8blk(P, 5, 5, P, None, None) == 1
+    assert L.lpq_quantize_fp8blk(P + 1, 5, 5, P, P, None) == 3
+    assert L.lpq_quantize_fp8blk(P, 5, 5, P, P + 2, None) == 3
+    assert L.lpq_dequantize_fp8blk(P, P, 5, 5, None, None) == 1
+    assert L.lpq_last_hip_error() == 0
+
+
+def _table(lib, rows):
+    t = (lib.lpq_tensor * len(rows))()
+    for i, (src, dst, scale, M, N, group, reserved) in enumerate(rows):
+        t[i].src, t[i].dst, t[i].scale = src, dst, scale
+        t[i].rows, t[i].cols, t[i].group, t[i].reserved = M, N, group, reserved
+    return t
+
+
+def test_grouped_validation(lib):
+    L = lib.raw()
+    good = (P, P, P, 8, 64, 0, 0)
+    t = _table(lib, [good, (P, P, P, 8, 64, 3, 0)])
+    assert L.lpq_quantize_nvfp4_grouped(t, P, 2, P, 2, P, None) == 4        # group 3 >= n_groups 2
+    assert L.lpq_quantize_nvfp4_grouped(t, P, 2, P, 4, None, None) == 1
+    assert L.lpq_quantize_nvfp4_grouped(t, P, 0, P, 4, P, None) == 2
+    assert L.lpq_quantize_nvfp4_grouped(None, P, 2, P, 4, P, None) == 1
+    assert L.lpq_quantize_nvfp4_grouped(t, None, 2, P, 4, P, None) == 1
+    assert L.lpq_quantize_nvfp4_grouped(t, P + 4, 2, P, 4, P, None) == 3
+    t2 = _table(lib, [good, (P, P, P, 8, 63, 0, 0)])
+    assert L.lpq_quantize_mxfp8_grouped(t2, P, 2, None) == 2
+    t3 = _table(lib, [good, (P, P, P, 8, 64, 0, 7)])
+    assert L.lpq_quantize_mxfp8_grouped(t3, P, 2, None) == 6
+    t4 = _table(lib, [good, (0, P, P, 8, 64, 0, 0)])
+    assert L.lpq_quantize_fp8blk_grouped(t4, P, 2, None) == 1
+    assert L.lpq_nvfp4_amax_grouped(t, P, 2, P, 2, 0, None) == 4
+    assert L.lpq_nvfp4_amax_grouped(t, P, 2, None, 4, 0, None) == 1
+    assert L.lpq_nvfp4_qdq_grouped(t, P, 2, P, 0, None) == 2
+    assert L.lpq_dequantize_nvfp4_grouped(t, P, 2, None, 4, None) == 1
+    assert L.lpq_last_hip_error() == 0
+
+
+def test_product_path_has_no_oracle_or_fallback():
+    """The package neither imports the oracle nor carries a CPU code path."""
+    pkg = os.path.join(ROOT, "precision_weight_quantization_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f
