@@ -1,0 +1,272 @@
+"""Throughput of the low-precision weight codecs on one MI355X.
+
+One step = one pass of the whole hot path over every full-size weight
+workload (see workloads.py): block-wise FP8 quantize + dequantize of the
+Qwen3-4B dense weights and of a DeepSeek-V3 MoE layer, MXFP8 quantize +
+dequantize of the Qwen3-30B-A3B experts, and NVFP4 group amax + quantize +
+dequantize + weight QDQ of those experts with q/k/v, plus the W4A4 activation
+amax + QDQ.  Inputs are generated on the device before timing; the timed
+region holds only the codec launches.
+
+value = algorithmic bytes of the step (each input and output byte counted
+once; the NVFP4 amax pre-passes are timed but not counted) / step time.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak, GB/s
+GB = 1e9
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in ("precision_weight_quantization_amd/csrc/lpq_kernels.hip",
+                "precision_weight_quantization_amd/csrc/lpq_device.hpp"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(op_name: str):
+    """HBM bytes per launch measured by rocprofv3 counters for this kernel source, if recorded."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    ent = rec.get("ops", {}).get(op_name)
+    return None if ent is None else ent.get("hbm_bytes_per_launch")
+
+
+# --------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(bench, stride: int, threads: int):
+    """Time the oracle on every `stride`-th tensor (NVFP4: sibling group) of each
+    workload, on `threads` host threads, and compare its outputs with the GPU's."""
+    import numpy as np
+    import torch
+
+    from oracle import oracle as O
+
+    def h8(t):
+        return t.contiguous().view(torch.uint8).cpu().numpy()
+
+    def h16(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    jobs = []        # (callable, algorithmic bytes); each callable returns a mismatch count
+    for op in bench.ops:
+        op.run()
+        torch.cuda.synchronize()
+        wl = op.workload
+        if wl in ("dense", "dsv3") or wl == "moe":
+            ws = bench.sets["moe_experts" if wl == "moe" else wl]
+            out = bench.outputs[wl]
+            for i in range(0, len(ws.specs), stride):
+                sp = ws.specs[i]
+                x = h16(ws.w[i])
+                if op.name.startswith("fp8blk.quantize"):
+                    q, s = h8(out["q"][i]), out["s"][i].cpu().numpy()
+
+                    def job(x=x, q=q, s=s):
+                        oq, os_ = O.fp8blk_quantize(x)
+                        return int((oq != q).sum() + (os_ != s).sum())
+                    jobs.append((job, 3 * sp.numel + 4 * s.size, "fp8blk"))
+                elif op.name.startswith("fp8blk.dequantize"):
+                    q, s, y = h8(out["q"][i]), out["s"][i].cpu().numpy(), h16(out["y"][i])
+                    jobs.append((lambda q=q, s=s, y=y: int((O.fp8blk_dequantize(q, s) != y).sum()),
+                                 3 * sp.numel + 4 * s.size, "fp8blk"))
+                elif op.name.startswith("mxfp8.quantize"):
+                    q, e = h8(out["q"][i]), h8(out["e"][i])
+                    jobs.append((lambda x=x, q=q, e=e: (lambda r: int((r[0] != q).sum() + (r[1] != e).sum()))(
+                        O.mxfp8_quantize(x)), 3 * sp.numel + sp.numel // 32, "mxfp8"))
+                elif op.name.startswith("mxfp8.dequantize"):
+                    q, e, y = h8(out["q"][i]), h8(out["e"][i]), h16(out["y"][i])
+                    jobs.append((lambda q=q, e=e, y=y: int((O.mxfp8_dequantize(q, e) != y).sum()),
+                                 3 * sp.numel + sp.numel // 32, "mxfp8"))
+        elif wl == "nvfp4" and op.counted:
+            ws = bench.sets["moe"]
+            out = bench.outputs["nvfp4"]
+            groups = {}
+            for i, sp in enumerate(ws.specs):
+                groups.setdefault(sp.group, []).append(i)
+            g_dev = out["g"].cpu().numpy()
+            for gid in sorted(groups)[::stride]:
+                idx = groups[gid]
+                xs = [h16(ws.w[i]) for i in idx]
+                n = sum(ws.specs[i].numel for i in idx)
+                if op.name.startswith("nvfp4.quantize"):
+                    ps, ss = [h8(out["p"][i]) for i in idx], [h8(out["s"][i]) for i in idx]
+                    gg = np.float32(g_dev[gid])
+
+                    def job(xs=xs, ps=ps, ss=ss, gg=gg):
+                        A, g, res = O.nvfp4_quantize_group(xs)
+                        bad = int(np.float32(g) != gg)
+                        for (p, s), pp, sg in zip(res, ps, ss):
+                            bad += int((p != pp).sum() + (s != sg).sum())
+                        return bad
+                    jobs.append((job, 2 * n + n // 2 + n // 16 + 4, "nvfp4"))
+                elif op.name.startswith("nvfp4.dequantize") or op.name.startswith("nvfp4.qdq"):
+                    ys = [h16(out["y"][i]) for i in idx]
+                    gg = float(g_dev[gid])
+                    if op.name.startswith("nvfp4.dequantize"):
+                        ps, ss = [h8(out["p"][i]) for i in idx], [h8(out["s"][i]) for i in idx]
+                        jobs.append((lambda ps=ps, ss=ss, ys=ys, gg=gg: sum(
+                            int((O.nvfp4_dequantize(p, s, gg) != y).sum()) for p, s, y in zip(ps, ss, ys)),
+                            2 * n + n // 2 + n // 16 + 4, "nvfp4"))
+                    else:
+                        jobs.append((lambda xs=xs, ys=ys: (lambda g: sum(
+                            int((O.nvfp4_qdq(x, g) != y).sum()) for x, y in zip(xs, ys)))(
+                            O.nvfp4_group_scale(xs)[1]), 4 * n, "nvfp4"))
+        elif wl == "act" and op.counted:
+            a = bench.outputs["act"]
+            x, y = h16(a["x"]), h16(a["y"])
+            jobs.append((lambda x=x, y=y: int((O.nvfp4_qdq(x, O.nvfp4_group_scale([x])[1]) != y).sum()),
+                         4 * x.size, "nvfp4"))
+    O.default()
+    t0 = time.perf_counter()
+    res = O.run_parallel(lambda j: j[0](), jobs, threads)
+    dt = time.perf_counter() - t0
+    total = sum(j[1] for j in jobs)
+    return {
+        "value": round(total / dt / GB, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": f"every {stride}th tensor (NVFP4: every {stride}th sibling group) of each workload op, plus the "
+                  f"whole activation QDQ: {len(jobs)} oracle calls, {total / GB:.2f} GB algorithmic, {dt:.1f} s",
+        "seconds": round(dt, 2),
+        "parity_mismatches": int(sum(res)),
+    }
+
+
+# --------------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--bucket", choices=("layer", "all"), default="layer")
+    ap.add_argument("--workloads", default="dense,moe,nvfp4,dsv3")
+    ap.add_argument("--cpu-stride", type=int, default=32)
+    ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--layers", type=int, default=0, help="reduced layer/expert count for quick checks (0 = full size)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the codecs need no cross-GPU exchange on this path "
+              "(sharding is described in DESIGN.md); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+    which = tuple(w for w in args.workloads.split(",") if w)
+    log(f"building workloads {which} (bucket={args.bucket}) on {torch.cuda.get_device_name(0)}")
+    t0 = time.perf_counter()
+    bench = workloads.Bench(which, bucket=args.bucket, device=dev, log=log, scale_layers=args.layers or None)
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s; "
+        f"{torch.cuda.memory_allocated() / GB:.1f} GB allocated; {len(bench.ops)} ops per step")
+
+    for i in range(args.warmup):
+        bench.step()
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{args.warmup} done")
+
+    nops = len(bench.ops)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nops)]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        for j, op in enumerate(bench.ops):
+            ev[k][j][0].record()
+            op.run()
+            ev[k][j][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"timed {args.steps} steps in {wall:.3f} s")
+
+    op_ms = [sum(ev[k][j][0].elapsed_time(ev[k][j][1]) for k in range(args.steps)) / args.steps for j in range(nops)]
+    ms_per_step = wall * 1e3 / args.steps
+    counted = bench.counted_bytes()
+    value = counted / (ms_per_step / 1e3) / GB
+    per_op = {}
+    for op, ms in zip(bench.ops, op_ms):
+        gbs = op.bytes / (ms / 1e3) / GB
+        per_op[op.name] = {"ms": round(ms, 3), "GB/s": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+                           "launches": len(op.launches), "algorithmic_GB": round(op.bytes / GB, 3),
+                           "in_metric": op.counted}
+        log(f"  {op.name:32s} {ms:8.3f} ms  {gbs:8.1f} GB/s  {100 * gbs / HBM_PEAK_GBS:5.1f}% of peak")
+
+    dom = max(range(nops), key=lambda j: op_ms[j])
+    dop = bench.ops[dom]
+    launches = len(dop.launches)
+    per_launch_bytes = dop.bytes / launches
+    per_launch_s = op_ms[dom] / 1e3 / launches
+    achieved = per_launch_bytes / per_launch_s / GB
+    traffic = load_traffic(dop.name)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": dop.name, "bytes_per_launch": int(per_launch_bytes),
+                "avg_launch_us": round(per_launch_s * 1e6, 2)}
+
+    cpu = None
+    if not args.no_cpu:
+        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        log(f"cpu baseline: oracle on a 1/{args.cpu_stride} sample with {threads} threads")
+        cpu = cpu_baseline(bench, args.cpu_stride, threads)
+        log(f"cpu baseline: {cpu['value']} GB/s, {cpu['parity_mismatches']} mismatches vs GPU, {cpu['seconds']} s")
+
+    result = {
+        "metric": "quantize+dequant GB/s (bytes in+out) and % of HBM peak, per format, 1 GPU",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "config": {
+            "workload": "all weight workloads at full size: Qwen3-4B dense (252 tensors) block-FP8 q+dq; "
+                        "Qwen3-30B-A3B experts (18,432 tensors) MXFP8 q+dq; the same experts + q/k/v "
+                        "(18,576 tensors, 12,336 sibling groups) NVFP4 amax+q+dq+QDQ and W4A4 activation "
+                        "QDQ 8192x2048; DeepSeek-V3 MoE layer (768 tensors) block-FP8 q+dq",
+            "workloads": list(which),
+            "bucket": args.bucket,
+            "algorithmic_GB_per_step": round(counted / GB, 3),
+        },
+        "per_op": per_op,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

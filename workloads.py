@@ -1,0 +1,311 @@
+"""Full-size synthetic workloads of the weight codecs, shared by bench.py and the
+full-size GPU parity test.
+
+Shapes follow the model families the pages train and serve ("Low Precision
+RL": Qwen3-4B, Qwen3-30B-A3B, DeepSeek-V3; "verl NVFP4 QAT" 2.4: q/k/v and
+gate/up sibling groups).  No checkpoints are available, so every weight is
+drawn by the seeded generator (``synth``), on the device, with the
+distributions named for each workload.
+
+  dense   Qwen3-4B: 36 layers x {q 4096x2560, k 1024x2560, v 1024x2560,
+          o 2560x4096, gate 9728x2560, up 9728x2560, down 2560x9728}
+          -> block-wise FP8 quantize + dequantize
+  moe     Qwen3-30B-A3B experts: 48 layers x 128 experts x {gate 768x2048,
+          up 768x2048, down 2048x768} -> MXFP8 quantize + dequantize
+  nvfp4   the same experts plus 48 x {q 4096x2048, k 512x2048, v 512x2048};
+          sibling groups {gate_e, up_e}, {down_e}, {q, k, v} (12,336 groups)
+          -> NVFP4 amax, quantize, dequantize and weight QDQ; plus W4A4
+          activation QDQ on 8192x2048 tokens
+  dsv3    DeepSeek-V3 MoE layer: 256 experts x {gate 2048x7168, up 2048x7168,
+          down 7168x2048} -> block-wise FP8 quantize + dequantize
+
+Buckets: one grouped launch per transformer layer (the unit a weight sync
+streams), or one launch over the whole workload.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import torch
+
+import precision_weight_quantization_amd as lpq
+from synth import gpu as sgpu
+from synth import synth
+
+GB = 1e9
+
+# projection ids inside a layer (part of each tensor's generator stream id)
+P_Q, P_K, P_V, P_O, P_GATE, P_UP, P_DOWN = range(7)
+
+
+@dataclasses.dataclass
+class TensorSpec:
+    name: str
+    layer: int
+    expert: int
+    proj: int
+    M: int
+    N: int
+    group: int = 0
+
+    @property
+    def numel(self) -> int:
+        return self.M * self.N
+
+
+def dense_specs(layers=36):
+    shapes = [(P_Q, 4096, 2560), (P_K, 1024, 2560), (P_V, 1024, 2560), (P_O, 2560, 4096),
+              (P_GATE, 9728, 2560), (P_UP, 9728, 2560), (P_DOWN, 2560, 9728)]
+    return [TensorSpec(f"L{l}.p{p}", l, 0, p, M, N) for l in range(layers) for (p, M, N) in shapes]
+
+
+def moe_specs(layers=48, experts=128, attention=False):
+    out = []
+    g = 0
+    for l in range(layers):
+        if attention:
+            for p, M in ((P_Q, 4096), (P_K, 512), (P_V, 512)):
+                out.append(TensorSpec(f"L{l}.attn.p{p}", l, 0xFFFF, p, M, 2048, g))
+            g += 1
+        for e in range(experts):
+            out.append(TensorSpec(f"L{l}.e{e}.gate", l, e, P_GATE, 768, 2048, g))
+            out.append(TensorSpec(f"L{l}.e{e}.up", l, e, P_UP, 768, 2048, g))
+            g += 1
+            out.append(TensorSpec(f"L{l}.e{e}.down", l, e, P_DOWN, 2048, 768, g))
+            g += 1
+    return out
+
+
+def dsv3_specs(experts=256):
+    out = []
+    for e in range(experts):
+        out.append(TensorSpec(f"e{e}.gate", 0, e, P_GATE, 2048, 7168))
+        out.append(TensorSpec(f"e{e}.up", 0, e, P_UP, 2048, 7168))
+        out.append(TensorSpec(f"e{e}.down", 0, e, P_DOWN, 7168, 2048))
+    return out
+
+
+class Slab:
+    """One device allocation carved into 256-byte aligned per-tensor views."""
+
+    def __init__(self, sizes_bytes, device, dtype=torch.uint8):
+        self.offsets = []
+        off = 0
+        for b in sizes_bytes:
+            self.offsets.append(off)
+            off += (b + 255) // 256 * 256
+        self.buf = torch.empty(max(off, 256), dtype=torch.uint8, device=device)
+        self.nbytes = off
+
+    def view(self, i, shape, dtype):
+        n = 1
+        for s in shape:
+            n *= s
+        nb = n * torch.empty((), dtype=dtype).element_size()
+        return self.buf[self.offsets[i]:self.offsets[i] + nb].view(dtype).view(shape)
+
+
+class WeightSet:
+    """BF16 weights of one workload, generated on the device."""
+
+    def __init__(self, config: int, specs, dist, device="cuda"):
+        self.config = config
+        self.specs = specs
+        self.seed = synth.seed_of(config)
+        self.dist = dist
+        self.slab = Slab([s.numel * 2 for s in specs], device)
+        self.w = [self.slab.view(i, (s.M, s.N), torch.bfloat16) for i, s in enumerate(specs)]
+        for s, w in zip(specs, self.w):
+            sgpu.fill(w, self.seed, synth.stream_of(s.layer, s.expert, s.proj), dist)
+
+    @property
+    def numel(self) -> int:
+        return sum(s.numel for s in self.specs)
+
+    def layers(self):
+        out = {}
+        for i, s in enumerate(self.specs):
+            out.setdefault(s.layer, []).append(i)
+        return [out[k] for k in sorted(out)]
+
+
+# --------------------------------------------------------------------------- operations
+
+@dataclasses.dataclass
+class Op:
+    name: str              # e.g. "mxfp8.quantize"
+    workload: str
+    bytes: float           # algorithmic bytes (in + out) of one run
+    launches: list         # callables, one per grouped launch
+    counted: bool = True   # False: in the step's time, not in its algorithmic bytes
+
+    def run(self):
+        for f in self.launches:
+            f()
+
+
+def _buckets(ws: WeightSet, bucket: str):
+    return ws.layers() if bucket == "layer" else [list(range(len(ws.specs)))]
+
+
+def fp8blk_ops(tag: str, ws: WeightSet, codes: Slab, scales: Slab, out: Slab, bucket: str):
+    specs = ws.specs
+    q = [codes.view(i, (s.M, s.N), torch.uint8) for i, s in enumerate(specs)]
+    sc = [scales.view(i, ((s.M + 127) // 128, (s.N + 127) // 128), torch.float32) for i, s in enumerate(specs)]
+    y = [out.view(i, (s.M, s.N), torch.bfloat16) for i, s in enumerate(specs)]
+    tq, tdq = [], []
+    for idx in _buckets(ws, bucket):
+        tq.append(lpq.TensorTable([(ws.w[i], q[i], sc[i], specs[i].M, specs[i].N, 0) for i in idx]))
+        tdq.append(lpq.TensorTable([(q[i], y[i], sc[i], specs[i].M, specs[i].N, 0) for i in idx]))
+    tiles = sum(((s.M + 127) // 128) * ((s.N + 127) // 128) for s in specs)
+    nbytes = 3 * ws.numel + 4 * tiles
+    return ([Op(f"fp8blk.quantize[{tag}]", tag, nbytes, [lambda t=t: lpq.lpq_quantize_fp8blk_grouped(t) for t in tq]),
+             Op(f"fp8blk.dequantize[{tag}]", tag, nbytes, [lambda t=t: lpq.lpq_dequantize_fp8blk_grouped(t) for t in tdq])],
+            dict(q=q, s=sc, y=y))
+
+
+def mxfp8_ops(tag: str, ws: WeightSet, codes: Slab, ebytes: Slab, out: Slab, bucket: str):
+    specs = ws.specs
+    q = [codes.view(i, (s.M, s.N), torch.uint8) for i, s in enumerate(specs)]
+    e = [ebytes.view(i, (s.M, s.N // 32), torch.uint8) for i, s in enumerate(specs)]
+    y = [out.view(i, (s.M, s.N), torch.bfloat16) for i, s in enumerate(specs)]
+    tq, tdq = [], []
+    for idx in _buckets(ws, bucket):
+        tq.append(lpq.TensorTable([(ws.w[i], q[i], e[i], specs[i].M, specs[i].N, 0) for i in idx]))
+        tdq.append(lpq.TensorTable([(q[i], y[i], e[i], specs[i].M, specs[i].N, 0) for i in idx]))
+    nbytes = 3 * ws.numel + ws.numel // 32
+    return ([Op(f"mxfp8.quantize[{tag}]", tag, nbytes, [lambda t=t: lpq.lpq_quantize_mxfp8_grouped(t) for t in tq]),
+             Op(f"mxfp8.dequantize[{tag}]", tag, nbytes, [lambda t=t: lpq.lpq_dequantize_mxfp8_grouped(t) for t in tdq])],
+            dict(q=q, e=e, y=y))
+
+
+def nvfp4_ops(tag: str, ws: WeightSet, packed: Slab, sbytes: Slab, out: Slab, bucket: str, device="cuda"):
+    specs = ws.specs
+    n_groups = max(s.group for s in specs) + 1
+    amax = torch.zeros(n_groups, dtype=torch.float32, device=device)
+    g = torch.zeros(n_groups, dtype=torch.float32, device=device)
+    p = [packed.view(i, (s.M, s.N // 2), torch.uint8) for i, s in enumerate(specs)]
+    sb = [sbytes.view(i, (s.M, s.N // 16), torch.uint8) for i, s in enumerate(specs)]
+    y = [out.view(i, (s.M, s.N), torch.bfloat16) for i, s in enumerate(specs)]
+    ta, tq, tdq, tqdq = [], [], [], []
+    for idx in _buckets(ws, bucket):
+        tq.append(lpq.TensorTable([(ws.w[i], p[i], sb[i], specs[i].M, specs[i].N, specs[i].group) for i in idx]))
+        tdq.append(lpq.TensorTable([(p[i], y[i], sb[i], specs[i].M, specs[i].N, specs[i].group) for i in idx]))
+        tqdq.append(lpq.TensorTable([(ws.w[i], y[i], None, specs[i].M, specs[i].N, specs[i].group) for i in idx]))
+    n = ws.numel
+    qbytes = 2 * n + n // 2 + n // 16 + 4 * n_groups
+    # the amax pass accumulates: zero all group slots first (a fill kernel), then max in
+    ops = [
+        Op(f"nvfp4.amax[{tag}]", tag, 2 * n,
+           [lambda: amax.zero_()] + [lambda t=t: lpq.lpq_nvfp4_amax_grouped(t, amax, accumulate=True) for t in tq],
+           counted=False),
+        Op(f"nvfp4.quantize[{tag}]", tag, qbytes, [lambda t=t: lpq.lpq_quantize_nvfp4_grouped(t, amax, g) for t in tq]),
+        Op(f"nvfp4.dequantize[{tag}]", tag, qbytes, [lambda t=t: lpq.lpq_dequantize_nvfp4_grouped(t, g) for t in tdq]),
+        Op(f"nvfp4.qdq[{tag}]", tag, 4 * n, [lambda t=t: lpq.lpq_nvfp4_qdq_grouped(t, amax) for t in tqdq]),
+    ]
+    return ops, dict(p=p, s=sb, y=y, amax=amax, g=g, n_groups=n_groups)
+
+
+def activation_ops(x: torch.Tensor, y: torch.Tensor):
+    amax = torch.zeros(1, dtype=torch.float32, device=x.device)
+    n = x.numel()
+    return ([Op("nvfp4.amax[act]", "act", 2 * n, [lambda: lpq.lpq_nvfp4_amax(x, amax)], counted=False),
+             Op("nvfp4.qdq[act]", "act", 4 * n, [lambda: lpq.lpq_nvfp4_qdq(x, amax, y)])],
+            dict(amax=amax))
+
+
+WORKLOADS = ("dense", "moe", "nvfp4", "dsv3")
+
+
+class Bench:
+    """All workloads' tensors and operations, buffers shared where the order allows."""
+
+    def __init__(self, which=WORKLOADS, bucket="layer", device="cuda", log=print, scale_layers=None):
+        self.ops = []
+        self.outputs = {}
+        self.sets = {}
+        L = scale_layers
+        need_moe = "moe" in which or "nvfp4" in which
+        if "dense" in which:
+            self.sets["dense"] = WeightSet(2, dense_specs(L or 36), synth.DIST_DENSE, device)
+            log(f"generated dense weights: {self.sets['dense'].numel * 2 / GB:.2f} GB")
+        if need_moe:
+            self.sets["moe"] = WeightSet(3, moe_specs(L or 48, attention=True), synth.DIST_MOE, device)
+            log(f"generated MoE expert + attention weights: {self.sets['moe'].numel * 2 / GB:.2f} GB")
+        if "dsv3" in which:
+            self.sets["dsv3"] = WeightSet(5, dsv3_specs(256 if L is None else max(4, L)), synth.DIST_MOE, device)
+            log(f"generated DeepSeek-V3 layer weights: {self.sets['dsv3'].numel * 2 / GB:.2f} GB")
+        # shared output slabs, sized for the largest user
+        maxspecs = max((ws.specs for ws in self.sets.values()), key=lambda sp: sum(s.numel for s in sp))
+        self.codes = Slab([s.numel for s in maxspecs], device)
+        self.out = Slab([2 * s.numel for s in maxspecs], device)
+        if "dense" in which:
+            ws = self.sets["dense"]
+            codes = self._reslab(self.codes, ws.specs, 1)
+            sc = Slab([4 * ((s.M + 127) // 128) * ((s.N + 127) // 128) for s in ws.specs], device)
+            out = self._reslab(self.out, ws.specs, 2)
+            ops, o = fp8blk_ops("dense", ws, codes, sc, out, bucket)
+            self.ops += ops
+            self.outputs["dense"] = o
+        if "moe" in which:
+            ws = self._experts_only(self.sets["moe"])
+            codes = self._reslab(self.codes, ws.specs, 1)
+            eb = Slab([s.numel // 32 for s in ws.specs], device)
+            out = self._reslab(self.out, ws.specs, 2)
+            ops, o = mxfp8_ops("moe", ws, codes, eb, out, bucket)
+            self.ops += ops
+            self.outputs["moe"] = o
+            self.sets["moe_experts"] = ws
+        if "nvfp4" in which:
+            ws = self.sets["moe"]
+            packed = self._reslab(self.codes, ws.specs, 0.5)
+            sb = Slab([s.numel // 16 for s in ws.specs], device)
+            out = self._reslab(self.out, ws.specs, 2)
+            ops, o = nvfp4_ops("nvfp4", ws, packed, sb, out, bucket, device)
+            self.ops += ops
+            self.outputs["nvfp4"] = o
+            x = torch.empty((8192, 2048), dtype=torch.bfloat16, device=device)
+            sgpu.fill(x, synth.seed_of(4), synth.stream_of(0xFFFF, 0xFFFFFF, 0xFFFF), synth.DIST_ACT)
+            ya = torch.empty_like(x)
+            ops, o = activation_ops(x, ya)
+            self.ops += ops
+            self.outputs["act"] = dict(x=x, y=ya, **o)
+        if "dsv3" in which:
+            ws = self.sets["dsv3"]
+            codes = self._reslab(self.codes, ws.specs, 1)
+            sc = Slab([4 * ((s.M + 127) // 128) * ((s.N + 127) // 128) for s in ws.specs], device)
+            out = self._reslab(self.out, ws.specs, 2)
+            ops, o = fp8blk_ops("dsv3", ws, codes, sc, out, bucket)
+            self.ops += ops
+            self.outputs["dsv3"] = o
+
+    @staticmethod
+    def _reslab(slab: Slab, specs, bytes_per_elem):
+        """A view-only slab over `slab`'s buffer laid out for `specs`."""
+        s = Slab.__new__(Slab)
+        s.buf = slab.buf
+        s.offsets = []
+        off = 0
+        for sp in specs:
+            s.offsets.append(off)
+            off += (int(sp.numel * bytes_per_elem) + 255) // 256 * 256
+        assert off <= slab.buf.numel(), "output slab too small"
+        s.nbytes = off
+        return s
+
+    @staticmethod
+    def _experts_only(ws: WeightSet) -> WeightSet:
+        sub = WeightSet.__new__(WeightSet)
+        keep = [i for i, s in enumerate(ws.specs) if s.expert != 0xFFFF]
+        sub.config, sub.seed, sub.dist = 3, ws.seed, ws.dist
+        sub.specs = [ws.specs[i] for i in keep]
+        sub.w = [ws.w[i] for i in keep]
+        sub.slab = ws.slab
+        return sub
+
+    def counted_bytes(self) -> float:
+        return sum(op.bytes for op in self.ops if op.counted)
+
+    def step(self):
+        for op in self.ops:
+            op.run()
