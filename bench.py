@@ -154,6 +154,55 @@ def cpu_baseline(bench, stride: int, threads: int):
     }
 
 
+# --------------------------------------------------------------------------- HBM copy reference
+
+COPY_BYTES = 4 * (1 << 30)
+
+
+def copy_bandwidth(reps: int = 10) -> float:
+    """Device-to-device copy rate (GB/s, read + write) of a plain 4 GiB copy on the
+    current stream: the achievable-bandwidth context for the codec figures, and
+    the kernel of known traffic used to calibrate the HBM byte counters."""
+    import torch
+    x = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        y.copy_(x)
+    b.record()
+    torch.cuda.synchronize()
+    sec = a.elapsed_time(b) / 1e3 / reps
+    del x, y
+    torch.cuda.empty_cache()
+    return 2 * COPY_BYTES / sec / GB
+
+
+def summarize_pmc(path: str) -> None:
+    """Per-kernel mean of each counter per dispatch, from rocprofv3 counter CSVs
+    found under `path` (grouped by kernel name and grid size)."""
+    import csv
+    import glob
+    import re
+    rows = []
+    for f in glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    acc = {}
+    for r in rows:
+        name = re.sub(r"\(.*", "", r.get("Kernel_Name", "?")).replace("(anonymous namespace)::", "")
+        key = (name, r.get("Grid_Size", "?"), r.get("Counter_Name", "?"))
+        d = acc.setdefault(key, [0, 0.0, set()])
+        d[1] += float(r.get("Counter_Value", 0))
+        d[2].add(r.get("Dispatch_Id", len(d[2])))
+    print("| kernel | grid size | counter | dispatches | mean per dispatch |")
+    print("|---|---|---|---|---|")
+    for (name, grid, ctr), (_, tot, disp) in sorted(acc.items()):
+        print(f"| {name} | {grid} | {ctr} | {len(disp)} | {tot / max(len(disp), 1):.1f} |")
+
+
 # --------------------------------------------------------------------------- main
 
 def main():
@@ -163,12 +212,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--bucket", choices=("layer", "all"), default="layer")
     ap.add_argument("--workloads", default="dense,moe,nvfp4,dsv3")
-    ap.add_argument("--cpu-stride", type=int, default=32)
+    ap.add_argument("--cpu-stride", type=int, default=12)
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--layers", type=int, default=0, help="reduced layer/expert count for quick checks (0 = full size)")
+    ap.add_argument("--ops", default="", help="regex: time only the matching ops (warmup still runs every op)")
+    ap.add_argument("--copy-only", action="store_true", help="only measure the plain HBM copy reference")
+    ap.add_argument("--summarize-pmc", default="", help="print a per-kernel summary of rocprofv3 counter CSVs")
     args = ap.parse_args()
 
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the codecs need no cross-GPU exchange on this path "
               "(sharding is described in DESIGN.md); run it with --gpus 1.", file=sys.stderr)
@@ -179,6 +234,11 @@ def main():
 
     torch.cuda.init()
     dev = torch.device("cuda:0")
+    if args.copy_only:
+        log(f"plain copy: {copy_bandwidth():.1f} GB/s")
+        return
+    copy_gbs = copy_bandwidth()
+    log(f"plain {COPY_BYTES >> 30} GiB device copy: {copy_gbs:.1f} GB/s")
     which = tuple(w for w in args.workloads.split(",") if w)
     log(f"building workloads {which} (bucket={args.bucket}) on {torch.cuda.get_device_name(0)}")
     t0 = time.perf_counter()
@@ -192,6 +252,10 @@ def main():
         torch.cuda.synchronize()
         log(f"warmup step {i + 1}/{args.warmup} done")
 
+    if args.ops:
+        import re
+        bench.ops = [op for op in bench.ops if re.search(args.ops, op.name)]
+        log(f"timing only: {[op.name for op in bench.ops]}")
     nops = len(bench.ops)
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nops)]
           for _ in range(args.steps)]
@@ -231,7 +295,7 @@ def main():
                 "avg_launch_us": round(per_launch_s * 1e6, 2)}
 
     cpu = None
-    if not args.no_cpu:
+    if not args.no_cpu and not args.ops:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         log(f"cpu baseline: oracle on a 1/{args.cpu_stride} sample with {threads} threads")
         cpu = cpu_baseline(bench, args.cpu_stride, threads)
@@ -251,6 +315,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "hbm_copy_GBs": round(copy_gbs, 1),
         "config": {
             "workload": "all weight workloads at full size: Qwen3-4B dense (252 tensors) block-FP8 q+dq; "
                         "Qwen3-30B-A3B experts (18,432 tensors) MXFP8 q+dq; the same experts + q/k/v "

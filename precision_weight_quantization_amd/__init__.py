@@ -18,7 +18,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "liblpq.so")
+# LPQ_LIBRARY may name another build of the same library (e.g. one compiled
+# with different launch parameters); the default is the in-tree build.
+LIB_PATH = os.environ.get("LPQ_LIBRARY") or os.path.join(_PKG, "liblpq.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m precision_weight_quantization_amd.build`")

@@ -32,6 +32,34 @@ namespace lpq {
 
 typedef short short2_t __attribute__((ext_vector_type(2)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));   // 16 bytes: 8 BF16 values
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));   // 8 bytes
+
+// Global loads and stores, optionally marked non-temporal (streamed data that
+// is not read again soon: keeps it from displacing useful cache lines).  The
+// pointers are taken to the global address space so that global_load /
+// global_store (not flat) instructions are emitted.
+template <typename T>
+using gptr = __attribute__((address_space(1))) T*;
+
+template <bool NT, typename T>
+__device__ __forceinline__ T load(const T* p) {
+    auto g = (__attribute__((address_space(1))) const T*)(p);
+    if constexpr (NT) return __builtin_nontemporal_load(g);
+    else return *g;
+}
+template <bool NT, typename T>
+__device__ __forceinline__ void store(T* p, T v) {
+    auto g = (gptr<T>)(p);
+    if constexpr (NT) __builtin_nontemporal_store(v, g);
+    else *g = v;
+}
+
+// Plain global byte access (scale bytes).
+__device__ __forceinline__ uint32_t load_u8(const uint8_t* p) {
+    return *(__attribute__((address_space(1))) const uint8_t*)(p);
+}
+__device__ __forceinline__ void store_u8(uint8_t* p, uint32_t v) { *(gptr<uint8_t>)(p) = (uint8_t)v; }
 
 constexpr float kE4M3Max = 448.0f;      // largest finite E4M3 value
 constexpr float kTinyScale = 0x1p-90f;  // below this a scale is pre-scaled by 2^64
@@ -84,7 +112,7 @@ __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b 
 // |x| maximum over the 8 BF16 values of a 16-byte vector, as binary32 bits.
 // BF16 magnitudes order like their 15-bit patterns, so the maximum is taken on
 // the masked integers and widened once.
-__device__ __forceinline__ uint32_t absmax8_bits(const uint4& v) {
+__device__ __forceinline__ uint32_t absmax8_bits(const v4u& v) {
     uint32_t a = v.x & 0x7fff7fffu, b = v.y & 0x7fff7fffu, c = v.z & 0x7fff7fffu, d = v.w & 0x7fff7fffu;
     uint32_t m0 = umax(umax(a & 0xffffu, a >> 16), umax(b & 0xffffu, b >> 16));
     uint32_t m1 = umax(umax(c & 0xffffu, c >> 16), umax(d & 0xffffu, d >> 16));

@@ -8,17 +8,22 @@
 // plus the NVFP4 fake-quant.  All of it is streaming work bound by HBM
 // bandwidth: no kernel here is a contraction, so none uses MFMA.
 //
-// Launch shape.  A grouped call covers many tensors in one launch: grid.y is
-// the tensor (its descriptor is read into scalar registers), grid.x the chunk
-// or tile inside it; workgroups past the end of a smaller tensor exit at once.
+// Launch shape.  A grouped call covers many tensors in one launch.  The grid
+// is one-dimensional and dense: the host lays the tensors' work units
+// (chunks, or 128x128 tiles) end to end and passes a short table of
+// equal-size runs in the kernel arguments; each workgroup finds its tensor
+// from that table with scalar compares and one division, then reads the
+// descriptor into scalar registers.
+// No workgroup is launched without work.
 //  * MXFP8 / NVFP4 are flat in memory (N is a multiple of the block), so a
-//    workgroup of 256 lanes streams 16-byte BF16 vectors, 8 elements per lane,
-//    UNROLL vectors per lane in flight; a 1x32 block is a quad of lanes and a
-//    1x16 block a pair, reduced with DPP lane permutations.
-//  * Block-wise FP8 gives one 256-lane workgroup a 128x128 tile: 16 lanes per
-//    256-byte row segment, 8 row passes, all 64 values of a lane kept in
-//    registers between the tile-amax reduction (DPP + LDS across the 4
-//    waves) and the encode, so HBM is read once.
+//    workgroup streams 16-byte BF16 vectors, 8 elements per lane, U vectors
+//    per lane; a 1x32 block is a quad of lanes and a 1x16 block a pair,
+//    reduced with DPP lane permutations.  U is 2 to 4 (16 for the read-only
+//    amax pass): enough bytes in flight per CU, short-lived workgroups.
+//  * Block-wise FP8 gives one workgroup a 128x128 tile: 16 lanes per 256-byte
+//    row segment, 2048/threads row passes, all values kept in registers
+//    between the tile-amax reduction (DPP + LDS across the waves) and the
+//    encode, so HBM is read once.
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
 #include <stdint.h>
@@ -26,43 +31,139 @@
 #include "lpq.h"
 #include "lpq_device.hpp"
 
+// Launch parameters (vectors per lane, workgroup size, non-temporal access);
+// the values are the measured best on MI355X for each kernel.
+#ifndef LPQ_MXQ_U
+#define LPQ_MXQ_U 2
+#endif
+#ifndef LPQ_MXD_U
+#define LPQ_MXD_U 2
+#endif
+#ifndef LPQ_NVQ_U
+#define LPQ_NVQ_U 4
+#endif
+#ifndef LPQ_NVD_U
+#define LPQ_NVD_U 2
+#endif
+#ifndef LPQ_QDQ_U
+#define LPQ_QDQ_U 2
+#endif
+#ifndef LPQ_AMAX_U
+#define LPQ_AMAX_U 16
+#endif
+#ifndef LPQ_TILEQ_THREADS
+#define LPQ_TILEQ_THREADS 256
+#endif
+#ifndef LPQ_TILED_THREADS
+#define LPQ_TILED_THREADS 1024
+#endif
+#ifndef LPQ_NTL
+#define LPQ_NTL 1
+#endif
+#ifndef LPQ_NTS
+#define LPQ_NTS 1
+#endif
+
 using namespace lpq;
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
-constexpr int64_t kFlatChunk = (int64_t)kThreads * 8 * kUnroll;  // elements per workgroup
-constexpr int kAmaxUnroll = 8;
-constexpr int64_t kAmaxChunk = (int64_t)kThreads * 8 * kAmaxUnroll;
+constexpr int kThreads = 256;            // flat kernels
 constexpr int kTile = 128;
+constexpr bool kNTL = LPQ_NTL != 0;
+constexpr bool kNTS = LPQ_NTS != 0;
+constexpr int kMaxSeg = 8;               // segments per launch (longer lists are split)
 
-__device__ __forceinline__ lpq_tensor load_desc(const lpq_tensor* table, const lpq_tensor& one) {
-    return table ? table[blockIdx.y] : one;
+template <int U>
+constexpr int64_t chunk_elems() { return (int64_t)kThreads * 8 * U; }
+
+// Dense work map of one launch.  Consecutive tensors with the same number of
+// work units form a segment: segment s starts at work unit first[s] and at
+// tensor tensor0[s], and each of its tensors owns units[s] work units.
+// Grouped calls over expert lists are one to a few segments, so a workgroup
+// finds its tensor with a handful of scalar compares and one division (no
+// dependent memory access).
+struct ChunkMap {
+    int32_t nseg;
+    uint32_t first[kMaxSeg];
+    uint32_t tensor0[kMaxSeg];
+    uint32_t units[kMaxSeg];
+    double inv_units[kMaxSeg];   // 1 / units[s]
+};
+
+struct Work {
+    lpq_tensor d;
+    int64_t unit;    // chunk or tile index inside the tensor
+};
+
+// The tensor and work unit of this workgroup.  Every quantity is uniform
+// across the workgroup and kept in scalar registers, so the descriptor of a
+// grouped call is fetched with scalar loads.
+template <bool G>
+__device__ __forceinline__ Work locate(const lpq_tensor* table, const lpq_tensor& one, const ChunkMap& m) {
+    Work w;
+    if constexpr (!G) {
+        w.d = one;
+        w.unit = blockIdx.x;
+        return w;
+    } else {
+        const uint32_t b = blockIdx.x;
+        // every table entry is read at a constant offset (one batch of scalar
+        // loads from the kernel arguments), then the segment is selected
+        uint32_t f = 0, u = m.units[0], t0 = 0;
+        double inv = m.inv_units[0];
+#pragma unroll
+        for (int k = 1; k < kMaxSeg; k++) {
+            if (k < m.nseg && m.first[k] <= b) {
+                f = m.first[k];
+                u = m.units[k];
+                t0 = m.tensor0[k];
+                inv = m.inv_units[k];
+            }
+        }
+        const uint32_t x = b - f;
+        // x / u from a double-precision estimate (off by at most one), corrected
+        uint32_t q = (uint32_t)((double)x * inv);
+        if ((uint64_t)(q + 1) * u <= x) q += 1;
+        else if ((uint64_t)q * u > x) q -= 1;
+        q = __builtin_amdgcn_readfirstlane(q);
+        const __attribute__((address_space(4))) lpq_tensor* t =
+            (const __attribute__((address_space(4))) lpq_tensor*)(table) + t0 + q;
+        w.d.src = t->src;
+        w.d.dst = t->dst;
+        w.d.scale = t->scale;
+        w.d.rows = t->rows;
+        w.d.cols = t->cols;
+        w.d.group = t->group;
+        w.d.reserved = 0;
+        w.unit = (int64_t)(x - q * u);
+        return w;
+    }
 }
 
 // ---------------------------------------------------------------------------
 // MXFP8
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(kThreads) void k_mxfp8_quant(const lpq_tensor* table, lpq_tensor one) {
-    const lpq_tensor d = load_desc(table, one);
+template <int U, bool GROUPED>
+__global__ __launch_bounds__(kThreads) void k_mxfp8_quant(const lpq_tensor* table, lpq_tensor one, ChunkMap map) {
+    const Work W = locate<GROUPED>(table, one, map);
+    const lpq_tensor& d = W.d;
     const int64_t total = d.rows * d.cols;
-    const int64_t base = (int64_t)blockIdx.x * kFlatChunk;
-    if (base >= total) return;
-    const uint4* src = reinterpret_cast<const uint4*>(d.src);
-    uint2* dst = reinterpret_cast<uint2*>(d.dst);
+    const int64_t base = W.unit * chunk_elems<U>();
+    const v4u* src = reinterpret_cast<const v4u*>(d.src);
+    v2u* dst = reinterpret_cast<v2u*>(d.dst);
     uint8_t* esc = reinterpret_cast<uint8_t*>(d.scale);
     const int tid = threadIdx.x;
 
-    uint4 v[kUnroll];
+    v4u v[U];
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
+    for (int u = 0; u < U; u++) {
         const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
-        v[u] = e0 < total ? src[e0 >> 3] : make_uint4(0, 0, 0, 0);
+        v[u] = e0 < total ? load<kNTL>(src + (e0 >> 3)) : v4u{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
+    for (int u = 0; u < U; u++) {
         const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
         // a quad of lanes is one 32-element block; blocks never straddle the end
         const uint32_t amax = quad_max(absmax8_bits(v[u]));
@@ -73,40 +174,41 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_quant(const lpq_tensor* tabl
         short2_t c23 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((short2_t){0, 0}, bf16_lo(v[u].z), bf16_hi(v[u].z), X, false);
         c23 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c23, bf16_lo(v[u].w), bf16_hi(v[u].w), X, true);
         if (e0 < total) {
-            dst[e0 >> 3] = make_uint2(__builtin_bit_cast(uint32_t, c01), __builtin_bit_cast(uint32_t, c23));
-            if ((tid & 3) == 0) esc[e0 >> 5] = (uint8_t)byte;
+            store<kNTS>(dst + (e0 >> 3), v2u{__builtin_bit_cast(uint32_t, c01), __builtin_bit_cast(uint32_t, c23)});
+            if ((tid & 3) == 0) store_u8(esc + (e0 >> 5), byte);
         }
     }
 }
 
-__global__ __launch_bounds__(kThreads) void k_mxfp8_dequant(const lpq_tensor* table, lpq_tensor one) {
-    const lpq_tensor d = load_desc(table, one);
+template <int U, bool GROUPED>
+__global__ __launch_bounds__(kThreads) void k_mxfp8_dequant(const lpq_tensor* table, lpq_tensor one, ChunkMap map) {
+    const Work W = locate<GROUPED>(table, one, map);
+    const lpq_tensor& d = W.d;
     const int64_t total = d.rows * d.cols;
-    const int64_t base = (int64_t)blockIdx.x * kFlatChunk;
-    if (base >= total) return;
-    const uint2* src = reinterpret_cast<const uint2*>(d.src);
-    uint4* dst = reinterpret_cast<uint4*>(d.dst);
+    const int64_t base = W.unit * chunk_elems<U>();
+    const v2u* src = reinterpret_cast<const v2u*>(d.src);
+    v4u* dst = reinterpret_cast<v4u*>(d.dst);
     const uint8_t* esc = reinterpret_cast<const uint8_t*>(d.scale);
     const int tid = threadIdx.x;
 
-    uint2 c[kUnroll];
-    uint32_t b[kUnroll];
+    v2u c[U];
+    uint32_t b[U];
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
+    for (int u = 0; u < U; u++) {
         const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
-        c[u] = e0 < total ? src[e0 >> 3] : make_uint2(0, 0);
-        b[u] = e0 < total ? esc[e0 >> 5] : 127u;
+        c[u] = e0 < total ? load<kNTL>(src + (e0 >> 3)) : v2u{0, 0};
+        b[u] = e0 < total ? load_u8(esc + (e0 >> 5)) : 127u;
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
+    for (int u = 0; u < U; u++) {
         const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
         const float X = ue8m0_operand(b[u]);
-        uint4 o;
+        v4u o;
         o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[u].x, X, false));
         o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[u].x, X, true));
         o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[u].y, X, false));
         o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[u].y, X, true));
-        if (e0 < total) dst[e0 >> 3] = o;
+        if (e0 < total) store<kNTS>(dst + (e0 >> 3), o);
     }
 }
 
@@ -162,7 +264,7 @@ __device__ __forceinline__ BlockScale block_scale(uint32_t bmax_bits, const Glob
 }
 
 // 8 BF16 values -> 8 E2M1 codes (one 32-bit word, element 0 in the low nibble).
-__device__ __forceinline__ uint32_t e2m1x8(const uint4& v, const BlockScale& B) {
+__device__ __forceinline__ uint32_t e2m1x8(const v4u& v, const BlockScale& B) {
     float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
                   bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
     if (B.xpre != 1.0f) {
@@ -181,12 +283,12 @@ __device__ __forceinline__ uint32_t e2m1x8(const uint4& v, const BlockScale& B) 
 }
 
 // 8 E2M1 codes (one word) times S -> 8 BF16 values.
-__device__ __forceinline__ uint4 e2m1x8_to_bf16(uint32_t p, float S) {
+__device__ __forceinline__ v4u e2m1x8_to_bf16(uint32_t p, float S) {
     float2_t f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 0);
     float2_t f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 1);
     float2_t f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 2);
     float2_t f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 3);
-    uint4 o;
+    v4u o;
     o.x = bf16x2(f0[0] * S, f0[1] * S);
     o.y = bf16x2(f1[0] * S, f1[1] * S);
     o.z = bf16x2(f2[0] * S, f2[1] * S);
@@ -201,115 +303,120 @@ __global__ __launch_bounds__(kThreads) void k_fill_f32(float* p, int64_t n, floa
 
 // max |w| of each tensor, max-accumulated into its group slot (binary32 bits
 // of non-negative values order like unsigned integers).
-__global__ __launch_bounds__(kThreads) void k_amax(const lpq_tensor* table, lpq_tensor one, float* group_amax) {
-    const lpq_tensor d = load_desc(table, one);
+template <int U, bool GROUPED>
+__global__ __launch_bounds__(kThreads) void k_amax(const lpq_tensor* table, lpq_tensor one, ChunkMap map,
+                                                   float* group_amax) {
+    const Work W = locate<GROUPED>(table, one, map);
+    const lpq_tensor& d = W.d;
     const int64_t total = d.rows * d.cols;
-    const int64_t base = (int64_t)blockIdx.x * kAmaxChunk;
-    if (base >= total) return;
-    const uint4* src = reinterpret_cast<const uint4*>(d.src);
+    const int64_t base = W.unit * chunk_elems<U>();
+    const v4u* src = reinterpret_cast<const v4u*>(d.src);
     const int tid = threadIdx.x;
-    uint4 v[kAmaxUnroll];
+    v4u v[U];
 #pragma unroll
-    for (int u = 0; u < kAmaxUnroll; u++) {
+    for (int u = 0; u < U; u++) {
         const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
-        v[u] = e0 < total ? src[e0 >> 3] : make_uint4(0, 0, 0, 0);
+        v[u] = e0 < total ? load<kNTL>(src + (e0 >> 3)) : v4u{0, 0, 0, 0};
     }
     uint32_t m = 0;
 #pragma unroll
-    for (int u = 0; u < kAmaxUnroll; u++) m = umax(m, absmax8_bits(v[u]));
+    for (int u = 0; u < U; u++) m = umax(m, absmax8_bits(v[u]));
     m = wave_max(m);
     __shared__ uint32_t part[kThreads / 64];
     if ((tid & 63) == 0) part[tid >> 6] = m;
     __syncthreads();
     if (tid == 0) {
         uint32_t w = umax(umax(part[0], part[1]), umax(part[2], part[3]));
-        atomicMax(reinterpret_cast<unsigned int*>(group_amax + (table ? d.group : 0)), w);
+        atomicMax(reinterpret_cast<unsigned int*>(group_amax + (GROUPED ? d.group : 0)), w);
     }
 }
 
-__global__ __launch_bounds__(kThreads) void k_nvfp4_quant(const lpq_tensor* table, lpq_tensor one,
+template <int U, bool GROUPED>
+__global__ __launch_bounds__(kThreads) void k_nvfp4_quant(const lpq_tensor* table, lpq_tensor one, ChunkMap map,
                                                           const float* group_amax, float* group_g) {
-    const lpq_tensor d = load_desc(table, one);
+    const Work W = locate<GROUPED>(table, one, map);
+    const lpq_tensor& d = W.d;
     const int64_t total = d.rows * d.cols;
-    const int64_t base = (int64_t)blockIdx.x * kFlatChunk;
-    if (base >= total) return;
-    const int gi = table ? d.group : 0;
+    const int64_t base = W.unit * chunk_elems<U>();
+    const int gi = GROUPED ? d.group : 0;
     const GlobalScale G = global_scale(group_amax[gi]);
     const int tid = threadIdx.x;
-    if (blockIdx.x == 0 && tid == 0) group_g[gi] = G.g;   // same value from every member
-    const uint4* src = reinterpret_cast<const uint4*>(d.src);
+    if (W.unit == 0 && tid == 0) group_g[gi] = G.g;   // same value from every member
+    const v4u* src = reinterpret_cast<const v4u*>(d.src);
     uint32_t* dst = reinterpret_cast<uint32_t*>(d.dst);
     uint8_t* ssc = reinterpret_cast<uint8_t*>(d.scale);
 
-    uint4 v[kUnroll];
+    v4u v[U];
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
+    for (int u = 0; u < U; u++) {
         const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
-        v[u] = e0 < total ? src[e0 >> 3] : make_uint4(0, 0, 0, 0);
+        v[u] = e0 < total ? load<kNTL>(src + (e0 >> 3)) : v4u{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
+    for (int u = 0; u < U; u++) {
         const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
         const BlockScale B = block_scale(pair_max(absmax8_bits(v[u])), G);
         const uint32_t p = e2m1x8(v[u], B);
         if (e0 < total) {
-            dst[e0 >> 3] = p;
-            if ((tid & 1) == 0) ssc[e0 >> 4] = (uint8_t)B.code;
+            store<kNTS>(dst + (e0 >> 3), p);
+            if ((tid & 1) == 0) store_u8(ssc + (e0 >> 4), B.code);
         }
     }
 }
 
-__global__ __launch_bounds__(kThreads) void k_nvfp4_dequant(const lpq_tensor* table, lpq_tensor one,
+template <int U, bool GROUPED>
+__global__ __launch_bounds__(kThreads) void k_nvfp4_dequant(const lpq_tensor* table, lpq_tensor one, ChunkMap map,
                                                             const float* group_g) {
-    const lpq_tensor d = load_desc(table, one);
+    const Work W = locate<GROUPED>(table, one, map);
+    const lpq_tensor& d = W.d;
     const int64_t total = d.rows * d.cols;
-    const int64_t base = (int64_t)blockIdx.x * kFlatChunk;
-    if (base >= total) return;
-    const float g = group_g[table ? d.group : 0];
+    const int64_t base = W.unit * chunk_elems<U>();
+    const float g = group_g[GROUPED ? d.group : 0];
     const uint32_t* src = reinterpret_cast<const uint32_t*>(d.src);
     const uint8_t* ssc = reinterpret_cast<const uint8_t*>(d.scale);
-    uint4* dst = reinterpret_cast<uint4*>(d.dst);
+    v4u* dst = reinterpret_cast<v4u*>(d.dst);
     const int tid = threadIdx.x;
 
-    uint32_t p[kUnroll], sb[kUnroll];
+    uint32_t p[U], sb[U];
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
+    for (int u = 0; u < U; u++) {
         const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
-        p[u] = e0 < total ? src[e0 >> 3] : 0u;
-        sb[u] = e0 < total ? ssc[e0 >> 4] : 0u;
+        p[u] = e0 < total ? load<kNTL>(src + (e0 >> 3)) : 0u;
+        sb[u] = e0 < total ? load_u8(ssc + (e0 >> 4)) : 0u;
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
+    for (int u = 0; u < U; u++) {
         const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
         const float S = e4m3_to_f32(sb[u]) * g;
-        const uint4 o = e2m1x8_to_bf16(p[u], S);
-        if (e0 < total) dst[e0 >> 3] = o;
+        const v4u o = e2m1x8_to_bf16(p[u], S);
+        if (e0 < total) store<kNTS>(dst + (e0 >> 3), o);
     }
 }
 
-__global__ __launch_bounds__(kThreads) void k_nvfp4_qdq(const lpq_tensor* table, lpq_tensor one,
+template <int U, bool GROUPED>
+__global__ __launch_bounds__(kThreads) void k_nvfp4_qdq(const lpq_tensor* table, lpq_tensor one, ChunkMap map,
                                                         const float* group_amax) {
-    const lpq_tensor d = load_desc(table, one);
+    const Work W = locate<GROUPED>(table, one, map);
+    const lpq_tensor& d = W.d;
     const int64_t total = d.rows * d.cols;
-    const int64_t base = (int64_t)blockIdx.x * kFlatChunk;
-    if (base >= total) return;
-    const GlobalScale G = global_scale(group_amax[table ? d.group : 0]);
-    const uint4* src = reinterpret_cast<const uint4*>(d.src);
-    uint4* dst = reinterpret_cast<uint4*>(d.dst);
+    const int64_t base = W.unit * chunk_elems<U>();
+    const GlobalScale G = global_scale(group_amax[GROUPED ? d.group : 0]);
+    const v4u* src = reinterpret_cast<const v4u*>(d.src);
+    v4u* dst = reinterpret_cast<v4u*>(d.dst);
     const int tid = threadIdx.x;
 
-    uint4 v[kUnroll];
+    v4u v[U];
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
+    for (int u = 0; u < U; u++) {
         const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
-        v[u] = e0 < total ? src[e0 >> 3] : make_uint4(0, 0, 0, 0);
+        v[u] = e0 < total ? load<kNTL>(src + (e0 >> 3)) : v4u{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
+    for (int u = 0; u < U; u++) {
         const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
         const BlockScale B = block_scale(pair_max(absmax8_bits(v[u])), G);
-        const uint4 o = e2m1x8_to_bf16(e2m1x8(v[u], B), B.S);
-        if (e0 < total) dst[e0 >> 3] = o;
+        const v4u o = e2m1x8_to_bf16(e2m1x8(v[u], B), B.S);
+        if (e0 < total) store<kNTS>(dst + (e0 >> 3), o);
     }
 }
 
@@ -318,15 +425,24 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_qdq(const lpq_tensor* table,
 // ---------------------------------------------------------------------------
 
 // Lane layout inside a tile: lane t covers columns 8*(t%16) .. +8 of rows
-// 16*pass + t/16, pass = 0..7.
+// R*pass + t/16, R = TT/16 rows per pass for TT threads.
+template <int TT>
+struct TileShape {
+    static constexpr int rows_per_pass = TT / 16;
+    static constexpr int passes = kTile / rows_per_pass;
+    static constexpr int waves = TT / 64;
+};
+
 struct TileGeom {
     int64_t r0, c0, rows, cols;   // tile origin and clipped extent
+    int64_t index;                // position in the [ceil(M/128), ceil(N/128)] scale grid
     bool fast;                    // full tile and 16-byte aligned rows
 };
 
 __device__ __forceinline__ TileGeom tile_geom(const lpq_tensor& d, int64_t tile) {
     const int64_t tn = (d.cols + kTile - 1) / kTile;
     TileGeom T;
+    T.index = tile;
     T.r0 = (tile / tn) * kTile;
     T.c0 = (tile % tn) * kTile;
     T.rows = d.rows - T.r0 < kTile ? d.rows - T.r0 : kTile;
@@ -336,61 +452,64 @@ __device__ __forceinline__ TileGeom tile_geom(const lpq_tensor& d, int64_t tile)
     return T;
 }
 
-__global__ __launch_bounds__(kThreads) void k_fp8blk_quant(const lpq_tensor* table, lpq_tensor one) {
-    const lpq_tensor d = load_desc(table, one);
-    const int64_t tiles = ((d.rows + kTile - 1) / kTile) * ((d.cols + kTile - 1) / kTile);
-    const int64_t tile = blockIdx.x;
-    if (tile >= tiles) return;
-    const TileGeom T = tile_geom(d, tile);
+template <int TT>
+__device__ __forceinline__ uint32_t block_reduce_max(uint32_t m) {
+    m = wave_max(m);
+    __shared__ uint32_t part[TileShape<TT>::waves];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+    __syncthreads();
+    uint32_t r = part[0];
+#pragma unroll
+    for (int k = 1; k < TileShape<TT>::waves; k++) r = umax(r, part[k]);
+    return r;
+}
+
+template <int TT, bool GROUPED>
+__global__ __launch_bounds__(TT) void k_fp8blk_quant(const lpq_tensor* table, lpq_tensor one, ChunkMap map) {
+    const Work W = locate<GROUPED>(table, one, map);
+    const lpq_tensor& d = W.d;
+    const TileGeom T = tile_geom(d, W.unit);
     const uint16_t* w = reinterpret_cast<const uint16_t*>(d.src);
     uint8_t* q = reinterpret_cast<uint8_t*>(d.dst);
     const int tid = threadIdx.x;
     const int lr = tid >> 4;           // row inside a pass
     const int lc = (tid & 15) * 8;     // first column of the lane's segment
 
-    uint4 v[8];
+    v4u v[TileShape<TT>::passes];
     if (T.fast) {
 #pragma unroll
-        for (int p = 0; p < 8; p++) {
-            const int64_t off = (T.r0 + 16 * p + lr) * d.cols + T.c0 + lc;
-            v[p] = *reinterpret_cast<const uint4*>(w + off);
+        for (int p = 0; p < TileShape<TT>::passes; p++) {
+            const int64_t off = (T.r0 + TileShape<TT>::rows_per_pass * p + lr) * d.cols + T.c0 + lc;
+            v[p] = load<kNTL>(reinterpret_cast<const v4u*>(w + off));
         }
     } else {
-        for (int p = 0; p < 8; p++) {
-            const int64_t r = 16 * p + lr;
+        for (int p = 0; p < TileShape<TT>::passes; p++) {
+            const int64_t r = TileShape<TT>::rows_per_pass * p + lr;
             uint32_t h[8];
             for (int k = 0; k < 8; k++) {
                 const bool in = r < T.rows && lc + k < T.cols;
                 h[k] = in ? w[(T.r0 + r) * d.cols + T.c0 + lc + k] : 0u;
             }
-            v[p] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+            v[p] = v4u{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
         }
     }
     uint32_t m = 0;
 #pragma unroll
-    for (int p = 0; p < 8; p++) m = umax(m, absmax8_bits(v[p]));
-    m = wave_max(m);
-    __shared__ uint32_t part[kThreads / 64];
-    if ((tid & 63) == 0) part[tid >> 6] = m;
-    __syncthreads();
-    const float amax = __uint_as_float(umax(umax(part[0], part[1]), umax(part[2], part[3])));
+    for (int p = 0; p < TileShape<TT>::passes; p++) m = umax(m, absmax8_bits(v[p]));
+    const float amax = __uint_as_float(block_reduce_max<TT>(m));
     const float s = amax / kE4M3Max;   // correctly rounded division
-    if (tid == 0) {
-        const int64_t tn = (d.cols + kTile - 1) / kTile;
-        reinterpret_cast<float*>(d.scale)[(T.r0 / kTile) * tn + T.c0 / kTile] = s;
-    }
+    if (tid == 0) reinterpret_cast<float*>(d.scale)[T.index] = s;
     const bool tiny = s > 0.0f && s < kTinyScale;
     const float sd = tiny ? s * kPreScale : s;
     const float r = s > 0.0f ? rcp_rn(sd) : 0.0f;
-    const float xpre = tiny ? kPreScale : 1.0f;
 
 #pragma unroll
-    for (int p = 0; p < 8; p++) {
+    for (int p = 0; p < TileShape<TT>::passes; p++) {
         float x[8] = {bf16_lo(v[p].x), bf16_hi(v[p].x), bf16_lo(v[p].y), bf16_hi(v[p].y),
                       bf16_lo(v[p].z), bf16_hi(v[p].z), bf16_lo(v[p].w), bf16_hi(v[p].w)};
         if (tiny) {
 #pragma unroll
-            for (int k = 0; k < 8; k++) x[k] *= xpre;
+            for (int k = 0; k < 8; k++) x[k] *= kPreScale;
         }
         float qq[8];
 #pragma unroll
@@ -399,61 +518,59 @@ __global__ __launch_bounds__(kThreads) void k_fp8blk_quant(const lpq_tensor* tab
         lo = e4m3x2<true>(qq[2], qq[3], lo);
         uint32_t hi = e4m3x2<false>(qq[4], qq[5], 0u);
         hi = e4m3x2<true>(qq[6], qq[7], hi);
-        const int64_t r = 16 * p + lr;
+        const int64_t row = TileShape<TT>::rows_per_pass * p + lr;
         if (T.fast) {
-            *reinterpret_cast<uint2*>(q + (T.r0 + r) * d.cols + T.c0 + lc) = make_uint2(lo, hi);
-        } else if (r < T.rows) {
+            store<kNTS>(reinterpret_cast<v2u*>(q + (T.r0 + row) * d.cols + T.c0 + lc), v2u{lo, hi});
+        } else if (row < T.rows) {
             const uint32_t c8[2] = {lo, hi};
             for (int k = 0; k < 8; k++)
-                if (lc + k < T.cols) q[(T.r0 + r) * d.cols + T.c0 + lc + k] = (uint8_t)(c8[k >> 2] >> (8 * (k & 3)));
+                if (lc + k < T.cols) q[(T.r0 + row) * d.cols + T.c0 + lc + k] = (uint8_t)(c8[k >> 2] >> (8 * (k & 3)));
         }
     }
 }
 
-__global__ __launch_bounds__(kThreads) void k_fp8blk_dequant(const lpq_tensor* table, lpq_tensor one) {
-    const lpq_tensor d = load_desc(table, one);
-    const int64_t tn = (d.cols + kTile - 1) / kTile;
-    const int64_t tiles = ((d.rows + kTile - 1) / kTile) * tn;
-    const int64_t tile = blockIdx.x;
-    if (tile >= tiles) return;
-    const TileGeom T = tile_geom(d, tile);
+template <int TT, bool GROUPED>
+__global__ __launch_bounds__(TT) void k_fp8blk_dequant(const lpq_tensor* table, lpq_tensor one, ChunkMap map) {
+    const Work W = locate<GROUPED>(table, one, map);
+    const lpq_tensor& d = W.d;
+    const TileGeom T = tile_geom(d, W.unit);
     const uint8_t* q = reinterpret_cast<const uint8_t*>(d.src);
     uint16_t* y = reinterpret_cast<uint16_t*>(d.dst);
-    const float s = reinterpret_cast<const float*>(d.scale)[(T.r0 / kTile) * tn + T.c0 / kTile];
+    const float s = reinterpret_cast<const float*>(d.scale)[T.index];
     const int tid = threadIdx.x;
     const int lr = tid >> 4;
     const int lc = (tid & 15) * 8;
 
-    uint2 c[8];
+    v2u c[TileShape<TT>::passes];
     if (T.fast) {
 #pragma unroll
-        for (int p = 0; p < 8; p++)
-            c[p] = *reinterpret_cast<const uint2*>(q + (T.r0 + 16 * p + lr) * d.cols + T.c0 + lc);
+        for (int p = 0; p < TileShape<TT>::passes; p++)
+            c[p] = load<kNTL>(reinterpret_cast<const v2u*>(q + (T.r0 + TileShape<TT>::rows_per_pass * p + lr) * d.cols + T.c0 + lc));
     } else {
-        for (int p = 0; p < 8; p++) {
-            const int64_t r = 16 * p + lr;
+        for (int p = 0; p < TileShape<TT>::passes; p++) {
+            const int64_t r = TileShape<TT>::rows_per_pass * p + lr;
             uint32_t b[8];
             for (int k = 0; k < 8; k++) {
                 const bool in = r < T.rows && lc + k < T.cols;
                 b[k] = in ? q[(T.r0 + r) * d.cols + T.c0 + lc + k] : 0u;
             }
-            c[p] = make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24), b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
+            c[p] = v2u{b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24), b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24)};
         }
     }
 #pragma unroll
-    for (int p = 0; p < 8; p++) {
+    for (int p = 0; p < TileShape<TT>::passes; p++) {
         const float2_t f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[p].x, false);
         const float2_t f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[p].x, true);
         const float2_t f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[p].y, false);
         const float2_t f3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[p].y, true);
-        uint4 o;
+        v4u o;
         o.x = bf16x2(f0[0] * s, f0[1] * s);
         o.y = bf16x2(f1[0] * s, f1[1] * s);
         o.z = bf16x2(f2[0] * s, f2[1] * s);
         o.w = bf16x2(f3[0] * s, f3[1] * s);
-        const int64_t r = 16 * p + lr;
+        const int64_t r = TileShape<TT>::rows_per_pass * p + lr;
         if (T.fast) {
-            *reinterpret_cast<uint4*>(y + (T.r0 + r) * d.cols + T.c0 + lc) = o;
+            store<kNTS>(reinterpret_cast<v4u*>(y + (T.r0 + r) * d.cols + T.c0 + lc), o);
         } else if (r < T.rows) {
             const uint32_t h[4] = {o.x, o.y, o.z, o.w};
             for (int k = 0; k < 8; k++)
@@ -471,8 +588,6 @@ __global__ __launch_bounds__(kThreads) void k_fp8blk_dequant(const lpq_tensor* t
 namespace {
 
 thread_local int g_last_hip_error = 0;
-
-constexpr int kMaxGridY = 65535;
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -499,7 +614,6 @@ lpq_status check_tensor(Kind k, const lpq_tensor& t, int32_t n_groups) {
     case FP8BLK_Q:
     case FP8BLK_DQ:
         if (!aligned(k == FP8BLK_Q ? t.src : t.dst, 2) || !aligned(t.scale, 4)) return LPQ_ERR_ALIGN;
-        if ((t.rows + kTile - 1) / kTile * ((t.cols + kTile - 1) / kTile) > INT32_MAX) return LPQ_ERR_SHAPE;
         break;
     case MXFP8_Q:
         if (t.cols % 32) return LPQ_ERR_SHAPE;
@@ -523,48 +637,80 @@ lpq_status check_tensor(Kind k, const lpq_tensor& t, int32_t n_groups) {
     return LPQ_OK;
 }
 
-int64_t grid_x(Kind k, const lpq_tensor& t) {
+// Work units (workgroups) of one tensor.
+int64_t units(Kind k, const lpq_tensor& t) {
+    const int64_t n = t.rows * t.cols;
     switch (k) {
     case FP8BLK_Q:
-    case FP8BLK_DQ:
-        return ((t.rows + kTile - 1) / kTile) * ((t.cols + kTile - 1) / kTile);
-    case NV_AMAX:
-        return (t.rows * t.cols + kAmaxChunk - 1) / kAmaxChunk;
-    default:
-        return (t.rows * t.cols + kFlatChunk - 1) / kFlatChunk;
+    case FP8BLK_DQ: return ((t.rows + kTile - 1) / kTile) * ((t.cols + kTile - 1) / kTile);
+    case MXFP8_Q: return (n + chunk_elems<LPQ_MXQ_U>() - 1) / chunk_elems<LPQ_MXQ_U>();
+    case MXFP8_DQ: return (n + chunk_elems<LPQ_MXD_U>() - 1) / chunk_elems<LPQ_MXD_U>();
+    case NV_AMAX: return (n + chunk_elems<LPQ_AMAX_U>() - 1) / chunk_elems<LPQ_AMAX_U>();
+    case NV_Q: return (n + chunk_elems<LPQ_NVQ_U>() - 1) / chunk_elems<LPQ_NVQ_U>();
+    case NV_DQ: return (n + chunk_elems<LPQ_NVD_U>() - 1) / chunk_elems<LPQ_NVD_U>();
+    case NV_QDQ: return (n + chunk_elems<LPQ_QDQ_U>() - 1) / chunk_elems<LPQ_QDQ_U>();
     }
+    return 0;
 }
 
-// One launch of kernel `k` for a single tensor (table == nullptr) or for the
-// tensors dev[0..n) (in slices of at most 65535 along grid.y).
+constexpr int64_t kMaxGridX = 0x7fffffffLL;
+
+// Launch kernel `k` over tensors [0, n) of `host`/`dev` (single tensor: dev ==
+// nullptr, `one` used), in slices of at most kMaxSeg segments and 2^31-1 work
+// units.
 lpq_status launch(Kind k, const lpq_tensor* host, const lpq_tensor* dev, int32_t n, const lpq_tensor& one,
                   const float* fa, float* fb, hipStream_t stream) {
-    int64_t gx = 0;
-    if (dev) {
-        for (int32_t i = 0; i < n; i++) {
-            int64_t x = grid_x(k, host[i]);
-            if (x > gx) gx = x;
+    const int32_t count = dev ? n : 1;
+    int32_t i0 = 0;
+    while (i0 < count) {
+        ChunkMap map = {};
+        int64_t total = 0;
+        int32_t nseg = 0, i = i0;
+        while (i < count) {
+            const int64_t u = units(k, dev ? host[i] : one);
+            if (u > kMaxGridX) return LPQ_ERR_SHAPE;
+            if (total + u > kMaxGridX) break;
+            if (nseg == 0 || (int64_t)map.units[nseg - 1] != u) {
+                if (nseg == kMaxSeg) break;
+                map.first[nseg] = (uint32_t)total;
+                map.tensor0[nseg] = (uint32_t)(i - i0);
+                map.units[nseg] = (uint32_t)u;
+                map.inv_units[nseg] = 1.0 / (double)u;
+                nseg++;
+            }
+            total += u;
+            i++;
         }
-    } else {
-        gx = grid_x(k, one);
-    }
-    if (gx > INT32_MAX) return LPQ_ERR_SHAPE;
-    for (int32_t i0 = 0; i0 < (dev ? n : 1); i0 += kMaxGridY) {
-        const int32_t ny = dev ? (n - i0 < kMaxGridY ? n - i0 : kMaxGridY) : 1;
+        map.nseg = nseg;
         const lpq_tensor* tab = dev ? dev + i0 : nullptr;
-        dim3 grid((unsigned)gx, (unsigned)ny), block(kThreads);
-        switch (k) {
-        case FP8BLK_Q: hipLaunchKernelGGL(k_fp8blk_quant, grid, block, 0, stream, tab, one); break;
-        case FP8BLK_DQ: hipLaunchKernelGGL(k_fp8blk_dequant, grid, block, 0, stream, tab, one); break;
-        case MXFP8_Q: hipLaunchKernelGGL(k_mxfp8_quant, grid, block, 0, stream, tab, one); break;
-        case MXFP8_DQ: hipLaunchKernelGGL(k_mxfp8_dequant, grid, block, 0, stream, tab, one); break;
-        case NV_AMAX: hipLaunchKernelGGL(k_amax, grid, block, 0, stream, tab, one, fb); break;
-        case NV_Q: hipLaunchKernelGGL(k_nvfp4_quant, grid, block, 0, stream, tab, one, fa, fb); break;
-        case NV_DQ: hipLaunchKernelGGL(k_nvfp4_dequant, grid, block, 0, stream, tab, one, fa); break;
-        case NV_QDQ: hipLaunchKernelGGL(k_nvfp4_qdq, grid, block, 0, stream, tab, one, fa); break;
+        const dim3 grid((unsigned)total);
+        const dim3 flat(kThreads), tileq(LPQ_TILEQ_THREADS), tiled(LPQ_TILED_THREADS);
+        if (dev) {
+            switch (k) {
+            case FP8BLK_Q: hipLaunchKernelGGL((k_fp8blk_quant<LPQ_TILEQ_THREADS, true>), grid, tileq, 0, stream, tab, one, map); break;
+            case FP8BLK_DQ: hipLaunchKernelGGL((k_fp8blk_dequant<LPQ_TILED_THREADS, true>), grid, tiled, 0, stream, tab, one, map); break;
+            case MXFP8_Q: hipLaunchKernelGGL((k_mxfp8_quant<LPQ_MXQ_U, true>), grid, flat, 0, stream, tab, one, map); break;
+            case MXFP8_DQ: hipLaunchKernelGGL((k_mxfp8_dequant<LPQ_MXD_U, true>), grid, flat, 0, stream, tab, one, map); break;
+            case NV_AMAX: hipLaunchKernelGGL((k_amax<LPQ_AMAX_U, true>), grid, flat, 0, stream, tab, one, map, fb); break;
+            case NV_Q: hipLaunchKernelGGL((k_nvfp4_quant<LPQ_NVQ_U, true>), grid, flat, 0, stream, tab, one, map, fa, fb); break;
+            case NV_DQ: hipLaunchKernelGGL((k_nvfp4_dequant<LPQ_NVD_U, true>), grid, flat, 0, stream, tab, one, map, fa); break;
+            case NV_QDQ: hipLaunchKernelGGL((k_nvfp4_qdq<LPQ_QDQ_U, true>), grid, flat, 0, stream, tab, one, map, fa); break;
+            }
+        } else {
+            switch (k) {
+            case FP8BLK_Q: hipLaunchKernelGGL((k_fp8blk_quant<LPQ_TILEQ_THREADS, false>), grid, tileq, 0, stream, tab, one, map); break;
+            case FP8BLK_DQ: hipLaunchKernelGGL((k_fp8blk_dequant<LPQ_TILED_THREADS, false>), grid, tiled, 0, stream, tab, one, map); break;
+            case MXFP8_Q: hipLaunchKernelGGL((k_mxfp8_quant<LPQ_MXQ_U, false>), grid, flat, 0, stream, tab, one, map); break;
+            case MXFP8_DQ: hipLaunchKernelGGL((k_mxfp8_dequant<LPQ_MXD_U, false>), grid, flat, 0, stream, tab, one, map); break;
+            case NV_AMAX: hipLaunchKernelGGL((k_amax<LPQ_AMAX_U, false>), grid, flat, 0, stream, tab, one, map, fb); break;
+            case NV_Q: hipLaunchKernelGGL((k_nvfp4_quant<LPQ_NVQ_U, false>), grid, flat, 0, stream, tab, one, map, fa, fb); break;
+            case NV_DQ: hipLaunchKernelGGL((k_nvfp4_dequant<LPQ_NVD_U, false>), grid, flat, 0, stream, tab, one, map, fa); break;
+            case NV_QDQ: hipLaunchKernelGGL((k_nvfp4_qdq<LPQ_QDQ_U, false>), grid, flat, 0, stream, tab, one, map, fa); break;
+            }
         }
         lpq_status st = launched();
         if (st != LPQ_OK) return st;
+        i0 = i;
     }
     return LPQ_OK;
 }
