@@ -192,7 +192,8 @@ def summarize_pmc(path: str) -> None:
             rows += list(csv.DictReader(fh))
     acc = {}
     for r in rows:
-        name = re.sub(r"\(.*", "", r.get("Kernel_Name", "?")).replace("(anonymous namespace)::", "")
+        name = r.get("Kernel_Name", "?").replace("(anonymous namespace)::", "").replace("void ", "")
+        name = re.sub(r"\(.*", "", name)
         key = (name, r.get("Grid_Size", "?"), r.get("Counter_Name", "?"))
         d = acc.setdefault(key, [0, 0.0, set()])
         d[1] += float(r.get("Counter_Value", 0))
