@@ -99,12 +99,17 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
     return __builtin_amdgcn_cvt_pk_f32_fp8((int)code, false)[0];
 }
 
-// Packed pair of BF16 (low = a) from two binary32 values, nearest even.
+// Packed pair of BF16 (low = a) from two binary32 values, nearest even: one
+// v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t bf16x2(float a, float b) {
-    uint32_t ua = __builtin_bit_cast(uint16_t, __float2bfloat16(a));
-    uint32_t ub = __builtin_bit_cast(uint16_t, __float2bfloat16(b));
-    return ua | (ub << 16);
+    const float2_t f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
+
+// True for the whole wave when any active lane has `p` (a wave-uniform branch
+// condition for rare slow paths).
+__device__ __forceinline__ bool any_lane(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
 // Maximum of two non-negative binary32 values through their bit patterns.
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
@@ -117,6 +122,27 @@ __device__ __forceinline__ uint32_t absmax8_bits(const v4u& v) {
     uint32_t m0 = umax(umax(a & 0xffffu, a >> 16), umax(b & 0xffffu, b >> 16));
     uint32_t m1 = umax(umax(c & 0xffffu, c >> 16), umax(d & 0xffffu, d >> 16));
     return umax(m0, m1) << 16;
+}
+
+// The 8 BF16 values of a 16-byte vector widened to binary32 (exact).
+struct F8 {
+    float x[8];
+};
+__device__ __forceinline__ F8 widen8(const v4u& v) {
+    F8 f;
+    f.x[0] = bf16_lo(v.x); f.x[1] = bf16_hi(v.x); f.x[2] = bf16_lo(v.y); f.x[3] = bf16_hi(v.y);
+    f.x[4] = bf16_lo(v.z); f.x[5] = bf16_hi(v.z); f.x[6] = bf16_lo(v.w); f.x[7] = bf16_hi(v.w);
+    return f;
+}
+
+// max |x| of 8 widened values as binary32 bits (three-input maximum with
+// absolute-value operands: 4 instructions).
+__device__ __forceinline__ uint32_t absmax8_f32(const F8& f) {
+    float m = fmaxf(fmaxf(fabsf(f.x[0]), fabsf(f.x[1])), fabsf(f.x[2]));
+    m = fmaxf(fmaxf(m, fabsf(f.x[3])), fabsf(f.x[4]));
+    m = fmaxf(fmaxf(m, fabsf(f.x[5])), fabsf(f.x[6]));
+    m = fmaxf(m, fabsf(f.x[7]));
+    return __float_as_uint(m);
 }
 
 // Cross-lane maxima inside groups of 2 / 4 lanes (DPP quad permutations).

@@ -49,7 +49,7 @@
 #define LPQ_QDQ_U 2
 #endif
 #ifndef LPQ_AMAX_U
-#define LPQ_AMAX_U 16
+#define LPQ_AMAX_U 32
 #endif
 #ifndef LPQ_TILEQ_THREADS
 #define LPQ_TILEQ_THREADS 256
@@ -76,6 +76,24 @@ constexpr int kMaxSeg = 8;               // segments per launch (longer lists ar
 
 template <int U>
 constexpr int64_t chunk_elems() { return (int64_t)kThreads * 8 * U; }
+
+// Loads the lane's U vectors of a flat chunk: lane t of vector u holds the 8
+// elements starting at base + (u * kThreads + t) * 8.  A full chunk (the
+// common case) loads without per-lane bounds checks.
+template <int U, typename T>
+__device__ __forceinline__ void load_chunk(T (&v)[U], const T* src, int64_t base, int64_t total, bool full) {
+    const T* p = src + (base >> 3) + threadIdx.x;
+    if (full) {
+#pragma unroll
+        for (int u = 0; u < U; u++) v[u] = load<kNTL>(p + u * kThreads);
+    } else {
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int64_t e0 = base + (int64_t)(u * kThreads + threadIdx.x) * 8;
+            v[u] = e0 < total ? load<kNTL>(p + u * kThreads) : T{};
+        }
+    }
+}
 
 // Dense work map of one launch.  Consecutive tensors with the same number of
 // work units form a segment: segment s starts at work unit first[s] and at
@@ -156,24 +174,23 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_quant(const lpq_tensor* tabl
     uint8_t* esc = reinterpret_cast<uint8_t*>(d.scale);
     const int tid = threadIdx.x;
 
+    // every chunk but the last of a tensor is full: no per-lane bounds checks
+    const bool full = base + chunk_elems<U>() <= total;
     v4u v[U];
-#pragma unroll
-    for (int u = 0; u < U; u++) {
-        const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
-        v[u] = e0 < total ? load<kNTL>(src + (e0 >> 3)) : v4u{0, 0, 0, 0};
-    }
+    load_chunk<U>(v, src, base, total, full);
 #pragma unroll
     for (int u = 0; u < U; u++) {
         const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
         // a quad of lanes is one 32-element block; blocks never straddle the end
-        const uint32_t amax = quad_max(absmax8_bits(v[u]));
+        const F8 f = widen8(v[u]);
+        const uint32_t amax = quad_max(absmax8_f32(f));
         const uint32_t byte = mx_scale_byte(amax);
         const float X = ue8m0_operand(byte);
-        short2_t c01 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((short2_t){0, 0}, bf16_lo(v[u].x), bf16_hi(v[u].x), X, false);
-        c01 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c01, bf16_lo(v[u].y), bf16_hi(v[u].y), X, true);
-        short2_t c23 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((short2_t){0, 0}, bf16_lo(v[u].z), bf16_hi(v[u].z), X, false);
-        c23 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c23, bf16_lo(v[u].w), bf16_hi(v[u].w), X, true);
-        if (e0 < total) {
+        short2_t c01 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((short2_t){0, 0}, f.x[0], f.x[1], X, false);
+        c01 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c01, f.x[2], f.x[3], X, true);
+        short2_t c23 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((short2_t){0, 0}, f.x[4], f.x[5], X, false);
+        c23 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c23, f.x[6], f.x[7], X, true);
+        if (full || e0 < total) {
             store<kNTS>(dst + (e0 >> 3), v2u{__builtin_bit_cast(uint32_t, c01), __builtin_bit_cast(uint32_t, c23)});
             if ((tid & 3) == 0) store_u8(esc + (e0 >> 5), byte);
         }
@@ -191,13 +208,14 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_dequant(const lpq_tensor* ta
     const uint8_t* esc = reinterpret_cast<const uint8_t*>(d.scale);
     const int tid = threadIdx.x;
 
+    const bool full = base + chunk_elems<U>() <= total;
     v2u c[U];
     uint32_t b[U];
+    load_chunk<U>(c, src, base, total, full);
 #pragma unroll
     for (int u = 0; u < U; u++) {
         const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
-        c[u] = e0 < total ? load<kNTL>(src + (e0 >> 3)) : v2u{0, 0};
-        b[u] = e0 < total ? load_u8(esc + (e0 >> 5)) : 127u;
+        b[u] = (full || e0 < total) ? load_u8(esc + (e0 >> 5)) : 127u;
     }
 #pragma unroll
     for (int u = 0; u < U; u++) {
@@ -208,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_dequant(const lpq_tensor* ta
         o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[u].x, X, true));
         o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[u].y, X, false));
         o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[u].y, X, true));
-        if (e0 < total) store<kNTS>(dst + (e0 >> 3), o);
+        if (full || e0 < total) store<kNTS>(dst + (e0 >> 3), o);
     }
 }
 
@@ -251,7 +269,9 @@ __device__ __forceinline__ BlockScale block_scale(uint32_t bmax_bits, const Glob
     // fl(b / 6): the short sequence is exact while the quotient is normal;
     // tinier blocks take the full correctly rounded division.
     float t6 = quot_rn(b, 6.0f, kRcp6);
-    if (b < 0x1p-100f) t6 = b / 6.0f;
+    if (any_lane(b < 0x1p-100f)) {
+        if (b < 0x1p-100f) t6 = b / 6.0f;
+    }
     const float t = t6 * G.tpre;                             // maybe pre-scaled by 2^64
     const float u = quot_rn(t, G.gd, G.rg);                  // fl(fl(b / 6) / g)
     B.code = G.g > 0.0f ? (e4m3x2<false>(u, 0.0f, 0u) & 0xffu) : 0u;
@@ -264,12 +284,13 @@ __device__ __forceinline__ BlockScale block_scale(uint32_t bmax_bits, const Glob
 }
 
 // 8 BF16 values -> 8 E2M1 codes (one 32-bit word, element 0 in the low nibble).
-__device__ __forceinline__ uint32_t e2m1x8(const v4u& v, const BlockScale& B) {
-    float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                  bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-    if (B.xpre != 1.0f) {
+__device__ __forceinline__ uint32_t e2m1x8(const F8& f, const BlockScale& B) {
+    float x[8];
 #pragma unroll
-        for (int k = 0; k < 8; k++) x[k] *= kPreScale;
+    for (int k = 0; k < 8; k++) x[k] = f.x[k];
+    if (any_lane(B.xpre != 1.0f)) {
+#pragma unroll
+        for (int k = 0; k < 8; k++) x[k] *= B.xpre;
     }
     float q[8];
 #pragma unroll
@@ -312,12 +333,10 @@ __global__ __launch_bounds__(kThreads) void k_amax(const lpq_tensor* table, lpq_
     const int64_t base = W.unit * chunk_elems<U>();
     const v4u* src = reinterpret_cast<const v4u*>(d.src);
     const int tid = threadIdx.x;
+    // every chunk but the last of a tensor is full: no per-lane bounds checks
+    const bool full = base + chunk_elems<U>() <= total;
     v4u v[U];
-#pragma unroll
-    for (int u = 0; u < U; u++) {
-        const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
-        v[u] = e0 < total ? load<kNTL>(src + (e0 >> 3)) : v4u{0, 0, 0, 0};
-    }
+    load_chunk<U>(v, src, base, total, full);
     uint32_t m = 0;
 #pragma unroll
     for (int u = 0; u < U; u++) m = umax(m, absmax8_bits(v[u]));
@@ -346,18 +365,17 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_quant(const lpq_tensor* tabl
     uint32_t* dst = reinterpret_cast<uint32_t*>(d.dst);
     uint8_t* ssc = reinterpret_cast<uint8_t*>(d.scale);
 
+    // every chunk but the last of a tensor is full: no per-lane bounds checks
+    const bool full = base + chunk_elems<U>() <= total;
     v4u v[U];
+    load_chunk<U>(v, src, base, total, full);
 #pragma unroll
     for (int u = 0; u < U; u++) {
         const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
-        v[u] = e0 < total ? load<kNTL>(src + (e0 >> 3)) : v4u{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < U; u++) {
-        const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
-        const BlockScale B = block_scale(pair_max(absmax8_bits(v[u])), G);
-        const uint32_t p = e2m1x8(v[u], B);
-        if (e0 < total) {
+        const F8 f = widen8(v[u]);
+        const BlockScale B = block_scale(pair_max(absmax8_f32(f)), G);
+        const uint32_t p = e2m1x8(f, B);
+        if (full || e0 < total) {
             store<kNTS>(dst + (e0 >> 3), p);
             if ((tid & 1) == 0) store_u8(ssc + (e0 >> 4), B.code);
         }
@@ -377,19 +395,20 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_dequant(const lpq_tensor* ta
     v4u* dst = reinterpret_cast<v4u*>(d.dst);
     const int tid = threadIdx.x;
 
+    const bool full = base + chunk_elems<U>() <= total;
     uint32_t p[U], sb[U];
+    load_chunk<U>(p, src, base, total, full);
 #pragma unroll
     for (int u = 0; u < U; u++) {
         const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
-        p[u] = e0 < total ? load<kNTL>(src + (e0 >> 3)) : 0u;
-        sb[u] = e0 < total ? load_u8(ssc + (e0 >> 4)) : 0u;
+        sb[u] = (full || e0 < total) ? load_u8(ssc + (e0 >> 4)) : 0u;
     }
 #pragma unroll
     for (int u = 0; u < U; u++) {
         const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
         const float S = e4m3_to_f32(sb[u]) * g;
         const v4u o = e2m1x8_to_bf16(p[u], S);
-        if (e0 < total) store<kNTS>(dst + (e0 >> 3), o);
+        if (full || e0 < total) store<kNTS>(dst + (e0 >> 3), o);
     }
 }
 
@@ -405,18 +424,17 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_qdq(const lpq_tensor* table,
     v4u* dst = reinterpret_cast<v4u*>(d.dst);
     const int tid = threadIdx.x;
 
+    // every chunk but the last of a tensor is full: no per-lane bounds checks
+    const bool full = base + chunk_elems<U>() <= total;
     v4u v[U];
+    load_chunk<U>(v, src, base, total, full);
 #pragma unroll
     for (int u = 0; u < U; u++) {
         const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
-        v[u] = e0 < total ? load<kNTL>(src + (e0 >> 3)) : v4u{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < U; u++) {
-        const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
-        const BlockScale B = block_scale(pair_max(absmax8_bits(v[u])), G);
-        const v4u o = e2m1x8_to_bf16(e2m1x8(v[u], B), B.S);
-        if (e0 < total) store<kNTS>(dst + (e0 >> 3), o);
+        const F8 f = widen8(v[u]);
+        const BlockScale B = block_scale(pair_max(absmax8_f32(f)), G);
+        const v4u o = e2m1x8_to_bf16(e2m1x8(f, B), B.S);
+        if (full || e0 < total) store<kNTS>(dst + (e0 >> 3), o);
     }
 }
 
@@ -510,7 +528,7 @@ __global__ __launch_bounds__(TT) void k_fp8blk_quant(const lpq_tensor* table, lp
         if (tiny) {
 #pragma unroll
             for (int k = 0; k < 8; k++) x[k] *= kPreScale;
-        }
+        }   // tile-uniform
         float qq[8];
 #pragma unroll
         for (int k = 0; k < 8; k++) qq[k] = quot_rn(x[k], sd, r);
