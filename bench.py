@@ -280,6 +280,7 @@ def main():
         gbs = op.bytes / (ms / 1e3) / GB
         per_op[op.name] = {"ms": round(ms, 3), "GB/s": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
                            "launches": len(op.launches), "algorithmic_GB": round(op.bytes / GB, 3),
+                           "algorithmic_bytes": int(op.bytes),
                            "in_metric": op.counted}
         log(f"  {op.name:32s} {ms:8.3f} ms  {gbs:8.1f} GB/s  {100 * gbs / HBM_PEAK_GBS:5.1f}% of peak")
 

@@ -153,6 +153,9 @@ lpq_status lpq_nvfp4_qdq(const uint16_t* x, int64_t M, int64_t N, const float* a
  *   nvfp4_qdq_grouped           BF16           BF16              unused
  * `group` is the NVFP4 sibling-group index of the tensor (q/k/v share one,
  * gate/up share one, a lone tensor has its own); other formats ignore it.
+ * A call is split into one launch per run of up to 8 changes of tensor size:
+ * placing tensors of equal shape next to each other (e.g. all experts of a
+ * layer) keeps a call to a single launch.
  */
 typedef struct lpq_tensor {
     const void* src;

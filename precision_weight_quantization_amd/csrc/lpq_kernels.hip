@@ -54,6 +54,9 @@
 #ifndef LPQ_TILEQ_THREADS
 #define LPQ_TILEQ_THREADS 256
 #endif
+#ifndef LPQ_TILEQ_WAVES_PER_SIMD
+#define LPQ_TILEQ_WAVES_PER_SIMD 6
+#endif
 #ifndef LPQ_TILED_THREADS
 #define LPQ_TILED_THREADS 1024
 #endif
@@ -483,7 +486,7 @@ __device__ __forceinline__ uint32_t block_reduce_max(uint32_t m) {
 }
 
 template <int TT, bool GROUPED>
-__global__ __launch_bounds__(TT) void k_fp8blk_quant(const lpq_tensor* table, lpq_tensor one, ChunkMap map) {
+__global__ __launch_bounds__(TT, LPQ_TILEQ_WAVES_PER_SIMD) void k_fp8blk_quant(const lpq_tensor* table, lpq_tensor one, ChunkMap map) {
     const Work W = locate<GROUPED>(table, one, map);
     const lpq_tensor& d = W.d;
     const TileGeom T = tile_geom(d, W.unit);

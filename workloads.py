@@ -187,7 +187,11 @@ def nvfp4_ops(tag: str, ws: WeightSet, packed: Slab, sbytes: Slab, out: Slab, bu
     p = [packed.view(i, (s.M, s.N // 2), torch.uint8) for i, s in enumerate(specs)]
     sb = [sbytes.view(i, (s.M, s.N // 16), torch.uint8) for i, s in enumerate(specs)]
     y = [out.view(i, (s.M, s.N), torch.bfloat16) for i, s in enumerate(specs)]
-    ta, tq, tdq, tqdq = [], [], [], []
+    tq, tdq, tqdq = [], [], []
+    # the amax pre-pass covers the whole model in one grouped call; tensors of
+    # equal shape are put next to each other so that the call is one launch
+    by_shape = sorted(range(len(specs)), key=lambda i: (specs[i].M, specs[i].N, i))
+    tamax = lpq.TensorTable([(ws.w[i], None, None, specs[i].M, specs[i].N, specs[i].group) for i in by_shape])
     for idx in _buckets(ws, bucket):
         tq.append(lpq.TensorTable([(ws.w[i], p[i], sb[i], specs[i].M, specs[i].N, specs[i].group) for i in idx]))
         tdq.append(lpq.TensorTable([(p[i], y[i], sb[i], specs[i].M, specs[i].N, specs[i].group) for i in idx]))
@@ -197,8 +201,7 @@ def nvfp4_ops(tag: str, ws: WeightSet, packed: Slab, sbytes: Slab, out: Slab, bu
     # the amax pass accumulates: zero all group slots first (a fill kernel), then max in
     ops = [
         Op(f"nvfp4.amax[{tag}]", tag, 2 * n,
-           [lambda: amax.zero_()] + [lambda t=t: lpq.lpq_nvfp4_amax_grouped(t, amax, accumulate=True) for t in tq],
-           counted=False),
+           [lambda: lpq.lpq_nvfp4_amax_grouped(tamax, amax, accumulate=False)], counted=False),
         Op(f"nvfp4.quantize[{tag}]", tag, qbytes, [lambda t=t: lpq.lpq_quantize_nvfp4_grouped(t, amax, g) for t in tq]),
         Op(f"nvfp4.dequantize[{tag}]", tag, qbytes, [lambda t=t: lpq.lpq_dequantize_nvfp4_grouped(t, g) for t in tdq]),
         Op(f"nvfp4.qdq[{tag}]", tag, 4 * n, [lambda t=t: lpq.lpq_nvfp4_qdq_grouped(t, amax) for t in tqdq]),
