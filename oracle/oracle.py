@@ -229,6 +229,25 @@ class Oracle:
         A, g = self.nvfp4_group_scale(members)
         return A, g, [self.nvfp4_quantize(m, g) for m in members]
 
+    # ------------------------------------------------------------------ re-quantization of FP8 weights
+    # "低精度训练与 Rollout" (vime and slime documentation), section
+    # "FP8 训练 + FP8 Rollout", implementation note 3: with FP8 training, the
+    # weight update first turns the trainer's block-wise FP8 weights back into
+    # BF16 and then quantizes that BF16 tensor for the rollout engine.  The
+    # oracle is that composition, step by step, with nothing fused.
+    def fp8blk_requantize_mxfp8(self, q: np.ndarray, s: np.ndarray):
+        """Block-wise FP8 (codes, tile scales) -> BF16 -> MXFP8 (codes, UE8M0 bytes)."""
+        return self.mxfp8_quantize(self.fp8blk_dequantize(q, s))
+
+    def fp8blk_amax(self, q: np.ndarray, s: np.ndarray) -> float:
+        """max |y| of the dequantized BF16 tensor y (the NVFP4 amax of the re-quantized weight)."""
+        return self.amax(self.fp8blk_dequantize(q, s))
+
+    def fp8blk_requantize_nvfp4_group(self, members):
+        """One sibling group of block-wise FP8 tensors [(q, s), ...] -> BF16 -> NVFP4 under the
+        group's shared global scale.  Returns (A, g, [(packed, scales), ...])."""
+        return self.nvfp4_quantize_group([self.fp8blk_dequantize(q, s) for q, s in members])
+
 
 _default = None
 

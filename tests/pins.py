@@ -530,4 +530,72 @@ def pin_config1_layout(O):
     assert not s[128:, 8:16].any() and not p[128:, 64:128].any()
 
 
+# --------------------------------------------------------------------------- re-quantization of FP8 weights
+
+def pin_requant_mxfp8_identity(O):
+    """Block-wise FP8 tensor with a power-of-two scale 2^k per tile (a different k per
+    tile, ragged 200 x 320 so that the last tile column is 64 wide) and a +-448 code
+    in every 1x32 block: the dequantized BF16 values are code * 2^k exactly, so the
+    MXFP8 re-quantization keeps every code and sets each byte to 127 + k of its tile."""
+    rng = np.random.default_rng(21)
+    M, N = 200, 320
+    tm, tn = (M + 127) // 128, (N + 127) // 128
+    k = rng.integers(-100, 100, (tm, tn))
+    tab = e4m3_table()
+    pool = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    q = rng.choice(pool, (M, N)).astype(np.uint8)
+    for r in range(M):
+        for b in range(N // 32):
+            q[r, 32 * b + int(rng.integers(0, 32))] = 0x7E | (0x80 if rng.integers(0, 2) else 0)
+    s = np.ldexp(1.0, k).astype(np.float32)
+    qo, e = O.fp8blk_requantize_mxfp8(q, s)
+    kk = np.repeat(np.repeat(k, 128, 0), 128, 1)[:M, :N]
+    assert np.array_equal(e.astype(np.int64), (127 + kk)[:, ::32])
+    assert np.array_equal(qo, q)
+    y = O.fp8blk_dequantize(q, s)
+    assert np.array_equal(bf16_f32(y).astype(np.float64), np.ldexp(tab[q].astype(np.float64), kk))
+
+
+def pin_requant_nvfp4_round_trip(O):
+    """A sibling group of two block-wise FP8 tensors.  The first dequantizes to E2M1
+    grid values times s_b * 2^k per 1x16 block (one +-6 per block, s_b in {2^j,
+    1.5 * 2^j}), with a different power-of-two tile scale per tile; the second holds
+    one code 448 under the tile scale 6 * 2^k, so the group amax is 2688 * 2^k and
+    g = 2^k.  Then the block-scale codes are s_b, the element codes the grid codes,
+    and the NVFP4 dequantization returns the FP8 tensor's BF16 values."""
+    rng = np.random.default_rng(22)
+    grid = read_grid_file()
+    tab = e4m3_table()
+    code_of = {float(v): c for c, v in enumerate(tab[:0x7F])}
+    for k in (-30, 0, 9):
+        M, N = 140, 272
+        nb = N // 16
+        tm, tn = (M + 127) // 128, (N + 127) // 128
+        sb = np.ldexp(np.where(rng.integers(0, 2, (M, nb)) == 1, 1.5, 1.0), rng.integers(-3, 4, (M, nb)))
+        gc = rng.integers(0, 16, (M, N))
+        for r in range(M):
+            for b in range(nb):
+                gc[r, 16 * b + int(rng.integers(0, 16))] = 7 | (8 if rng.integers(0, 2) else 0)
+        gv = grid[gc & 7] * np.where(gc & 8, -1.0, 1.0)
+        kt = k + rng.integers(-2, 3, (tm, tn))
+        ktt = np.repeat(np.repeat(kt, 128, 0), 128, 1)[:M, :N]
+        cv = gv * np.repeat(sb, 16, 1) * np.ldexp(1.0, k - ktt)
+        q1 = np.array([code_of[abs(v)] | (0x80 if v < 0 else 0) for v in cv.ravel()], np.uint8).reshape(M, N)
+        s1 = np.ldexp(1.0, kt).astype(np.float32)
+        q2 = np.zeros((2, 32), np.uint8)
+        q2[1, 7] = 0x7E
+        s2 = np.full((1, 1), np.ldexp(6.0, k), np.float32)
+        assert O.fp8blk_amax(q2, s2) == np.ldexp(2688.0, k)
+        A, g, outs = O.fp8blk_requantize_nvfp4_group([(q1, s1), (q2, s2)])
+        assert A == np.ldexp(2688.0, k) and g == np.ldexp(1.0, k)
+        p, s = outs[0]
+        assert np.array_equal(tab[s].astype(np.float64), sb)
+        codes = np.empty((M, N), np.int64)
+        codes[:, 0::2] = p & 15
+        codes[:, 1::2] = p >> 4
+        assert np.all((codes & 7) == (gc & 7))
+        assert np.all(((codes & 8) == (gc & 8)) | ((gc & 7) == 0))
+        assert np.array_equal(O.nvfp4_dequantize(p, s, g), O.fp8blk_dequantize(q1, s1))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
