@@ -197,6 +197,55 @@ lpq_status lpq_dequantize_nvfp4_grouped(const lpq_tensor* host, const lpq_tensor
 lpq_status lpq_nvfp4_qdq_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n,
                                  const float* group_amax, int32_t n_groups, void* stream);
 
+/* ======================================================================== */
+/* Re-quantization of block-wise FP8 weights into MXFP8 or NVFP4, for the
+ * FP8-training weight sync.  "低精度训练与 Rollout" (vime and slime
+ * documentation), section "FP8 训练 + FP8 Rollout", implementation note 3:
+ * at a weight update the trainer's FP8 weights go back to BF16 and are then
+ * quantized again for the rollout engine.  These calls do both steps in one
+ * pass; the BF16 tensor never reaches HBM.  The results are
+ * bit-identical to lpq_dequantize_fp8blk followed by lpq_quantize_mxfp8, or
+ * by the NVFP4 amax pass and lpq_quantize_nvfp4, on the dequantized BF16
+ * values y = BF16(fl(E4M3value(q) * s_tile)).
+ * q: [M, N] E4M3 codes (not the NaN patterns 0x7F / 0xFF); s: [ceil(M/128),
+ * ceil(N/128)] finite FP32 tile scales, of either sign, such that every y is
+ * finite.  N % 32 == 0 (MXFP8) or N % 16 == 0 (amax, NVFP4), else
+ * LPQ_ERR_SHAPE.  Alignment: q 16 bytes, MXFP8 q_out 16 bytes, NVFP4 p 8
+ * bytes, FP32 arrays 4 bytes; scale-byte arrays none.  Outputs and layouts are
+ * those of lpq_quantize_mxfp8 / lpq_quantize_nvfp4. */
+lpq_status lpq_requantize_fp8blk_mxfp8(const uint8_t* q, const float* s, int64_t M, int64_t N,
+                                       uint8_t* q_out, uint8_t* e_out, void* stream);
+
+/* max |y| of the dequantized tensor, max-accumulated into *amax when
+ * accumulate != 0, else overwritten (1 FP32 on the device). */
+lpq_status lpq_fp8blk_amax(const uint8_t* q, const float* s, int64_t M, int64_t N, float* amax,
+                           int accumulate, void* stream);
+
+/* amax: 1 FP32 (device) holding A of the sibling group of the dequantized
+ * tensors.  p, sb, g as for lpq_quantize_nvfp4. */
+lpq_status lpq_requantize_fp8blk_nvfp4(const uint8_t* q, const float* s, int64_t M, int64_t N,
+                                       const float* amax, uint8_t* p, uint8_t* sb, float* g, void* stream);
+
+/* Grouped forms.  A re-quantization descriptor names both scale arrays. */
+typedef struct lpq_requant_tensor {
+    const uint8_t* src;        /* E4M3 codes [M, N] */
+    const float* src_scale;    /* FP32 tile scales */
+    void* dst;                 /* MXFP8 codes [M, N] or NVFP4 packed [M, N/2] */
+    void* dst_scale;           /* UE8M0 bytes [M, N/32] or E4M3 block scales [M, N/16] */
+    int64_t rows;
+    int64_t cols;
+    int32_t group;             /* NVFP4 sibling group */
+    int32_t reserved;          /* must be 0 */
+} lpq_requant_tensor;
+
+lpq_status lpq_requantize_fp8blk_mxfp8_grouped(const lpq_requant_tensor* host, const lpq_requant_tensor* dev,
+                                               int32_t n, void* stream);
+lpq_status lpq_fp8blk_amax_grouped(const lpq_requant_tensor* host, const lpq_requant_tensor* dev, int32_t n,
+                                   float* group_amax, int32_t n_groups, int accumulate, void* stream);
+lpq_status lpq_requantize_fp8blk_nvfp4_grouped(const lpq_requant_tensor* host, const lpq_requant_tensor* dev,
+                                               int32_t n, const float* group_amax, int32_t n_groups,
+                                               float* group_g, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

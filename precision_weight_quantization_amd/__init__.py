@@ -49,8 +49,18 @@ class lpq_tensor(ctypes.Structure):
 
 assert ctypes.sizeof(lpq_tensor) == 48
 
+
+class lpq_requant_tensor(ctypes.Structure):
+    _fields_ = [("src", ctypes.c_void_p), ("src_scale", ctypes.c_void_p), ("dst", ctypes.c_void_p),
+                ("dst_scale", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("group", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+assert ctypes.sizeof(lpq_requant_tensor) == 56
+
 _vp, _i64, _i32, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
 _tp = ctypes.POINTER(lpq_tensor)
+_rp = ctypes.POINTER(lpq_requant_tensor)
 _SIG = {
     "lpq_status_string": (ctypes.c_char_p, [_int]),
     "lpq_last_hip_error": (_int, []),
@@ -71,6 +81,12 @@ _SIG = {
     "lpq_quantize_nvfp4_grouped": (_int, [_tp, _vp, _i32, _vp, _i32, _vp, _vp]),
     "lpq_dequantize_nvfp4_grouped": (_int, [_tp, _vp, _i32, _vp, _i32, _vp]),
     "lpq_nvfp4_qdq_grouped": (_int, [_tp, _vp, _i32, _vp, _i32, _vp]),
+    "lpq_requantize_fp8blk_mxfp8": (_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
+    "lpq_fp8blk_amax": (_int, [_vp, _vp, _i64, _i64, _vp, _int, _vp]),
+    "lpq_requantize_fp8blk_nvfp4": (_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
+    "lpq_requantize_fp8blk_mxfp8_grouped": (_int, [_rp, _vp, _i32, _vp]),
+    "lpq_fp8blk_amax_grouped": (_int, [_rp, _vp, _i32, _vp, _i32, _int, _vp]),
+    "lpq_requantize_fp8blk_nvfp4_grouped": (_int, [_rp, _vp, _i32, _vp, _i32, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIG.items():
     _fn = getattr(_L, _name)
@@ -197,6 +213,54 @@ def lpq_nvfp4_qdq(x, amax, y=None, stream=None):
     return y
 
 
+# --------------------------------------------------------------------------- FP8 re-quantization
+
+def _codes_in(q, name: str):
+    if q.dim() != 2:
+        raise ValueError(f"{name} must be 2-D [M, N]")
+    if q.element_size() != 1:
+        raise TypeError(f"{name} must hold 1-byte E4M3 codes, got {q.dtype}")
+    if not q.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return q.contiguous()
+
+
+def lpq_requantize_fp8blk_mxfp8(q, s, q_out=None, e_out=None, stream=None):
+    """Block-wise FP8 (codes [M,N], FP32 tile scales) -> MXFP8 (codes [M,N] float8_e4m3fn,
+    UE8M0 bytes [M,N/32] uint8) of the dequantized BF16 values, in one pass."""
+    q = _codes_in(q, "q")
+    M, N = q.shape
+    q_out = _empty((M, N), torch.float8_e4m3fn, q) if q_out is None else q_out
+    e_out = _empty((M, max(N // 32, 1)), torch.uint8, q) if e_out is None else e_out
+    _check(_L.lpq_requantize_fp8blk_mxfp8(q.data_ptr(), s.data_ptr(), M, N, q_out.data_ptr(), e_out.data_ptr(),
+                                          _stream(stream)), "lpq_requantize_fp8blk_mxfp8")
+    return q_out, e_out
+
+
+def lpq_fp8blk_amax(q, s, amax=None, accumulate=False, stream=None):
+    """max |y| of the dequantized BF16 values into a 1-element FP32 device tensor."""
+    q = _codes_in(q, "q")
+    M, N = q.shape
+    amax = _empty((1,), torch.float32, q) if amax is None else amax
+    _check(_L.lpq_fp8blk_amax(q.data_ptr(), s.data_ptr(), M, N, amax.data_ptr(), int(bool(accumulate)),
+                              _stream(stream)), "lpq_fp8blk_amax")
+    return amax
+
+
+def lpq_requantize_fp8blk_nvfp4(q, s, amax, p=None, sb=None, g=None, stream=None):
+    """Block-wise FP8 -> NVFP4 (packed [M,N/2] uint8, E4M3 block scales [M,N/16], global scale [1])
+    of the dequantized BF16 values under the group amax (1-element FP32 device tensor)."""
+    q = _codes_in(q, "q")
+    M, N = q.shape
+    p = _empty((M, max(N // 2, 1)), torch.uint8, q) if p is None else p
+    sb = _empty((M, max(N // 16, 1)), torch.float8_e4m3fn, q) if sb is None else sb
+    g = _empty((1,), torch.float32, q) if g is None else g
+    _check(_L.lpq_requantize_fp8blk_nvfp4(q.data_ptr(), s.data_ptr(), M, N, amax.data_ptr(), p.data_ptr(),
+                                          sb.data_ptr(), g.data_ptr(), _stream(stream)),
+           "lpq_requantize_fp8blk_nvfp4")
+    return p, sb, g
+
+
 # --------------------------------------------------------------------------- grouped
 
 class TensorTable:
@@ -220,6 +284,28 @@ class TensorTable:
             self.host[i].group = int(group)
             self.host[i].reserved = 0
             self.keep.append((src, dst, scale))
+        raw = torch.frombuffer(bytearray(bytes(self.host)), dtype=torch.uint8)
+        dev = device if device is not None else entries[0][0].device
+        self.dev = raw.to(dev)
+        self.n = n
+
+    def args(self):
+        return self.host, self.dev.data_ptr(), self.n
+
+
+class RequantTable:
+    """Descriptors of a grouped re-quantization call: ``entries`` is a list of
+    (src codes, src tile scales, dst, dst scales, rows, cols, group)."""
+
+    def __init__(self, entries, device=None):
+        n = len(entries)
+        self.host = (lpq_requant_tensor * n)()
+        self.keep = []
+        for i, (src, src_scale, dst, dst_scale, rows, cols, group) in enumerate(entries):
+            h = self.host[i]
+            h.src, h.src_scale, h.dst, h.dst_scale = _ptr(src), _ptr(src_scale), _ptr(dst), _ptr(dst_scale)
+            h.rows, h.cols, h.group, h.reserved = int(rows), int(cols), int(group), 0
+            self.keep.append((src, src_scale, dst, dst_scale))
         raw = torch.frombuffer(bytearray(bytes(self.host)), dtype=torch.uint8)
         dev = device if device is not None else entries[0][0].device
         self.dev = raw.to(dev)
@@ -265,6 +351,24 @@ def lpq_dequantize_nvfp4_grouped(table: TensorTable, group_g, stream=None):
 def lpq_nvfp4_qdq_grouped(table: TensorTable, group_amax, stream=None):
     _check(_L.lpq_nvfp4_qdq_grouped(*table.args(), group_amax.data_ptr(), group_amax.numel(), _stream(stream)),
            "lpq_nvfp4_qdq_grouped")
+
+
+def lpq_requantize_fp8blk_mxfp8_grouped(table: RequantTable, stream=None):
+    _check(_L.lpq_requantize_fp8blk_mxfp8_grouped(*table.args(), _stream(stream)),
+           "lpq_requantize_fp8blk_mxfp8_grouped")
+
+
+def lpq_fp8blk_amax_grouped(table: RequantTable, group_amax, accumulate=False, stream=None):
+    _check(_L.lpq_fp8blk_amax_grouped(*table.args(), group_amax.data_ptr(), group_amax.numel(),
+                                      int(bool(accumulate)), _stream(stream)), "lpq_fp8blk_amax_grouped")
+    return group_amax
+
+
+def lpq_requantize_fp8blk_nvfp4_grouped(table: RequantTable, group_amax, group_g, stream=None):
+    _check(_L.lpq_requantize_fp8blk_nvfp4_grouped(*table.args(), group_amax.data_ptr(), group_amax.numel(),
+                                                  group_g.data_ptr(), _stream(stream)),
+           "lpq_requantize_fp8blk_nvfp4_grouped")
+    return group_g
 
 
 def raw():

@@ -51,6 +51,15 @@
 #ifndef LPQ_AMAX_U
 #define LPQ_AMAX_U 32
 #endif
+#ifndef LPQ_RQM_U
+#define LPQ_RQM_U 2
+#endif
+#ifndef LPQ_RQA_U
+#define LPQ_RQA_U 16
+#endif
+#ifndef LPQ_RQN_U
+#define LPQ_RQN_U 2
+#endif
 #ifndef LPQ_TILEQ_THREADS
 #define LPQ_TILEQ_THREADS 256
 #endif
@@ -80,19 +89,19 @@ constexpr int kMaxSeg = 8;               // segments per launch (longer lists ar
 template <int U>
 constexpr int64_t chunk_elems() { return (int64_t)kThreads * 8 * U; }
 
-// Loads the lane's U vectors of a flat chunk: lane t of vector u holds the 8
-// elements starting at base + (u * kThreads + t) * 8.  A full chunk (the
+// Loads the lane's U vectors of a flat chunk: lane t of vector u holds the EV
+// elements starting at base + (u * kThreads + t) * EV.  A full chunk (the
 // common case) loads without per-lane bounds checks.
-template <int U, typename T>
+template <int U, int EV = 8, typename T>
 __device__ __forceinline__ void load_chunk(T (&v)[U], const T* src, int64_t base, int64_t total, bool full) {
-    const T* p = src + (base >> 3) + threadIdx.x;
+    const T* p = src + base / EV + threadIdx.x;
     if (full) {
 #pragma unroll
         for (int u = 0; u < U; u++) v[u] = load<kNTL>(p + u * kThreads);
     } else {
 #pragma unroll
         for (int u = 0; u < U; u++) {
-            const int64_t e0 = base + (int64_t)(u * kThreads + threadIdx.x) * 8;
+            const int64_t e0 = base + (int64_t)(u * kThreads + threadIdx.x) * EV;
             v[u] = e0 < total ? load<kNTL>(p + u * kThreads) : T{};
         }
     }
@@ -112,17 +121,43 @@ struct ChunkMap {
     double inv_units[kMaxSeg];   // 1 / units[s]
 };
 
-struct Work {
-    lpq_tensor d;
+template <typename D>
+struct WorkT {
+    D d;
     int64_t unit;    // chunk or tile index inside the tensor
 };
+using Work = WorkT<lpq_tensor>;
+
+template <typename T>
+using cptr = const __attribute__((address_space(4))) T*;   // constant address space: uniform scalar loads
+
+__device__ __forceinline__ void read_desc(lpq_tensor& o, cptr<lpq_tensor> t) {
+    o.src = t->src;
+    o.dst = t->dst;
+    o.scale = t->scale;
+    o.rows = t->rows;
+    o.cols = t->cols;
+    o.group = t->group;
+    o.reserved = 0;
+}
+
+__device__ __forceinline__ void read_desc(lpq_requant_tensor& o, cptr<lpq_requant_tensor> t) {
+    o.src = t->src;
+    o.src_scale = t->src_scale;
+    o.dst = t->dst;
+    o.dst_scale = t->dst_scale;
+    o.rows = t->rows;
+    o.cols = t->cols;
+    o.group = t->group;
+    o.reserved = 0;
+}
 
 // The tensor and work unit of this workgroup.  Every quantity is uniform
 // across the workgroup and kept in scalar registers, so the descriptor of a
 // grouped call is fetched with scalar loads.
-template <bool G>
-__device__ __forceinline__ Work locate(const lpq_tensor* table, const lpq_tensor& one, const ChunkMap& m) {
-    Work w;
+template <bool G, typename D>
+__device__ __forceinline__ WorkT<D> locate(const D* table, const D& one, const ChunkMap& m) {
+    WorkT<D> w;
     if constexpr (!G) {
         w.d = one;
         w.unit = blockIdx.x;
@@ -148,15 +183,7 @@ __device__ __forceinline__ Work locate(const lpq_tensor* table, const lpq_tensor
         if ((uint64_t)(q + 1) * u <= x) q += 1;
         else if ((uint64_t)q * u > x) q -= 1;
         q = __builtin_amdgcn_readfirstlane(q);
-        const __attribute__((address_space(4))) lpq_tensor* t =
-            (const __attribute__((address_space(4))) lpq_tensor*)(table) + t0 + q;
-        w.d.src = t->src;
-        w.d.dst = t->dst;
-        w.d.scale = t->scale;
-        w.d.rows = t->rows;
-        w.d.cols = t->cols;
-        w.d.group = t->group;
-        w.d.reserved = 0;
+        read_desc(w.d, (cptr<D>)(table) + t0 + q);
         w.unit = (int64_t)(x - q * u);
         return w;
     }
@@ -165,6 +192,15 @@ __device__ __forceinline__ Work locate(const lpq_tensor* table, const lpq_tensor
 // ---------------------------------------------------------------------------
 // MXFP8
 // ---------------------------------------------------------------------------
+
+// 8 values -> 8 E4M3 codes of RN(x / 2^(byte - 127)), X carrying the byte.
+__device__ __forceinline__ v2u mx_encode8(const F8& f, float X) {
+    short2_t c01 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((short2_t){0, 0}, f.x[0], f.x[1], X, false);
+    c01 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c01, f.x[2], f.x[3], X, true);
+    short2_t c23 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((short2_t){0, 0}, f.x[4], f.x[5], X, false);
+    c23 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c23, f.x[6], f.x[7], X, true);
+    return v2u{__builtin_bit_cast(uint32_t, c01), __builtin_bit_cast(uint32_t, c23)};
+}
 
 template <int U, bool GROUPED>
 __global__ __launch_bounds__(kThreads) void k_mxfp8_quant(const lpq_tensor* table, lpq_tensor one, ChunkMap map) {
@@ -188,13 +224,9 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_quant(const lpq_tensor* tabl
         const F8 f = widen8(v[u]);
         const uint32_t amax = quad_max(absmax8_f32(f));
         const uint32_t byte = mx_scale_byte(amax);
-        const float X = ue8m0_operand(byte);
-        short2_t c01 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((short2_t){0, 0}, f.x[0], f.x[1], X, false);
-        c01 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c01, f.x[2], f.x[3], X, true);
-        short2_t c23 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((short2_t){0, 0}, f.x[4], f.x[5], X, false);
-        c23 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c23, f.x[6], f.x[7], X, true);
+        const v2u codes = mx_encode8(f, ue8m0_operand(byte));
         if (full || e0 < total) {
-            store<kNTS>(dst + (e0 >> 3), v2u{__builtin_bit_cast(uint32_t, c01), __builtin_bit_cast(uint32_t, c23)});
+            store<kNTS>(dst + (e0 >> 3), codes);
             if ((tid & 3) == 0) store_u8(esc + (e0 >> 5), byte);
         }
     }
@@ -600,6 +632,188 @@ __global__ __launch_bounds__(TT) void k_fp8blk_dequant(const lpq_tensor* table, 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Re-quantization of block-wise FP8 weights into MXFP8 / NVFP4
+// ---------------------------------------------------------------------------
+//
+// The source is E4M3 codes with one FP32 scale per 128x128 tile; the values
+// re-quantized are the BF16 dequantization y = BF16(fl(code * s_tile)),
+// formed in registers and never stored.  Flat layout as above, but a lane
+// takes 16 codes (one 16-byte vector) per step: a 1x16 NVFP4 block is one
+// lane, a 1x32 MXFP8 block a pair of lanes.  N % 16 == 0 keeps a lane's 16
+// elements inside one row and one 128-column tile, so each step needs one
+// tile-scale lookup, found from the lane's (row, column).
+
+template <int U>
+constexpr int64_t rq_chunk_elems() { return (int64_t)kThreads * 16 * U; }
+
+struct RowCol {
+    int64_t r, c;
+};
+
+// (row, column) of flat element e < 2^40 of a row-major [*, N] tensor: the
+// double-precision quotient estimate is within 2^-11 of e / N, so at most one
+// correction step is needed.
+__device__ __forceinline__ RowCol rowcol(int64_t e, int64_t N, double invN) {
+    int64_t q = (int64_t)((double)e * invN);
+    int64_t c = e - q * N;
+    if (c < 0) {
+        q -= 1;
+        c += N;
+    } else if (c >= N) {
+        q += 1;
+        c -= N;
+    }
+    return RowCol{q, c};
+}
+
+// Tile scales of the lane's U vectors (0 for vectors past the end).
+template <int U>
+__device__ __forceinline__ void tile_scales(float (&s)[U], const lpq_requant_tensor& d, int64_t base, int64_t total,
+                                            bool full) {
+    const int64_t N = d.cols;
+    const double invN = 1.0 / (double)N;
+    const int64_t tn = (N + kTile - 1) / kTile;
+    const float* sc = d.src_scale;
+    RowCol p = rowcol(base + (int64_t)threadIdx.x * 16, N, invN);
+    const RowCol step = rowcol((int64_t)kThreads * 16, N, invN);
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const int64_t e0 = base + (int64_t)(u * kThreads + threadIdx.x) * 16;
+        s[u] = (full || e0 < total) ? load<false>(sc + (p.r >> 7) * tn + (p.c >> 7)) : 0.0f;   // 128 = kTile
+        p.r += step.r;
+        p.c += step.c;
+        if (p.c >= N) {
+            p.c -= N;
+            p.r += 1;
+        }
+    }
+}
+
+// The 8 codes of one 8-byte half of a vector times s, rounded to BF16 and
+// widened back to binary32 (exact): the dequantized values.
+__device__ __forceinline__ F8 fp8blk_values8(uint32_t lo, uint32_t hi, float s) {
+    const float2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
+    const float2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+    const float2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+    const float2_t e = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+    const v4u y = v4u{bf16x2(a[0] * s, a[1] * s), bf16x2(b[0] * s, b[1] * s), bf16x2(c[0] * s, c[1] * s),
+                      bf16x2(e[0] * s, e[1] * s)};
+    return widen8(y);
+}
+
+template <int U, bool GROUPED>
+__global__ __launch_bounds__(kThreads) void k_requant_mxfp8(const lpq_requant_tensor* table, lpq_requant_tensor one,
+                                                            ChunkMap map) {
+    const WorkT<lpq_requant_tensor> W = locate<GROUPED>(table, one, map);
+    const lpq_requant_tensor& d = W.d;
+    const int64_t total = d.rows * d.cols;
+    const int64_t base = W.unit * rq_chunk_elems<U>();
+    const v4u* src = reinterpret_cast<const v4u*>(d.src);
+    v4u* dst = reinterpret_cast<v4u*>(d.dst);
+    uint8_t* esc = reinterpret_cast<uint8_t*>(d.dst_scale);
+    const int tid = threadIdx.x;
+
+    const bool full = base + rq_chunk_elems<U>() <= total;
+    v4u c[U];
+    float s[U];
+    load_chunk<U, 16>(c, src, base, total, full);
+    tile_scales<U>(s, d, base, total, full);
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 16;
+        const F8 f0 = fp8blk_values8(c[u].x, c[u].y, s[u]);
+        const F8 f1 = fp8blk_values8(c[u].z, c[u].w, s[u]);
+        // a pair of lanes is one 32-element block
+        const uint32_t byte = mx_scale_byte(pair_max(umax(absmax8_f32(f0), absmax8_f32(f1))));
+        const float X = ue8m0_operand(byte);
+        const v2u q0 = mx_encode8(f0, X);
+        const v2u q1 = mx_encode8(f1, X);
+        if (full || e0 < total) {
+            store<kNTS>(dst + (e0 >> 4), v4u{q0.x, q0.y, q1.x, q1.y});
+            if ((tid & 1) == 0) store_u8(esc + (e0 >> 5), byte);
+        }
+    }
+}
+
+// max |y| of each tensor's dequantized values, max-accumulated into its group
+// slot.  |fl(code * s)| = fl(|code| * |s|) and BF16 rounding is monotone, so
+// the maximum is taken over fl(max|code| * |s|) and rounded once.
+template <int U, bool GROUPED>
+__global__ __launch_bounds__(kThreads) void k_requant_amax(const lpq_requant_tensor* table, lpq_requant_tensor one,
+                                                           ChunkMap map, float* group_amax) {
+    const WorkT<lpq_requant_tensor> W = locate<GROUPED>(table, one, map);
+    const lpq_requant_tensor& d = W.d;
+    const int64_t total = d.rows * d.cols;
+    const int64_t base = W.unit * rq_chunk_elems<U>();
+    const v4u* src = reinterpret_cast<const v4u*>(d.src);
+    const int tid = threadIdx.x;
+
+    const bool full = base + rq_chunk_elems<U>() <= total;
+    v4u c[U];
+    float s[U];
+    load_chunk<U, 16>(c, src, base, total, full);
+    tile_scales<U>(s, d, base, total, full);
+    float m = 0.0f;
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        float cm = 0.0f;
+        const uint32_t w[4] = {c[u].x, c[u].y, c[u].z, c[u].w};
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const float2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
+            const float2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);
+            cm = fmaxf(fmaxf(cm, fabsf(a[0])), fabsf(a[1]));
+            cm = fmaxf(fmaxf(cm, fabsf(b[0])), fabsf(b[1]));
+        }
+        m = fmaxf(m, cm * fabsf(s[u]));   // vectors past the end have codes and scale 0
+    }
+    uint32_t mb = (bf16x2(m, 0.0f) & 0xffffu) << 16;
+    mb = wave_max(mb);
+    __shared__ uint32_t part[kThreads / 64];
+    if ((tid & 63) == 0) part[tid >> 6] = mb;
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t r = umax(umax(part[0], part[1]), umax(part[2], part[3]));
+        atomicMax(reinterpret_cast<unsigned int*>(group_amax + (GROUPED ? d.group : 0)), r);
+    }
+}
+
+template <int U, bool GROUPED>
+__global__ __launch_bounds__(kThreads) void k_requant_nvfp4(const lpq_requant_tensor* table, lpq_requant_tensor one,
+                                                            ChunkMap map, const float* group_amax, float* group_g) {
+    const WorkT<lpq_requant_tensor> W = locate<GROUPED>(table, one, map);
+    const lpq_requant_tensor& d = W.d;
+    const int64_t total = d.rows * d.cols;
+    const int64_t base = W.unit * rq_chunk_elems<U>();
+    const int gi = GROUPED ? d.group : 0;
+    const GlobalScale G = global_scale(group_amax[gi]);
+    const int tid = threadIdx.x;
+    if (W.unit == 0 && tid == 0) group_g[gi] = G.g;   // same value from every member
+    const v4u* src = reinterpret_cast<const v4u*>(d.src);
+    v2u* dst = reinterpret_cast<v2u*>(d.dst);
+    uint8_t* ssc = reinterpret_cast<uint8_t*>(d.dst_scale);
+
+    const bool full = base + rq_chunk_elems<U>() <= total;
+    v4u c[U];
+    float s[U];
+    load_chunk<U, 16>(c, src, base, total, full);
+    tile_scales<U>(s, d, base, total, full);
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 16;
+        const F8 f0 = fp8blk_values8(c[u].x, c[u].y, s[u]);
+        const F8 f1 = fp8blk_values8(c[u].z, c[u].w, s[u]);
+        // one lane is one 16-element block
+        const BlockScale B = block_scale(umax(absmax8_f32(f0), absmax8_f32(f1)), G);
+        const v2u p = v2u{e2m1x8(f0, B), e2m1x8(f1, B)};
+        if (full || e0 < total) {
+            store<kNTS>(dst + (e0 >> 4), p);
+            store_u8(ssc + (e0 >> 4), B.code);
+        }
+    }
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -621,7 +835,7 @@ inline lpq_status launched() {
     return LPQ_OK;
 }
 
-enum Kind { FP8BLK_Q, FP8BLK_DQ, MXFP8_Q, MXFP8_DQ, NV_AMAX, NV_Q, NV_DQ, NV_QDQ };
+enum Kind { FP8BLK_Q, FP8BLK_DQ, MXFP8_Q, MXFP8_DQ, NV_AMAX, NV_Q, NV_DQ, NV_QDQ, RQ_MX, RQ_AMAX, RQ_NV };
 
 // Shape and pointer checks of one tensor for one kind of call.
 lpq_status check_tensor(Kind k, const lpq_tensor& t, int32_t n_groups) {
@@ -654,7 +868,22 @@ lpq_status check_tensor(Kind k, const lpq_tensor& t, int32_t n_groups) {
         if ((k == NV_DQ || k == NV_QDQ) && !aligned(t.dst, 16)) return LPQ_ERR_ALIGN;
         if (n_groups > 0 && (t.group < 0 || t.group >= n_groups)) return LPQ_ERR_GROUP;
         break;
+    default: return LPQ_ERR_ARG;
     }
+    return LPQ_OK;
+}
+
+lpq_status check_tensor(Kind k, const lpq_requant_tensor& t, int32_t n_groups) {
+    if (t.rows <= 0 || t.cols <= 0) return LPQ_ERR_SHAPE;
+    if (t.rows > (int64_t(1) << 40) / t.cols) return LPQ_ERR_SHAPE;
+    if (!t.src || !t.src_scale) return LPQ_ERR_NULL;
+    if (k != RQ_AMAX && (!t.dst || !t.dst_scale)) return LPQ_ERR_NULL;
+    if (t.reserved != 0) return LPQ_ERR_ARG;
+    if (t.cols % (k == RQ_MX ? 32 : 16)) return LPQ_ERR_SHAPE;
+    if (!aligned(t.src, 16) || !aligned(t.src_scale, 4)) return LPQ_ERR_ALIGN;
+    if (k == RQ_MX && !aligned(t.dst, 16)) return LPQ_ERR_ALIGN;
+    if (k == RQ_NV && !aligned(t.dst, 8)) return LPQ_ERR_ALIGN;
+    if (k != RQ_MX && n_groups > 0 && (t.group < 0 || t.group >= n_groups)) return LPQ_ERR_GROUP;
     return LPQ_OK;
 }
 
@@ -670,17 +899,78 @@ int64_t units(Kind k, const lpq_tensor& t) {
     case NV_Q: return (n + chunk_elems<LPQ_NVQ_U>() - 1) / chunk_elems<LPQ_NVQ_U>();
     case NV_DQ: return (n + chunk_elems<LPQ_NVD_U>() - 1) / chunk_elems<LPQ_NVD_U>();
     case NV_QDQ: return (n + chunk_elems<LPQ_QDQ_U>() - 1) / chunk_elems<LPQ_QDQ_U>();
+    default: return 0;
     }
-    return 0;
+}
+
+int64_t units(Kind k, const lpq_requant_tensor& t) {
+    const int64_t n = t.rows * t.cols;
+    switch (k) {
+    case RQ_MX: return (n + rq_chunk_elems<LPQ_RQM_U>() - 1) / rq_chunk_elems<LPQ_RQM_U>();
+    case RQ_AMAX: return (n + rq_chunk_elems<LPQ_RQA_U>() - 1) / rq_chunk_elems<LPQ_RQA_U>();
+    case RQ_NV: return (n + rq_chunk_elems<LPQ_RQN_U>() - 1) / rq_chunk_elems<LPQ_RQN_U>();
+    default: return 0;
+    }
 }
 
 constexpr int64_t kMaxGridX = 0x7fffffffLL;
 
+void dispatch(Kind k, dim3 grid, hipStream_t stream, const lpq_tensor* tab, const lpq_tensor& one, const ChunkMap& map,
+              const float* fa, float* fb) {
+    const dim3 flat(kThreads), tileq(LPQ_TILEQ_THREADS), tiled(LPQ_TILED_THREADS);
+    if (tab) {
+        switch (k) {
+        case FP8BLK_Q: hipLaunchKernelGGL((k_fp8blk_quant<LPQ_TILEQ_THREADS, true>), grid, tileq, 0, stream, tab, one, map); break;
+        case FP8BLK_DQ: hipLaunchKernelGGL((k_fp8blk_dequant<LPQ_TILED_THREADS, true>), grid, tiled, 0, stream, tab, one, map); break;
+        case MXFP8_Q: hipLaunchKernelGGL((k_mxfp8_quant<LPQ_MXQ_U, true>), grid, flat, 0, stream, tab, one, map); break;
+        case MXFP8_DQ: hipLaunchKernelGGL((k_mxfp8_dequant<LPQ_MXD_U, true>), grid, flat, 0, stream, tab, one, map); break;
+        case NV_AMAX: hipLaunchKernelGGL((k_amax<LPQ_AMAX_U, true>), grid, flat, 0, stream, tab, one, map, fb); break;
+        case NV_Q: hipLaunchKernelGGL((k_nvfp4_quant<LPQ_NVQ_U, true>), grid, flat, 0, stream, tab, one, map, fa, fb); break;
+        case NV_DQ: hipLaunchKernelGGL((k_nvfp4_dequant<LPQ_NVD_U, true>), grid, flat, 0, stream, tab, one, map, fa); break;
+        case NV_QDQ: hipLaunchKernelGGL((k_nvfp4_qdq<LPQ_QDQ_U, true>), grid, flat, 0, stream, tab, one, map, fa); break;
+        default: break;
+        }
+    } else {
+        switch (k) {
+        case FP8BLK_Q: hipLaunchKernelGGL((k_fp8blk_quant<LPQ_TILEQ_THREADS, false>), grid, tileq, 0, stream, tab, one, map); break;
+        case FP8BLK_DQ: hipLaunchKernelGGL((k_fp8blk_dequant<LPQ_TILED_THREADS, false>), grid, tiled, 0, stream, tab, one, map); break;
+        case MXFP8_Q: hipLaunchKernelGGL((k_mxfp8_quant<LPQ_MXQ_U, false>), grid, flat, 0, stream, tab, one, map); break;
+        case MXFP8_DQ: hipLaunchKernelGGL((k_mxfp8_dequant<LPQ_MXD_U, false>), grid, flat, 0, stream, tab, one, map); break;
+        case NV_AMAX: hipLaunchKernelGGL((k_amax<LPQ_AMAX_U, false>), grid, flat, 0, stream, tab, one, map, fb); break;
+        case NV_Q: hipLaunchKernelGGL((k_nvfp4_quant<LPQ_NVQ_U, false>), grid, flat, 0, stream, tab, one, map, fa, fb); break;
+        case NV_DQ: hipLaunchKernelGGL((k_nvfp4_dequant<LPQ_NVD_U, false>), grid, flat, 0, stream, tab, one, map, fa); break;
+        case NV_QDQ: hipLaunchKernelGGL((k_nvfp4_qdq<LPQ_QDQ_U, false>), grid, flat, 0, stream, tab, one, map, fa); break;
+        default: break;
+        }
+    }
+}
+
+void dispatch(Kind k, dim3 grid, hipStream_t stream, const lpq_requant_tensor* tab, const lpq_requant_tensor& one,
+              const ChunkMap& map, const float* fa, float* fb) {
+    const dim3 flat(kThreads);
+    if (tab) {
+        switch (k) {
+        case RQ_MX: hipLaunchKernelGGL((k_requant_mxfp8<LPQ_RQM_U, true>), grid, flat, 0, stream, tab, one, map); break;
+        case RQ_AMAX: hipLaunchKernelGGL((k_requant_amax<LPQ_RQA_U, true>), grid, flat, 0, stream, tab, one, map, fb); break;
+        case RQ_NV: hipLaunchKernelGGL((k_requant_nvfp4<LPQ_RQN_U, true>), grid, flat, 0, stream, tab, one, map, fa, fb); break;
+        default: break;
+        }
+    } else {
+        switch (k) {
+        case RQ_MX: hipLaunchKernelGGL((k_requant_mxfp8<LPQ_RQM_U, false>), grid, flat, 0, stream, tab, one, map); break;
+        case RQ_AMAX: hipLaunchKernelGGL((k_requant_amax<LPQ_RQA_U, false>), grid, flat, 0, stream, tab, one, map, fb); break;
+        case RQ_NV: hipLaunchKernelGGL((k_requant_nvfp4<LPQ_RQN_U, false>), grid, flat, 0, stream, tab, one, map, fa, fb); break;
+        default: break;
+        }
+    }
+}
+
 // Launch kernel `k` over tensors [0, n) of `host`/`dev` (single tensor: dev ==
 // nullptr, `one` used), in slices of at most kMaxSeg segments and 2^31-1 work
 // units.
-lpq_status launch(Kind k, const lpq_tensor* host, const lpq_tensor* dev, int32_t n, const lpq_tensor& one,
-                  const float* fa, float* fb, hipStream_t stream) {
+template <typename D>
+lpq_status launch(Kind k, const D* host, const D* dev, int32_t n, const D& one, const float* fa, float* fb,
+                  hipStream_t stream) {
     const int32_t count = dev ? n : 1;
     int32_t i0 = 0;
     while (i0 < count) {
@@ -703,32 +993,7 @@ lpq_status launch(Kind k, const lpq_tensor* host, const lpq_tensor* dev, int32_t
             i++;
         }
         map.nseg = nseg;
-        const lpq_tensor* tab = dev ? dev + i0 : nullptr;
-        const dim3 grid((unsigned)total);
-        const dim3 flat(kThreads), tileq(LPQ_TILEQ_THREADS), tiled(LPQ_TILED_THREADS);
-        if (dev) {
-            switch (k) {
-            case FP8BLK_Q: hipLaunchKernelGGL((k_fp8blk_quant<LPQ_TILEQ_THREADS, true>), grid, tileq, 0, stream, tab, one, map); break;
-            case FP8BLK_DQ: hipLaunchKernelGGL((k_fp8blk_dequant<LPQ_TILED_THREADS, true>), grid, tiled, 0, stream, tab, one, map); break;
-            case MXFP8_Q: hipLaunchKernelGGL((k_mxfp8_quant<LPQ_MXQ_U, true>), grid, flat, 0, stream, tab, one, map); break;
-            case MXFP8_DQ: hipLaunchKernelGGL((k_mxfp8_dequant<LPQ_MXD_U, true>), grid, flat, 0, stream, tab, one, map); break;
-            case NV_AMAX: hipLaunchKernelGGL((k_amax<LPQ_AMAX_U, true>), grid, flat, 0, stream, tab, one, map, fb); break;
-            case NV_Q: hipLaunchKernelGGL((k_nvfp4_quant<LPQ_NVQ_U, true>), grid, flat, 0, stream, tab, one, map, fa, fb); break;
-            case NV_DQ: hipLaunchKernelGGL((k_nvfp4_dequant<LPQ_NVD_U, true>), grid, flat, 0, stream, tab, one, map, fa); break;
-            case NV_QDQ: hipLaunchKernelGGL((k_nvfp4_qdq<LPQ_QDQ_U, true>), grid, flat, 0, stream, tab, one, map, fa); break;
-            }
-        } else {
-            switch (k) {
-            case FP8BLK_Q: hipLaunchKernelGGL((k_fp8blk_quant<LPQ_TILEQ_THREADS, false>), grid, tileq, 0, stream, tab, one, map); break;
-            case FP8BLK_DQ: hipLaunchKernelGGL((k_fp8blk_dequant<LPQ_TILED_THREADS, false>), grid, tiled, 0, stream, tab, one, map); break;
-            case MXFP8_Q: hipLaunchKernelGGL((k_mxfp8_quant<LPQ_MXQ_U, false>), grid, flat, 0, stream, tab, one, map); break;
-            case MXFP8_DQ: hipLaunchKernelGGL((k_mxfp8_dequant<LPQ_MXD_U, false>), grid, flat, 0, stream, tab, one, map); break;
-            case NV_AMAX: hipLaunchKernelGGL((k_amax<LPQ_AMAX_U, false>), grid, flat, 0, stream, tab, one, map, fb); break;
-            case NV_Q: hipLaunchKernelGGL((k_nvfp4_quant<LPQ_NVQ_U, false>), grid, flat, 0, stream, tab, one, map, fa, fb); break;
-            case NV_DQ: hipLaunchKernelGGL((k_nvfp4_dequant<LPQ_NVD_U, false>), grid, flat, 0, stream, tab, one, map, fa); break;
-            case NV_QDQ: hipLaunchKernelGGL((k_nvfp4_qdq<LPQ_QDQ_U, false>), grid, flat, 0, stream, tab, one, map, fa); break;
-            }
-        }
+        dispatch(k, dim3((unsigned)total), stream, dev ? dev + i0 : nullptr, one, map, fa, fb);
         lpq_status st = launched();
         if (st != LPQ_OK) return st;
         i0 = i;
@@ -748,14 +1013,16 @@ lpq_tensor make_one(const void* src, void* dst, void* scale, int64_t M, int64_t 
     return t;
 }
 
-lpq_status single(Kind k, const lpq_tensor& one, const float* fa, float* fb, void* stream) {
+template <typename D>
+lpq_status single(Kind k, const D& one, const float* fa, float* fb, void* stream) {
     lpq_status st = check_tensor(k, one, 0);
     if (st != LPQ_OK) return st;
-    return launch(k, nullptr, nullptr, 0, one, fa, fb, (hipStream_t)stream);
+    return launch<D>(k, nullptr, nullptr, 0, one, fa, fb, (hipStream_t)stream);
 }
 
-lpq_status grouped(Kind k, const lpq_tensor* host, const lpq_tensor* dev, int32_t n, int32_t n_groups,
-                   const float* fa, float* fb, void* stream) {
+template <typename D>
+lpq_status grouped(Kind k, const D* host, const D* dev, int32_t n, int32_t n_groups, const float* fa, float* fb,
+                   void* stream) {
     if (!host || !dev) return LPQ_ERR_NULL;
     if (n <= 0) return LPQ_ERR_SHAPE;
     if (!aligned(dev, 8)) return LPQ_ERR_ALIGN;
@@ -763,7 +1030,20 @@ lpq_status grouped(Kind k, const lpq_tensor* host, const lpq_tensor* dev, int32_
         lpq_status st = check_tensor(k, host[i], n_groups);
         if (st != LPQ_OK) return st;
     }
-    return launch(k, host, dev, n, make_one(nullptr, nullptr, nullptr, 0, 0), fa, fb, (hipStream_t)stream);
+    return launch<D>(k, host, dev, n, D{}, fa, fb, (hipStream_t)stream);
+}
+
+lpq_requant_tensor make_requant(const uint8_t* q, const float* s, void* dst, void* dst_scale, int64_t M, int64_t N) {
+    lpq_requant_tensor t;
+    t.src = q;
+    t.src_scale = s;
+    t.dst = dst;
+    t.dst_scale = dst_scale;
+    t.rows = M;
+    t.cols = N;
+    t.group = 0;
+    t.reserved = 0;
+    return t;
 }
 
 lpq_status fill(float* p, int64_t n, float v, void* stream) {
@@ -816,7 +1096,7 @@ lpq_status lpq_nvfp4_amax(const uint16_t* w, int64_t M, int64_t N, float* amax, 
     lpq_status st = check_tensor(NV_AMAX, one, 0);
     if (st != LPQ_OK) return st;
     if (!accumulate && (st = fill(amax, 1, 0.0f, stream)) != LPQ_OK) return st;
-    return launch(NV_AMAX, nullptr, nullptr, 0, one, nullptr, amax, (hipStream_t)stream);
+    return launch<lpq_tensor>(NV_AMAX, nullptr, nullptr, 0, one, nullptr, amax, (hipStream_t)stream);
 }
 
 lpq_status lpq_quantize_nvfp4(const uint16_t* w, int64_t M, int64_t N, const float* amax, uint8_t* p, uint8_t* s,
@@ -895,6 +1175,61 @@ lpq_status lpq_nvfp4_qdq_grouped(const lpq_tensor* host, const lpq_tensor* dev, 
     if (n_groups <= 0) return LPQ_ERR_SHAPE;
     if (!aligned(group_amax, 4)) return LPQ_ERR_ALIGN;
     return grouped(NV_QDQ, host, dev, n, n_groups, group_amax, nullptr, stream);
+}
+
+lpq_status lpq_requantize_fp8blk_mxfp8(const uint8_t* q, const float* s, int64_t M, int64_t N, uint8_t* q_out,
+                                       uint8_t* e_out, void* stream) {
+    return single(RQ_MX, make_requant(q, s, q_out, e_out, M, N), nullptr, nullptr, stream);
+}
+
+lpq_status lpq_fp8blk_amax(const uint8_t* q, const float* s, int64_t M, int64_t N, float* amax, int accumulate,
+                           void* stream) {
+    if (!amax) return LPQ_ERR_NULL;
+    if (!aligned(amax, 4)) return LPQ_ERR_ALIGN;
+    const lpq_requant_tensor one = make_requant(q, s, nullptr, nullptr, M, N);
+    lpq_status st = check_tensor(RQ_AMAX, one, 0);
+    if (st != LPQ_OK) return st;
+    if (!accumulate && (st = fill(amax, 1, 0.0f, stream)) != LPQ_OK) return st;
+    return launch<lpq_requant_tensor>(RQ_AMAX, nullptr, nullptr, 0, one, nullptr, amax, (hipStream_t)stream);
+}
+
+lpq_status lpq_requantize_fp8blk_nvfp4(const uint8_t* q, const float* s, int64_t M, int64_t N, const float* amax,
+                                       uint8_t* p, uint8_t* sb, float* g, void* stream) {
+    if (!amax || !g) return LPQ_ERR_NULL;
+    if (!aligned(amax, 4) || !aligned(g, 4)) return LPQ_ERR_ALIGN;
+    return single(RQ_NV, make_requant(q, s, p, sb, M, N), amax, g, stream);
+}
+
+lpq_status lpq_requantize_fp8blk_mxfp8_grouped(const lpq_requant_tensor* host, const lpq_requant_tensor* dev,
+                                               int32_t n, void* stream) {
+    return grouped(RQ_MX, host, dev, n, 0, nullptr, nullptr, stream);
+}
+
+lpq_status lpq_fp8blk_amax_grouped(const lpq_requant_tensor* host, const lpq_requant_tensor* dev, int32_t n,
+                                   float* group_amax, int32_t n_groups, int accumulate, void* stream) {
+    if (!group_amax) return LPQ_ERR_NULL;
+    if (n_groups <= 0) return LPQ_ERR_SHAPE;
+    if (!aligned(group_amax, 4)) return LPQ_ERR_ALIGN;
+    if (!host || !dev) return LPQ_ERR_NULL;
+    if (n <= 0) return LPQ_ERR_SHAPE;
+    for (int32_t i = 0; i < n; i++) {
+        lpq_status st = check_tensor(RQ_AMAX, host[i], n_groups);
+        if (st != LPQ_OK) return st;
+    }
+    if (!accumulate) {
+        lpq_status st = fill(group_amax, n_groups, 0.0f, stream);
+        if (st != LPQ_OK) return st;
+    }
+    return grouped(RQ_AMAX, host, dev, n, n_groups, nullptr, group_amax, stream);
+}
+
+lpq_status lpq_requantize_fp8blk_nvfp4_grouped(const lpq_requant_tensor* host, const lpq_requant_tensor* dev,
+                                               int32_t n, const float* group_amax, int32_t n_groups,
+                                               float* group_g, void* stream) {
+    if (!group_amax || !group_g) return LPQ_ERR_NULL;
+    if (n_groups <= 0) return LPQ_ERR_SHAPE;
+    if (!aligned(group_amax, 4) || !aligned(group_g, 4)) return LPQ_ERR_ALIGN;
+    return grouped(RQ_NV, host, dev, n, n_groups, group_amax, group_g, stream);
 }
 
 }  // extern "C"

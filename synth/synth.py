@@ -122,6 +122,43 @@ def generate(seed: int, stream: int, M: int, N: int, sigma: float, row_sigma: fl
     return f32_to_bf16_bits(w.astype(np.float32))
 
 
+def random_bytes(seed: int, stream: int, n: int, exclude=()) -> np.ndarray:
+    """n uniform bytes from the (seed, stream) stream, skipping the values in
+    ``exclude`` (redrawn from the next counter block)."""
+    key = stream_key(seed, stream)
+    out = np.empty(0, np.uint8)
+    base = 0
+    while out.size < n:
+        m = max(n - out.size, 64)
+        b = (_draw(key, np.arange(base, base + m, dtype=np.uint64)) >> np.uint64(56)).astype(np.uint8)
+        if exclude:
+            b = b[~np.isin(b, np.asarray(exclude, np.uint8))]
+        out = np.concatenate([out, b])
+        base += m
+    return out[:n]
+
+
+def e4m3_codes(seed: int, stream: int, M: int, N: int) -> np.ndarray:
+    """[M, N] float8_e4m3fn bit patterns, uniform over the 254 that are not NaN
+    (0x7F and 0xFF are the format's only NaNs)."""
+    return random_bytes(seed, stream, M * N, exclude=(0x7F, 0xFF)).reshape(M, N)
+
+
+def random_f32(seed: int, stream: int, shape, lo_exp: int, hi_exp: int, signed: bool = False) -> np.ndarray:
+    """float32 values 1.m * 2^e with a uniform 23-bit m and e uniform in [lo_exp, hi_exp]
+    (normal floats; subnormal exponents are not produced)."""
+    n = int(np.prod(shape))
+    d = _draw(stream_key(seed, stream), np.arange(n, dtype=np.uint64))
+    mant = (d & np.uint64(0x7FFFFF)).astype(np.uint32)
+    span = hi_exp - lo_exp + 1
+    e = ((d >> np.uint64(23)) % np.uint64(span)).astype(np.int64) + lo_exp
+    assert -126 <= lo_exp and hi_exp <= 127
+    bits = ((e + 127).astype(np.uint32) << np.uint32(23)) | mant
+    if signed:
+        bits |= ((d >> np.uint64(63)).astype(np.uint32) << np.uint32(31))
+    return bits.view(np.float32).reshape(shape)
+
+
 # --------------------------------------------------------------------------- named workloads
 
 # (sigma, row_sigma, outlier_p, outlier_factor) of each distribution named by the workloads.

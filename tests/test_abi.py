@@ -103,6 +103,41 @@ def test_grouped_validation(lib):
     assert L.lpq_last_hip_error() == 0
 
 
+def test_requant_validation(lib):
+    L = lib.raw()
+    assert L.lpq_requantize_fp8blk_mxfp8(None, P, 4, 32, P, P, None) == 1
+    assert L.lpq_requantize_fp8blk_mxfp8(P, None, 4, 32, P, P, None) == 1
+    assert L.lpq_requantize_fp8blk_mxfp8(P, P, 4, 32, None, P, None) == 1
+    assert L.lpq_requantize_fp8blk_mxfp8(P, P, 4, 32, P, None, None) == 1
+    assert L.lpq_requantize_fp8blk_mxfp8(P, P, 4, 48, P, P, None) == 2       # N % 32
+    assert L.lpq_requantize_fp8blk_mxfp8(P, P, 0, 32, P, P, None) == 2
+    assert L.lpq_requantize_fp8blk_mxfp8(P + 8, P, 4, 32, P, P, None) == 3   # codes need 16 bytes
+    assert L.lpq_requantize_fp8blk_mxfp8(P, P + 2, 4, 32, P, P, None) == 3   # FP32 scales
+    assert L.lpq_requantize_fp8blk_mxfp8(P, P, 4, 32, P + 8, P, None) == 3
+    assert L.lpq_fp8blk_amax(P, P, 4, 32, None, 0, None) == 1
+    assert L.lpq_fp8blk_amax(P, P, 4, 24, P, 0, None) == 2                   # N % 16
+    assert L.lpq_fp8blk_amax(P, P, 4, 32, P + 2, 0, None) == 3
+    assert L.lpq_requantize_fp8blk_nvfp4(P, P, 4, 32, None, P, P, P, None) == 1
+    assert L.lpq_requantize_fp8blk_nvfp4(P, P, 4, 32, P, P, P, None, None) == 1
+    assert L.lpq_requantize_fp8blk_nvfp4(P, P, 4, 32, P, P + 4, P, P, None) == 3   # packed needs 8 bytes
+    assert L.lpq_requantize_fp8blk_nvfp4(P, P, 4, 40, P, P, P, P, None) == 2
+    t = (lib.lpq_requant_tensor * 2)()
+    for i in range(2):
+        t[i].src = t[i].src_scale = t[i].dst = t[i].dst_scale = P
+        t[i].rows, t[i].cols, t[i].group, t[i].reserved = 8, 64, i, 0
+    assert L.lpq_requantize_fp8blk_nvfp4_grouped(t, P, 2, P, 1, P, None) == 4    # group 1 >= n_groups 1
+    assert L.lpq_fp8blk_amax_grouped(t, P, 2, P, 1, 0, None) == 4
+    assert L.lpq_fp8blk_amax_grouped(t, P, 2, None, 2, 0, None) == 1
+    assert L.lpq_requantize_fp8blk_nvfp4_grouped(t, P, 2, P, 2, None, None) == 1
+    assert L.lpq_requantize_fp8blk_mxfp8_grouped(t, P + 4, 2, None) == 3
+    assert L.lpq_requantize_fp8blk_mxfp8_grouped(t, P, 0, None) == 2
+    t[1].reserved = 1
+    assert L.lpq_requantize_fp8blk_mxfp8_grouped(t, P, 2, None) == 6
+    t[1].reserved, t[1].src_scale = 0, 0
+    assert L.lpq_requantize_fp8blk_mxfp8_grouped(t, P, 2, None) == 1
+    assert L.lpq_last_hip_error() == 0
+
+
 def test_product_path_has_no_oracle_or_fallback():
     """The package neither imports the oracle nor carries a CPU code path."""
     pkg = os.path.join(ROOT, "precision_weight_quantization_amd")
