@@ -11,6 +11,11 @@ region holds only the codec launches.
 value = algorithmic bytes of the step (each input and output byte counted
 once; the NVFP4 amax pre-passes are timed but not counted) / step time.
 
+The fp8train workload (fused re-quantization of block-wise FP8 weights into
+MXFP8 / NVFP4, next to the unfused sequences) is timed after the step, over
+the same number of iterations, and reported under "next_rows"; it is not part
+of value or ms_per_step.
+
 Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -154,6 +159,61 @@ def cpu_baseline(bench, stride: int, threads: int):
     }
 
 
+def next_rows_parity(bench, stride: int, threads: int):
+    """Run each widening-row op and compare every `stride`-th tensor (NVFP4: sibling
+    group) of its outputs with the oracle.  The oracle starts from the BF16 weights:
+    it forms its own block-wise FP8 copy, then re-quantizes that."""
+    import numpy as np
+    import torch
+
+    from oracle import oracle as O
+
+    def h8(t):
+        return t.contiguous().view(torch.uint8).cpu().numpy()
+
+    def h16(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    jobs = []
+    for op in bench.next_ops:
+        op.run()
+        torch.cuda.synchronize()
+        if op.workload != "fp8train" or op.name.startswith("requant.amax"):
+            continue
+        ws = bench.sets["moe"]
+        out = bench.outputs["fp8train"]
+        if op.name.startswith("requant.mxfp8"):
+            for i in out["ex"][::stride]:
+                x, q, e = h16(ws.w[i]), h8(out["mq"][i]), h8(out["me"][i])
+
+                def job(x=x, q=q, e=e):
+                    oq, oe = O.fp8blk_requantize_mxfp8(*O.fp8blk_quantize(x))
+                    return int((oq != q).sum() + (oe != e).sum())
+                jobs.append(job)
+        elif op.name.startswith("requant.nvfp4"):
+            groups = {}
+            for i, sp in enumerate(ws.specs):
+                groups.setdefault(sp.group, []).append(i)
+            amax_d, g_d = out["amax"].cpu().numpy(), out["g"].cpu().numpy()
+            for gid in sorted(groups)[::stride]:
+                idx = groups[gid]
+                xs = [h16(ws.w[i]) for i in idx]
+                ps, ss = [h8(out["p"][i]) for i in idx], [h8(out["sb"][i]) for i in idx]
+                A_d, gg_d = np.float32(amax_d[gid]), np.float32(g_d[gid])
+
+                def job(xs=xs, ps=ps, ss=ss, A_d=A_d, gg_d=gg_d):
+                    A, g, res = O.fp8blk_requantize_nvfp4_group([O.fp8blk_quantize(x) for x in xs])
+                    bad = int(np.float32(A) != A_d) + int(np.float32(g) != gg_d)
+                    for (p, s), pp, sg in zip(res, ps, ss):
+                        bad += int((p != pp).sum() + (s != sg).sum())
+                    return bad
+                jobs.append(job)
+    O.default()
+    t0 = time.perf_counter()
+    res = O.run_parallel(lambda j: j(), jobs, threads)
+    return {"checked": len(jobs), "parity_mismatches": int(sum(res)), "seconds": round(time.perf_counter() - t0, 2)}
+
+
 # --------------------------------------------------------------------------- HBM copy reference
 
 COPY_BYTES = 4 * (1 << 30)
@@ -204,6 +264,44 @@ def summarize_pmc(path: str) -> None:
         print(f"| {name} | {grid} | {ctr} | {len(disp)} | {tot / max(len(disp), 1):.1f} |")
 
 
+# --------------------------------------------------------------------------- widening rows
+
+def time_next_rows(bench, steps: int):
+    """Time the widening-row ops (outside the step) and compare fused with unfused."""
+    import torch
+    ops = bench.next_ops
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for k in range(steps):
+        for j, op in enumerate(ops):
+            ev[k][j][0].record()
+            op.run()
+            ev[k][j][1].record()
+    torch.cuda.synchronize()
+    out = {"ops": {}}
+    ms = {}
+    for j, op in enumerate(ops):
+        m = sum(ev[k][j][0].elapsed_time(ev[k][j][1]) for k in range(steps)) / steps
+        ms[op.name] = m
+        gbs = op.bytes / (m / 1e3) / GB
+        out["ops"][op.name] = {"ms": round(m, 3), "GB/s": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+                               "launches": len(op.launches), "algorithmic_bytes": int(op.bytes)}
+        log(f"  {op.name:36s} {m:8.3f} ms  {gbs:8.1f} GB/s  {100 * gbs / HBM_PEAK_GBS:5.1f}% of peak")
+    sp = {}
+    if "requant.mxfp8[fp8train]" in ms and "requant.mxfp8.unfused[fp8train]" in ms:
+        sp["mxfp8"] = round(ms["requant.mxfp8.unfused[fp8train]"] / ms["requant.mxfp8[fp8train]"], 3)
+    if all(k in ms for k in ("requant.amax[fp8train]", "requant.nvfp4[fp8train]", "requant.nvfp4.unfused[fp8train]")):
+        sp["nvfp4"] = round(ms["requant.nvfp4.unfused[fp8train]"]
+                            / (ms["requant.amax[fp8train]"] + ms["requant.nvfp4[fp8train]"]), 3)
+    out["fused_speedup_vs_unfused"] = sp
+    out["workload"] = ("Qwen3-30B-A3B weights held in block-wise FP8 (128x128 tiles, FP32 scales): 18,432 expert "
+                       "tensors -> MXFP8; the experts + 48 q/k/v (12,336 sibling groups) -> NVFP4 with the "
+                       "model-wide amax pass; unfused = dequantize to BF16 in HBM, then quantize")
+    log(f"  fused speedup vs unfused: {sp}")
+    return out
+
+
 # --------------------------------------------------------------------------- main
 
 def main():
@@ -212,7 +310,7 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--bucket", choices=("layer", "all"), default="layer")
-    ap.add_argument("--workloads", default="dense,moe,nvfp4,dsv3")
+    ap.add_argument("--workloads", default="dense,moe,nvfp4,dsv3,fp8train")
     ap.add_argument("--cpu-stride", type=int, default=12)
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -250,13 +348,15 @@ def main():
 
     for i in range(args.warmup):
         bench.step()
+        bench.next_step()
         torch.cuda.synchronize()
         log(f"warmup step {i + 1}/{args.warmup} done")
 
     if args.ops:
         import re
         bench.ops = [op for op in bench.ops if re.search(args.ops, op.name)]
-        log(f"timing only: {[op.name for op in bench.ops]}")
+        bench.next_ops = [op for op in bench.next_ops if re.search(args.ops, op.name)]
+        log(f"timing only: {[op.name for op in bench.ops + bench.next_ops]}")
     nops = len(bench.ops)
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nops)]
           for _ in range(args.steps)]
@@ -284,17 +384,21 @@ def main():
                            "in_metric": op.counted}
         log(f"  {op.name:32s} {ms:8.3f} ms  {gbs:8.1f} GB/s  {100 * gbs / HBM_PEAK_GBS:5.1f}% of peak")
 
-    dom = max(range(nops), key=lambda j: op_ms[j])
-    dop = bench.ops[dom]
-    launches = len(dop.launches)
-    per_launch_bytes = dop.bytes / launches
-    per_launch_s = op_ms[dom] / 1e3 / launches
-    achieved = per_launch_bytes / per_launch_s / GB
-    traffic = load_traffic(dop.name)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": dop.name, "bytes_per_launch": int(per_launch_bytes),
-                "avg_launch_us": round(per_launch_s * 1e6, 2)}
+    next_rows = time_next_rows(bench, args.steps) if bench.next_ops else None
+
+    roofline = None
+    if nops:
+        dom = max(range(nops), key=lambda j: op_ms[j])
+        dop = bench.ops[dom]
+        launches = len(dop.launches)
+        per_launch_bytes = dop.bytes / launches
+        per_launch_s = op_ms[dom] / 1e3 / launches
+        achieved = per_launch_bytes / per_launch_s / GB
+        traffic = load_traffic(dop.name)
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "kernel": dop.name, "bytes_per_launch": int(per_launch_bytes),
+                    "avg_launch_us": round(per_launch_s * 1e6, 2)}
 
     cpu = None
     if not args.no_cpu and not args.ops:
@@ -329,6 +433,7 @@ def main():
         },
         "per_op": per_op,
         "roofline": roofline,
+        "next_rows": next_rows,
         "cpu_baseline": cpu,
         "kernel_source_hash": kernel_source_hash(),
     }

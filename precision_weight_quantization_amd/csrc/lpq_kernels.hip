@@ -58,7 +58,7 @@
 #define LPQ_RQA_U 16
 #endif
 #ifndef LPQ_RQN_U
-#define LPQ_RQN_U 2
+#define LPQ_RQN_U 8
 #endif
 #ifndef LPQ_TILEQ_THREADS
 #define LPQ_TILEQ_THREADS 256
@@ -305,7 +305,9 @@ __device__ __forceinline__ BlockScale block_scale(uint32_t bmax_bits, const Glob
     // tinier blocks take the full correctly rounded division.
     float t6 = quot_rn(b, 6.0f, kRcp6);
     if (any_lane(b < 0x1p-100f)) {
-        if (b < 0x1p-100f) t6 = b / 6.0f;
+        float bb = b;
+        __asm__ volatile("" : "+v"(bb));   // an empty barrier: keeps the long division inside the branch
+        if (bb < 0x1p-100f) t6 = bb / 6.0f;
     }
     const float t = t6 * G.tpre;                             // maybe pre-scaled by 2^64
     const float u = quot_rn(t, G.gd, G.rg);                  // fl(fl(b / 6) / g)
@@ -642,118 +644,159 @@ __global__ __launch_bounds__(TT) void k_fp8blk_dequant(const lpq_tensor* table, 
 // takes 16 codes (one 16-byte vector) per step: a 1x16 NVFP4 block is one
 // lane, a 1x32 MXFP8 block a pair of lanes.  N % 16 == 0 keeps a lane's 16
 // elements inside one row and one 128-column tile, so each step needs one
-// tile-scale lookup, found from the lane's (row, column).
+// tile-scale lookup, found from the lane's (row, column).  These kernels do
+// little memory traffic per element, so the per-wave set-up and per-step
+// index work are kept to 32-bit integer steps (the host limits M and N to
+// below 2^31), and full chunks run a straight-line body.
 
 template <int U>
 constexpr int64_t rq_chunk_elems() { return (int64_t)kThreads * 16 * U; }
 
-struct RowCol {
-    int64_t r, c;
-};
+constexpr uint32_t kRqStep = kThreads * 16;   // elements between a lane's consecutive vectors
 
-// (row, column) of flat element e < 2^40 of a row-major [*, N] tensor: the
-// double-precision quotient estimate is within 2^-11 of e / N, so at most one
-// correction step is needed.
-__device__ __forceinline__ RowCol rowcol(int64_t e, int64_t N, double invN) {
-    int64_t q = (int64_t)((double)e * invN);
-    int64_t c = e - q * N;
-    if (c < 0) {
-        q -= 1;
-        c += N;
-    } else if (c >= N) {
-        q += 1;
-        c -= N;
+// Walks the (row, column) of a lane's vectors and looks up their tile scales.
+struct TileCursor {
+    const float* scale;   // tile scales of the tensor
+    uint32_t N, tn;       // columns, tiles per row
+    uint32_t sr, sc;      // kRqStep = sr * N + sc
+    uint32_t r, c;        // position of the lane's current vector
+
+    __device__ __forceinline__ TileCursor(const lpq_requant_tensor& d, int64_t base) {
+        scale = d.src_scale;
+        N = (uint32_t)d.cols;
+        tn = (N + kTile - 1) / kTile;
+        sr = kRqStep / N;
+        sc = kRqStep - sr * N;
+        // chunk origin (uniform): a double-precision quotient estimate (base < 2^40,
+        // error below 2^-11), corrected by one step
+        const double invN = 1.0 / (double)N;
+        int64_t r0 = (int64_t)((double)base * invN);
+        int64_t c0 = base - r0 * (int64_t)N;
+        if (c0 < 0) {
+            r0 -= 1;
+            c0 += N;
+        } else if (c0 >= (int64_t)N) {
+            r0 += 1;
+            c0 -= N;
+        }
+        // the lane's offset from the origin: t < N + kRqStep < 2^32 and
+        // t / N < 4097, so the single-precision estimate is within one
+        const uint32_t t = (uint32_t)c0 + threadIdx.x * 16u;
+        uint32_t q = (uint32_t)((float)t * __builtin_amdgcn_rcpf((float)N));
+        if (q * N > t) q -= 1;
+        else if (t - q * N >= N) q += 1;
+        r = (uint32_t)r0 + q;
+        c = t - q * N;
     }
-    return RowCol{q, c};
-}
 
-// Tile scales of the lane's U vectors (0 for vectors past the end).
-template <int U>
-__device__ __forceinline__ void tile_scales(float (&s)[U], const lpq_requant_tensor& d, int64_t base, int64_t total,
-                                            bool full) {
-    const int64_t N = d.cols;
-    const double invN = 1.0 / (double)N;
-    const int64_t tn = (N + kTile - 1) / kTile;
-    const float* sc = d.src_scale;
-    RowCol p = rowcol(base + (int64_t)threadIdx.x * 16, N, invN);
-    const RowCol step = rowcol((int64_t)kThreads * 16, N, invN);
-#pragma unroll
-    for (int u = 0; u < U; u++) {
-        const int64_t e0 = base + (int64_t)(u * kThreads + threadIdx.x) * 16;
-        s[u] = (full || e0 < total) ? load<false>(sc + (p.r >> 7) * tn + (p.c >> 7)) : 0.0f;   // 128 = kTile
-        p.r += step.r;
-        p.c += step.c;
-        if (p.c >= N) {
-            p.c -= N;
-            p.r += 1;
+    __device__ __forceinline__ const float* ptr() const { return scale + (r >> 7) * tn + (c >> 7); }   // 128 = kTile
+
+    __device__ __forceinline__ void next() {
+        r += sr;
+        c += sc;
+        if (c >= N) {
+            c -= N;
+            r += 1;
         }
     }
+};
+
+// The 16 codes of a vector times s, rounded to BF16 and widened back to
+// binary32 (exact): the dequantized values, in two halves of 8.  `amax` is
+// max |y| as binary32 bits: BF16 rounding is monotone, so it is the rounding
+// of the largest |product| (taken on the products, which the compiler knows
+// to be canonical floats).
+struct Y16 {
+    F8 lo, hi;
+    uint32_t amax;
+};
+
+__device__ __forceinline__ Y16 fp8blk_values16(const v4u& c, float s) {
+    float p[16];
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const float2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
+        const float2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);
+        p[4 * k + 0] = a[0] * s;
+        p[4 * k + 1] = a[1] * s;
+        p[4 * k + 2] = b[0] * s;
+        p[4 * k + 3] = b[1] * s;
+    }
+    float m = fmaxf(fmaxf(fabsf(p[0]), fabsf(p[1])), fabsf(p[2]));
+#pragma unroll
+    for (int k = 3; k < 15; k += 2) m = fmaxf(fmaxf(m, fabsf(p[k])), fabsf(p[k + 1]));
+    m = fmaxf(m, fabsf(p[15]));
+    Y16 y;
+    y.amax = (bf16x2(m, 0.0f) & 0xffffu) << 16;
+    y.lo = widen8(v4u{bf16x2(p[0], p[1]), bf16x2(p[2], p[3]), bf16x2(p[4], p[5]), bf16x2(p[6], p[7])});
+    y.hi = widen8(v4u{bf16x2(p[8], p[9]), bf16x2(p[10], p[11]), bf16x2(p[12], p[13]), bf16x2(p[14], p[15])});
+    return y;
 }
 
-// The 8 codes of one 8-byte half of a vector times s, rounded to BF16 and
-// widened back to binary32 (exact): the dequantized values.
-__device__ __forceinline__ F8 fp8blk_values8(uint32_t lo, uint32_t hi, float s) {
-    const float2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
-    const float2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
-    const float2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
-    const float2_t e = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
-    const v4u y = v4u{bf16x2(a[0] * s, a[1] * s), bf16x2(b[0] * s, b[1] * s), bf16x2(c[0] * s, c[1] * s),
-                      bf16x2(e[0] * s, e[1] * s)};
-    return widen8(y);
+// Loads of a lane's U code vectors and their tile scales; with FULL every
+// vector is in range, else vectors past the end read as codes 0, scale 0.
+template <int U, bool FULL>
+__device__ __forceinline__ void rq_load(v4u (&c)[U], float (&s)[U], const lpq_requant_tensor& d, int64_t base,
+                                        int64_t total) {
+    const v4u* src = reinterpret_cast<const v4u*>(d.src) + base / 16 + threadIdx.x;
+    TileCursor cur(d, base);
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        if (FULL) {
+            c[u] = load<kNTL>(src + u * kThreads);
+            s[u] = load<false>(cur.ptr());
+        } else {
+            const bool in = base + (int64_t)(u * kThreads + threadIdx.x) * 16 < total;
+            c[u] = in ? load<kNTL>(src + u * kThreads) : v4u{0u, 0u, 0u, 0u};
+            s[u] = in ? load<false>(cur.ptr()) : 0.0f;
+        }
+        cur.next();
+    }
 }
 
-template <int U, bool GROUPED>
-__global__ __launch_bounds__(kThreads) void k_requant_mxfp8(const lpq_requant_tensor* table, lpq_requant_tensor one,
-                                                            ChunkMap map) {
-    const WorkT<lpq_requant_tensor> W = locate<GROUPED>(table, one, map);
-    const lpq_requant_tensor& d = W.d;
-    const int64_t total = d.rows * d.cols;
-    const int64_t base = W.unit * rq_chunk_elems<U>();
-    const v4u* src = reinterpret_cast<const v4u*>(d.src);
+template <int U, bool FULL>
+__device__ __forceinline__ void rq_mxfp8_body(const lpq_requant_tensor& d, int64_t base, int64_t total) {
     v4u* dst = reinterpret_cast<v4u*>(d.dst);
     uint8_t* esc = reinterpret_cast<uint8_t*>(d.dst_scale);
     const int tid = threadIdx.x;
-
-    const bool full = base + rq_chunk_elems<U>() <= total;
     v4u c[U];
     float s[U];
-    load_chunk<U, 16>(c, src, base, total, full);
-    tile_scales<U>(s, d, base, total, full);
+    rq_load<U, FULL>(c, s, d, base, total);
 #pragma unroll
     for (int u = 0; u < U; u++) {
         const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 16;
-        const F8 f0 = fp8blk_values8(c[u].x, c[u].y, s[u]);
-        const F8 f1 = fp8blk_values8(c[u].z, c[u].w, s[u]);
+        const Y16 y = fp8blk_values16(c[u], s[u]);
         // a pair of lanes is one 32-element block
-        const uint32_t byte = mx_scale_byte(pair_max(umax(absmax8_f32(f0), absmax8_f32(f1))));
+        const uint32_t byte = mx_scale_byte(pair_max(y.amax));
         const float X = ue8m0_operand(byte);
-        const v2u q0 = mx_encode8(f0, X);
-        const v2u q1 = mx_encode8(f1, X);
-        if (full || e0 < total) {
+        const v2u q0 = mx_encode8(y.lo, X);
+        const v2u q1 = mx_encode8(y.hi, X);
+        if (FULL || e0 < total) {
             store<kNTS>(dst + (e0 >> 4), v4u{q0.x, q0.y, q1.x, q1.y});
             if ((tid & 1) == 0) store_u8(esc + (e0 >> 5), byte);
         }
     }
 }
 
+template <int U, bool GROUPED>
+__global__ __launch_bounds__(kThreads) void k_requant_mxfp8(const lpq_requant_tensor* table, lpq_requant_tensor one,
+                                                            ChunkMap map) {
+    const WorkT<lpq_requant_tensor> W = locate<GROUPED>(table, one, map);
+    const int64_t total = W.d.rows * W.d.cols;
+    const int64_t base = W.unit * rq_chunk_elems<U>();
+    if (base + rq_chunk_elems<U>() <= total) rq_mxfp8_body<U, true>(W.d, base, total);
+    else rq_mxfp8_body<U, false>(W.d, base, total);
+}
+
 // max |y| of each tensor's dequantized values, max-accumulated into its group
 // slot.  |fl(code * s)| = fl(|code| * |s|) and BF16 rounding is monotone, so
 // the maximum is taken over fl(max|code| * |s|) and rounded once.
-template <int U, bool GROUPED>
-__global__ __launch_bounds__(kThreads) void k_requant_amax(const lpq_requant_tensor* table, lpq_requant_tensor one,
-                                                           ChunkMap map, float* group_amax) {
-    const WorkT<lpq_requant_tensor> W = locate<GROUPED>(table, one, map);
-    const lpq_requant_tensor& d = W.d;
-    const int64_t total = d.rows * d.cols;
-    const int64_t base = W.unit * rq_chunk_elems<U>();
-    const v4u* src = reinterpret_cast<const v4u*>(d.src);
-    const int tid = threadIdx.x;
-
-    const bool full = base + rq_chunk_elems<U>() <= total;
+template <int U, bool FULL>
+__device__ __forceinline__ float rq_amax_body(const lpq_requant_tensor& d, int64_t base, int64_t total) {
     v4u c[U];
     float s[U];
-    load_chunk<U, 16>(c, src, base, total, full);
-    tile_scales<U>(s, d, base, total, full);
+    rq_load<U, FULL>(c, s, d, base, total);
     float m = 0.0f;
 #pragma unroll
     for (int u = 0; u < U; u++) {
@@ -768,6 +811,18 @@ __global__ __launch_bounds__(kThreads) void k_requant_amax(const lpq_requant_ten
         }
         m = fmaxf(m, cm * fabsf(s[u]));   // vectors past the end have codes and scale 0
     }
+    return m;
+}
+
+template <int U, bool GROUPED>
+__global__ __launch_bounds__(kThreads) void k_requant_amax(const lpq_requant_tensor* table, lpq_requant_tensor one,
+                                                           ChunkMap map, float* group_amax) {
+    const WorkT<lpq_requant_tensor> W = locate<GROUPED>(table, one, map);
+    const int64_t total = W.d.rows * W.d.cols;
+    const int64_t base = W.unit * rq_chunk_elems<U>();
+    const int tid = threadIdx.x;
+    const float m = base + rq_chunk_elems<U>() <= total ? rq_amax_body<U, true>(W.d, base, total)
+                                                        : rq_amax_body<U, false>(W.d, base, total);
     uint32_t mb = (bf16x2(m, 0.0f) & 0xffffu) << 16;
     mb = wave_max(mb);
     __shared__ uint32_t part[kThreads / 64];
@@ -775,7 +830,29 @@ __global__ __launch_bounds__(kThreads) void k_requant_amax(const lpq_requant_ten
     __syncthreads();
     if (tid == 0) {
         const uint32_t r = umax(umax(part[0], part[1]), umax(part[2], part[3]));
-        atomicMax(reinterpret_cast<unsigned int*>(group_amax + (GROUPED ? d.group : 0)), r);
+        atomicMax(reinterpret_cast<unsigned int*>(group_amax + (GROUPED ? W.d.group : 0)), r);
+    }
+}
+
+template <int U, bool FULL>
+__device__ __forceinline__ void rq_nvfp4_body(const lpq_requant_tensor& d, int64_t base, int64_t total,
+                                              const GlobalScale& G) {
+    v2u* dst = reinterpret_cast<v2u*>(d.dst);
+    uint8_t* ssc = reinterpret_cast<uint8_t*>(d.dst_scale);
+    v4u c[U];
+    float s[U];
+    rq_load<U, FULL>(c, s, d, base, total);
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const int64_t e0 = base + (int64_t)(u * kThreads + threadIdx.x) * 16;
+        const Y16 y = fp8blk_values16(c[u], s[u]);
+        // one lane is one 16-element block
+        const BlockScale B = block_scale(y.amax, G);
+        const v2u p = v2u{e2m1x8(y.lo, B), e2m1x8(y.hi, B)};
+        if (FULL || e0 < total) {
+            store<kNTS>(dst + (e0 >> 4), p);
+            store_u8(ssc + (e0 >> 4), B.code);
+        }
     }
 }
 
@@ -783,35 +860,13 @@ template <int U, bool GROUPED>
 __global__ __launch_bounds__(kThreads) void k_requant_nvfp4(const lpq_requant_tensor* table, lpq_requant_tensor one,
                                                             ChunkMap map, const float* group_amax, float* group_g) {
     const WorkT<lpq_requant_tensor> W = locate<GROUPED>(table, one, map);
-    const lpq_requant_tensor& d = W.d;
-    const int64_t total = d.rows * d.cols;
+    const int64_t total = W.d.rows * W.d.cols;
     const int64_t base = W.unit * rq_chunk_elems<U>();
-    const int gi = GROUPED ? d.group : 0;
+    const int gi = GROUPED ? W.d.group : 0;
     const GlobalScale G = global_scale(group_amax[gi]);
-    const int tid = threadIdx.x;
-    if (W.unit == 0 && tid == 0) group_g[gi] = G.g;   // same value from every member
-    const v4u* src = reinterpret_cast<const v4u*>(d.src);
-    v2u* dst = reinterpret_cast<v2u*>(d.dst);
-    uint8_t* ssc = reinterpret_cast<uint8_t*>(d.dst_scale);
-
-    const bool full = base + rq_chunk_elems<U>() <= total;
-    v4u c[U];
-    float s[U];
-    load_chunk<U, 16>(c, src, base, total, full);
-    tile_scales<U>(s, d, base, total, full);
-#pragma unroll
-    for (int u = 0; u < U; u++) {
-        const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 16;
-        const F8 f0 = fp8blk_values8(c[u].x, c[u].y, s[u]);
-        const F8 f1 = fp8blk_values8(c[u].z, c[u].w, s[u]);
-        // one lane is one 16-element block
-        const BlockScale B = block_scale(umax(absmax8_f32(f0), absmax8_f32(f1)), G);
-        const v2u p = v2u{e2m1x8(f0, B), e2m1x8(f1, B)};
-        if (full || e0 < total) {
-            store<kNTS>(dst + (e0 >> 4), p);
-            store_u8(ssc + (e0 >> 4), B.code);
-        }
-    }
+    if (W.unit == 0 && threadIdx.x == 0) group_g[gi] = G.g;   // same value from every member
+    if (base + rq_chunk_elems<U>() <= total) rq_nvfp4_body<U, true>(W.d, base, total, G);
+    else rq_nvfp4_body<U, false>(W.d, base, total, G);
 }
 
 }  // namespace
@@ -880,6 +935,7 @@ lpq_status check_tensor(Kind k, const lpq_requant_tensor& t, int32_t n_groups) {
     if (k != RQ_AMAX && (!t.dst || !t.dst_scale)) return LPQ_ERR_NULL;
     if (t.reserved != 0) return LPQ_ERR_ARG;
     if (t.cols % (k == RQ_MX ? 32 : 16)) return LPQ_ERR_SHAPE;
+    if (t.rows >= (int64_t(1) << 31) || t.cols >= (int64_t(1) << 31) - kRqStep) return LPQ_ERR_SHAPE;
     if (!aligned(t.src, 16) || !aligned(t.src_scale, 4)) return LPQ_ERR_ALIGN;
     if (k == RQ_MX && !aligned(t.dst, 16)) return LPQ_ERR_ALIGN;
     if (k == RQ_NV && !aligned(t.dst, 8)) return LPQ_ERR_ALIGN;

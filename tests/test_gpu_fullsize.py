@@ -2,7 +2,8 @@
 
 Builds every weight workload at its full size on the device (Qwen3-4B dense,
 Qwen3-30B-A3B experts with q/k/v sibling groups, DeepSeek-V3 MoE layer, W4A4
-activations), runs each operation exactly as the benchmark step does (grouped
+activations, and the block-wise FP8 copy of the Qwen3-30B-A3B weights for
+re-quantization), runs each operation exactly as the benchmark does (grouped
 launches per layer), and compares sampled outputs -- every 48th tensor, every
 48th NVFP4 sibling group, and the whole activation QDQ -- with the oracle,
 bit for bit.  The sampled inputs are copied back from the device; the
@@ -21,10 +22,11 @@ def full_bench():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     free, _ = torch.cuda.mem_get_info()
-    if free < 200e9:
-        pytest.skip(f"full-size workloads need ~185 GB of device memory, {free / 1e9:.0f} GB free")
+    if free < 230e9:
+        pytest.skip(f"full-size workloads need ~215 GB of device memory, {free / 1e9:.0f} GB free")
     import workloads
-    b = workloads.Bench(workloads.WORKLOADS, bucket="layer", device="cuda", log=lambda *a: print(*a, flush=True))
+    b = workloads.Bench(workloads.WORKLOADS + workloads.NEXT_WORKLOADS, bucket="layer", device="cuda",
+                        log=lambda *a: print(*a, flush=True))
     b.step()
     torch.cuda.synchronize()
     yield b
@@ -37,6 +39,14 @@ def test_fullsize_sampled_parity(full_bench):
     res = bench.cpu_baseline(full_bench, stride=48, threads=min(16, os.cpu_count() or 1))
     print(res["sample"], flush=True)
     assert res["parity_mismatches"] == 0
+
+
+def test_fullsize_requant_sampled_parity(full_bench):
+    """Fused and unfused FP8 re-quantization at full size, sampled, against the oracle."""
+    import bench
+    res = bench.next_rows_parity(full_bench, stride=48, threads=min(16, os.cpu_count() or 1))
+    print(res, flush=True)
+    assert res["checked"] > 0 and res["parity_mismatches"] == 0
 
 
 def test_fullsize_group_scales_shared(full_bench):

@@ -18,6 +18,12 @@ distributions named for each workload.
           activation QDQ on 8192x2048 tokens
   dsv3    DeepSeek-V3 MoE layer: 256 experts x {gate 2048x7168, up 2048x7168,
           down 7168x2048} -> block-wise FP8 quantize + dequantize
+  fp8train  the nvfp4 workload's weights held in block-wise FP8 (as an FP8
+          trainer keeps them; made once by this library's quantizer) ->
+          fused re-quantization into MXFP8 (experts) and NVFP4 (experts and
+          q/k/v, sibling groups as above), each next to the unfused
+          dequantize-then-quantize sequence on the same data.  Timed apart
+          from the step.
 
 Buckets: one grouped launch per transformer layer (the unit a weight sync
 streams), or one launch over the whole workload.
@@ -209,6 +215,89 @@ def nvfp4_ops(tag: str, ws: WeightSet, packed: Slab, sbytes: Slab, out: Slab, bu
     return ops, dict(p=p, s=sb, y=y, amax=amax, g=g, n_groups=n_groups)
 
 
+def tiles_of(s: TensorSpec) -> int:
+    return ((s.M + 127) // 128) * ((s.N + 127) // 128)
+
+
+def fp8_source(ws: WeightSet, device):
+    """Block-wise FP8 copies (codes, tile scales) of every weight of ``ws``."""
+    specs = ws.specs
+    qslab = Slab([s.numel for s in specs], device)
+    sslab = Slab([4 * tiles_of(s) for s in specs], device)
+    q = [qslab.view(i, (s.M, s.N), torch.uint8) for i, s in enumerate(specs)]
+    sc = [sslab.view(i, ((s.M + 127) // 128, (s.N + 127) // 128), torch.float32) for i, s in enumerate(specs)]
+    for idx in ws.layers():
+        lpq.lpq_quantize_fp8blk_grouped(lpq.TensorTable([(ws.w[i], q[i], sc[i], specs[i].M, specs[i].N, 0)
+                                                         for i in idx]))
+    return q, sc, (qslab, sslab)
+
+
+def requant_ops(ws: WeightSet, q8, s8, codes: Slab, out: Slab, bucket: str, device="cuda"):
+    """Fused FP8 -> MXFP8 (experts) and FP8 -> NVFP4 (all tensors) re-quantization,
+    and the unfused sequences they replace, writing into the shared slabs."""
+    specs = ws.specs
+    ex = [i for i, s in enumerate(specs) if s.expert != 0xFFFF]
+    n_ex, t_ex = sum(specs[i].numel for i in ex), sum(tiles_of(specs[i]) for i in ex)
+    n, t = ws.numel, sum(tiles_of(s) for s in specs)
+    n_groups = max(s.group for s in specs) + 1
+    exset = set(ex)
+
+    # MXFP8 targets of the experts
+    mcodes = reslab(codes, [specs[i] for i in ex], 1)
+    eb = Slab([specs[i].numel // 32 for i in ex], device)
+    mq = {i: mcodes.view(k, (specs[i].M, specs[i].N), torch.uint8) for k, i in enumerate(ex)}
+    me = {i: eb.view(k, (specs[i].M, specs[i].N // 32), torch.uint8) for k, i in enumerate(ex)}
+    # NVFP4 targets of every tensor; BF16 staging of the unfused sequences
+    packed = reslab(codes, specs, 0.5)
+    sbs = Slab([s.numel // 16 for s in specs], device)
+    p = [packed.view(i, (s.M, s.N // 2), torch.uint8) for i, s in enumerate(specs)]
+    sb = [sbs.view(i, (s.M, s.N // 16), torch.uint8) for i, s in enumerate(specs)]
+    ys = reslab(out, specs, 2)
+    y = [ys.view(i, (s.M, s.N), torch.bfloat16) for i, s in enumerate(specs)]
+    amax = torch.zeros(n_groups, dtype=torch.float32, device=device)
+    g = torch.zeros(n_groups, dtype=torch.float32, device=device)
+
+    by_shape = sorted(range(len(specs)), key=lambda i: (specs[i].M, specs[i].N, i))
+    tamax = lpq.RequantTable([(q8[i], s8[i], None, None, specs[i].M, specs[i].N, specs[i].group) for i in by_shape])
+    rmx, rnv, dq_mx, q_mx, dq_nv, a_nv, q_nv = [], [], [], [], [], [], []
+    for idx in _buckets(ws, bucket):
+        ie = [i for i in idx if i in exset]
+        rmx.append(lpq.RequantTable([(q8[i], s8[i], mq[i], me[i], specs[i].M, specs[i].N, 0) for i in ie]))
+        rnv.append(lpq.RequantTable([(q8[i], s8[i], p[i], sb[i], specs[i].M, specs[i].N, specs[i].group)
+                                     for i in idx]))
+        dq_mx.append(lpq.TensorTable([(q8[i], y[i], s8[i], specs[i].M, specs[i].N, 0) for i in ie]))
+        q_mx.append(lpq.TensorTable([(y[i], mq[i], me[i], specs[i].M, specs[i].N, 0) for i in ie]))
+        dq_nv.append(lpq.TensorTable([(q8[i], y[i], s8[i], specs[i].M, specs[i].N, 0) for i in idx]))
+        q_nv.append(lpq.TensorTable([(y[i], p[i], sb[i], specs[i].M, specs[i].N, specs[i].group) for i in idx]))
+    # the unfused NVFP4 sequence stages every BF16 tensor, takes the model-wide amax
+    # over them (as the fused sequence does over the FP8 copies), then quantizes
+    a_nv = lpq.TensorTable([(y[i], None, None, specs[i].M, specs[i].N, specs[i].group) for i in by_shape])
+
+    def unfused_mx(k):
+        lpq.lpq_dequantize_fp8blk_grouped(dq_mx[k])
+        lpq.lpq_quantize_mxfp8_grouped(q_mx[k])
+
+
+    mx_bytes = 2 * n_ex + n_ex // 32 + 4 * t_ex
+    amax_bytes = n + 4 * t
+    nv_bytes = n + 4 * t + n // 2 + n // 16 + 4 * n_groups
+    ops = [
+        Op("requant.mxfp8[fp8train]", "fp8train", mx_bytes,
+           [lambda r=r: lpq.lpq_requantize_fp8blk_mxfp8_grouped(r) for r in rmx]),
+        Op("requant.mxfp8.unfused[fp8train]", "fp8train", mx_bytes,
+           [lambda k=k: unfused_mx(k) for k in range(len(rmx))]),
+        Op("requant.amax[fp8train]", "fp8train", amax_bytes,
+           [lambda: lpq.lpq_fp8blk_amax_grouped(tamax, amax, accumulate=False)]),
+        Op("requant.nvfp4[fp8train]", "fp8train", nv_bytes,
+           [lambda r=r: lpq.lpq_requantize_fp8blk_nvfp4_grouped(r, amax, g) for r in rnv]),
+        Op("requant.nvfp4.unfused[fp8train]", "fp8train", amax_bytes + nv_bytes,
+           [lambda t=t: lpq.lpq_dequantize_fp8blk_grouped(t) for t in dq_nv]
+           + [lambda: lpq.lpq_nvfp4_amax_grouped(a_nv, amax, accumulate=False)]
+           + [lambda t=t: lpq.lpq_quantize_nvfp4_grouped(t, amax, g) for t in q_nv]),
+    ]
+    return ops, dict(ex=ex, mq=mq, me=me, p=p, sb=sb, amax=amax, g=g, n_groups=n_groups, q8=q8, s8=s8)
+
+
 def activation_ops(x: torch.Tensor, y: torch.Tensor):
     amax = torch.zeros(1, dtype=torch.float32, device=x.device)
     n = x.numel()
@@ -218,6 +307,21 @@ def activation_ops(x: torch.Tensor, y: torch.Tensor):
 
 
 WORKLOADS = ("dense", "moe", "nvfp4", "dsv3")
+NEXT_WORKLOADS = ("fp8train",)
+
+
+def reslab(slab: Slab, specs, bytes_per_elem):
+    """A view-only slab over `slab`'s buffer laid out for `specs`."""
+    s = Slab.__new__(Slab)
+    s.buf = slab.buf
+    s.offsets = []
+    off = 0
+    for sp in specs:
+        s.offsets.append(off)
+        off += (int(sp.numel * bytes_per_elem) + 255) // 256 * 256
+    assert off <= slab.buf.numel(), "output slab too small"
+    s.nbytes = off
+    return s
 
 
 class Bench:
@@ -225,10 +329,11 @@ class Bench:
 
     def __init__(self, which=WORKLOADS, bucket="layer", device="cuda", log=print, scale_layers=None):
         self.ops = []
+        self.next_ops = []      # widening rows: timed apart from the step
         self.outputs = {}
         self.sets = {}
         L = scale_layers
-        need_moe = "moe" in which or "nvfp4" in which
+        need_moe = "moe" in which or "nvfp4" in which or "fp8train" in which
         if "dense" in which:
             self.sets["dense"] = WeightSet(2, dense_specs(L or 36), synth.DIST_DENSE, device)
             log(f"generated dense weights: {self.sets['dense'].numel * 2 / GB:.2f} GB")
@@ -281,20 +386,16 @@ class Bench:
             ops, o = fp8blk_ops("dsv3", ws, codes, sc, out, bucket)
             self.ops += ops
             self.outputs["dsv3"] = o
+        if "fp8train" in which:
+            ws = self.sets["moe"]
+            q8, s8, keep = fp8_source(ws, device)
+            log(f"block-wise FP8 copies of the MoE + attention weights: {sum(k.nbytes for k in keep) / GB:.2f} GB")
+            ops, o = requant_ops(ws, q8, s8, self.codes, self.out, bucket, device)
+            o["keep"] = keep
+            self.next_ops += ops
+            self.outputs["fp8train"] = o
 
-    @staticmethod
-    def _reslab(slab: Slab, specs, bytes_per_elem):
-        """A view-only slab over `slab`'s buffer laid out for `specs`."""
-        s = Slab.__new__(Slab)
-        s.buf = slab.buf
-        s.offsets = []
-        off = 0
-        for sp in specs:
-            s.offsets.append(off)
-            off += (int(sp.numel * bytes_per_elem) + 255) // 256 * 256
-        assert off <= slab.buf.numel(), "output slab too small"
-        s.nbytes = off
-        return s
+    _reslab = staticmethod(reslab)
 
     @staticmethod
     def _experts_only(ws: WeightSet) -> WeightSet:
@@ -311,4 +412,8 @@ class Bench:
 
     def step(self):
         for op in self.ops:
+            op.run()
+
+    def next_step(self):
+        for op in self.next_ops:
             op.run()
