@@ -235,6 +235,10 @@ class Oracle:
     # weight update first turns the trainer's block-wise FP8 weights back into
     # BF16 and then quantizes that BF16 tensor for the rollout engine.  The
     # oracle is that composition, step by step, with nothing fused.
+    def fp8blk_requantize_fp8blk(self, q: np.ndarray, s: np.ndarray):
+        """Block-wise FP8 (codes, tile scales) -> BF16 -> block-wise FP8 (codes, new tile scales)."""
+        return self.fp8blk_quantize(self.fp8blk_dequantize(q, s))
+
     def fp8blk_requantize_mxfp8(self, q: np.ndarray, s: np.ndarray):
         """Block-wise FP8 (codes, tile scales) -> BF16 -> MXFP8 (codes, UE8M0 bytes)."""
         return self.mxfp8_quantize(self.fp8blk_dequantize(q, s))

@@ -21,6 +21,7 @@ Independent routes used here (none re-types the oracle's own arithmetic):
 from __future__ import annotations
 
 import os
+from fractions import Fraction
 
 import numpy as np
 import torch
@@ -115,6 +116,15 @@ def random_f32(n, seed, lo_exp=-140, hi_exp=12) -> np.ndarray:
     e = rng.integers(max(lo_exp + 127, 0), min(hi_exp + 127, 254), n, dtype=np.uint32)
     s = rng.integers(0, 2, n, dtype=np.uint32)
     return ((s << 31) | (e << 23) | m).view(np.float32)
+
+
+def rn_f32_of(x: Fraction) -> np.float32:
+    """The binary32 value nearest to the exact rational x (ties to even), by comparing
+    exact distances to the float32 neighbours of a first guess."""
+    f = np.float32(float(x))
+    cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+    best = min(cands, key=lambda c: (abs(Fraction(float(c)) - x), int(np.float32(c).view(np.uint32)) & 1))
+    return np.float32(best)
 
 
 def sign_bit(v) -> np.ndarray:
@@ -554,6 +564,33 @@ def pin_requant_mxfp8_identity(O):
     assert np.array_equal(qo, q)
     y = O.fp8blk_dequantize(q, s)
     assert np.array_equal(bf16_f32(y).astype(np.float64), np.ldexp(tab[q].astype(np.float64), kk))
+
+
+def pin_requant_fp8blk(O):
+    """Block-wise FP8 -> BF16 -> block-wise FP8.  With a power-of-two scale 2^k per tile and a
+    +-448 code in every tile, the BF16 values are code * 2^k exactly, so the new scale is 2^k
+    and the codes come back unchanged.  With a tile scale s that is not a power of two, the
+    new scale is fl(BF16(448 * s) / 448) (the tile holds a 448 code), worked here in float64
+    from PyTorch's BF16 cast."""
+    rng = np.random.default_rng(23)
+    M, N = 300, 200
+    tm, tn = (M + 127) // 128, (N + 127) // 128
+    pool = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    q = rng.choice(pool, (M, N)).astype(np.uint8)
+    for i in range(tm):
+        for j in range(tn):
+            r = 128 * i + int(rng.integers(0, min(128, M - 128 * i)))
+            c = 128 * j + int(rng.integers(0, min(128, N - 128 * j)))
+            q[r, c] = 0x7E | (0x80 if rng.integers(0, 2) else 0)
+    k = rng.integers(-60, 60, (tm, tn))
+    s = np.ldexp(1.0, k).astype(np.float32)
+    q2, s2 = O.fp8blk_requantize_fp8blk(q, s)
+    assert np.array_equal(s2, s) and np.array_equal(q2, q)
+    s = (s * np.float32(1.3)).astype(np.float32)
+    _, s3 = O.fp8blk_requantize_fp8blk(q, s)
+    amax = bf16_f32(f32_to_bf16_torch((s.astype(np.float64) * 448.0).astype(np.float32)))
+    want = np.array([rn_f32_of(Fraction(float(a)) / 448) for a in amax.ravel()], np.float32).reshape(s.shape)
+    assert np.array_equal(s3, want)
 
 
 def pin_requant_nvfp4_round_trip(O):
