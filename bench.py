@@ -182,7 +182,15 @@ def next_rows_parity(bench, stride: int, threads: int):
             continue
         ws = bench.sets["moe"]
         out = bench.outputs["fp8train"]
-        if op.name.startswith("requant.mxfp8"):
+        if op.name.startswith("requant.fp8blk"):
+            for i in range(0, len(ws.specs), stride):
+                x, q, s8 = h16(ws.w[i]), h8(out["fq"][i]), out["fs"][i].cpu().numpy()
+
+                def job(x=x, q=q, s8=s8):
+                    oq, os_ = O.fp8blk_requantize_fp8blk(*O.fp8blk_quantize(x))
+                    return int((oq != q).sum() + (os_.view(np.uint32) != s8.view(np.uint32)).sum())
+                jobs.append(job)
+        elif op.name.startswith("requant.mxfp8"):
             for i in out["ex"][::stride]:
                 x, q, e = h16(ws.w[i]), h8(out["mq"][i]), h8(out["me"][i])
 
@@ -286,18 +294,22 @@ def time_next_rows(bench, steps: int):
         ms[op.name] = m
         gbs = op.bytes / (m / 1e3) / GB
         out["ops"][op.name] = {"ms": round(m, 3), "GB/s": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
-                               "launches": len(op.launches), "algorithmic_bytes": int(op.bytes)}
+                               "launches": len(op.launches), "algorithmic_bytes": int(op.bytes),
+                               "traffic_hbm_bytes_per_launch": load_traffic(op.name)}
         log(f"  {op.name:36s} {m:8.3f} ms  {gbs:8.1f} GB/s  {100 * gbs / HBM_PEAK_GBS:5.1f}% of peak")
     sp = {}
+    if "requant.fp8blk[fp8train]" in ms and "requant.fp8blk.unfused[fp8train]" in ms:
+        sp["fp8blk"] = round(ms["requant.fp8blk.unfused[fp8train]"] / ms["requant.fp8blk[fp8train]"], 3)
     if "requant.mxfp8[fp8train]" in ms and "requant.mxfp8.unfused[fp8train]" in ms:
         sp["mxfp8"] = round(ms["requant.mxfp8.unfused[fp8train]"] / ms["requant.mxfp8[fp8train]"], 3)
     if all(k in ms for k in ("requant.amax[fp8train]", "requant.nvfp4[fp8train]", "requant.nvfp4.unfused[fp8train]")):
         sp["nvfp4"] = round(ms["requant.nvfp4.unfused[fp8train]"]
                             / (ms["requant.amax[fp8train]"] + ms["requant.nvfp4[fp8train]"]), 3)
     out["fused_speedup_vs_unfused"] = sp
-    out["workload"] = ("Qwen3-30B-A3B weights held in block-wise FP8 (128x128 tiles, FP32 scales): 18,432 expert "
-                       "tensors -> MXFP8; the experts + 48 q/k/v (12,336 sibling groups) -> NVFP4 with the "
-                       "model-wide amax pass; unfused = dequantize to BF16 in HBM, then quantize")
+    out["workload"] = ("Qwen3-30B-A3B weights held in block-wise FP8 (128x128 tiles, FP32 scales): the experts + "
+                       "48 q/k/v (18,576 tensors) -> block-wise FP8; the 18,432 expert tensors -> MXFP8; the experts "
+                       "+ q/k/v (12,336 sibling groups) -> NVFP4 with the model-wide amax pass; unfused = dequantize "
+                       "to BF16 in HBM, then quantize")
     log(f"  fused speedup vs unfused: {sp}")
     return out
 

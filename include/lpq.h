@@ -198,21 +198,44 @@ lpq_status lpq_nvfp4_qdq_grouped(const lpq_tensor* host, const lpq_tensor* dev, 
                                  const float* group_amax, int32_t n_groups, void* stream);
 
 /* ======================================================================== */
-/* Re-quantization of block-wise FP8 weights into MXFP8 or NVFP4, for the
- * FP8-training weight sync.  "低精度训练与 Rollout" (vime and slime
- * documentation), section "FP8 训练 + FP8 Rollout", implementation note 3:
- * at a weight update the trainer's FP8 weights go back to BF16 and are then
- * quantized again for the rollout engine.  These calls do both steps in one
- * pass; the BF16 tensor never reaches HBM.  The results are
- * bit-identical to lpq_dequantize_fp8blk followed by lpq_quantize_mxfp8, or
- * by the NVFP4 amax pass and lpq_quantize_nvfp4, on the dequantized BF16
- * values y = BF16(fl(E4M3value(q) * s_tile)).
- * q: [M, N] E4M3 codes (not the NaN patterns 0x7F / 0xFF); s: [ceil(M/128),
- * ceil(N/128)] finite FP32 tile scales, of either sign, such that every y is
- * finite.  N % 32 == 0 (MXFP8) or N % 16 == 0 (amax, NVFP4), else
- * LPQ_ERR_SHAPE.  Alignment: q 16 bytes, MXFP8 q_out 16 bytes, NVFP4 p 8
- * bytes, FP32 arrays 4 bytes; scale-byte arrays none.  Outputs and layouts are
- * those of lpq_quantize_mxfp8 / lpq_quantize_nvfp4. */
+/* Re-quantization of block-wise FP8 weights, for the FP8-training weight
+ * sync.  "低精度训练与 Rollout" (vime and slime documentation), section
+ * "FP8 训练 + FP8 Rollout", implementation note 3: at a weight update the
+ * trainer's FP8 weights go back to BF16 and are then quantized again for the
+ * rollout engine.  These calls do both steps in one pass; the BF16 tensor
+ * never reaches HBM.  Each result is bit-identical to lpq_dequantize_fp8blk
+ * followed by the target format's quantizer (for NVFP4: the amax pass, then
+ * lpq_quantize_nvfp4), applied to the dequantized BF16 values
+ * y = BF16(fl(E4M3value(q) * s_tile)).
+ *
+ * Inputs: q, [M, N] E4M3 codes (never the NaN patterns 0x7F / 0xFF); s,
+ * [ceil(M/128), ceil(N/128)] finite FP32 tile scales of either sign such that
+ * every y is finite.  Outputs and their layouts are those of the target
+ * format's quantizer. */
+
+/* Grouped descriptor: both scale arrays are named. */
+typedef struct lpq_requant_tensor {
+    const uint8_t* src;        /* E4M3 codes [M, N] */
+    const float* src_scale;    /* FP32 tile scales */
+    void* dst;                 /* target codes: E4M3 [M, N] (block FP8, MXFP8) or NVFP4 packed [M, N/2] */
+    void* dst_scale;           /* FP32 tile scales (block FP8), UE8M0 bytes [M, N/32] (MXFP8), or E4M3 block
+                                  scales [M, N/16] (NVFP4) */
+    int64_t rows;
+    int64_t cols;
+    int32_t group;             /* NVFP4 sibling group */
+    int32_t reserved;          /* must be 0 */
+} lpq_requant_tensor;
+
+/* Block-wise FP8 -> block-wise FP8 (the page's own case).  Any M, N > 0; q and
+ * q_out any alignment (16-byte aligned rows with N % 16 == 0 take the fast
+ * path); s and s_out 4-byte aligned.  The new tile scale is fl(amax(y)/448). */
+lpq_status lpq_requantize_fp8blk(const uint8_t* q, const float* s, int64_t M, int64_t N, uint8_t* q_out,
+                                 float* s_out, void* stream);
+
+/* The flat-target calls below need N % 32 == 0 (MXFP8) or N % 16 == 0 (amax,
+ * NVFP4), and M, N < 2^31 - 4096, else LPQ_ERR_SHAPE.  Alignment: q 16 bytes,
+ * MXFP8 q_out 16 bytes, NVFP4 p 8 bytes, FP32 arrays 4 bytes; scale-byte
+ * arrays none. */
 lpq_status lpq_requantize_fp8blk_mxfp8(const uint8_t* q, const float* s, int64_t M, int64_t N,
                                        uint8_t* q_out, uint8_t* e_out, void* stream);
 
@@ -226,18 +249,11 @@ lpq_status lpq_fp8blk_amax(const uint8_t* q, const float* s, int64_t M, int64_t 
 lpq_status lpq_requantize_fp8blk_nvfp4(const uint8_t* q, const float* s, int64_t M, int64_t N,
                                        const float* amax, uint8_t* p, uint8_t* sb, float* g, void* stream);
 
-/* Grouped forms.  A re-quantization descriptor names both scale arrays. */
-typedef struct lpq_requant_tensor {
-    const uint8_t* src;        /* E4M3 codes [M, N] */
-    const float* src_scale;    /* FP32 tile scales */
-    void* dst;                 /* MXFP8 codes [M, N] or NVFP4 packed [M, N/2] */
-    void* dst_scale;           /* UE8M0 bytes [M, N/32] or E4M3 block scales [M, N/16] */
-    int64_t rows;
-    int64_t cols;
-    int32_t group;             /* NVFP4 sibling group */
-    int32_t reserved;          /* must be 0 */
-} lpq_requant_tensor;
-
+/* Grouped forms, one launch per call where the work map allows (tensors of
+ * equal size kept adjacent).  group_amax / group_g as for the NVFP4 grouped
+ * calls; the amax call overwrites or max-accumulates as lpq_fp8blk_amax. */
+lpq_status lpq_requantize_fp8blk_grouped(const lpq_requant_tensor* host, const lpq_requant_tensor* dev, int32_t n,
+                                         void* stream);
 lpq_status lpq_requantize_fp8blk_mxfp8_grouped(const lpq_requant_tensor* host, const lpq_requant_tensor* dev,
                                                int32_t n, void* stream);
 lpq_status lpq_fp8blk_amax_grouped(const lpq_requant_tensor* host, const lpq_requant_tensor* dev, int32_t n,

@@ -23,7 +23,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("LPQ_LIBRARY") or os.path.join(_PKG, "liblpq.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m precision_weight_quantization_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -c \"import __graft_entry__ as g; g.build()\"`")
 
 _L = ctypes.CDLL(LIB_PATH)
 
@@ -81,6 +81,8 @@ _SIG = {
     "lpq_quantize_nvfp4_grouped": (_int, [_tp, _vp, _i32, _vp, _i32, _vp, _vp]),
     "lpq_dequantize_nvfp4_grouped": (_int, [_tp, _vp, _i32, _vp, _i32, _vp]),
     "lpq_nvfp4_qdq_grouped": (_int, [_tp, _vp, _i32, _vp, _i32, _vp]),
+    "lpq_requantize_fp8blk": (_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
+    "lpq_requantize_fp8blk_grouped": (_int, [_rp, _vp, _i32, _vp]),
     "lpq_requantize_fp8blk_mxfp8": (_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
     "lpq_fp8blk_amax": (_int, [_vp, _vp, _i64, _i64, _vp, _int, _vp]),
     "lpq_requantize_fp8blk_nvfp4": (_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
@@ -225,6 +227,18 @@ def _codes_in(q, name: str):
     return q.contiguous()
 
 
+def lpq_requantize_fp8blk(q, s, q_out=None, s_out=None, stream=None):
+    """Block-wise FP8 (codes [M,N], FP32 tile scales) -> block-wise FP8 of the dequantized
+    BF16 values (codes [M,N] float8_e4m3fn, new FP32 tile scales), in one pass."""
+    q = _codes_in(q, "q")
+    M, N = q.shape
+    q_out = _empty((M, N), torch.float8_e4m3fn, q) if q_out is None else q_out
+    s_out = _empty(fp8blk_scale_shape(M, N), torch.float32, q) if s_out is None else s_out
+    _check(_L.lpq_requantize_fp8blk(q.data_ptr(), s.data_ptr(), M, N, q_out.data_ptr(), s_out.data_ptr(),
+                                    _stream(stream)), "lpq_requantize_fp8blk")
+    return q_out, s_out
+
+
 def lpq_requantize_fp8blk_mxfp8(q, s, q_out=None, e_out=None, stream=None):
     """Block-wise FP8 (codes [M,N], FP32 tile scales) -> MXFP8 (codes [M,N] float8_e4m3fn,
     UE8M0 bytes [M,N/32] uint8) of the dequantized BF16 values, in one pass."""
@@ -351,6 +365,10 @@ def lpq_dequantize_nvfp4_grouped(table: TensorTable, group_g, stream=None):
 def lpq_nvfp4_qdq_grouped(table: TensorTable, group_amax, stream=None):
     _check(_L.lpq_nvfp4_qdq_grouped(*table.args(), group_amax.data_ptr(), group_amax.numel(), _stream(stream)),
            "lpq_nvfp4_qdq_grouped")
+
+
+def lpq_requantize_fp8blk_grouped(table: RequantTable, stream=None):
+    _check(_L.lpq_requantize_fp8blk_grouped(*table.args(), _stream(stream)), "lpq_requantize_fp8blk_grouped")
 
 
 def lpq_requantize_fp8blk_mxfp8_grouped(table: RequantTable, stream=None):

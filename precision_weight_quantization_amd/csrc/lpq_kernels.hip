@@ -60,6 +60,15 @@
 #ifndef LPQ_RQN_U
 #define LPQ_RQN_U 8
 #endif
+#ifndef LPQ_DQF_U
+#define LPQ_DQF_U 2
+#endif
+#ifndef LPQ_RQT_THREADS
+#define LPQ_RQT_THREADS 256
+#endif
+#ifndef LPQ_RQT_WAVES_PER_SIMD
+#define LPQ_RQT_WAVES_PER_SIMD 1
+#endif
 #ifndef LPQ_TILEQ_THREADS
 #define LPQ_TILEQ_THREADS 256
 #endif
@@ -655,18 +664,20 @@ constexpr int64_t rq_chunk_elems() { return (int64_t)kThreads * 16 * U; }
 constexpr uint32_t kRqStep = kThreads * 16;   // elements between a lane's consecutive vectors
 
 // Walks the (row, column) of a lane's vectors and looks up their tile scales.
+template <int EV>
 struct TileCursor {
+    static constexpr uint32_t kStep = kThreads * EV;   // elements between a lane's consecutive vectors
     const float* scale;   // tile scales of the tensor
     uint32_t N, tn;       // columns, tiles per row
-    uint32_t sr, sc;      // kRqStep = sr * N + sc
+    uint32_t sr, sc;      // kStep = sr * N + sc
     uint32_t r, c;        // position of the lane's current vector
 
-    __device__ __forceinline__ TileCursor(const lpq_requant_tensor& d, int64_t base) {
-        scale = d.src_scale;
-        N = (uint32_t)d.cols;
+    __device__ __forceinline__ TileCursor(const float* tile_scales, int64_t cols, int64_t base) {
+        scale = tile_scales;
+        N = (uint32_t)cols;
         tn = (N + kTile - 1) / kTile;
-        sr = kRqStep / N;
-        sc = kRqStep - sr * N;
+        sr = kStep / N;
+        sc = kStep - sr * N;
         // chunk origin (uniform): a double-precision quotient estimate (base < 2^40,
         // error below 2^-11), corrected by one step
         const double invN = 1.0 / (double)N;
@@ -679,9 +690,9 @@ struct TileCursor {
             r0 += 1;
             c0 -= N;
         }
-        // the lane's offset from the origin: t < N + kRqStep < 2^32 and
+        // the lane's offset from the origin: t < N + kStep < 2^32 and
         // t / N < 4097, so the single-precision estimate is within one
-        const uint32_t t = (uint32_t)c0 + threadIdx.x * 16u;
+        const uint32_t t = (uint32_t)c0 + threadIdx.x * (uint32_t)EV;
         uint32_t q = (uint32_t)((float)t * __builtin_amdgcn_rcpf((float)N));
         if (q * N > t) q -= 1;
         else if (t - q * N >= N) q += 1;
@@ -734,13 +745,18 @@ __device__ __forceinline__ Y16 fp8blk_values16(const v4u& c, float s) {
     return y;
 }
 
+// The block-FP8 codes and tile scales a descriptor names.
+__device__ __forceinline__ const void* codes_of(const lpq_requant_tensor& d) { return d.src; }
+__device__ __forceinline__ const float* tile_scales_of(const lpq_requant_tensor& d) { return d.src_scale; }
+__device__ __forceinline__ const void* codes_of(const lpq_tensor& d) { return d.src; }
+__device__ __forceinline__ const float* tile_scales_of(const lpq_tensor& d) { return reinterpret_cast<const float*>(d.scale); }
+
 // Loads of a lane's U code vectors and their tile scales; with FULL every
 // vector is in range, else vectors past the end read as codes 0, scale 0.
-template <int U, bool FULL>
-__device__ __forceinline__ void rq_load(v4u (&c)[U], float (&s)[U], const lpq_requant_tensor& d, int64_t base,
-                                        int64_t total) {
-    const v4u* src = reinterpret_cast<const v4u*>(d.src) + base / 16 + threadIdx.x;
-    TileCursor cur(d, base);
+template <int U, bool FULL, typename D>
+__device__ __forceinline__ void rq_load(v4u (&c)[U], float (&s)[U], const D& d, int64_t base, int64_t total) {
+    const v4u* src = reinterpret_cast<const v4u*>(codes_of(d)) + base / 16 + threadIdx.x;
+    TileCursor<16> cur(tile_scales_of(d), d.cols, base);
 #pragma unroll
     for (int u = 0; u < U; u++) {
         if (FULL) {
@@ -869,6 +885,149 @@ __global__ __launch_bounds__(kThreads) void k_requant_nvfp4(const lpq_requant_te
     else rq_nvfp4_body<U, false>(W.d, base, total, G);
 }
 
+// Block-wise FP8 dequantization in the flat layout: used when N % 16 == 0 and
+// the arrays are 16-byte aligned (the host checks every tensor of the call), so
+// the codes stream contiguously instead of in 128-byte tile rows.  Same
+// arithmetic as k_fp8blk_dequant: y = BF16(fl(code * s_tile)).
+// A lane takes 8 codes (8 bytes) per step so that its 16 output bytes make
+// each store instruction one contiguous span across the wave.
+template <int U, bool FULL>
+__device__ __forceinline__ void fp8blk_dequant_flat_body(const lpq_tensor& d, int64_t base, int64_t total) {
+    const v2u* src = reinterpret_cast<const v2u*>(d.src) + base / 8 + threadIdx.x;
+    v4u* dst = reinterpret_cast<v4u*>(d.dst);
+    TileCursor<8> cur(reinterpret_cast<const float*>(d.scale), d.cols, base);
+    v2u c[U];
+    float s[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const bool in = FULL || base + (int64_t)(u * kThreads + threadIdx.x) * 8 < total;
+        c[u] = in ? load<kNTL>(src + u * kThreads) : v2u{0u, 0u};
+        s[u] = in ? load<false>(cur.ptr()) : 0.0f;
+        cur.next();
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const int64_t e0 = base + (int64_t)(u * kThreads + threadIdx.x) * 8;
+        const float2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[u].x, false);
+        const float2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[u].x, true);
+        const float2_t e = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[u].y, false);
+        const float2_t f = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[u].y, true);
+        const float sc = s[u];
+        const v4u o = v4u{bf16x2(a[0] * sc, a[1] * sc), bf16x2(b[0] * sc, b[1] * sc), bf16x2(e[0] * sc, e[1] * sc),
+                          bf16x2(f[0] * sc, f[1] * sc)};
+        if (FULL || e0 < total) store<kNTS>(dst + (e0 >> 3), o);
+    }
+}
+
+template <int U>
+constexpr int64_t dqf_chunk_elems() { return (int64_t)kThreads * 8 * U; }
+
+template <int U, bool GROUPED>
+__global__ __launch_bounds__(kThreads) void k_fp8blk_dequant_flat(const lpq_tensor* table, lpq_tensor one,
+                                                                  ChunkMap map) {
+    const Work W = locate<GROUPED>(table, one, map);
+    const int64_t total = W.d.rows * W.d.cols;
+    const int64_t base = W.unit * dqf_chunk_elems<U>();
+    if (base + dqf_chunk_elems<U>() <= total) fp8blk_dequant_flat_body<U, true>(W.d, base, total);
+    else fp8blk_dequant_flat_body<U, false>(W.d, base, total);
+}
+
+// Block-wise FP8 -> block-wise FP8, one 128x128 tile per workgroup: the
+// tile's dequantized values y = BF16(fl(code * s)) stay in registers (16
+// codes per lane per pass), their amax gives the new scale s' = fl(amax/448),
+// and each y is encoded as E4M3(fl(y / s')).
+template <int TT>
+struct RqTileShape {
+    static constexpr int rows_per_pass = TT / 8;   // 8 lanes x 16 codes per 128-column row
+    static constexpr int passes = kTile / rows_per_pass;
+};
+
+template <int TT, bool GROUPED>
+__global__ __launch_bounds__(TT, LPQ_RQT_WAVES_PER_SIMD) void k_requant_fp8blk(const lpq_requant_tensor* table, lpq_requant_tensor one,
+                                                       ChunkMap map) {
+    using S = RqTileShape<TT>;
+    const WorkT<lpq_requant_tensor> W = locate<GROUPED>(table, one, map);
+    const lpq_requant_tensor& d = W.d;
+    const int64_t M = d.rows, N = d.cols;
+    const int64_t tn = (N + kTile - 1) / kTile;
+    const int64_t tile = W.unit;
+    const int64_t r0 = (tile / tn) * kTile, c0 = (tile % tn) * kTile;
+    const int64_t rows = M - r0 < kTile ? M - r0 : kTile;
+    const int64_t cols = N - c0 < kTile ? N - c0 : kTile;
+    const bool fast = rows == kTile && cols == kTile && (N & 15) == 0 &&
+                      ((reinterpret_cast<uintptr_t>(d.src) | reinterpret_cast<uintptr_t>(d.dst)) & 15) == 0;
+    const uint8_t* q = d.src;
+    uint8_t* qo = reinterpret_cast<uint8_t*>(d.dst);
+    const float s = d.src_scale[tile];
+    const int tid = threadIdx.x;
+    const int lr = tid >> 3;           // row inside a pass
+    const int lc = (tid & 7) * 16;     // first column of the lane's 16 codes
+
+    v4u c[S::passes];
+    if (fast) {
+#pragma unroll
+        for (int p = 0; p < S::passes; p++)
+            c[p] = load<kNTL>(reinterpret_cast<const v4u*>(q + (r0 + S::rows_per_pass * p + lr) * N + c0 + lc));
+    } else {
+        for (int p = 0; p < S::passes; p++) {
+            const int64_t r = S::rows_per_pass * p + lr;
+            uint32_t w[4] = {0u, 0u, 0u, 0u};
+            for (int k = 0; k < 16; k++)
+                if (r < rows && lc + k < cols) w[k >> 2] |= (uint32_t)q[(r0 + r) * N + c0 + lc + k] << (8 * (k & 3));
+            c[p] = v4u{w[0], w[1], w[2], w[3]};
+        }
+    }
+    // tile amax of y: BF16 rounding is monotone, so round fl(max|code| * |s|) once
+    float cm = 0.0f;
+#pragma unroll
+    for (int p = 0; p < S::passes; p++) {
+        const uint32_t w[4] = {c[p].x, c[p].y, c[p].z, c[p].w};
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const float2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
+            const float2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);
+            cm = fmaxf(fmaxf(cm, fabsf(a[0])), fabsf(a[1]));
+            cm = fmaxf(fmaxf(cm, fabsf(b[0])), fabsf(b[1]));
+        }
+    }
+    const uint32_t mb = (bf16x2(cm * fabsf(s), 0.0f) & 0xffffu) << 16;   // codes outside the tile read as 0
+    const float amax = __uint_as_float(block_reduce_max<TT>(mb));
+    const float s2 = amax / kE4M3Max;   // correctly rounded division
+    if (tid == 0) reinterpret_cast<float*>(d.dst_scale)[tile] = s2;
+    const bool tiny = s2 > 0.0f && s2 < kTinyScale;
+    const float sd = tiny ? s2 * kPreScale : s2;
+    const float r = s2 > 0.0f ? rcp_rn(sd) : 0.0f;
+
+#pragma unroll
+    for (int p = 0; p < S::passes; p++) {
+        const Y16 y = fp8blk_values16(c[p], s);
+        float x[16];
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            x[k] = y.lo.x[k];
+            x[8 + k] = y.hi.x[k];
+        }
+        if (tiny) {
+#pragma unroll
+            for (int k = 0; k < 16; k++) x[k] *= kPreScale;
+        }   // tile-uniform
+        uint32_t o[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const float q0 = quot_rn(x[4 * k + 0], sd, r), q1 = quot_rn(x[4 * k + 1], sd, r);
+            const float q2 = quot_rn(x[4 * k + 2], sd, r), q3 = quot_rn(x[4 * k + 3], sd, r);
+            o[k] = e4m3x2<true>(q2, q3, e4m3x2<false>(q0, q1, 0u));
+        }
+        const int64_t row = S::rows_per_pass * p + lr;
+        if (fast) {
+            store<kNTS>(reinterpret_cast<v4u*>(qo + (r0 + row) * N + c0 + lc), v4u{o[0], o[1], o[2], o[3]});
+        } else if (row < rows) {
+            for (int k = 0; k < 16; k++)
+                if (lc + k < cols) qo[(r0 + row) * N + c0 + lc + k] = (uint8_t)(o[k >> 2] >> (8 * (k & 3)));
+        }
+    }
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -890,7 +1049,7 @@ inline lpq_status launched() {
     return LPQ_OK;
 }
 
-enum Kind { FP8BLK_Q, FP8BLK_DQ, MXFP8_Q, MXFP8_DQ, NV_AMAX, NV_Q, NV_DQ, NV_QDQ, RQ_MX, RQ_AMAX, RQ_NV };
+enum Kind { FP8BLK_Q, FP8BLK_DQ, FP8BLK_DQF, MXFP8_Q, MXFP8_DQ, NV_AMAX, NV_Q, NV_DQ, NV_QDQ, RQ_FP8, RQ_MX, RQ_AMAX, RQ_NV };
 
 // Shape and pointer checks of one tensor for one kind of call.
 lpq_status check_tensor(Kind k, const lpq_tensor& t, int32_t n_groups) {
@@ -904,6 +1063,10 @@ lpq_status check_tensor(Kind k, const lpq_tensor& t, int32_t n_groups) {
     case FP8BLK_Q:
     case FP8BLK_DQ:
         if (!aligned(k == FP8BLK_Q ? t.src : t.dst, 2) || !aligned(t.scale, 4)) return LPQ_ERR_ALIGN;
+        break;
+    case FP8BLK_DQF:   // not a caller-visible kind: the flat layout's extra conditions
+        if (t.cols % 8 || t.rows >= (int64_t(1) << 31) || t.cols >= (int64_t(1) << 31) - kRqStep) return LPQ_ERR_SHAPE;
+        if (!aligned(t.src, 8) || !aligned(t.dst, 16) || !aligned(t.scale, 4)) return LPQ_ERR_ALIGN;
         break;
     case MXFP8_Q:
         if (t.cols % 32) return LPQ_ERR_SHAPE;
@@ -934,6 +1097,7 @@ lpq_status check_tensor(Kind k, const lpq_requant_tensor& t, int32_t n_groups) {
     if (!t.src || !t.src_scale) return LPQ_ERR_NULL;
     if (k != RQ_AMAX && (!t.dst || !t.dst_scale)) return LPQ_ERR_NULL;
     if (t.reserved != 0) return LPQ_ERR_ARG;
+    if (k == RQ_FP8) return aligned(t.src_scale, 4) && aligned(t.dst_scale, 4) ? LPQ_OK : LPQ_ERR_ALIGN;
     if (t.cols % (k == RQ_MX ? 32 : 16)) return LPQ_ERR_SHAPE;
     if (t.rows >= (int64_t(1) << 31) || t.cols >= (int64_t(1) << 31) - kRqStep) return LPQ_ERR_SHAPE;
     if (!aligned(t.src, 16) || !aligned(t.src_scale, 4)) return LPQ_ERR_ALIGN;
@@ -949,6 +1113,7 @@ int64_t units(Kind k, const lpq_tensor& t) {
     switch (k) {
     case FP8BLK_Q:
     case FP8BLK_DQ: return ((t.rows + kTile - 1) / kTile) * ((t.cols + kTile - 1) / kTile);
+    case FP8BLK_DQF: return (n + dqf_chunk_elems<LPQ_DQF_U>() - 1) / dqf_chunk_elems<LPQ_DQF_U>();
     case MXFP8_Q: return (n + chunk_elems<LPQ_MXQ_U>() - 1) / chunk_elems<LPQ_MXQ_U>();
     case MXFP8_DQ: return (n + chunk_elems<LPQ_MXD_U>() - 1) / chunk_elems<LPQ_MXD_U>();
     case NV_AMAX: return (n + chunk_elems<LPQ_AMAX_U>() - 1) / chunk_elems<LPQ_AMAX_U>();
@@ -962,6 +1127,7 @@ int64_t units(Kind k, const lpq_tensor& t) {
 int64_t units(Kind k, const lpq_requant_tensor& t) {
     const int64_t n = t.rows * t.cols;
     switch (k) {
+    case RQ_FP8: return ((t.rows + kTile - 1) / kTile) * ((t.cols + kTile - 1) / kTile);
     case RQ_MX: return (n + rq_chunk_elems<LPQ_RQM_U>() - 1) / rq_chunk_elems<LPQ_RQM_U>();
     case RQ_AMAX: return (n + rq_chunk_elems<LPQ_RQA_U>() - 1) / rq_chunk_elems<LPQ_RQA_U>();
     case RQ_NV: return (n + rq_chunk_elems<LPQ_RQN_U>() - 1) / rq_chunk_elems<LPQ_RQN_U>();
@@ -978,6 +1144,7 @@ void dispatch(Kind k, dim3 grid, hipStream_t stream, const lpq_tensor* tab, cons
         switch (k) {
         case FP8BLK_Q: hipLaunchKernelGGL((k_fp8blk_quant<LPQ_TILEQ_THREADS, true>), grid, tileq, 0, stream, tab, one, map); break;
         case FP8BLK_DQ: hipLaunchKernelGGL((k_fp8blk_dequant<LPQ_TILED_THREADS, true>), grid, tiled, 0, stream, tab, one, map); break;
+        case FP8BLK_DQF: hipLaunchKernelGGL((k_fp8blk_dequant_flat<LPQ_DQF_U, true>), grid, flat, 0, stream, tab, one, map); break;
         case MXFP8_Q: hipLaunchKernelGGL((k_mxfp8_quant<LPQ_MXQ_U, true>), grid, flat, 0, stream, tab, one, map); break;
         case MXFP8_DQ: hipLaunchKernelGGL((k_mxfp8_dequant<LPQ_MXD_U, true>), grid, flat, 0, stream, tab, one, map); break;
         case NV_AMAX: hipLaunchKernelGGL((k_amax<LPQ_AMAX_U, true>), grid, flat, 0, stream, tab, one, map, fb); break;
@@ -990,6 +1157,7 @@ void dispatch(Kind k, dim3 grid, hipStream_t stream, const lpq_tensor* tab, cons
         switch (k) {
         case FP8BLK_Q: hipLaunchKernelGGL((k_fp8blk_quant<LPQ_TILEQ_THREADS, false>), grid, tileq, 0, stream, tab, one, map); break;
         case FP8BLK_DQ: hipLaunchKernelGGL((k_fp8blk_dequant<LPQ_TILED_THREADS, false>), grid, tiled, 0, stream, tab, one, map); break;
+        case FP8BLK_DQF: hipLaunchKernelGGL((k_fp8blk_dequant_flat<LPQ_DQF_U, false>), grid, flat, 0, stream, tab, one, map); break;
         case MXFP8_Q: hipLaunchKernelGGL((k_mxfp8_quant<LPQ_MXQ_U, false>), grid, flat, 0, stream, tab, one, map); break;
         case MXFP8_DQ: hipLaunchKernelGGL((k_mxfp8_dequant<LPQ_MXD_U, false>), grid, flat, 0, stream, tab, one, map); break;
         case NV_AMAX: hipLaunchKernelGGL((k_amax<LPQ_AMAX_U, false>), grid, flat, 0, stream, tab, one, map, fb); break;
@@ -1003,9 +1171,10 @@ void dispatch(Kind k, dim3 grid, hipStream_t stream, const lpq_tensor* tab, cons
 
 void dispatch(Kind k, dim3 grid, hipStream_t stream, const lpq_requant_tensor* tab, const lpq_requant_tensor& one,
               const ChunkMap& map, const float* fa, float* fb) {
-    const dim3 flat(kThreads);
+    const dim3 flat(kThreads), tile(LPQ_RQT_THREADS);
     if (tab) {
         switch (k) {
+        case RQ_FP8: hipLaunchKernelGGL((k_requant_fp8blk<LPQ_RQT_THREADS, true>), grid, tile, 0, stream, tab, one, map); break;
         case RQ_MX: hipLaunchKernelGGL((k_requant_mxfp8<LPQ_RQM_U, true>), grid, flat, 0, stream, tab, one, map); break;
         case RQ_AMAX: hipLaunchKernelGGL((k_requant_amax<LPQ_RQA_U, true>), grid, flat, 0, stream, tab, one, map, fb); break;
         case RQ_NV: hipLaunchKernelGGL((k_requant_nvfp4<LPQ_RQN_U, true>), grid, flat, 0, stream, tab, one, map, fa, fb); break;
@@ -1013,6 +1182,7 @@ void dispatch(Kind k, dim3 grid, hipStream_t stream, const lpq_requant_tensor* t
         }
     } else {
         switch (k) {
+        case RQ_FP8: hipLaunchKernelGGL((k_requant_fp8blk<LPQ_RQT_THREADS, false>), grid, tile, 0, stream, tab, one, map); break;
         case RQ_MX: hipLaunchKernelGGL((k_requant_mxfp8<LPQ_RQM_U, false>), grid, flat, 0, stream, tab, one, map); break;
         case RQ_AMAX: hipLaunchKernelGGL((k_requant_amax<LPQ_RQA_U, false>), grid, flat, 0, stream, tab, one, map, fb); break;
         case RQ_NV: hipLaunchKernelGGL((k_requant_nvfp4<LPQ_RQN_U, false>), grid, flat, 0, stream, tab, one, map, fa, fb); break;
@@ -1134,7 +1304,9 @@ lpq_status lpq_quantize_fp8blk(const uint16_t* w, int64_t M, int64_t N, uint8_t*
 }
 
 lpq_status lpq_dequantize_fp8blk(const uint8_t* q, const float* s, int64_t M, int64_t N, uint16_t* y, void* stream) {
-    return single(FP8BLK_DQ, make_one(q, y, const_cast<float*>(s), M, N), nullptr, nullptr, stream);
+    const lpq_tensor one = make_one(q, y, const_cast<float*>(s), M, N);
+    const bool flat = check_tensor(FP8BLK_DQ, one, 0) == LPQ_OK && check_tensor(FP8BLK_DQF, one, 0) == LPQ_OK;
+    return single(flat ? FP8BLK_DQF : FP8BLK_DQ, one, nullptr, nullptr, stream);
 }
 
 lpq_status lpq_quantize_mxfp8(const uint16_t* w, int64_t M, int64_t N, uint8_t* q, uint8_t* e, void* stream) {
@@ -1180,7 +1352,10 @@ lpq_status lpq_quantize_fp8blk_grouped(const lpq_tensor* host, const lpq_tensor*
 }
 
 lpq_status lpq_dequantize_fp8blk_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, void* stream) {
-    return grouped(FP8BLK_DQ, host, dev, n, 0, nullptr, nullptr, stream);
+    // the flat kernel when every tensor allows it, else the tile kernel for all
+    bool flat = host != nullptr && n > 0;
+    for (int32_t i = 0; flat && i < n; i++) flat = check_tensor(FP8BLK_DQF, host[i], 0) == LPQ_OK;
+    return grouped(flat ? FP8BLK_DQF : FP8BLK_DQ, host, dev, n, 0, nullptr, nullptr, stream);
 }
 
 lpq_status lpq_quantize_mxfp8_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, void* stream) {
@@ -1231,6 +1406,16 @@ lpq_status lpq_nvfp4_qdq_grouped(const lpq_tensor* host, const lpq_tensor* dev, 
     if (n_groups <= 0) return LPQ_ERR_SHAPE;
     if (!aligned(group_amax, 4)) return LPQ_ERR_ALIGN;
     return grouped(NV_QDQ, host, dev, n, n_groups, group_amax, nullptr, stream);
+}
+
+lpq_status lpq_requantize_fp8blk(const uint8_t* q, const float* s, int64_t M, int64_t N, uint8_t* q_out, float* s_out,
+                                 void* stream) {
+    return single(RQ_FP8, make_requant(q, s, q_out, s_out, M, N), nullptr, nullptr, stream);
+}
+
+lpq_status lpq_requantize_fp8blk_grouped(const lpq_requant_tensor* host, const lpq_requant_tensor* dev, int32_t n,
+                                         void* stream) {
+    return grouped(RQ_FP8, host, dev, n, 0, nullptr, nullptr, stream);
 }
 
 lpq_status lpq_requantize_fp8blk_mxfp8(const uint8_t* q, const float* s, int64_t M, int64_t N, uint8_t* q_out,

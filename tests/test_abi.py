@@ -105,6 +105,11 @@ def test_grouped_validation(lib):
 
 def test_requant_validation(lib):
     L = lib.raw()
+    assert L.lpq_requantize_fp8blk(None, P, 4, 5, P, P, None) == 1
+    assert L.lpq_requantize_fp8blk(P, P, 4, 5, P, None, None) == 1
+    assert L.lpq_requantize_fp8blk(P, P, 0, 5, P, P, None) == 2
+    assert L.lpq_requantize_fp8blk(P, P + 2, 4, 5, P, P, None) == 3          # FP32 scales
+    assert L.lpq_requantize_fp8blk(P, P, 4, 5, P, P + 1, None) == 3
     assert L.lpq_requantize_fp8blk_mxfp8(None, P, 4, 32, P, P, None) == 1
     assert L.lpq_requantize_fp8blk_mxfp8(P, None, 4, 32, P, P, None) == 1
     assert L.lpq_requantize_fp8blk_mxfp8(P, P, 4, 32, None, P, None) == 1
@@ -114,6 +119,7 @@ def test_requant_validation(lib):
     assert L.lpq_requantize_fp8blk_mxfp8(P + 8, P, 4, 32, P, P, None) == 3   # codes need 16 bytes
     assert L.lpq_requantize_fp8blk_mxfp8(P, P + 2, 4, 32, P, P, None) == 3   # FP32 scales
     assert L.lpq_requantize_fp8blk_mxfp8(P, P, 4, 32, P + 8, P, None) == 3
+    assert L.lpq_requantize_fp8blk_mxfp8(P, P, 1 << 31, 32, P, P, None) == 2  # flat targets: M < 2^31
     assert L.lpq_fp8blk_amax(P, P, 4, 32, None, 0, None) == 1
     assert L.lpq_fp8blk_amax(P, P, 4, 24, P, 0, None) == 2                   # N % 16
     assert L.lpq_fp8blk_amax(P, P, 4, 32, P + 2, 0, None) == 3

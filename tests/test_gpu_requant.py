@@ -1,8 +1,8 @@
 """Re-quantization of block-wise FP8 weights (FP8 codes + FP32 tile scales) into
-MXFP8 and NVFP4, HIP path vs the CPU oracle, bit for bit.
+block-wise FP8, MXFP8 and NVFP4, HIP path vs the CPU oracle, bit for bit.
 
 The oracle is the unfused composition: block-FP8 dequantization to BF16, then
-the MXFP8 or NVFP4 quantizer.  All calls go through the C ABI; the tolerance is
+the target format's quantizer.  All calls go through the C ABI; the tolerance is
 zero for codes, scale bytes, the group amax and the global scale.
 """
 import numpy as np
@@ -36,6 +36,15 @@ def f32_bits(t) -> np.ndarray:
     return np.asarray(t, np.float32).view(np.uint32)
 
 
+def check_fp8(lpq, q_np, s_np, name, q_dev=None, out=None):
+    q = dev_u8(q_np) if q_dev is None else q_dev
+    qo, so = lpq.lpq_requantize_fp8blk(q, dev_f32(s_np), *(out or (None, None)))
+    oq, os_ = O.fp8blk_requantize_fp8blk(q_np, s_np)
+    bad = report(f"requant fp8blk codes {name}", host_u8(qo), oq)
+    bad += report(f"requant fp8blk scales {name}", f32_bits(so.cpu().numpy()), f32_bits(os_))
+    return bad
+
+
 def check_mx(lpq, q_np, s_np, name):
     qo, eo = lpq.lpq_requantize_fp8blk_mxfp8(dev_u8(q_np), dev_f32(s_np))
     oq, oe = O.fp8blk_requantize_mxfp8(q_np, s_np)
@@ -67,6 +76,26 @@ def random_case(M, N, seed, lo=-20, hi=10, signed=False, zero_tile=True):
 SHAPES = [(1, 32), (3, 64), (200, 320), (130, 2080), (257, 96), (40, 4128), (2, 16416), (1000, 7168)]
 
 
+@pytest.mark.parametrize("M,N", [(1, 1), (7, 3), (130, 200), (128, 128), (257, 1000), (1000, 544), (256, 2048),
+                                 (129, 4100)])
+def test_requant_fp8blk_random(lpq, M, N):
+    q, s = random_case(M, N, 700 + M + N)
+    assert check_fp8(lpq, q, s, f"{M}x{N}") == 0
+
+
+def test_requant_fp8blk_unaligned(lpq):
+    """Code arrays that are not 16-byte aligned, in and out (the per-byte path)."""
+    M, N = 256, 384
+    q, s = random_case(M, N, 77)
+    buf = torch.zeros(M * N + 64, dtype=torch.uint8, device=DEV)
+    qin = buf[3:3 + M * N].view(M, N)
+    qin.copy_(dev_u8(q))
+    obuf = torch.zeros(M * N + 64, dtype=torch.uint8, device=DEV)
+    qout = obuf[5:5 + M * N].view(M, N)
+    sout = torch.empty(O.fp8blk_scale_shape(M, N), dtype=torch.float32, device=DEV)
+    assert check_fp8(lpq, q, s, "unaligned", q_dev=qin, out=(qout, sout)) == 0
+
+
 @pytest.mark.parametrize("M,N", SHAPES)
 def test_requant_mxfp8_random(lpq, M, N):
     q, s = random_case(M, N, 100 + M + N)
@@ -89,6 +118,7 @@ def test_requant_scale_extremes(lpq, lo, hi, signed):
     q, s = random_case(M, N, 300 + lo + hi, lo, hi, signed)
     bad = check_mx(lpq, q, s, f"[{lo},{hi}] signed={signed}")
     bad += check_nv(lpq, q, s, f"[{lo},{hi}] signed={signed}")
+    bad += check_fp8(lpq, q, s, f"[{lo},{hi}] signed={signed}")
     assert bad == 0
 
 
@@ -103,6 +133,7 @@ def test_requant_zero_and_sign(lpq):
     s[1, 2] = -0.0
     bad = check_mx(lpq, q, s, "zeros")
     bad += check_nv(lpq, q, s, "zeros")
+    bad += check_fp8(lpq, q, s, "zeros")
     assert bad == 0
 
 
@@ -113,6 +144,7 @@ def test_requant_quantized_weights(lpq):
     q, s = O.fp8blk_quantize(w)
     bad = check_mx(lpq, q, s, "gate 768x2048")
     bad += check_nv(lpq, q, s, "gate 768x2048")
+    bad += check_fp8(lpq, q, s, "gate 768x2048")
     assert bad == 0
 
 
@@ -133,6 +165,10 @@ def test_requant_matches_unfused_kernels(lpq):
     p2, s2, g2 = lpq.lpq_requantize_fp8blk_nvfp4(q, s, a2)
     bad += report("fused vs unfused nvfp4 packed", host_u8(p2), host_u8(p1))
     bad += report("fused vs unfused nvfp4 scales", host_u8(s2), host_u8(s1))
+    bq, bs = lpq.lpq_quantize_fp8blk(y)
+    fq8, fs8 = lpq.lpq_requantize_fp8blk(q, s)
+    bad += report("fused vs unfused fp8blk codes", host_u8(fq8), host_u8(bq))
+    bad += report("fused vs unfused fp8blk scales", f32_bits(fs8.cpu().numpy()), f32_bits(bs.cpu().numpy()))
     assert bad == 0
 
 
@@ -148,12 +184,25 @@ def test_requant_grouped(lpq):
     qd = [dev_u8(q) for q, _ in src]
     sd = [dev_f32(s) for _, s in src]
 
+    # block-wise FP8 (ragged shapes added: any N)
+    fshapes = shapes + [(5, 7), (130, 333)]
+    fsrc = src + [random_case(M, N, 900 + i) for i, (M, N) in enumerate(fshapes[len(shapes):])]
+    fq = [torch.empty((M, N), dtype=torch.uint8, device=DEV) for M, N in fshapes]
+    fs = [torch.empty(O.fp8blk_scale_shape(M, N), dtype=torch.float32, device=DEV) for M, N in fshapes]
+    t = lpq.RequantTable([(dev_u8(q), dev_f32(s), fq[i], fs[i], M, N, 0)
+                          for i, ((q, s), (M, N)) in enumerate(zip(fsrc, fshapes))])
+    lpq.lpq_requantize_fp8blk_grouped(t)
+    bad = 0
+    for i, (q, s) in enumerate(fsrc):
+        oq, os_ = O.fp8blk_requantize_fp8blk(q, s)
+        bad += report(f"grouped fp8blk codes #{i}", host_u8(fq[i]), oq)
+        bad += report(f"grouped fp8blk scales #{i}", f32_bits(fs[i].cpu().numpy()), f32_bits(os_))
+
     # MXFP8
     mq = [torch.empty((M, N), dtype=torch.uint8, device=DEV) for M, N in shapes]
     me = [torch.empty((M, N // 32), dtype=torch.uint8, device=DEV) for M, N in shapes]
     t = lpq.RequantTable([(qd[i], sd[i], mq[i], me[i], M, N, 0) for i, (M, N) in enumerate(shapes)])
     lpq.lpq_requantize_fp8blk_mxfp8_grouped(t)
-    bad = 0
     for i, (q, s) in enumerate(src):
         oq, oe = O.fp8blk_requantize_mxfp8(q, s)
         bad += report(f"grouped mxfp8 codes #{i}", host_u8(mq[i]), oq)

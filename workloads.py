@@ -20,10 +20,10 @@ distributions named for each workload.
           down 7168x2048} -> block-wise FP8 quantize + dequantize
   fp8train  the nvfp4 workload's weights held in block-wise FP8 (as an FP8
           trainer keeps them; made once by this library's quantizer) ->
-          fused re-quantization into MXFP8 (experts) and NVFP4 (experts and
-          q/k/v, sibling groups as above), each next to the unfused
-          dequantize-then-quantize sequence on the same data.  Timed apart
-          from the step.
+          fused re-quantization into block-wise FP8 (all tensors), MXFP8
+          (experts) and NVFP4 (experts and q/k/v, sibling groups as above),
+          each next to the unfused dequantize-then-quantize sequence on the
+          same data.  Timed apart from the step.
 
 Buckets: one grouped launch per transformer layer (the unit a weight sync
 streams), or one launch over the whole workload.
@@ -242,6 +242,11 @@ def requant_ops(ws: WeightSet, q8, s8, codes: Slab, out: Slab, bucket: str, devi
     n_groups = max(s.group for s in specs) + 1
     exset = set(ex)
 
+    # block-FP8 targets of every tensor (the page's FP8 -> BF16 -> FP8 sync)
+    fcodes = reslab(codes, specs, 1)
+    fsl = Slab([4 * tiles_of(s) for s in specs], device)
+    fq = [fcodes.view(i, (s.M, s.N), torch.uint8) for i, s in enumerate(specs)]
+    fs = [fsl.view(i, ((s.M + 127) // 128, (s.N + 127) // 128), torch.float32) for i, s in enumerate(specs)]
     # MXFP8 targets of the experts
     mcodes = reslab(codes, [specs[i] for i in ex], 1)
     eb = Slab([specs[i].numel // 32 for i in ex], device)
@@ -260,8 +265,11 @@ def requant_ops(ws: WeightSet, q8, s8, codes: Slab, out: Slab, bucket: str, devi
     by_shape = sorted(range(len(specs)), key=lambda i: (specs[i].M, specs[i].N, i))
     tamax = lpq.RequantTable([(q8[i], s8[i], None, None, specs[i].M, specs[i].N, specs[i].group) for i in by_shape])
     rmx, rnv, dq_mx, q_mx, dq_nv, a_nv, q_nv = [], [], [], [], [], [], []
+    rf8, q_f8 = [], []
     for idx in _buckets(ws, bucket):
         ie = [i for i in idx if i in exset]
+        rf8.append(lpq.RequantTable([(q8[i], s8[i], fq[i], fs[i], specs[i].M, specs[i].N, 0) for i in idx]))
+        q_f8.append(lpq.TensorTable([(y[i], fq[i], fs[i], specs[i].M, specs[i].N, 0) for i in idx]))
         rmx.append(lpq.RequantTable([(q8[i], s8[i], mq[i], me[i], specs[i].M, specs[i].N, 0) for i in ie]))
         rnv.append(lpq.RequantTable([(q8[i], s8[i], p[i], sb[i], specs[i].M, specs[i].N, specs[i].group)
                                      for i in idx]))
@@ -278,10 +286,16 @@ def requant_ops(ws: WeightSet, q8, s8, codes: Slab, out: Slab, bucket: str, devi
         lpq.lpq_quantize_mxfp8_grouped(q_mx[k])
 
 
+    f8_bytes = 2 * n + 8 * t
     mx_bytes = 2 * n_ex + n_ex // 32 + 4 * t_ex
     amax_bytes = n + 4 * t
     nv_bytes = n + 4 * t + n // 2 + n // 16 + 4 * n_groups
     ops = [
+        Op("requant.fp8blk[fp8train]", "fp8train", f8_bytes,
+           [lambda r=r: lpq.lpq_requantize_fp8blk_grouped(r) for r in rf8]),
+        Op("requant.fp8blk.unfused[fp8train]", "fp8train", f8_bytes,
+           [f for k in range(len(rf8)) for f in (lambda k=k: lpq.lpq_dequantize_fp8blk_grouped(dq_nv[k]),
+                                                  lambda k=k: lpq.lpq_quantize_fp8blk_grouped(q_f8[k]))]),
         Op("requant.mxfp8[fp8train]", "fp8train", mx_bytes,
            [lambda r=r: lpq.lpq_requantize_fp8blk_mxfp8_grouped(r) for r in rmx]),
         Op("requant.mxfp8.unfused[fp8train]", "fp8train", mx_bytes,
@@ -295,7 +309,7 @@ def requant_ops(ws: WeightSet, q8, s8, codes: Slab, out: Slab, bucket: str, devi
            + [lambda: lpq.lpq_nvfp4_amax_grouped(a_nv, amax, accumulate=False)]
            + [lambda t=t: lpq.lpq_quantize_nvfp4_grouped(t, amax, g) for t in q_nv]),
     ]
-    return ops, dict(ex=ex, mq=mq, me=me, p=p, sb=sb, amax=amax, g=g, n_groups=n_groups, q8=q8, s8=s8)
+    return ops, dict(ex=ex, fq=fq, fs=fs, mq=mq, me=me, p=p, sb=sb, amax=amax, g=g, n_groups=n_groups, q8=q8, s8=s8)
 
 
 def activation_ops(x: torch.Tensor, y: torch.Tensor):
