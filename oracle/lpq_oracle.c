@@ -199,8 +199,10 @@ OC_API void oc_fp8blk_dequantize(const uint8_t* q, const float* s, int64_t M, in
 /* ([LPRL] "3. Unified MXFP8")                                               */
 /* ------------------------------------------------------------------------ */
 
-/* N must be a multiple of 32.  q: [M, N] codes; e: [M, N/32] scale bytes. */
-OC_API void oc_mxfp8_quantize(const uint16_t* w, int64_t M, int64_t N, uint8_t* q, uint8_t* e) {
+/* N must be a multiple of 32.  q: [M, N] codes; e: [M, N/32] scale bytes.
+ * `rule` turns the block amax into the scale byte. */
+static void mxfp8_quantize_with(const uint16_t* w, int64_t M, int64_t N, uint8_t* q, uint8_t* e,
+                                uint8_t (*rule)(float)) {
     int64_t nb = N / 32;
     for (int64_t r = 0; r < M; r++)
         for (int64_t b = 0; b < nb; b++) {
@@ -210,12 +212,38 @@ OC_API void oc_mxfp8_quantize(const uint16_t* w, int64_t M, int64_t N, uint8_t* 
                 float a = fabsf(oc_bf16_to_f32(blk[k]));
                 if (a > amax) amax = a;
             }
-            uint8_t byte = oc_mxfp8_scale_byte(amax);
+            uint8_t byte = rule(amax);
             e[r * nb + b] = byte;
             float X = oc_ue8m0_decode(byte);              /* 2^(byte-127) */
             for (int k = 0; k < 32; k++)
                 q[r * N + b * 32 + k] = oc_e4m3_encode(oc_bf16_to_f32(blk[k]) / X);
         }
+}
+
+OC_API void oc_mxfp8_quantize(const uint16_t* w, int64_t M, int64_t N, uint8_t* q, uint8_t* e) {
+    mxfp8_quantize_with(w, M, N, q, e, oc_mxfp8_scale_byte);
+}
+
+/* MXFP8 with the floor exponent rule of the OCP Microscaling (MX) Formats
+ * specification v1.0 (conversion of FP32 vectors to MX, section 6.3): the
+ * shared exponent is floor(log2(amax)) minus the largest exponent of the
+ * element format (8 for E4M3, whose maximum is 1.75 * 2^8), and a scaled
+ * element beyond 448 saturates.  The pages fix only "UE8M0 power-of-two
+ * scales"; this is the alternative to the no-saturation rule above.  A block
+ * of zeros gets byte 0; the byte is clamped to [0, 254]. */
+OC_API uint8_t oc_mxfp8_floor_scale_byte(float amax) {
+    if (amax == 0.0f) return 0;
+    int k;
+    (void)frexp((double)amax, &k);          /* amax = m * 2^k, 0.5 <= m < 1 */
+    int e = (k - 1) - 8;                    /* floor(log2 amax) - 8 */
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return (uint8_t)(e + 127);
+}
+
+/* Same layout as oc_mxfp8_quantize; codes E4M3(fl(x / 2^(byte-127))), saturating. */
+OC_API void oc_mxfp8_floor_quantize(const uint16_t* w, int64_t M, int64_t N, uint8_t* q, uint8_t* e) {
+    mxfp8_quantize_with(w, M, N, q, e, oc_mxfp8_floor_scale_byte);
 }
 
 /* y = BF16(fl(E4M3value * 2^(byte-127))). */
@@ -246,6 +274,12 @@ OC_API float oc_amax_bf16(const uint16_t* w, int64_t n) {
 /* Global scale g = fl(A / (6 * 448)); 6 * 448 = 2688 is exact.  A is the
  * amax of the tensor, or of its whole sibling group ([VERL] 2.4). */
 OC_API float oc_nvfp4_global_scale(float A) { return A / (6.0f * 448.0f); }
+
+/* The same global scale in the reciprocal form some exporters store
+ * ("verl NVFP4 QAT" 2.5: a compressed-tensors export whose sibling groups
+ * are fused by taking the minimum of this form): fl(2688 / A).  A group of
+ * zeros gives +Inf (the IEEE quotient). */
+OC_API float oc_nvfp4_global_scale_reciprocal(float A) { return (6.0f * 448.0f) / A; }
 
 /* The E4M3 block-scale code of a block with amax b under global scale g. */
 OC_API uint8_t oc_nvfp4_block_scale(float b, float g) {
@@ -333,4 +367,7 @@ OC_API void oc_f32_to_bf16_n(const float* v, int64_t n, uint16_t* out) {
 }
 OC_API void oc_mxfp8_scale_byte_n(const float* amax, int64_t n, uint8_t* out) {
     for (int64_t i = 0; i < n; i++) out[i] = oc_mxfp8_scale_byte(amax[i]);
+}
+OC_API void oc_mxfp8_floor_scale_byte_n(const float* amax, int64_t n, uint8_t* out) {
+    for (int64_t i = 0; i < n; i++) out[i] = oc_mxfp8_floor_scale_byte(amax[i]);
 }

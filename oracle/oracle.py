@@ -74,6 +74,9 @@ _SIG = {
     "oc_e2m1_encode_n": (None, [_f32p, _i64, _u8p]),
     "oc_f32_to_bf16_n": (None, [_f32p, _i64, _u16p]),
     "oc_mxfp8_scale_byte_n": (None, [_f32p, _i64, _u8p]),
+    "oc_mxfp8_floor_scale_byte_n": (None, [_f32p, _i64, _u8p]),
+    "oc_mxfp8_floor_quantize": (None, [_u16p, _i64, _i64, _u8p, _u8p]),
+    "oc_nvfp4_global_scale_reciprocal": (ctypes.c_float, [ctypes.c_float]),
 }
 
 
@@ -167,6 +170,19 @@ class Oracle:
         self.L.oc_mxfp8_quantize(_p(w, _u16p), M, N, _p(q, _u8p), _p(e, _u8p))
         return q, e
 
+    def mxfp8_floor_scale_byte(self, amax) -> np.ndarray:
+        return self._vec(self.L.oc_mxfp8_floor_scale_byte_n, amax, np.uint8)
+
+    def mxfp8_floor_quantize(self, w: np.ndarray):
+        """BF16 [M,N] (N % 32 == 0) -> (E4M3 codes, UE8M0 bytes) under the floor exponent rule."""
+        w = _bf16(w)
+        M, N = w.shape
+        assert N % 32 == 0
+        q = np.empty((M, N), np.uint8)
+        e = np.empty((M, N // 32), np.uint8)
+        self.L.oc_mxfp8_floor_quantize(_p(w, _u16p), M, N, _p(q, _u8p), _p(e, _u8p))
+        return q, e
+
     def mxfp8_dequantize(self, q: np.ndarray, e: np.ndarray) -> np.ndarray:
         q = np.ascontiguousarray(q, dtype=np.uint8)
         e = np.ascontiguousarray(e, dtype=np.uint8)
@@ -183,6 +199,9 @@ class Oracle:
 
     def nvfp4_global_scale(self, A: float) -> float:
         return float(self.L.oc_nvfp4_global_scale(float(A)))
+
+    def nvfp4_global_scale_reciprocal(self, A: float) -> float:
+        return float(self.L.oc_nvfp4_global_scale_reciprocal(float(A)))
 
     def nvfp4_block_scale(self, b: float, g: float) -> int:
         return int(self.L.oc_nvfp4_block_scale(float(b), float(g)))

@@ -233,6 +233,72 @@ def pin_mxfp8_byte_closed_form(O):
     assert got.max() <= 254
 
 
+def pin_mxfp8_floor_byte_closed_form(O):
+    """The floor rule of the OCP MX specification on all 32,640 non-negative finite BF16
+    amax values: byte = max(0, Eb - 8) read off the exponent bits (floor(log2 amax) = Eb - 127
+    for normal values, and E4M3's largest exponent is 8); it is the ceiling rule's byte
+    whenever the significand is at most 1.75 and one less otherwise."""
+    u = all_finite_bf16()
+    u = u[u < 0x8000]
+    amax = bf16_f32(u)
+    got = O.mxfp8_floor_scale_byte(amax).astype(np.int64)
+    Eb = (u.astype(np.int64) >> 7) & 0xFF
+    m7 = u.astype(np.int64) & 0x7F
+    assert np.array_equal(got, np.maximum(0, Eb - 8))
+    ceil = O.mxfp8_scale_byte(amax).astype(np.int64)
+    big = (m7 > 96) & (Eb >= 8)
+    assert np.array_equal(got[~big], ceil[~big]) and np.array_equal(got[big], ceil[big] - 1)
+
+
+def pin_mxfp8_floor_quantize(O):
+    """Floor-rule MXFP8 on blocks of E4M3 values times 2^k: with the block amax in
+    [256, 448] * 2^k the byte is 127 + k and every code is the value's own; with one
+    element at 480 * 2^k (a BF16 value above E4M3's 448) the byte is still 127 + k, that
+    element saturates to 448 and the others keep their codes.  Elsewhere (random MoE-like
+    data) each code is the nearest-even E4M3 point of w / 2^(byte-127), saturating."""
+    rng = np.random.default_rng(31)
+    M, N = 24, 256
+    nb = N // 32
+    k = rng.integers(-100, 100, (M, nb))
+    vals = _e4m3_values(rng, M * N).reshape(M, N)
+    vals = np.where(np.abs(vals) > 240.0, vals / 4.0, vals)    # still E4M3 values, all below 256
+    sat = rng.integers(0, 2, (M, nb)).astype(bool)
+    pos = rng.integers(0, 32, (M, nb))
+    for r in range(M):
+        for b in range(nb):
+            sgn = 1.0 if rng.integers(0, 2) else -1.0
+            vals[r, 32 * b + pos[r, b]] = sgn * (480.0 if sat[r, b] else 448.0)
+    x = np.ldexp(vals, np.repeat(k, 32, 1)).astype(np.float32)
+    w = f32_to_bf16_torch(x).reshape(M, N)
+    assert np.array_equal(bf16_f32(w), x)
+    q, e = O.mxfp8_floor_quantize(w)
+    assert np.array_equal(e.astype(np.int64), 127 + k)
+    want = np.clip(vals, -448.0, 448.0)
+    assert np.array_equal(e4m3_table()[q].astype(np.float64), want)
+    w2 = _moe_like(rng, 16, 128)
+    q2, e2 = O.mxfp8_floor_quantize(w2)
+    grid, codes = e4m3_positive_grid()
+    v = bf16_f32(w2).astype(np.float64) / np.ldexp(1.0, np.repeat(e2.astype(np.int64) - 127, 32, 1))
+    mag = nearest_even_codes(v.ravel(), grid, codes).reshape(v.shape)
+    assert np.array_equal(q2 & 0x7F, mag)
+    assert np.array_equal(q2 >> 7, sign_bit(bf16_f32(w2)))
+
+
+def pin_nvfp4_reciprocal_global_scale(O):
+    """fl(2688 / A), the reciprocal form of the global scale: equal to the float64 quotient
+    rounded once to binary32 (double rounding of a quotient of binary32 values through a
+    53-bit format is harmless, 53 >= 2 * 24 + 2), exactly 2^-k for A = 2688 * 2^k, +Inf for 0."""
+    rng = np.random.default_rng(32)
+    A = np.concatenate([random_f32(4000, 33, lo_exp=-140, hi_exp=127), np.ldexp(2688.0, np.arange(-20, 20))])
+    A = np.abs(A[np.isfinite(A) & (A != 0)]).astype(np.float32)
+    got = np.array([O.nvfp4_global_scale_reciprocal(a) for a in A], np.float32)
+    with np.errstate(over="ignore"):      # quotients beyond binary32's range round to +Inf
+        want = (np.float64(2688.0) / A.astype(np.float64)).astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    assert O.nvfp4_global_scale_reciprocal(0.0) == np.inf
+    assert all(O.nvfp4_global_scale_reciprocal(np.ldexp(2688.0, k)) == np.ldexp(1.0, -k) for k in range(-30, 30))
+
+
 # --------------------------------------------------------------------------- worked examples
 
 def _read_examples():

@@ -74,6 +74,15 @@ MUTANTS = [
     ("nvfp4 qdq block amax over 8 elements",
      "const uint16_t* blk = x + r * N + b * 16;\n            float bmax = 0.0f;\n            for (int k = 0; k < 16; k++) {",
      "const uint16_t* blk = x + r * N + b * 16;\n            float bmax = 0.0f;\n            for (int k = 0; k < 8; k++) {"),
+    ("mxfp8 floor rule off by one",
+     "int e = (k - 1) - 8;",
+     "int e = k - 8;"),
+    ("mxfp8 floor quantizer uses the ceiling byte",
+     "mxfp8_quantize_with(w, M, N, q, e, oc_mxfp8_floor_scale_byte);",
+     "mxfp8_quantize_with(w, M, N, q, e, oc_mxfp8_scale_byte);"),
+    ("nvfp4 reciprocal global scale formed from the multiplier",
+     "return (6.0f * 448.0f) / A;",
+     "return 1.0f / (A / (6.0f * 448.0f));"),
     ("nvfp4 qdq does not multiply back by the global scale",
      "float S = oc_nvfp4_effective_scale(oc_nvfp4_block_scale(bmax, g), g);",
      "float S = oc_e4m3_decode(oc_nvfp4_block_scale(bmax, g)) * (g > 0.0f ? 1.0f : 0.0f);"),
