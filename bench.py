@@ -178,6 +178,17 @@ def next_rows_parity(bench, stride: int, threads: int):
     for op in bench.next_ops:
         op.run()
         torch.cuda.synchronize()
+        if op.name.startswith("mxfp8.quantize.floor"):
+            ws = bench.sets["moe_experts"]
+            out = bench.outputs["moe"]
+            for i in range(0, len(ws.specs), stride):
+                x, q, e = h16(ws.w[i]), h8(out["q"][i]), h8(out["e"][i])
+
+                def job(x=x, q=q, e=e):
+                    oq, oe = O.mxfp8_floor_quantize(x)
+                    return int((oq != q).sum() + (oe != e).sum())
+                jobs.append(job)
+            continue
         if op.workload != "fp8train" or op.name.startswith("requant.amax"):
             continue
         ws = bench.sets["moe"]
@@ -306,7 +317,8 @@ def time_next_rows(bench, steps: int):
         sp["nvfp4"] = round(ms["requant.nvfp4.unfused[fp8train]"]
                             / (ms["requant.amax[fp8train]"] + ms["requant.nvfp4[fp8train]"]), 3)
     out["fused_speedup_vs_unfused"] = sp
-    out["workload"] = ("Qwen3-30B-A3B weights held in block-wise FP8 (128x128 tiles, FP32 scales): the experts + "
+    out["workload"] = ("Qwen3-30B-A3B experts (18,432 tensors) quantized to MXFP8 with the OCP floor exponent rule; "
+                       "the Qwen3-30B-A3B weights held in block-wise FP8 (128x128 tiles, FP32 scales): the experts + "
                        "48 q/k/v (18,576 tensors) -> block-wise FP8; the 18,432 expert tensors -> MXFP8; the experts "
                        "+ q/k/v (12,336 sibling groups) -> NVFP4 with the model-wide amax pass; unfused = dequantize "
                        "to BF16 in HBM, then quantize")

@@ -102,6 +102,16 @@ lpq_status lpq_quantize_mxfp8(const uint16_t* w, int64_t M, int64_t N,
 lpq_status lpq_dequantize_mxfp8(const uint8_t* q, const uint8_t* e, int64_t M, int64_t N,
                                 uint16_t* y, void* stream);
 
+/* MXFP8 with the shared-exponent rule of the OCP Microscaling (MX) Formats
+ * specification v1.0, section 6.3: X = 2^(floor(log2 amax) - 8) (8 is E4M3's
+ * largest exponent), byte = max(0, floor(log2 amax) - 8 + 127), codes
+ * E4M3(w / X) saturating at +-448 -- an element up to 1.14x beyond 448 * X
+ * clamps.  The pages fix only power-of-two UE8M0 scales ("Low Precision RL",
+ * "3. Unified MXFP8"); this is the alternative to lpq_quantize_mxfp8's rule,
+ * for engines that expect it.  Same layouts, alignment and checks;
+ * lpq_dequantize_mxfp8 decodes it. */
+lpq_status lpq_quantize_mxfp8_floor(const uint16_t* w, int64_t M, int64_t N, uint8_t* q, uint8_t* e, void* stream);
+
 /* ======================================================================== */
 /* NVFP4: "Low Precision RL", "4. NVFP4"; "verl NVFP4 QAT", sections 2.3-2.5
  * and 3.3 -- E2M1 values in 1 x 16 blocks, an E4M3 block scale and an FP32
@@ -261,6 +271,18 @@ lpq_status lpq_fp8blk_amax_grouped(const lpq_requant_tensor* host, const lpq_req
 lpq_status lpq_requantize_fp8blk_nvfp4_grouped(const lpq_requant_tensor* host, const lpq_requant_tensor* dev,
                                                int32_t n, const float* group_amax, int32_t n_groups,
                                                float* group_g, void* stream);
+
+/* Grouped form of lpq_quantize_mxfp8_floor (descriptors as for lpq_quantize_mxfp8_grouped). */
+lpq_status lpq_quantize_mxfp8_floor_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, void* stream);
+
+/* The NVFP4 global scale in its reciprocal form, out[i] = fl(2688 / A_i)
+ * (correctly rounded; A_i = 0 gives +Inf), from the n_groups group amax
+ * values (device, FP32).  "verl NVFP4 QAT" section 2.5: a compressed-tensors
+ * export stores weight_global_scale in this form and fuses q/k/v and gate/up
+ * by the minimum of it (the same value as the maximum amax).  Multiplying the
+ * exported codes back needs the multiplier g of lpq_quantize_nvfp4*, which
+ * is not 1/out[i] in general. */
+lpq_status lpq_nvfp4_global_scale_reciprocal(const float* group_amax, int32_t n_groups, float* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -69,6 +69,9 @@ _SIG = {
     "lpq_dequantize_fp8blk": (_int, [_vp, _vp, _i64, _i64, _vp, _vp]),
     "lpq_quantize_mxfp8": (_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "lpq_dequantize_mxfp8": (_int, [_vp, _vp, _i64, _i64, _vp, _vp]),
+    "lpq_quantize_mxfp8_floor": (_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
+    "lpq_quantize_mxfp8_floor_grouped": (_int, [_tp, _vp, _i32, _vp]),
+    "lpq_nvfp4_global_scale_reciprocal": (_int, [_vp, _i32, _vp, _vp]),
     "lpq_nvfp4_amax": (_int, [_vp, _i64, _i64, _vp, _int, _vp]),
     "lpq_quantize_nvfp4": (_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "lpq_dequantize_nvfp4": (_int, [_vp, _vp, _vp, _i64, _i64, _vp, _vp]),
@@ -165,6 +168,17 @@ def lpq_quantize_mxfp8(w, q=None, e=None, stream=None):
     return q, e
 
 
+def lpq_quantize_mxfp8_floor(w, q=None, e=None, stream=None):
+    """As lpq_quantize_mxfp8, with the OCP MX floor exponent rule (saturating)."""
+    w = _bf16_in(w, "w")
+    M, N = w.shape
+    q = _empty((M, N), torch.float8_e4m3fn, w) if q is None else q
+    e = _empty((M, max(N // 32, 1)), torch.uint8, w) if e is None else e
+    _check(_L.lpq_quantize_mxfp8_floor(w.data_ptr(), M, N, q.data_ptr(), e.data_ptr(), _stream(stream)),
+           "lpq_quantize_mxfp8_floor")
+    return q, e
+
+
 def lpq_dequantize_mxfp8(q, e, y=None, stream=None):
     M, N = q.shape
     y = _empty((M, N), torch.bfloat16, q) if y is None else y
@@ -196,6 +210,14 @@ def lpq_quantize_nvfp4(w, amax, p=None, s=None, g=None, stream=None):
     _check(_L.lpq_quantize_nvfp4(w.data_ptr(), M, N, amax.data_ptr(), p.data_ptr(), s.data_ptr(), g.data_ptr(),
                                  _stream(stream)), "lpq_quantize_nvfp4")
     return p, s, g
+
+
+def lpq_nvfp4_global_scale_reciprocal(group_amax, out=None, stream=None):
+    """fl(2688 / A) per group (the reciprocal export form of the global scale)."""
+    out = torch.empty_like(group_amax) if out is None else out
+    _check(_L.lpq_nvfp4_global_scale_reciprocal(group_amax.data_ptr(), group_amax.numel(), out.data_ptr(),
+                                                _stream(stream)), "lpq_nvfp4_global_scale_reciprocal")
+    return out
 
 
 def lpq_dequantize_nvfp4(p, s, g, y=None, stream=None):
@@ -339,6 +361,10 @@ def lpq_dequantize_fp8blk_grouped(table: TensorTable, stream=None):
 
 def lpq_quantize_mxfp8_grouped(table: TensorTable, stream=None):
     _check(_L.lpq_quantize_mxfp8_grouped(*table.args(), _stream(stream)), "lpq_quantize_mxfp8_grouped")
+
+
+def lpq_quantize_mxfp8_floor_grouped(table: TensorTable, stream=None):
+    _check(_L.lpq_quantize_mxfp8_floor_grouped(*table.args(), _stream(stream)), "lpq_quantize_mxfp8_floor_grouped")
 
 
 def lpq_dequantize_mxfp8_grouped(table: TensorTable, stream=None):

@@ -172,6 +172,14 @@ __device__ __forceinline__ uint32_t mx_scale_byte(uint32_t amax_bits) {
     return (uint32_t)(e > 0 ? e : 0);
 }
 
+// The floor rule of the OCP MX specification: byte = floor(log2 amax) - 8 + 127
+// = max(0, Eb - 8) from the biased exponent of a BF16 amax (a subnormal amax
+// clamps to 0).
+__device__ __forceinline__ uint32_t mx_floor_scale_byte(uint32_t amax_bits) {
+    const int e = (int)(amax_bits >> 23) - 8;
+    return (uint32_t)(e > 0 ? e : 0);
+}
+
 // The binary32 operand that carries a UE8M0 byte for the scaled converts.
 __device__ __forceinline__ float ue8m0_operand(uint32_t byte) { return __uint_as_float(byte << 23); }
 

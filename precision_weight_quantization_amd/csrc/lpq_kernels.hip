@@ -211,7 +211,10 @@ __device__ __forceinline__ v2u mx_encode8(const F8& f, float X) {
     return v2u{__builtin_bit_cast(uint32_t, c01), __builtin_bit_cast(uint32_t, c23)};
 }
 
-template <int U, bool GROUPED>
+// FLOOR selects the shared-exponent rule of the OCP MX specification
+// (floor(log2 amax) - 8, elements beyond 448 saturate) instead of the default
+// no-saturation rule.
+template <int U, bool GROUPED, bool FLOOR = false>
 __global__ __launch_bounds__(kThreads) void k_mxfp8_quant(const lpq_tensor* table, lpq_tensor one, ChunkMap map) {
     const Work W = locate<GROUPED>(table, one, map);
     const lpq_tensor& d = W.d;
@@ -230,9 +233,15 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_quant(const lpq_tensor* tabl
     for (int u = 0; u < U; u++) {
         const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
         // a quad of lanes is one 32-element block; blocks never straddle the end
-        const F8 f = widen8(v[u]);
+        F8 f = widen8(v[u]);
         const uint32_t amax = quad_max(absmax8_f32(f));
-        const uint32_t byte = mx_scale_byte(amax);
+        const uint32_t byte = FLOOR ? mx_floor_scale_byte(amax) : mx_scale_byte(amax);
+        if constexpr (FLOOR) {
+            // saturation: clamp to +-448 * 2^(byte-127) (exact; byte <= 246 keeps it finite)
+            const float L = __uint_as_float(((byte + 8u) << 23) | 0x600000u);
+#pragma unroll
+            for (int k = 0; k < 8; k++) f.x[k] = __builtin_amdgcn_fmed3f(f.x[k], -L, L);
+        }
         const v2u codes = mx_encode8(f, ue8m0_operand(byte));
         if (full || e0 < total) {
             store<kNTS>(dst + (e0 >> 3), codes);
@@ -361,6 +370,12 @@ __device__ __forceinline__ v4u e2m1x8_to_bf16(uint32_t p, float S) {
     o.z = bf16x2(f2[0] * S, f2[1] * S);
     o.w = bf16x2(f3[0] * S, f3[1] * S);
     return o;
+}
+
+// fl(2688 / A) per group: the reciprocal form of the global scale.
+__global__ __launch_bounds__(kThreads) void k_global_scale_reciprocal(const float* amax, int32_t n, float* out) {
+    const int32_t i = blockIdx.x * kThreads + threadIdx.x;
+    if (i < n) out[i] = 2688.0f / amax[i];   // correctly rounded division
 }
 
 __global__ __launch_bounds__(kThreads) void k_fill_f32(float* p, int64_t n, float v) {
@@ -1049,7 +1064,7 @@ inline lpq_status launched() {
     return LPQ_OK;
 }
 
-enum Kind { FP8BLK_Q, FP8BLK_DQ, FP8BLK_DQF, MXFP8_Q, MXFP8_DQ, NV_AMAX, NV_Q, NV_DQ, NV_QDQ, RQ_FP8, RQ_MX, RQ_AMAX, RQ_NV };
+enum Kind { FP8BLK_Q, FP8BLK_DQ, FP8BLK_DQF, MXFP8_Q, MXFP8_QF, MXFP8_DQ, NV_AMAX, NV_Q, NV_DQ, NV_QDQ, RQ_FP8, RQ_MX, RQ_AMAX, RQ_NV };
 
 // Shape and pointer checks of one tensor for one kind of call.
 lpq_status check_tensor(Kind k, const lpq_tensor& t, int32_t n_groups) {
@@ -1069,6 +1084,7 @@ lpq_status check_tensor(Kind k, const lpq_tensor& t, int32_t n_groups) {
         if (!aligned(t.src, 8) || !aligned(t.dst, 16) || !aligned(t.scale, 4)) return LPQ_ERR_ALIGN;
         break;
     case MXFP8_Q:
+    case MXFP8_QF:
         if (t.cols % 32) return LPQ_ERR_SHAPE;
         if (!aligned(t.src, 16) || !aligned(t.dst, 8)) return LPQ_ERR_ALIGN;
         break;
@@ -1114,7 +1130,8 @@ int64_t units(Kind k, const lpq_tensor& t) {
     case FP8BLK_Q:
     case FP8BLK_DQ: return ((t.rows + kTile - 1) / kTile) * ((t.cols + kTile - 1) / kTile);
     case FP8BLK_DQF: return (n + dqf_chunk_elems<LPQ_DQF_U>() - 1) / dqf_chunk_elems<LPQ_DQF_U>();
-    case MXFP8_Q: return (n + chunk_elems<LPQ_MXQ_U>() - 1) / chunk_elems<LPQ_MXQ_U>();
+    case MXFP8_Q:
+    case MXFP8_QF: return (n + chunk_elems<LPQ_MXQ_U>() - 1) / chunk_elems<LPQ_MXQ_U>();
     case MXFP8_DQ: return (n + chunk_elems<LPQ_MXD_U>() - 1) / chunk_elems<LPQ_MXD_U>();
     case NV_AMAX: return (n + chunk_elems<LPQ_AMAX_U>() - 1) / chunk_elems<LPQ_AMAX_U>();
     case NV_Q: return (n + chunk_elems<LPQ_NVQ_U>() - 1) / chunk_elems<LPQ_NVQ_U>();
@@ -1146,6 +1163,7 @@ void dispatch(Kind k, dim3 grid, hipStream_t stream, const lpq_tensor* tab, cons
         case FP8BLK_DQ: hipLaunchKernelGGL((k_fp8blk_dequant<LPQ_TILED_THREADS, true>), grid, tiled, 0, stream, tab, one, map); break;
         case FP8BLK_DQF: hipLaunchKernelGGL((k_fp8blk_dequant_flat<LPQ_DQF_U, true>), grid, flat, 0, stream, tab, one, map); break;
         case MXFP8_Q: hipLaunchKernelGGL((k_mxfp8_quant<LPQ_MXQ_U, true>), grid, flat, 0, stream, tab, one, map); break;
+        case MXFP8_QF: hipLaunchKernelGGL((k_mxfp8_quant<LPQ_MXQ_U, true, true>), grid, flat, 0, stream, tab, one, map); break;
         case MXFP8_DQ: hipLaunchKernelGGL((k_mxfp8_dequant<LPQ_MXD_U, true>), grid, flat, 0, stream, tab, one, map); break;
         case NV_AMAX: hipLaunchKernelGGL((k_amax<LPQ_AMAX_U, true>), grid, flat, 0, stream, tab, one, map, fb); break;
         case NV_Q: hipLaunchKernelGGL((k_nvfp4_quant<LPQ_NVQ_U, true>), grid, flat, 0, stream, tab, one, map, fa, fb); break;
@@ -1159,6 +1177,7 @@ void dispatch(Kind k, dim3 grid, hipStream_t stream, const lpq_tensor* tab, cons
         case FP8BLK_DQ: hipLaunchKernelGGL((k_fp8blk_dequant<LPQ_TILED_THREADS, false>), grid, tiled, 0, stream, tab, one, map); break;
         case FP8BLK_DQF: hipLaunchKernelGGL((k_fp8blk_dequant_flat<LPQ_DQF_U, false>), grid, flat, 0, stream, tab, one, map); break;
         case MXFP8_Q: hipLaunchKernelGGL((k_mxfp8_quant<LPQ_MXQ_U, false>), grid, flat, 0, stream, tab, one, map); break;
+        case MXFP8_QF: hipLaunchKernelGGL((k_mxfp8_quant<LPQ_MXQ_U, false, true>), grid, flat, 0, stream, tab, one, map); break;
         case MXFP8_DQ: hipLaunchKernelGGL((k_mxfp8_dequant<LPQ_MXD_U, false>), grid, flat, 0, stream, tab, one, map); break;
         case NV_AMAX: hipLaunchKernelGGL((k_amax<LPQ_AMAX_U, false>), grid, flat, 0, stream, tab, one, map, fb); break;
         case NV_Q: hipLaunchKernelGGL((k_nvfp4_quant<LPQ_NVQ_U, false>), grid, flat, 0, stream, tab, one, map, fa, fb); break;
@@ -1311,6 +1330,23 @@ lpq_status lpq_dequantize_fp8blk(const uint8_t* q, const float* s, int64_t M, in
 
 lpq_status lpq_quantize_mxfp8(const uint16_t* w, int64_t M, int64_t N, uint8_t* q, uint8_t* e, void* stream) {
     return single(MXFP8_Q, make_one(w, q, e, M, N), nullptr, nullptr, stream);
+}
+
+lpq_status lpq_quantize_mxfp8_floor(const uint16_t* w, int64_t M, int64_t N, uint8_t* q, uint8_t* e, void* stream) {
+    return single(MXFP8_QF, make_one(w, q, e, M, N), nullptr, nullptr, stream);
+}
+
+lpq_status lpq_quantize_mxfp8_floor_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, void* stream) {
+    return grouped(MXFP8_QF, host, dev, n, 0, nullptr, nullptr, stream);
+}
+
+lpq_status lpq_nvfp4_global_scale_reciprocal(const float* group_amax, int32_t n_groups, float* out, void* stream) {
+    if (!group_amax || !out) return LPQ_ERR_NULL;
+    if (n_groups <= 0) return LPQ_ERR_SHAPE;
+    if (!aligned(group_amax, 4) || !aligned(out, 4)) return LPQ_ERR_ALIGN;
+    hipLaunchKernelGGL(k_global_scale_reciprocal, dim3((unsigned)((n_groups + kThreads - 1) / kThreads)), dim3(kThreads),
+                       0, (hipStream_t)stream, group_amax, n_groups, out);
+    return launched();
 }
 
 lpq_status lpq_dequantize_mxfp8(const uint8_t* q, const uint8_t* e, int64_t M, int64_t N, uint16_t* y, void* stream) {

@@ -50,6 +50,12 @@ def test_single_call_validation(lib):
     assert L.lpq_quantize_mxfp8(P, -1, 32, P, P, None) == 2
     assert L.lpq_quantize_mxfp8(P + 2, 4, 32, P, P, None) == 3
     assert L.lpq_quantize_mxfp8(P, 4, 32, P + 4, P, None) == 3
+    assert L.lpq_quantize_mxfp8_floor(P, 4, 48, P, P, None) == 2
+    assert L.lpq_quantize_mxfp8_floor(P + 2, 4, 32, P, P, None) == 3
+    assert L.lpq_quantize_mxfp8_floor(P, 4, 32, None, P, None) == 1
+    assert L.lpq_nvfp4_global_scale_reciprocal(None, 4, P, None) == 1
+    assert L.lpq_nvfp4_global_scale_reciprocal(P, 0, P, None) == 2
+    assert L.lpq_nvfp4_global_scale_reciprocal(P, 4, P + 2, None) == 3
     assert L.lpq_dequantize_mxfp8(P, P, 4, 33, P, None) == 2
     assert L.lpq_dequantize_mxfp8(P + 4, P, 4, 32, P, None) == 3
     assert L.lpq_quantize_nvfp4(P, 4, 24, P, P, P, P, None) == 2
@@ -92,6 +98,7 @@ def test_grouped_validation(lib):
     assert L.lpq_quantize_nvfp4_grouped(t, P + 4, 2, P, 4, P, None) == 3
     t2 = _table(lib, [good, (P, P, P, 8, 63, 0, 0)])
     assert L.lpq_quantize_mxfp8_grouped(t2, P, 2, None) == 2
+    assert L.lpq_quantize_mxfp8_floor_grouped(t2, P, 2, None) == 2
     t3 = _table(lib, [good, (P, P, P, 8, 64, 0, 7)])
     assert L.lpq_quantize_mxfp8_grouped(t3, P, 2, None) == 6
     t4 = _table(lib, [good, (0, P, P, 8, 64, 0, 0)])

@@ -176,6 +176,45 @@ def test_bruteforce_mxfp8(lpq):
     check_mxfp8(lpq, w, "bruteforce")
 
 
+def test_bruteforce_mxfp8_floor(lpq):
+    """The OCP floor exponent rule (saturating) over every finite BF16 pattern, alone and
+    beside a larger anchor, and the default rule's dequantizer on its output."""
+    w_np = brute_blocks(32, 5)
+    w = to_dev_bf16(w_np)
+    q, e = lpq.lpq_quantize_mxfp8_floor(w)
+    y = lpq.lpq_dequantize_mxfp8(q, e)
+    oq, oe = O.mxfp8_floor_quantize(w_np)
+    bad = report("mxfp8 floor codes", host_u8(q), oq)
+    bad += report("mxfp8 floor bytes", host_u8(e), oe)
+    bad += report("mxfp8 floor dequant", host_u16(y), O.mxfp8_dequantize(oq, oe))
+    assert bad == 0
+
+
+@pytest.mark.parametrize("M,N", [(1, 32), (131, 160), (1000, 544)])
+def test_mxfp8_floor_shapes_grouped(lpq, M, N):
+    w_np = synth.generate(77, M + N, M, N, *synth.DIST_MOE)
+    oq, oe = O.mxfp8_floor_quantize(w_np)
+    w = to_dev_bf16(w_np)
+    q, e = lpq.lpq_quantize_mxfp8_floor(w)
+    bad = report(f"mxfp8 floor codes {M}x{N}", host_u8(q), oq) + report("bytes", host_u8(e), oe)
+    q2 = torch.empty((M, N), dtype=torch.uint8, device=w.device)
+    e2 = torch.empty((M, N // 32), dtype=torch.uint8, device=w.device)
+    lpq.lpq_quantize_mxfp8_floor_grouped(lpq.TensorTable([(w, q2, e2, M, N, 0), (w, q2, e2, M, N, 0)]))
+    bad += report("grouped codes", host_u8(q2), oq) + report("grouped bytes", host_u8(e2), oe)
+    assert bad == 0
+
+
+def test_nvfp4_global_scale_reciprocal(lpq):
+    """fl(2688 / A) on random, tiny, huge, exact and zero amax values."""
+    rng = np.random.default_rng(9)
+    bits = rng.integers(0, 0x7F800000, 20000, dtype=np.uint32)
+    A = np.concatenate([bits.view(np.float32), np.ldexp(np.float32(2688.0), np.arange(-40, 40)).astype(np.float32),
+                        np.array([0.0, 1e-45, 3.4e38], np.float32)]).astype(np.float32)
+    out = lpq.lpq_nvfp4_global_scale_reciprocal(torch.from_numpy(A).cuda())
+    want = np.array([O.nvfp4_global_scale_reciprocal(a) for a in A], np.float32)
+    assert report("reciprocal global scale", out.cpu().numpy().view(np.uint32), want.view(np.uint32)) == 0
+
+
 def test_bruteforce_nvfp4_grouped(lpq):
     """Each 1x16 block is its own tensor and its own sibling group (own global scale)."""
     w_np = brute_blocks(16, 2)

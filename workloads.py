@@ -182,7 +182,10 @@ def mxfp8_ops(tag: str, ws: WeightSet, codes: Slab, ebytes: Slab, out: Slab, buc
     nbytes = 3 * ws.numel + ws.numel // 32
     return ([Op(f"mxfp8.quantize[{tag}]", tag, nbytes, [lambda t=t: lpq.lpq_quantize_mxfp8_grouped(t) for t in tq]),
              Op(f"mxfp8.dequantize[{tag}]", tag, nbytes, [lambda t=t: lpq.lpq_dequantize_mxfp8_grouped(t) for t in tdq])],
-            dict(q=q, e=e, y=y))
+            dict(q=q, e=e, y=y),
+            # the OCP floor-rule variant (a widening row): same tensors and outputs
+            [Op(f"mxfp8.quantize.floor[{tag}]", tag, nbytes,
+                [lambda t=t: lpq.lpq_quantize_mxfp8_floor_grouped(t) for t in tq])])
 
 
 def nvfp4_ops(tag: str, ws: WeightSet, packed: Slab, sbytes: Slab, out: Slab, bucket: str, device="cuda"):
@@ -374,8 +377,9 @@ class Bench:
             codes = self._reslab(self.codes, ws.specs, 1)
             eb = Slab([s.numel // 32 for s in ws.specs], device)
             out = self._reslab(self.out, ws.specs, 2)
-            ops, o = mxfp8_ops("moe", ws, codes, eb, out, bucket)
+            ops, o, nxt = mxfp8_ops("moe", ws, codes, eb, out, bucket)
             self.ops += ops
+            self.next_ops += nxt
             self.outputs["moe"] = o
             self.sets["moe_experts"] = ws
         if "nvfp4" in which:
