@@ -355,6 +355,46 @@ OC_API void oc_nvfp4_qdq(const uint16_t* x, int64_t M, int64_t N, float g, uint1
         }
 }
 
+/* ------------------------------------------------------------------------ */
+/* W4A4 activation observers ("verl NVFP4 QAT" 2.2: activation_observer,     */
+/* default static_minmax, used only in W4A4 mode; 3.1: the choices           */
+/* static_minmax, memoryless_minmax, minmax).  The pages name the observers  */
+/* but do not define them.  Readings: each tracks the activations' min and   */
+/* max per tensor; memoryless_minmax keeps only the latest batch's,          */
+/* static_minmax the running extremes over every batch seen, and minmax a    */
+/* moving average m += c * (batch - m) (c is the caller's averaging         */
+/* constant; the first batch initialises it).  The activation global amax    */
+/* is max(|min|, |max|).  Min and max order -0 below +0.                     */
+/* ------------------------------------------------------------------------ */
+
+static int oc_below(float a, float b) {        /* a < b in the order with -0 < +0 */
+    return a < b || (a == b && signbit(a) && !signbit(b));
+}
+
+/* state[0] = min, state[1] = max, state[2] = batches seen (a count held in a
+ * float).  Returns the activation amax after the update. */
+OC_API float oc_observer_update(int kind, float c, float* state, const uint16_t* x, int64_t n) {
+    float bmin = oc_bf16_to_f32(x[0]), bmax = bmin;
+    for (int64_t i = 1; i < n; i++) {
+        float v = oc_bf16_to_f32(x[i]);
+        if (oc_below(v, bmin)) bmin = v;
+        if (oc_below(bmax, v)) bmax = v;
+    }
+    if (kind == 0 || state[2] == 0.0f) {        /* memoryless, or the first batch */
+        state[0] = bmin;
+        state[1] = bmax;
+    } else if (kind == 1) {                     /* static: running extremes */
+        if (oc_below(bmin, state[0])) state[0] = bmin;
+        if (oc_below(state[1], bmax)) state[1] = bmax;
+    } else {                                    /* minmax: moving average */
+        state[0] = state[0] + c * (bmin - state[0]);
+        state[1] = state[1] + c * (bmax - state[1]);
+    }
+    state[2] = state[2] + 1.0f;
+    float lo = fabsf(state[0]), hi = fabsf(state[1]);
+    return lo > hi ? lo : hi;
+}
+
 /* Vectorised scalar entry points for the tests (n independent elements). */
 OC_API void oc_e4m3_encode_n(const float* v, int64_t n, uint8_t* out) {
     for (int64_t i = 0; i < n; i++) out[i] = oc_e4m3_encode(v[i]);

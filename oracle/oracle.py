@@ -77,6 +77,7 @@ _SIG = {
     "oc_mxfp8_floor_scale_byte_n": (None, [_f32p, _i64, _u8p]),
     "oc_mxfp8_floor_quantize": (None, [_u16p, _i64, _i64, _u8p, _u8p]),
     "oc_nvfp4_global_scale_reciprocal": (ctypes.c_float, [ctypes.c_float]),
+    "oc_observer_update": (ctypes.c_float, [ctypes.c_int, ctypes.c_float, _f32p, _u16p, _i64]),
 }
 
 
@@ -235,6 +236,18 @@ class Oracle:
         y = np.empty((M, N), np.uint16)
         self.L.oc_nvfp4_qdq(_p(x, _u16p), M, N, float(g), _p(y, _u16p))
         return y
+
+    # ------------------------------------------------------------------ W4A4 activation observers
+    OBSERVERS = {"memoryless_minmax": 0, "static_minmax": 1, "minmax": 2}
+
+    def observer_update(self, kind: str, state: np.ndarray, x: np.ndarray, c: float = 0.01) -> float:
+        """Update ``state`` (float32 [3]: min, max, batches seen) with the BF16 batch ``x``
+        under the named observer; returns the activation amax max(|min|, |max|)."""
+        assert state.dtype == np.float32 and state.shape == (3,) and state.flags["C_CONTIGUOUS"]
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        assert x.size > 0
+        return float(self.L.oc_observer_update(self.OBSERVERS[kind], float(c), _p(state, _f32p),
+                                               _p(x, _u16p), x.size))
 
     def nvfp4_group_scale(self, members) -> tuple[float, float]:
         """Sibling group: A = max over every member's amax, g = fl(A / 2688)."""

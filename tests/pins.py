@@ -299,6 +299,41 @@ def pin_nvfp4_reciprocal_global_scale(O):
     assert all(O.nvfp4_global_scale_reciprocal(np.ldexp(2688.0, k)) == np.ldexp(1.0, -k) for k in range(-30, 30))
 
 
+def pin_observers(O):
+    """W4A4 activation observers against closed forms: memoryless keeps the last batch's
+    extremes, static the extremes of everything seen (numpy min/max of the concatenation);
+    the moving average with c = 0 stays at the first batch and with c = 1/2 over batches
+    whose max is 2^k after a first batch of zeros reaches 2^k (1 - 2^-(t-1)) exactly;
+    -0 orders below +0; amax = max(|min|, |max|)."""
+    rng = np.random.default_rng(41)
+    batches = [_moe_like(rng, 8, 64, scale=float(sc)) for sc in (0.5, 2.0, 0.1, 1.0, 3.0)]
+    f = [bf16_f32(b).astype(np.float64) for b in batches]
+    for kind in ("memoryless_minmax", "static_minmax"):
+        st = np.zeros(3, np.float32)
+        for t, b in enumerate(batches):
+            a = O.observer_update(kind, st, b)
+            seen = np.concatenate([x.ravel() for x in (f[t:t + 1] if kind == "memoryless_minmax" else f[:t + 1])])
+            assert st[0] == seen.min() and st[1] == seen.max() and st[2] == t + 1
+            assert a == max(abs(seen.min()), abs(seen.max())) == O.amax(np.concatenate(
+                [x.ravel() for x in (batches[t:t + 1] if kind == "memoryless_minmax" else batches[:t + 1])]))
+    st = np.zeros(3, np.float32)
+    for t, b in enumerate(batches):
+        O.observer_update("minmax", st, b, c=0.0)
+        assert st[0] == f[0].min() and st[1] == f[0].max()
+    for k in (-20, 0, 30):
+        st = np.zeros(3, np.float32)
+        O.observer_update("minmax", st, np.zeros((2, 16), np.uint16), c=0.5)
+        for t in range(2, 20):
+            x = np.zeros((2, 16), np.float32)
+            x[1, 3], x[0, 5] = np.ldexp(1.0, k), -np.ldexp(1.0, k - 1)
+            a = O.observer_update("minmax", st, f32_to_bf16_torch(x).reshape(2, 16), c=0.5)
+            assert st[1] == np.ldexp(1.0 - 2.0 ** -(t - 1), k) and st[0] == -np.ldexp(1.0 - 2.0 ** -(t - 1), k - 1)
+            assert a == st[1]
+    st = np.zeros(3, np.float32)
+    O.observer_update("static_minmax", st, np.array([[0x8000, 0x0000]], np.uint16))
+    assert st[0] == 0 and np.signbit(st[0]) and st[1] == 0 and not np.signbit(st[1])
+
+
 # --------------------------------------------------------------------------- worked examples
 
 def _read_examples():

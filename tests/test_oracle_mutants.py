@@ -83,6 +83,15 @@ MUTANTS = [
     ("nvfp4 reciprocal global scale formed from the multiplier",
      "return (6.0f * 448.0f) / A;",
      "return 1.0f / (A / (6.0f * 448.0f));"),
+    ("observer: static keeps the latest batch",
+     "if (oc_below(bmin, state[0])) state[0] = bmin;",
+     "state[0] = bmin;"),
+    ("observer: moving average without the constant",
+     "state[1] = state[1] + c * (bmax - state[1]);",
+     "state[1] = state[1] + (bmax - state[1]);"),
+    ("observer: amax from the max only",
+     "return lo > hi ? lo : hi;",
+     "return hi;"),
     ("nvfp4 qdq does not multiply back by the global scale",
      "float S = oc_nvfp4_effective_scale(oc_nvfp4_block_scale(bmax, g), g);",
      "float S = oc_e4m3_decode(oc_nvfp4_block_scale(bmax, g)) * (g > 0.0f ? 1.0f : 0.0f);"),
