@@ -189,6 +189,12 @@ def next_rows_parity(bench, stride: int, threads: int):
                     return int((oq != q).sum() + (oe != e).sum())
                 jobs.append(job)
             continue
+        if op.name.startswith("nvfp4.observe+qdq"):
+            # the same batch every time: the static observer's extremes are that batch's
+            a = bench.outputs["act"]
+            x, y = h16(a["x"]), h16(a["y"])
+            jobs.append(lambda x=x, y=y: int((O.nvfp4_qdq(x, O.nvfp4_group_scale([x])[1]) != y).sum()))
+            continue
         if op.workload != "fp8train" or op.name.startswith("requant.amax"):
             continue
         ws = bench.sets["moe"]
@@ -317,7 +323,8 @@ def time_next_rows(bench, steps: int):
         sp["nvfp4"] = round(ms["requant.nvfp4.unfused[fp8train]"]
                             / (ms["requant.amax[fp8train]"] + ms["requant.nvfp4[fp8train]"]), 3)
     out["fused_speedup_vs_unfused"] = sp
-    out["workload"] = ("Qwen3-30B-A3B experts (18,432 tensors) quantized to MXFP8 with the OCP floor exponent rule; "
+    out["workload"] = ("W4A4 activations 8192x2048: static_minmax observer update, then QDQ under its amax; "
+                       "Qwen3-30B-A3B experts (18,432 tensors) quantized to MXFP8 with the OCP floor exponent rule; "
                        "the Qwen3-30B-A3B weights held in block-wise FP8 (128x128 tiles, FP32 scales): the experts + "
                        "48 q/k/v (18,576 tensors) -> block-wise FP8; the 18,432 expert tensors -> MXFP8; the experts "
                        "+ q/k/v (12,336 sibling groups) -> NVFP4 with the model-wide amax pass; unfused = dequantize "

@@ -284,6 +284,42 @@ lpq_status lpq_quantize_mxfp8_floor_grouped(const lpq_tensor* host, const lpq_te
  * is not 1/out[i] in general. */
 lpq_status lpq_nvfp4_global_scale_reciprocal(const float* group_amax, int32_t n_groups, float* out, void* stream);
 
+/* ======================================================================== */
+/* W4A4 activation observers.  "verl NVFP4 QAT" 2.2 (activation_observer,
+ * default static_minmax, W4A4 mode only) and 3.1 (the choices static_minmax,
+ * memoryless_minmax, minmax); the pages name them without defining them.
+ * Readings: an observer tracks the activations' min and max per tensor --
+ *   LPQ_OBSERVER_MEMORYLESS_MINMAX  the latest batch's extremes;
+ *   LPQ_OBSERVER_STATIC_MINMAX      the extremes over every batch seen;
+ *   LPQ_OBSERVER_MINMAX             a moving average, m = fl(m + fl(c * fl(b - m)))
+ *                                   for each of min and max, c = averaging_constant;
+ * the first batch after a reset initialises every kind.  The activation amax
+ * is max(|min|, |max|); min and max order -0 below +0.
+ *
+ * state: LPQ_OBSERVER_STATE_FLOATS words of caller-owned device memory, 4-byte
+ * aligned, one per observed tensor: [0] min, [1] max, [2] batches seen (FP32),
+ * the rest scratch of the calls below.  Reset it once before first use; calls
+ * on one state must not overlap.  The amax feeds lpq_nvfp4_qdq (the W4A4
+ * activation fake-quant) or lpq_nvfp4_global_scale[_reciprocal] (the exported
+ * input_scale / input_global_scale). */
+#define LPQ_OBSERVER_MEMORYLESS_MINMAX 0
+#define LPQ_OBSERVER_STATIC_MINMAX 1
+#define LPQ_OBSERVER_MINMAX 2
+#define LPQ_OBSERVER_STATE_FLOATS 8
+
+lpq_status lpq_observer_reset(float* state, void* stream);
+
+/* Observe one BF16 batch x [M, N] (N % 16 == 0, x 16-byte aligned): updates
+ * the state and writes the activation amax (1 FP32, device).  observer outside
+ * the three kinds: LPQ_ERR_ARG. */
+lpq_status lpq_nvfp4_observe(const uint16_t* x, int64_t M, int64_t N, int observer, float averaging_constant,
+                             float* state, float* amax, void* stream);
+
+/* The multiplier form of a global scale, out[i] = fl(amax[i] / 2688), for n
+ * device FP32 values (the input_scale / weight_scale_2 export of "verl NVFP4
+ * QAT" 3.3). */
+lpq_status lpq_nvfp4_global_scale(const float* amax, int32_t n, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -72,6 +72,9 @@ _SIG = {
     "lpq_quantize_mxfp8_floor": (_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "lpq_quantize_mxfp8_floor_grouped": (_int, [_tp, _vp, _i32, _vp]),
     "lpq_nvfp4_global_scale_reciprocal": (_int, [_vp, _i32, _vp, _vp]),
+    "lpq_nvfp4_global_scale": (_int, [_vp, _i32, _vp, _vp]),
+    "lpq_observer_reset": (_int, [_vp, _vp]),
+    "lpq_nvfp4_observe": (_int, [_vp, _i64, _i64, _int, ctypes.c_float, _vp, _vp, _vp]),
     "lpq_nvfp4_amax": (_int, [_vp, _i64, _i64, _vp, _int, _vp]),
     "lpq_quantize_nvfp4": (_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "lpq_dequantize_nvfp4": (_int, [_vp, _vp, _vp, _i64, _i64, _vp, _vp]),
@@ -218,6 +221,38 @@ def lpq_nvfp4_global_scale_reciprocal(group_amax, out=None, stream=None):
     _check(_L.lpq_nvfp4_global_scale_reciprocal(group_amax.data_ptr(), group_amax.numel(), out.data_ptr(),
                                                 _stream(stream)), "lpq_nvfp4_global_scale_reciprocal")
     return out
+
+
+def lpq_nvfp4_global_scale(amax, out=None, stream=None):
+    """fl(A / 2688) per entry (the multiplier form of a global scale)."""
+    out = torch.empty_like(amax) if out is None else out
+    _check(_L.lpq_nvfp4_global_scale(amax.data_ptr(), amax.numel(), out.data_ptr(), _stream(stream)),
+           "lpq_nvfp4_global_scale")
+    return out
+
+
+# W4A4 activation observers (the C constants of the same names)
+OBSERVERS = {"memoryless_minmax": 0, "static_minmax": 1, "minmax": 2}
+OBSERVER_STATE_FLOATS = 8
+
+
+def lpq_observer_reset(state=None, device=None, stream=None):
+    """A reset observer state (8 FP32 words on the device; allocated when not given)."""
+    if state is None:
+        state = torch.empty(OBSERVER_STATE_FLOATS, dtype=torch.float32, device=device or "cuda")
+    _check(_L.lpq_observer_reset(state.data_ptr(), _stream(stream)), "lpq_observer_reset")
+    return state
+
+
+def lpq_nvfp4_observe(x, state, observer="static_minmax", averaging_constant=0.01, amax=None, stream=None):
+    """Update the observer state with the BF16 batch x; returns the activation amax (1 FP32, device)."""
+    x = _bf16_in(x, "x")
+    M, N = x.shape
+    amax = _empty((1,), torch.float32, x) if amax is None else amax
+    kind = OBSERVERS[observer] if isinstance(observer, str) else int(observer)
+    _check(_L.lpq_nvfp4_observe(x.data_ptr(), M, N, kind, float(averaging_constant), state.data_ptr(),
+                                amax.data_ptr(), _stream(stream)), "lpq_nvfp4_observe")
+    return amax
 
 
 def lpq_dequantize_nvfp4(p, s, g, y=None, stream=None):

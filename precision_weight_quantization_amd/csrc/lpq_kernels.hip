@@ -372,6 +372,103 @@ __device__ __forceinline__ v4u e2m1x8_to_bf16(uint32_t p, float S) {
     return o;
 }
 
+// ---------------------------------------------------------------------------
+// W4A4 activation observers
+// ---------------------------------------------------------------------------
+//
+// Observer state (caller-owned device memory, 8 words): [0] min, [1] max,
+// [2] batches seen (FP32), [4] / [5] the current batch's min / max as
+// order-preserving keys.  Keys map binary32 bits to unsigned integers whose
+// order is the values' order with -0 below +0: non-negative values get the
+// sign bit set, negative values have every bit flipped.
+
+__device__ __forceinline__ uint32_t order_key(uint32_t u) { return (u >> 31) ? ~u : (u | 0x80000000u); }
+__device__ __forceinline__ uint32_t key_bits(uint32_t k) { return (k >> 31) ? (k & 0x7fffffffu) : ~k; }
+__device__ __forceinline__ uint32_t umin(uint32_t a, uint32_t b) { return a < b ? a : b; }
+
+constexpr uint32_t kKeyMinIdentity = 0xffffffffu;
+constexpr uint32_t kKeyMaxIdentity = 0u;
+
+__global__ void k_observer_reset(uint32_t* state) {
+    const int i = threadIdx.x;
+    if (i < 8) state[i] = i == 4 ? kKeyMinIdentity : (i == 5 ? kKeyMaxIdentity : 0u);
+}
+
+// min / max of one BF16 tensor into the batch keys of the state.
+template <int U>
+__global__ __launch_bounds__(kThreads) void k_minmax(lpq_tensor one, uint32_t* state) {
+    const int64_t total = one.rows * one.cols;
+    const int64_t base = (int64_t)blockIdx.x * chunk_elems<U>();
+    const v4u* src = reinterpret_cast<const v4u*>(one.src);
+    const bool full = base + chunk_elems<U>() <= total;
+    v4u v[U];
+    load_chunk<U>(v, src, base, total, full);
+    uint32_t lo = kKeyMinIdentity, hi = kKeyMaxIdentity;
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const int64_t e0 = base + (int64_t)(u * kThreads + threadIdx.x) * 8;
+        if (!full && e0 >= total) continue;   // past the end (N % 8 == 0: vectors are whole)
+        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const uint32_t a = order_key(w[k] << 16), b = order_key(w[k] & 0xffff0000u);
+            lo = umin(lo, umin(a, b));
+            hi = umax(hi, umax(a, b));
+        }
+    }
+    lo = ~wave_max(~lo);   // min through the max reduction on complements
+    hi = wave_max(hi);
+    __shared__ uint32_t plo[kThreads / 64], phi[kThreads / 64];
+    if ((threadIdx.x & 63) == 0) {
+        plo[threadIdx.x >> 6] = lo;
+        phi[threadIdx.x >> 6] = hi;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t l = plo[0], h = phi[0];
+#pragma unroll
+        for (int k = 1; k < kThreads / 64; k++) {
+            l = umin(l, plo[k]);
+            h = umax(h, phi[k]);
+        }
+        atomicMin(state + 4, l);
+        atomicMax(state + 5, h);
+    }
+}
+
+// Applies the observer rule to the batch extremes (one thread), writes the
+// activation amax and re-arms the batch keys.  Same operations, in the same
+// order, as the definition: m += c * (b - m) for the moving average.
+__global__ void k_observer_update(int kind, float c, uint32_t* state, float* amax) {
+    if (threadIdx.x != 0) return;
+    float* f = reinterpret_cast<float*>(state);
+    const uint32_t kmin = state[4], kmax = state[5];
+    const float bmin = __uint_as_float(key_bits(kmin)), bmax = __uint_as_float(key_bits(kmax));
+    float mn = f[0], mx = f[1];
+    if (kind == LPQ_OBSERVER_MEMORYLESS_MINMAX || f[2] == 0.0f) {
+        mn = bmin;
+        mx = bmax;
+    } else if (kind == LPQ_OBSERVER_STATIC_MINMAX) {
+        if (kmin < order_key(__float_as_uint(mn))) mn = bmin;
+        if (kmax > order_key(__float_as_uint(mx))) mx = bmax;
+    } else {
+        mn = mn + c * (bmin - mn);
+        mx = mx + c * (bmax - mx);
+    }
+    f[0] = mn;
+    f[1] = mx;
+    f[2] = f[2] + 1.0f;
+    state[4] = kKeyMinIdentity;
+    state[5] = kKeyMaxIdentity;
+    *amax = fmaxf(fabsf(mn), fabsf(mx));
+}
+
+// fl(A / 2688) per entry: the multiplier form of a global scale.
+__global__ __launch_bounds__(kThreads) void k_global_scale(const float* amax, int32_t n, float* out) {
+    const int32_t i = blockIdx.x * kThreads + threadIdx.x;
+    if (i < n) out[i] = amax[i] / 2688.0f;   // correctly rounded division
+}
+
 // fl(2688 / A) per group: the reciprocal form of the global scale.
 __global__ __launch_bounds__(kThreads) void k_global_scale_reciprocal(const float* amax, int32_t n, float* out) {
     const int32_t i = blockIdx.x * kThreads + threadIdx.x;
@@ -1346,6 +1443,40 @@ lpq_status lpq_nvfp4_global_scale_reciprocal(const float* group_amax, int32_t n_
     if (!aligned(group_amax, 4) || !aligned(out, 4)) return LPQ_ERR_ALIGN;
     hipLaunchKernelGGL(k_global_scale_reciprocal, dim3((unsigned)((n_groups + kThreads - 1) / kThreads)), dim3(kThreads),
                        0, (hipStream_t)stream, group_amax, n_groups, out);
+    return launched();
+}
+
+lpq_status lpq_nvfp4_global_scale(const float* amax, int32_t n, float* out, void* stream) {
+    if (!amax || !out) return LPQ_ERR_NULL;
+    if (n <= 0) return LPQ_ERR_SHAPE;
+    if (!aligned(amax, 4) || !aligned(out, 4)) return LPQ_ERR_ALIGN;
+    hipLaunchKernelGGL(k_global_scale, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                       (hipStream_t)stream, amax, n, out);
+    return launched();
+}
+
+lpq_status lpq_observer_reset(float* state, void* stream) {
+    if (!state) return LPQ_ERR_NULL;
+    if (!aligned(state, 4)) return LPQ_ERR_ALIGN;
+    hipLaunchKernelGGL(k_observer_reset, dim3(1), dim3(64), 0, (hipStream_t)stream, reinterpret_cast<uint32_t*>(state));
+    return launched();
+}
+
+lpq_status lpq_nvfp4_observe(const uint16_t* x, int64_t M, int64_t N, int observer, float averaging_constant,
+                             float* state, float* amax, void* stream) {
+    if (!state || !amax) return LPQ_ERR_NULL;
+    if (!aligned(state, 4) || !aligned(amax, 4)) return LPQ_ERR_ALIGN;
+    if (observer < LPQ_OBSERVER_MEMORYLESS_MINMAX || observer > LPQ_OBSERVER_MINMAX) return LPQ_ERR_ARG;
+    const lpq_tensor one = make_one(x, nullptr, nullptr, M, N);
+    lpq_status st = check_tensor(NV_AMAX, one, 0);   // same shape and alignment rules as the amax pass
+    if (st != LPQ_OK) return st;
+    const int64_t units = (M * N + chunk_elems<LPQ_AMAX_U>() - 1) / chunk_elems<LPQ_AMAX_U>();
+    if (units > kMaxGridX) return LPQ_ERR_SHAPE;
+    uint32_t* s = reinterpret_cast<uint32_t*>(state);
+    hipLaunchKernelGGL((k_minmax<LPQ_AMAX_U>), dim3((unsigned)units), dim3(kThreads), 0, (hipStream_t)stream, one, s);
+    if ((st = launched()) != LPQ_OK) return st;
+    hipLaunchKernelGGL(k_observer_update, dim3(1), dim3(64), 0, (hipStream_t)stream, observer, averaging_constant, s,
+                       amax);
     return launched();
 }
 

@@ -56,6 +56,14 @@ def test_single_call_validation(lib):
     assert L.lpq_nvfp4_global_scale_reciprocal(None, 4, P, None) == 1
     assert L.lpq_nvfp4_global_scale_reciprocal(P, 0, P, None) == 2
     assert L.lpq_nvfp4_global_scale_reciprocal(P, 4, P + 2, None) == 3
+    assert L.lpq_nvfp4_global_scale(None, 4, P, None) == 1
+    assert L.lpq_nvfp4_global_scale(P, -1, P, None) == 2
+    assert L.lpq_observer_reset(None, None) == 1
+    assert L.lpq_observer_reset(P + 2, None) == 3
+    assert L.lpq_nvfp4_observe(P, 4, 32, 1, 0.01, None, P, None) == 1
+    assert L.lpq_nvfp4_observe(P, 4, 32, 3, 0.01, P, P, None) == 6            # unknown observer
+    assert L.lpq_nvfp4_observe(P, 4, 24, 1, 0.01, P, P, None) == 2            # N % 16
+    assert L.lpq_nvfp4_observe(P + 8, 4, 32, 1, 0.01, P, P, None) == 3
     assert L.lpq_dequantize_mxfp8(P, P, 4, 33, P, None) == 2
     assert L.lpq_dequantize_mxfp8(P + 4, P, 4, 32, P, None) == 3
     assert L.lpq_quantize_nvfp4(P, 4, 24, P, P, P, P, None) == 2

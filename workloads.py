@@ -318,9 +318,15 @@ def requant_ops(ws: WeightSet, q8, s8, codes: Slab, out: Slab, bucket: str, devi
 def activation_ops(x: torch.Tensor, y: torch.Tensor):
     amax = torch.zeros(1, dtype=torch.float32, device=x.device)
     n = x.numel()
+    # the W4A4 path with the default observer (a widening row): observe the batch, then QDQ
+    state = lpq.lpq_observer_reset(device=x.device)
+    oamax = torch.zeros(1, dtype=torch.float32, device=x.device)
     return ([Op("nvfp4.amax[act]", "act", 2 * n, [lambda: lpq.lpq_nvfp4_amax(x, amax)], counted=False),
              Op("nvfp4.qdq[act]", "act", 4 * n, [lambda: lpq.lpq_nvfp4_qdq(x, amax, y)])],
-            dict(amax=amax))
+            dict(amax=amax, state=state, observer_amax=oamax),
+            [Op("nvfp4.observe+qdq[act]", "act", 6 * n,
+                [lambda: lpq.lpq_nvfp4_observe(x, state, "static_minmax", amax=oamax),
+                 lambda: lpq.lpq_nvfp4_qdq(x, oamax, y)])])
 
 
 WORKLOADS = ("dense", "moe", "nvfp4", "dsv3")
@@ -393,8 +399,9 @@ class Bench:
             x = torch.empty((8192, 2048), dtype=torch.bfloat16, device=device)
             sgpu.fill(x, synth.seed_of(4), synth.stream_of(0xFFFF, 0xFFFFFF, 0xFFFF), synth.DIST_ACT)
             ya = torch.empty_like(x)
-            ops, o = activation_ops(x, ya)
+            ops, o, nxt = activation_ops(x, ya)
             self.ops += ops
+            self.next_ops += nxt
             self.outputs["act"] = dict(x=x, y=ya, **o)
         if "dsv3" in which:
             ws = self.sets["dsv3"]
