@@ -275,6 +275,15 @@ OC_API float oc_amax_bf16(const uint16_t* w, int64_t n) {
  * amax of the tensor, or of its whole sibling group ([VERL] 2.4). */
 OC_API float oc_nvfp4_global_scale(float A) { return A / (6.0f * 448.0f); }
 
+/* The global scale with another E4M3 maximum in the denominator:
+ * fl(A / (6 * e4m3_max)).  The vime pull request 503 review quotes a
+ * configuration in which the NVFP4 "4over6" switch with its "E4M3 use 256"
+ * flag sets e4m3_max to 256 instead of 448; the global scale of "verl NVFP4
+ * QAT" 2.3 is amax over (FP4 max x FP8 max), so it becomes A / 1536.  The
+ * per-block choice that gives "4over6" its name is not described on the
+ * pages and is not modelled here. */
+OC_API float oc_nvfp4_global_scale_max(float A, int e4m3_max) { return A / (6.0f * (float)e4m3_max); }
+
 /* The same global scale in the reciprocal form some exporters store
  * ("verl NVFP4 QAT" 2.5: a compressed-tensors export whose sibling groups
  * are fused by taking the minimum of this form): fl(2688 / A).  A group of

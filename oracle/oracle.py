@@ -78,6 +78,7 @@ _SIG = {
     "oc_mxfp8_floor_quantize": (None, [_u16p, _i64, _i64, _u8p, _u8p]),
     "oc_nvfp4_global_scale_reciprocal": (ctypes.c_float, [ctypes.c_float]),
     "oc_observer_update": (ctypes.c_float, [ctypes.c_int, ctypes.c_float, _f32p, _u16p, _i64]),
+    "oc_nvfp4_global_scale_max": (ctypes.c_float, [ctypes.c_float, ctypes.c_int]),
 }
 
 
@@ -198,8 +199,10 @@ class Oracle:
         w = np.ascontiguousarray(w, dtype=np.uint16)
         return float(self.L.oc_amax_bf16(_p(w, _u16p), w.size))
 
-    def nvfp4_global_scale(self, A: float) -> float:
-        return float(self.L.oc_nvfp4_global_scale(float(A)))
+    def nvfp4_global_scale(self, A: float, e4m3_max: int = 448) -> float:
+        if e4m3_max == 448:
+            return float(self.L.oc_nvfp4_global_scale(float(A)))
+        return float(self.L.oc_nvfp4_global_scale_max(float(A), int(e4m3_max)))
 
     def nvfp4_global_scale_reciprocal(self, A: float) -> float:
         return float(self.L.oc_nvfp4_global_scale_reciprocal(float(A)))
@@ -249,16 +252,16 @@ class Oracle:
         return float(self.L.oc_observer_update(self.OBSERVERS[kind], float(c), _p(state, _f32p),
                                                _p(x, _u16p), x.size))
 
-    def nvfp4_group_scale(self, members) -> tuple[float, float]:
-        """Sibling group: A = max over every member's amax, g = fl(A / 2688)."""
+    def nvfp4_group_scale(self, members, e4m3_max: int = 448) -> tuple[float, float]:
+        """Sibling group: A = max over every member's amax, g = fl(A / (6 * e4m3_max))."""
         A = max(self.amax(m) for m in members) if members else 0.0
-        return A, self.nvfp4_global_scale(A)
+        return A, self.nvfp4_global_scale(A, e4m3_max)
 
-    def nvfp4_quantize_group(self, members):
+    def nvfp4_quantize_group(self, members, e4m3_max: int = 448):
         """Quantize the tensors of one sibling group under their shared global scale.
 
         Returns (A, g, [(packed, scales), ...])."""
-        A, g = self.nvfp4_group_scale(members)
+        A, g = self.nvfp4_group_scale(members, e4m3_max)
         return A, g, [self.nvfp4_quantize(m, g) for m in members]
 
     # ------------------------------------------------------------------ re-quantization of FP8 weights

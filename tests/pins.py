@@ -284,6 +284,40 @@ def pin_mxfp8_floor_quantize(O):
     assert np.array_equal(q2 >> 7, sign_bit(bf16_f32(w2)))
 
 
+def pin_nvfp4_e4m3_max_256(O):
+    """With E4M3 maximum 256 the global scale is fl(A / 1536): 2^k for A = 1536 * 2^k, and the
+    float64 quotient rounded once elsewhere.  A group anchored at A = 1536 * 2^k whose blocks
+    hold E2M1 grid values times s_b * 2^k (s_b <= 256, one +-6 per block) round-trips exactly,
+    with block-scale codes s_b."""
+    rng = np.random.default_rng(34)
+    for k in range(-30, 30):
+        assert O.nvfp4_global_scale(np.ldexp(1536.0, k), 256) == np.ldexp(1.0, k)
+    A = np.abs(random_f32(2000, 35, lo_exp=-120, hi_exp=120)).astype(np.float32)
+    got = np.array([O.nvfp4_global_scale(a, 256) for a in A], np.float32)
+    want = (A.astype(np.float64) / 1536.0).astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    grid = read_grid_file()
+    M, N, k = 16, 64, 3
+    nb = N // 16
+    sb = np.abs(_e4m3_values(rng, M * nb, normal_only=True)).reshape(M, nb)
+    sb = np.where(sb > 256.0, sb / 4.0, sb)
+    gc = rng.integers(0, 16, (M, N))
+    for r in range(M):
+        for b in range(nb):
+            gc[r, 16 * b + int(rng.integers(0, 16))] = 7 | (8 if rng.integers(0, 2) else 0)
+    gv = grid[gc & 7] * np.where(gc & 8, -1.0, 1.0)
+    x = np.ldexp(gv * np.repeat(sb, 16, 1), k).astype(np.float32)
+    w1 = f32_to_bf16_torch(x).reshape(M, N)
+    assert np.array_equal(bf16_f32(w1), x)
+    anchor = np.zeros((1, 16), np.float32)
+    anchor[0, 2] = np.ldexp(1536.0, k)
+    A_, g, outs = O.nvfp4_quantize_group([w1, f32_to_bf16_torch(anchor).reshape(1, 16)], e4m3_max=256)
+    assert g == np.ldexp(1.0, k)
+    p, s = outs[0]
+    assert np.array_equal(e4m3_table()[s].astype(np.float64), sb)
+    assert np.array_equal(O.nvfp4_dequantize(p, s, g), w1)
+
+
 def pin_nvfp4_reciprocal_global_scale(O):
     """fl(2688 / A), the reciprocal form of the global scale: equal to the float64 quotient
     rounded once to binary32 (double rounding of a quotient of binary32 values through a

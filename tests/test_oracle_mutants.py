@@ -92,6 +92,9 @@ MUTANTS = [
     ("observer: amax from the max only",
      "return lo > hi ? lo : hi;",
      "return hi;"),
+    ("nvfp4 global scale ignores the E4M3 maximum",
+     "OC_API float oc_nvfp4_global_scale_max(float A, int e4m3_max) { return A / (6.0f * (float)e4m3_max); }",
+     "OC_API float oc_nvfp4_global_scale_max(float A, int e4m3_max) { return A / (6.0f * 448.0f); }"),
     ("nvfp4 qdq does not multiply back by the global scale",
      "float S = oc_nvfp4_effective_scale(oc_nvfp4_block_scale(bmax, g), g);",
      "float S = oc_e4m3_decode(oc_nvfp4_block_scale(bmax, g)) * (g > 0.0f ? 1.0f : 0.0f);"),
