@@ -285,6 +285,26 @@ lpq_status lpq_quantize_mxfp8_floor_grouped(const lpq_tensor* host, const lpq_te
 lpq_status lpq_nvfp4_global_scale_reciprocal(const float* group_amax, int32_t n_groups, float* out, void* stream);
 
 /* ======================================================================== */
+/* NVFP4 with another E4M3 maximum in the global scale: g = fl(A / (6 *
+ * e4m3_max)), e4m3_max 448 (the calls above) or 256, else LPQ_ERR_ARG.  The
+ * vime pull request 503 review quotes a configuration where the NVFP4
+ * "4over6" switch with its "E4M3 use 256" flag sets the E4M3 maximum to 256;
+ * the global scale of "verl NVFP4 QAT" 2.3 divides amax by FP4 max x FP8 max.
+ * Everything else is as for lpq_quantize_nvfp4 / lpq_nvfp4_qdq (and their
+ * grouped forms); lpq_dequantize_nvfp4* decode the output with the g it
+ * wrote.  The per-block choice between two scalings that gives "4over6" its
+ * name is not described on the pages and is not implemented. */
+lpq_status lpq_quantize_nvfp4_ex(const uint16_t* w, int64_t M, int64_t N, const float* amax, int e4m3_max,
+                                 uint8_t* p, uint8_t* s, float* g, void* stream);
+lpq_status lpq_nvfp4_qdq_ex(const uint16_t* x, int64_t M, int64_t N, const float* amax, int e4m3_max, uint16_t* y,
+                            void* stream);
+lpq_status lpq_quantize_nvfp4_grouped_ex(const lpq_tensor* host, const lpq_tensor* dev, int32_t n,
+                                         const float* group_amax, int32_t n_groups, int e4m3_max, float* group_g,
+                                         void* stream);
+lpq_status lpq_nvfp4_qdq_grouped_ex(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, const float* group_amax,
+                                    int32_t n_groups, int e4m3_max, void* stream);
+
+/* ======================================================================== */
 /* W4A4 activation observers.  "verl NVFP4 QAT" 2.2 (activation_observer,
  * default static_minmax, W4A4 mode only) and 3.1 (the choices static_minmax,
  * memoryless_minmax, minmax); the pages name them without defining them.

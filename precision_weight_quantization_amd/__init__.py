@@ -73,6 +73,10 @@ _SIG = {
     "lpq_quantize_mxfp8_floor_grouped": (_int, [_tp, _vp, _i32, _vp]),
     "lpq_nvfp4_global_scale_reciprocal": (_int, [_vp, _i32, _vp, _vp]),
     "lpq_nvfp4_global_scale": (_int, [_vp, _i32, _vp, _vp]),
+    "lpq_quantize_nvfp4_ex": (_int, [_vp, _i64, _i64, _vp, _int, _vp, _vp, _vp, _vp]),
+    "lpq_nvfp4_qdq_ex": (_int, [_vp, _i64, _i64, _vp, _int, _vp, _vp]),
+    "lpq_quantize_nvfp4_grouped_ex": (_int, [_tp, _vp, _i32, _vp, _i32, _int, _vp, _vp]),
+    "lpq_nvfp4_qdq_grouped_ex": (_int, [_tp, _vp, _i32, _vp, _i32, _int, _vp]),
     "lpq_observer_reset": (_int, [_vp, _vp]),
     "lpq_nvfp4_observe": (_int, [_vp, _i64, _i64, _int, ctypes.c_float, _vp, _vp, _vp]),
     "lpq_nvfp4_amax": (_int, [_vp, _i64, _i64, _vp, _int, _vp]),
@@ -200,6 +204,27 @@ def lpq_nvfp4_amax(w, amax=None, accumulate=False, stream=None):
     _check(_L.lpq_nvfp4_amax(w.data_ptr(), M, N, amax.data_ptr(), int(bool(accumulate)), _stream(stream)),
            "lpq_nvfp4_amax")
     return amax
+
+
+def lpq_quantize_nvfp4_ex(w, amax, e4m3_max=448, p=None, s=None, g=None, stream=None):
+    """lpq_quantize_nvfp4 with the global scale fl(A / (6 * e4m3_max)), e4m3_max 448 or 256."""
+    w = _bf16_in(w, "w")
+    M, N = w.shape
+    p = _empty((M, max(N // 2, 1)), torch.uint8, w) if p is None else p
+    s = _empty((M, max(N // 16, 1)), torch.float8_e4m3fn, w) if s is None else s
+    g = _empty((1,), torch.float32, w) if g is None else g
+    _check(_L.lpq_quantize_nvfp4_ex(w.data_ptr(), M, N, amax.data_ptr(), int(e4m3_max), p.data_ptr(), s.data_ptr(),
+                                    g.data_ptr(), _stream(stream)), "lpq_quantize_nvfp4_ex")
+    return p, s, g
+
+
+def lpq_nvfp4_qdq_ex(x, amax, e4m3_max=448, y=None, stream=None):
+    x = _bf16_in(x, "x")
+    M, N = x.shape
+    y = _empty((M, N), torch.bfloat16, x) if y is None else y
+    _check(_L.lpq_nvfp4_qdq_ex(x.data_ptr(), M, N, amax.data_ptr(), int(e4m3_max), y.data_ptr(), _stream(stream)),
+           "lpq_nvfp4_qdq_ex")
+    return y
 
 
 def lpq_quantize_nvfp4(w, amax, p=None, s=None, g=None, stream=None):
@@ -416,6 +441,17 @@ def lpq_quantize_nvfp4_grouped(table: TensorTable, group_amax, group_g, stream=N
     _check(_L.lpq_quantize_nvfp4_grouped(*table.args(), group_amax.data_ptr(), group_amax.numel(),
                                          group_g.data_ptr(), _stream(stream)), "lpq_quantize_nvfp4_grouped")
     return group_g
+
+
+def lpq_quantize_nvfp4_grouped_ex(table: TensorTable, group_amax, group_g, e4m3_max=448, stream=None):
+    _check(_L.lpq_quantize_nvfp4_grouped_ex(*table.args(), group_amax.data_ptr(), group_amax.numel(), int(e4m3_max),
+                                            group_g.data_ptr(), _stream(stream)), "lpq_quantize_nvfp4_grouped_ex")
+    return group_g
+
+
+def lpq_nvfp4_qdq_grouped_ex(table: TensorTable, group_amax, e4m3_max=448, stream=None):
+    _check(_L.lpq_nvfp4_qdq_grouped_ex(*table.args(), group_amax.data_ptr(), group_amax.numel(), int(e4m3_max),
+                                       _stream(stream)), "lpq_nvfp4_qdq_grouped_ex")
 
 
 def lpq_dequantize_nvfp4_grouped(table: TensorTable, group_g, stream=None):

@@ -124,6 +124,7 @@ __device__ __forceinline__ void load_chunk(T (&v)[U], const T* src, int64_t base
 // dependent memory access).
 struct ChunkMap {
     int32_t nseg;
+    float gdiv;                  // NVFP4 global-scale divisor 6 * E4M3 maximum (2688, or 1536)
     uint32_t first[kMaxSeg];
     uint32_t tensor0[kMaxSeg];
     uint32_t units[kMaxSeg];
@@ -296,9 +297,9 @@ struct GlobalScale {
     float tpre;    // 1, or 2^64 when g is tiny (applied to t before the division)
 };
 
-__device__ __forceinline__ GlobalScale global_scale(float A) {
+__device__ __forceinline__ GlobalScale global_scale(float A, float gdiv) {
     GlobalScale G;
-    G.g = A / 2688.0f;  // correctly rounded division
+    G.g = A / gdiv;  // correctly rounded division (gdiv = 6 * E4M3 maximum)
     const bool tiny = G.g < kTinyScale;
     G.tpre = tiny ? kPreScale : 1.0f;
     G.gd = tiny ? G.g * kPreScale : G.g;
@@ -516,7 +517,7 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_quant(const lpq_tensor* tabl
     const int64_t total = d.rows * d.cols;
     const int64_t base = W.unit * chunk_elems<U>();
     const int gi = GROUPED ? d.group : 0;
-    const GlobalScale G = global_scale(group_amax[gi]);
+    const GlobalScale G = global_scale(group_amax[gi], map.gdiv);
     const int tid = threadIdx.x;
     if (W.unit == 0 && tid == 0) group_g[gi] = G.g;   // same value from every member
     const v4u* src = reinterpret_cast<const v4u*>(d.src);
@@ -577,7 +578,7 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_qdq(const lpq_tensor* table,
     const lpq_tensor& d = W.d;
     const int64_t total = d.rows * d.cols;
     const int64_t base = W.unit * chunk_elems<U>();
-    const GlobalScale G = global_scale(group_amax[GROUPED ? d.group : 0]);
+    const GlobalScale G = global_scale(group_amax[GROUPED ? d.group : 0], map.gdiv);
     const v4u* src = reinterpret_cast<const v4u*>(d.src);
     v4u* dst = reinterpret_cast<v4u*>(d.dst);
     const int tid = threadIdx.x;
@@ -991,7 +992,7 @@ __global__ __launch_bounds__(kThreads) void k_requant_nvfp4(const lpq_requant_te
     const int64_t total = W.d.rows * W.d.cols;
     const int64_t base = W.unit * rq_chunk_elems<U>();
     const int gi = GROUPED ? W.d.group : 0;
-    const GlobalScale G = global_scale(group_amax[gi]);
+    const GlobalScale G = global_scale(group_amax[gi], map.gdiv);
     if (W.unit == 0 && threadIdx.x == 0) group_g[gi] = G.g;   // same value from every member
     if (base + rq_chunk_elems<U>() <= total) rq_nvfp4_body<U, true>(W.d, base, total, G);
     else rq_nvfp4_body<U, false>(W.d, base, total, G);
@@ -1312,7 +1313,7 @@ void dispatch(Kind k, dim3 grid, hipStream_t stream, const lpq_requant_tensor* t
 // units.
 template <typename D>
 lpq_status launch(Kind k, const D* host, const D* dev, int32_t n, const D& one, const float* fa, float* fb,
-                  hipStream_t stream) {
+                  hipStream_t stream, float gdiv = 2688.0f) {
     const int32_t count = dev ? n : 1;
     int32_t i0 = 0;
     while (i0 < count) {
@@ -1335,6 +1336,7 @@ lpq_status launch(Kind k, const D* host, const D* dev, int32_t n, const D& one, 
             i++;
         }
         map.nseg = nseg;
+        map.gdiv = gdiv;
         dispatch(k, dim3((unsigned)total), stream, dev ? dev + i0 : nullptr, one, map, fa, fb);
         lpq_status st = launched();
         if (st != LPQ_OK) return st;
@@ -1356,15 +1358,15 @@ lpq_tensor make_one(const void* src, void* dst, void* scale, int64_t M, int64_t 
 }
 
 template <typename D>
-lpq_status single(Kind k, const D& one, const float* fa, float* fb, void* stream) {
+lpq_status single(Kind k, const D& one, const float* fa, float* fb, void* stream, float gdiv = 2688.0f) {
     lpq_status st = check_tensor(k, one, 0);
     if (st != LPQ_OK) return st;
-    return launch<D>(k, nullptr, nullptr, 0, one, fa, fb, (hipStream_t)stream);
+    return launch<D>(k, nullptr, nullptr, 0, one, fa, fb, (hipStream_t)stream, gdiv);
 }
 
 template <typename D>
 lpq_status grouped(Kind k, const D* host, const D* dev, int32_t n, int32_t n_groups, const float* fa, float* fb,
-                   void* stream) {
+                   void* stream, float gdiv = 2688.0f) {
     if (!host || !dev) return LPQ_ERR_NULL;
     if (n <= 0) return LPQ_ERR_SHAPE;
     if (!aligned(dev, 8)) return LPQ_ERR_ALIGN;
@@ -1372,8 +1374,11 @@ lpq_status grouped(Kind k, const D* host, const D* dev, int32_t n, int32_t n_gro
         lpq_status st = check_tensor(k, host[i], n_groups);
         if (st != LPQ_OK) return st;
     }
-    return launch<D>(k, host, dev, n, D{}, fa, fb, (hipStream_t)stream);
+    return launch<D>(k, host, dev, n, D{}, fa, fb, (hipStream_t)stream, gdiv);
 }
+
+// 6 * the E4M3 maximum of an NVFP4 call, or 0 for an unsupported maximum.
+float gdiv_of(int e4m3_max) { return e4m3_max == 448 ? 2688.0f : (e4m3_max == 256 ? 1536.0f : 0.0f); }
 
 lpq_requant_tensor make_requant(const uint8_t* q, const float* s, void* dst, void* dst_scale, int64_t M, int64_t N) {
     lpq_requant_tensor t;
@@ -1512,6 +1517,41 @@ lpq_status lpq_nvfp4_qdq(const uint16_t* x, int64_t M, int64_t N, const float* a
     if (!amax) return LPQ_ERR_NULL;
     if (!aligned(amax, 4)) return LPQ_ERR_ALIGN;
     return single(NV_QDQ, make_one(x, y, nullptr, M, N), amax, nullptr, stream);
+}
+
+lpq_status lpq_quantize_nvfp4_ex(const uint16_t* w, int64_t M, int64_t N, const float* amax, int e4m3_max, uint8_t* p,
+                                 uint8_t* s, float* g, void* stream) {
+    if (!amax || !g) return LPQ_ERR_NULL;
+    if (!aligned(amax, 4) || !aligned(g, 4)) return LPQ_ERR_ALIGN;
+    if (gdiv_of(e4m3_max) == 0.0f) return LPQ_ERR_ARG;
+    return single(NV_Q, make_one(w, p, s, M, N), amax, g, stream, gdiv_of(e4m3_max));
+}
+
+lpq_status lpq_nvfp4_qdq_ex(const uint16_t* x, int64_t M, int64_t N, const float* amax, int e4m3_max, uint16_t* y,
+                            void* stream) {
+    if (!amax) return LPQ_ERR_NULL;
+    if (!aligned(amax, 4)) return LPQ_ERR_ALIGN;
+    if (gdiv_of(e4m3_max) == 0.0f) return LPQ_ERR_ARG;
+    return single(NV_QDQ, make_one(x, y, nullptr, M, N), amax, nullptr, stream, gdiv_of(e4m3_max));
+}
+
+lpq_status lpq_quantize_nvfp4_grouped_ex(const lpq_tensor* host, const lpq_tensor* dev, int32_t n,
+                                         const float* group_amax, int32_t n_groups, int e4m3_max, float* group_g,
+                                         void* stream) {
+    if (!group_amax || !group_g) return LPQ_ERR_NULL;
+    if (n_groups <= 0) return LPQ_ERR_SHAPE;
+    if (!aligned(group_amax, 4) || !aligned(group_g, 4)) return LPQ_ERR_ALIGN;
+    if (gdiv_of(e4m3_max) == 0.0f) return LPQ_ERR_ARG;
+    return grouped(NV_Q, host, dev, n, n_groups, group_amax, group_g, stream, gdiv_of(e4m3_max));
+}
+
+lpq_status lpq_nvfp4_qdq_grouped_ex(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, const float* group_amax,
+                                    int32_t n_groups, int e4m3_max, void* stream) {
+    if (!group_amax) return LPQ_ERR_NULL;
+    if (n_groups <= 0) return LPQ_ERR_SHAPE;
+    if (!aligned(group_amax, 4)) return LPQ_ERR_ALIGN;
+    if (gdiv_of(e4m3_max) == 0.0f) return LPQ_ERR_ARG;
+    return grouped(NV_QDQ, host, dev, n, n_groups, group_amax, nullptr, stream, gdiv_of(e4m3_max));
 }
 
 lpq_status lpq_quantize_fp8blk_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, void* stream) {

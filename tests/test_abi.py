@@ -56,6 +56,9 @@ def test_single_call_validation(lib):
     assert L.lpq_nvfp4_global_scale_reciprocal(None, 4, P, None) == 1
     assert L.lpq_nvfp4_global_scale_reciprocal(P, 0, P, None) == 2
     assert L.lpq_nvfp4_global_scale_reciprocal(P, 4, P + 2, None) == 3
+    assert L.lpq_quantize_nvfp4_ex(P, 4, 32, P, 300, P, P, P, None) == 6     # E4M3 maximum 448 or 256
+    assert L.lpq_nvfp4_qdq_ex(P, 4, 32, P, 0, P, None) == 6
+    assert L.lpq_nvfp4_qdq_ex(P, 4, 24, P, 256, P, None) == 2
     assert L.lpq_nvfp4_global_scale(None, 4, P, None) == 1
     assert L.lpq_nvfp4_global_scale(P, -1, P, None) == 2
     assert L.lpq_observer_reset(None, None) == 1

@@ -204,6 +204,21 @@ def test_mxfp8_floor_shapes_grouped(lpq, M, N):
     assert bad == 0
 
 
+@pytest.mark.parametrize("M,N", [(1, 16), (131, 160), (1000, 544)])
+def test_nvfp4_e4m3_max_256_single(lpq, M, N):
+    w_np = synth.generate(91, M + N, M, N, *synth.DIST_MOE)
+    w = to_dev_bf16(w_np)
+    amax = lpq.lpq_nvfp4_amax(w)
+    p, s, g = lpq.lpq_quantize_nvfp4_ex(w, amax, 256)
+    yq = lpq.lpq_nvfp4_qdq_ex(w, amax, 256)
+    A, og, [(op, os_)] = O.nvfp4_quantize_group([w_np], 256)
+    bad = int(np.float32(g.item()).view(np.uint32) != np.float32(og).view(np.uint32))
+    bad += report(f"nvfp4/256 packed {M}x{N}", host_u8(p), op) + report("scales", host_u8(s), os_)
+    bad += report("qdq", host_u16(yq), O.nvfp4_qdq(w_np, og))
+    assert int(host_u8(s).max()) <= 0x78   # block-scale codes stay at or below 256 (0x78)
+    assert bad == 0
+
+
 def test_nvfp4_global_scale_reciprocal(lpq):
     """fl(2688 / A) on random, tiny, huge, exact and zero amax values."""
     rng = np.random.default_rng(9)
@@ -215,9 +230,11 @@ def test_nvfp4_global_scale_reciprocal(lpq):
     assert report("reciprocal global scale", out.cpu().numpy().view(np.uint32), want.view(np.uint32)) == 0
 
 
-def test_bruteforce_nvfp4_grouped(lpq):
-    """Each 1x16 block is its own tensor and its own sibling group (own global scale)."""
-    w_np = brute_blocks(16, 2)
+@pytest.mark.parametrize("e4m3_max", [448, 256])
+def test_bruteforce_nvfp4_grouped(lpq, e4m3_max):
+    """Each 1x16 block is its own tensor and its own sibling group (own global scale);
+    with E4M3 maximum 448 (the default calls) and 256 (the *_ex calls)."""
+    w_np = brute_blocks(16, 2 if e4m3_max == 448 else 6)
     n = w_np.shape[0]
     w = to_dev_bf16(w_np)
     p = torch.empty((n, 8), dtype=torch.uint8, device="cuda")
@@ -230,14 +247,18 @@ def test_bruteforce_nvfp4_grouped(lpq):
     tdq = lpq.TensorTable([(p[i:i + 1], y[i:i + 1], s[i:i + 1], 1, 16, i) for i in range(n)])
     tqdq = lpq.TensorTable([(w[i:i + 1], yq[i:i + 1], None, 1, 16, i) for i in range(n)])
     lpq.lpq_nvfp4_amax_grouped(tq, amax)
-    lpq.lpq_quantize_nvfp4_grouped(tq, amax, g)
+    if e4m3_max == 448:
+        lpq.lpq_quantize_nvfp4_grouped(tq, amax, g)
+        lpq.lpq_nvfp4_qdq_grouped(tqdq, amax)
+    else:
+        lpq.lpq_quantize_nvfp4_grouped_ex(tq, amax, g, e4m3_max)
+        lpq.lpq_nvfp4_qdq_grouped_ex(tqdq, amax, e4m3_max)
     lpq.lpq_dequantize_nvfp4_grouped(tdq, g)
-    lpq.lpq_nvfp4_qdq_grouped(tqdq, amax)
     hp, hs, hy, hyq = host_u8(p), host_u8(s), host_u16(y), host_u16(yq)
     hg = g.cpu().numpy()
     op = np.empty_like(hp); os_ = np.empty_like(hs); oy = np.empty_like(hy); og = np.empty(n, np.float32)
     for i in range(n):
-        A, og[i], [(a, b)] = O.nvfp4_quantize_group([w_np[i:i + 1]])
+        A, og[i], [(a, b)] = O.nvfp4_quantize_group([w_np[i:i + 1]], e4m3_max)
         op[i], os_[i] = a[0], b[0]
     for i in range(n):
         oy[i] = O.nvfp4_dequantize(op[i:i + 1], os_[i:i + 1], float(og[i]))[0]
