@@ -825,6 +825,10 @@ struct TileCursor {
     }
 };
 
+// RN-to-BF16 of x as binary32 bits, in one convert: the pair (0, x) packs
+// BF16(x) into the high half over a zero low half.
+__device__ __forceinline__ uint32_t bf16_in_f32(float x) { return bf16x2(0.0f, x); }
+
 // The 16 codes of a vector times s, rounded to BF16 and widened back to
 // binary32 (exact): the dequantized values, in two halves of 8.  `amax` is
 // max |y| as binary32 bits: BF16 rounding is monotone, so it is the rounding
@@ -852,9 +856,12 @@ __device__ __forceinline__ Y16 fp8blk_values16(const v4u& c, float s) {
     for (int k = 3; k < 15; k += 2) m = fmaxf(fmaxf(m, fabsf(p[k])), fabsf(p[k + 1]));
     m = fmaxf(m, fabsf(p[15]));
     Y16 y;
-    y.amax = (bf16x2(m, 0.0f) & 0xffffu) << 16;
-    y.lo = widen8(v4u{bf16x2(p[0], p[1]), bf16x2(p[2], p[3]), bf16x2(p[4], p[5]), bf16x2(p[6], p[7])});
-    y.hi = widen8(v4u{bf16x2(p[8], p[9]), bf16x2(p[10], p[11]), bf16x2(p[12], p[13]), bf16x2(p[14], p[15])});
+    y.amax = bf16_in_f32(m);
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        y.lo.x[k] = __uint_as_float(bf16_in_f32(p[k]));
+        y.hi.x[k] = __uint_as_float(bf16_in_f32(p[8 + k]));
+    }
     return y;
 }
 
