@@ -63,17 +63,14 @@
 #ifndef LPQ_DQF_U
 #define LPQ_DQF_U 2
 #endif
-#ifndef LPQ_RQT_THREADS
-#define LPQ_RQT_THREADS 256
+#ifndef LPQ_RQT_TW
+#define LPQ_RQT_TW 2
 #endif
-#ifndef LPQ_RQT_WAVES_PER_SIMD
-#define LPQ_RQT_WAVES_PER_SIMD 1
-#endif
-#ifndef LPQ_TILEQ_THREADS
-#define LPQ_TILEQ_THREADS 256
+#ifndef LPQ_TILEQ_TW
+#define LPQ_TILEQ_TW 2
 #endif
 #ifndef LPQ_TILEQ_WAVES_PER_SIMD
-#define LPQ_TILEQ_WAVES_PER_SIMD 6
+#define LPQ_TILEQ_WAVES_PER_SIMD 4
 #endif
 #ifndef LPQ_TILED_THREADS
 #define LPQ_TILED_THREADS 1024
@@ -629,65 +626,102 @@ __device__ __forceinline__ TileGeom tile_geom(const lpq_tensor& d, int64_t tile)
     return T;
 }
 
-template <int TT>
-__device__ __forceinline__ uint32_t block_reduce_max(uint32_t m) {
-    m = wave_max(m);
-    __shared__ uint32_t part[TileShape<TT>::waves];
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
-    __syncthreads();
-    uint32_t r = part[0];
+// The quantizer's workgroup covers TW adjacent tiles of one tile row (128
+// rows x 128*TW columns, 256*TW threads): each pass reads one 256*TW-byte run
+// per row instead of 256 bytes, which the memory system serves better (an
+// access-pattern probe with no arithmetic: 70-72% of HBM peak for one tile,
+// 75-79% for two).  Lane t covers columns 8*(t % (16 TW)) .. +8 of rows
+// 16*pass + t / (16 TW); its tile within the strip is (t % (16 TW)) / 16.
+template <int TW>
+struct WideShape {
+    static constexpr int threads = 256 * TW;
+    static constexpr int lanes_per_row = 16 * TW;
+    static constexpr int rows_per_pass = threads / lanes_per_row;   // 16
+    static constexpr int passes = kTile / rows_per_pass;             // 8
+    static constexpr int waves = threads / 64;
+    static constexpr int rows_per_wave = 64 / lanes_per_row;         // 4 / TW
+};
+
+// Maximum of m over the lanes of each tile of a strip of TW tiles, for a
+// workgroup of THREADS lanes with LPT lanes per tile row (a row of the strip
+// is LPT * TW lanes); every lane gets its own tile's value.
+template <int LPT, int TW, int THREADS>
+__device__ __forceinline__ uint32_t strip_reduce_max(uint32_t m, int sub) {
+    constexpr int waves = THREADS / 64;
+    m = quad_max(m);
 #pragma unroll
-    for (int k = 1; k < TileShape<TT>::waves; k++) r = umax(r, part[k]);
+    for (int k = 4; k < LPT; k <<= 1) m = umax(m, (uint32_t)__shfl_xor((int)m, k));   // one row segment
+#pragma unroll
+    for (int k = LPT * TW; k < 64; k <<= 1) m = umax(m, (uint32_t)__shfl_xor((int)m, k));   // rows of the wave
+    __shared__ uint32_t part[waves][TW];
+    const int lane = threadIdx.x & 63;
+    if (lane < LPT * TW && lane % LPT == 0) part[threadIdx.x >> 6][lane / LPT] = m;
+    __syncthreads();
+    uint32_t r = part[0][sub];
+#pragma unroll
+    for (int k = 1; k < waves; k++) r = umax(r, part[k][sub]);
     return r;
 }
 
-template <int TT, bool GROUPED>
-__global__ __launch_bounds__(TT, LPQ_TILEQ_WAVES_PER_SIMD) void k_fp8blk_quant(const lpq_tensor* table, lpq_tensor one, ChunkMap map) {
+template <int TW, bool GROUPED>
+__global__ __launch_bounds__(256 * TW, LPQ_TILEQ_WAVES_PER_SIMD) void k_fp8blk_quant(const lpq_tensor* table,
+                                                                                      lpq_tensor one, ChunkMap map) {
+    using S = WideShape<TW>;
     const Work W = locate<GROUPED>(table, one, map);
     const lpq_tensor& d = W.d;
-    const TileGeom T = tile_geom(d, W.unit);
+    const int64_t M = d.rows, N = d.cols;
+    const int64_t tn = (N + kTile - 1) / kTile, tnw = (tn + TW - 1) / TW;
+    const int64_t tr = W.unit / tnw, tcw = W.unit % tnw;
+    const int64_t r0 = tr * kTile, c0 = tcw * kTile * TW;
+    const int64_t rows = M - r0 < kTile ? M - r0 : kTile;
+    const int64_t cols = N - c0 < kTile * TW ? N - c0 : kTile * TW;   // columns of the strip inside the tensor
+    const bool fast = rows == kTile && cols == kTile * TW && (N & 7) == 0 &&
+                      ((reinterpret_cast<uintptr_t>(d.src) | reinterpret_cast<uintptr_t>(d.dst)) & 15) == 0;
     const uint16_t* w = reinterpret_cast<const uint16_t*>(d.src);
     uint8_t* q = reinterpret_cast<uint8_t*>(d.dst);
     const int tid = threadIdx.x;
-    const int lr = tid >> 4;           // row inside a pass
-    const int lc = (tid & 15) * 8;     // first column of the lane's segment
+    const int lr = tid / S::lanes_per_row;          // row inside a pass
+    const int lc = (tid % S::lanes_per_row) * 8;    // first column of the lane's segment in the strip
+    const int sub = lc / kTile;                     // the lane's tile within the strip
 
-    v4u v[TileShape<TT>::passes];
-    if (T.fast) {
+    v4u v[S::passes];
+    if (fast) {
 #pragma unroll
-        for (int p = 0; p < TileShape<TT>::passes; p++) {
-            const int64_t off = (T.r0 + TileShape<TT>::rows_per_pass * p + lr) * d.cols + T.c0 + lc;
+        for (int p = 0; p < S::passes; p++) {
+            const int64_t off = (r0 + S::rows_per_pass * p + lr) * N + c0 + lc;
             v[p] = load<kNTL>(reinterpret_cast<const v4u*>(w + off));
         }
     } else {
-        for (int p = 0; p < TileShape<TT>::passes; p++) {
-            const int64_t r = TileShape<TT>::rows_per_pass * p + lr;
+        for (int p = 0; p < S::passes; p++) {
+            const int64_t r = S::rows_per_pass * p + lr;
             uint32_t h[8];
             for (int k = 0; k < 8; k++) {
-                const bool in = r < T.rows && lc + k < T.cols;
-                h[k] = in ? w[(T.r0 + r) * d.cols + T.c0 + lc + k] : 0u;
+                const bool in = r < rows && lc + k < cols;
+                h[k] = in ? w[(r0 + r) * N + c0 + lc + k] : 0u;
             }
             v[p] = v4u{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
         }
     }
     uint32_t m = 0;
 #pragma unroll
-    for (int p = 0; p < TileShape<TT>::passes; p++) m = umax(m, absmax8_bits(v[p]));
-    const float amax = __uint_as_float(block_reduce_max<TT>(m));
+    for (int p = 0; p < S::passes; p++) m = umax(m, absmax8_bits(v[p]));
+    const float amax = __uint_as_float(strip_reduce_max<16, TW, S::threads>(m, sub));
     const float s = amax / kE4M3Max;   // correctly rounded division
-    if (tid == 0) reinterpret_cast<float*>(d.scale)[T.index] = s;
+    if (lr == 0 && (lc & (kTile - 1)) == 0 && sub * kTile < cols)
+        reinterpret_cast<float*>(d.scale)[tr * tn + tcw * TW + sub] = s;
     const bool tiny = s > 0.0f && s < kTinyScale;
     const float sd = tiny ? s * kPreScale : s;
     const float r = s > 0.0f ? rcp_rn(sd) : 0.0f;
+    const bool any_tiny = any_lane(tiny);
 
 #pragma unroll
-    for (int p = 0; p < TileShape<TT>::passes; p++) {
+    for (int p = 0; p < S::passes; p++) {
         float x[8] = {bf16_lo(v[p].x), bf16_hi(v[p].x), bf16_lo(v[p].y), bf16_hi(v[p].y),
                       bf16_lo(v[p].z), bf16_hi(v[p].z), bf16_lo(v[p].w), bf16_hi(v[p].w)};
-        if (tiny) {
+        if (any_tiny) {
 #pragma unroll
-            for (int k = 0; k < 8; k++) x[k] *= kPreScale;
-        }   // tile-uniform
+            for (int k = 0; k < 8; k++) x[k] *= tiny ? kPreScale : 1.0f;
+        }
         float qq[8];
 #pragma unroll
         for (int k = 0; k < 8; k++) qq[k] = quot_rn(x[k], sd, r);
@@ -695,13 +729,13 @@ __global__ __launch_bounds__(TT, LPQ_TILEQ_WAVES_PER_SIMD) void k_fp8blk_quant(c
         lo = e4m3x2<true>(qq[2], qq[3], lo);
         uint32_t hi = e4m3x2<false>(qq[4], qq[5], 0u);
         hi = e4m3x2<true>(qq[6], qq[7], hi);
-        const int64_t row = TileShape<TT>::rows_per_pass * p + lr;
-        if (T.fast) {
-            store<kNTS>(reinterpret_cast<v2u*>(q + (T.r0 + row) * d.cols + T.c0 + lc), v2u{lo, hi});
-        } else if (row < T.rows) {
+        const int64_t row = S::rows_per_pass * p + lr;
+        if (fast) {
+            store<kNTS>(reinterpret_cast<v2u*>(q + (r0 + row) * N + c0 + lc), v2u{lo, hi});
+        } else if (row < rows) {
             const uint32_t c8[2] = {lo, hi};
             for (int k = 0; k < 8; k++)
-                if (lc + k < T.cols) q[(T.r0 + row) * d.cols + T.c0 + lc + k] = (uint8_t)(c8[k >> 2] >> (8 * (k & 3)));
+                if (lc + k < cols) q[(r0 + row) * N + c0 + lc + k] = (uint8_t)(c8[k >> 2] >> (8 * (k & 3)));
         }
     }
 }
@@ -1052,36 +1086,41 @@ __global__ __launch_bounds__(kThreads) void k_fp8blk_dequant_flat(const lpq_tens
     else fp8blk_dequant_flat_body<U, false>(W.d, base, total);
 }
 
-// Block-wise FP8 -> block-wise FP8, one 128x128 tile per workgroup: the
-// tile's dequantized values y = BF16(fl(code * s)) stay in registers (16
+// Block-wise FP8 -> block-wise FP8, TW adjacent 128x128 tiles per workgroup:
+// each tile's dequantized values y = BF16(fl(code * s)) stay in registers (16
 // codes per lane per pass), their amax gives the new scale s' = fl(amax/448),
-// and each y is encoded as E4M3(fl(y / s')).
-template <int TT>
-struct RqTileShape {
-    static constexpr int rows_per_pass = TT / 8;   // 8 lanes x 16 codes per 128-column row
-    static constexpr int passes = kTile / rows_per_pass;
+// and each y is encoded as E4M3(fl(y / s')).  Lane t covers codes
+// 16*(t % (8 TW)) .. +16 of rows (TW*256/(8 TW))*pass + t / (8 TW).
+template <int TW>
+struct RqWideShape {
+    static constexpr int threads = 256 * TW;
+    static constexpr int lanes_per_row = 8 * TW;
+    static constexpr int rows_per_pass = threads / lanes_per_row;   // 32
+    static constexpr int passes = kTile / rows_per_pass;             // 4
 };
 
-template <int TT, bool GROUPED>
-__global__ __launch_bounds__(TT, LPQ_RQT_WAVES_PER_SIMD) void k_requant_fp8blk(const lpq_requant_tensor* table, lpq_requant_tensor one,
-                                                       ChunkMap map) {
-    using S = RqTileShape<TT>;
+template <int TW, bool GROUPED>
+__global__ __launch_bounds__(256 * TW) void k_requant_fp8blk(const lpq_requant_tensor* table, lpq_requant_tensor one,
+                                                             ChunkMap map) {
+    using S = RqWideShape<TW>;
     const WorkT<lpq_requant_tensor> W = locate<GROUPED>(table, one, map);
     const lpq_requant_tensor& d = W.d;
     const int64_t M = d.rows, N = d.cols;
-    const int64_t tn = (N + kTile - 1) / kTile;
-    const int64_t tile = W.unit;
-    const int64_t r0 = (tile / tn) * kTile, c0 = (tile % tn) * kTile;
+    const int64_t tn = (N + kTile - 1) / kTile, tnw = (tn + TW - 1) / TW;
+    const int64_t tr = W.unit / tnw, tcw = W.unit % tnw;
+    const int64_t r0 = tr * kTile, c0 = tcw * kTile * TW;
     const int64_t rows = M - r0 < kTile ? M - r0 : kTile;
-    const int64_t cols = N - c0 < kTile ? N - c0 : kTile;
-    const bool fast = rows == kTile && cols == kTile && (N & 15) == 0 &&
+    const int64_t cols = N - c0 < kTile * TW ? N - c0 : kTile * TW;
+    const bool fast = rows == kTile && cols == kTile * TW && (N & 15) == 0 &&
                       ((reinterpret_cast<uintptr_t>(d.src) | reinterpret_cast<uintptr_t>(d.dst)) & 15) == 0;
     const uint8_t* q = d.src;
     uint8_t* qo = reinterpret_cast<uint8_t*>(d.dst);
-    const float s = d.src_scale[tile];
     const int tid = threadIdx.x;
-    const int lr = tid >> 3;           // row inside a pass
-    const int lc = (tid & 7) * 16;     // first column of the lane's 16 codes
+    const int lr = tid / S::lanes_per_row;          // row inside a pass
+    const int lc = (tid % S::lanes_per_row) * 16;   // first column of the lane's 16 codes in the strip
+    const int sub = lc / kTile;                     // the lane's tile within the strip
+    const bool present = sub * kTile < cols;
+    const float s = present ? d.src_scale[tr * tn + tcw * TW + sub] : 0.0f;
 
     v4u c[S::passes];
     if (fast) {
@@ -1110,13 +1149,14 @@ __global__ __launch_bounds__(TT, LPQ_RQT_WAVES_PER_SIMD) void k_requant_fp8blk(c
             cm = fmaxf(fmaxf(cm, fabsf(b[0])), fabsf(b[1]));
         }
     }
-    const uint32_t mb = (bf16x2(cm * fabsf(s), 0.0f) & 0xffffu) << 16;   // codes outside the tile read as 0
-    const float amax = __uint_as_float(block_reduce_max<TT>(mb));
+    const uint32_t mb = bf16_in_f32(cm * fabsf(s));   // codes outside the tensor read as 0
+    const float amax = __uint_as_float(strip_reduce_max<8, TW, S::threads>(mb, sub));
     const float s2 = amax / kE4M3Max;   // correctly rounded division
-    if (tid == 0) reinterpret_cast<float*>(d.dst_scale)[tile] = s2;
+    if (lr == 0 && (lc & (kTile - 1)) == 0 && present) reinterpret_cast<float*>(d.dst_scale)[tr * tn + tcw * TW + sub] = s2;
     const bool tiny = s2 > 0.0f && s2 < kTinyScale;
     const float sd = tiny ? s2 * kPreScale : s2;
     const float r = s2 > 0.0f ? rcp_rn(sd) : 0.0f;
+    const bool any_tiny = any_lane(tiny);
 
 #pragma unroll
     for (int p = 0; p < S::passes; p++) {
@@ -1127,10 +1167,10 @@ __global__ __launch_bounds__(TT, LPQ_RQT_WAVES_PER_SIMD) void k_requant_fp8blk(c
             x[k] = y.lo.x[k];
             x[8 + k] = y.hi.x[k];
         }
-        if (tiny) {
+        if (any_tiny) {
 #pragma unroll
-            for (int k = 0; k < 16; k++) x[k] *= kPreScale;
-        }   // tile-uniform
+            for (int k = 0; k < 16; k++) x[k] *= tiny ? kPreScale : 1.0f;
+        }
         uint32_t o[4];
 #pragma unroll
         for (int k = 0; k < 4; k++) {
@@ -1232,7 +1272,7 @@ lpq_status check_tensor(Kind k, const lpq_requant_tensor& t, int32_t n_groups) {
 int64_t units(Kind k, const lpq_tensor& t) {
     const int64_t n = t.rows * t.cols;
     switch (k) {
-    case FP8BLK_Q:
+    case FP8BLK_Q: return ((t.rows + kTile - 1) / kTile) * ((t.cols + kTile * LPQ_TILEQ_TW - 1) / (kTile * LPQ_TILEQ_TW));
     case FP8BLK_DQ: return ((t.rows + kTile - 1) / kTile) * ((t.cols + kTile - 1) / kTile);
     case FP8BLK_DQF: return (n + dqf_chunk_elems<LPQ_DQF_U>() - 1) / dqf_chunk_elems<LPQ_DQF_U>();
     case MXFP8_Q:
@@ -1249,7 +1289,7 @@ int64_t units(Kind k, const lpq_tensor& t) {
 int64_t units(Kind k, const lpq_requant_tensor& t) {
     const int64_t n = t.rows * t.cols;
     switch (k) {
-    case RQ_FP8: return ((t.rows + kTile - 1) / kTile) * ((t.cols + kTile - 1) / kTile);
+    case RQ_FP8: return ((t.rows + kTile - 1) / kTile) * ((t.cols + kTile * LPQ_RQT_TW - 1) / (kTile * LPQ_RQT_TW));
     case RQ_MX: return (n + rq_chunk_elems<LPQ_RQM_U>() - 1) / rq_chunk_elems<LPQ_RQM_U>();
     case RQ_AMAX: return (n + rq_chunk_elems<LPQ_RQA_U>() - 1) / rq_chunk_elems<LPQ_RQA_U>();
     case RQ_NV: return (n + rq_chunk_elems<LPQ_RQN_U>() - 1) / rq_chunk_elems<LPQ_RQN_U>();
@@ -1261,10 +1301,10 @@ constexpr int64_t kMaxGridX = 0x7fffffffLL;
 
 void dispatch(Kind k, dim3 grid, hipStream_t stream, const lpq_tensor* tab, const lpq_tensor& one, const ChunkMap& map,
               const float* fa, float* fb) {
-    const dim3 flat(kThreads), tileq(LPQ_TILEQ_THREADS), tiled(LPQ_TILED_THREADS);
+    const dim3 flat(kThreads), tileq(256 * LPQ_TILEQ_TW), tiled(LPQ_TILED_THREADS);
     if (tab) {
         switch (k) {
-        case FP8BLK_Q: hipLaunchKernelGGL((k_fp8blk_quant<LPQ_TILEQ_THREADS, true>), grid, tileq, 0, stream, tab, one, map); break;
+        case FP8BLK_Q: hipLaunchKernelGGL((k_fp8blk_quant<LPQ_TILEQ_TW, true>), grid, tileq, 0, stream, tab, one, map); break;
         case FP8BLK_DQ: hipLaunchKernelGGL((k_fp8blk_dequant<LPQ_TILED_THREADS, true>), grid, tiled, 0, stream, tab, one, map); break;
         case FP8BLK_DQF: hipLaunchKernelGGL((k_fp8blk_dequant_flat<LPQ_DQF_U, true>), grid, flat, 0, stream, tab, one, map); break;
         case MXFP8_Q: hipLaunchKernelGGL((k_mxfp8_quant<LPQ_MXQ_U, true>), grid, flat, 0, stream, tab, one, map); break;
@@ -1278,7 +1318,7 @@ void dispatch(Kind k, dim3 grid, hipStream_t stream, const lpq_tensor* tab, cons
         }
     } else {
         switch (k) {
-        case FP8BLK_Q: hipLaunchKernelGGL((k_fp8blk_quant<LPQ_TILEQ_THREADS, false>), grid, tileq, 0, stream, tab, one, map); break;
+        case FP8BLK_Q: hipLaunchKernelGGL((k_fp8blk_quant<LPQ_TILEQ_TW, false>), grid, tileq, 0, stream, tab, one, map); break;
         case FP8BLK_DQ: hipLaunchKernelGGL((k_fp8blk_dequant<LPQ_TILED_THREADS, false>), grid, tiled, 0, stream, tab, one, map); break;
         case FP8BLK_DQF: hipLaunchKernelGGL((k_fp8blk_dequant_flat<LPQ_DQF_U, false>), grid, flat, 0, stream, tab, one, map); break;
         case MXFP8_Q: hipLaunchKernelGGL((k_mxfp8_quant<LPQ_MXQ_U, false>), grid, flat, 0, stream, tab, one, map); break;
@@ -1295,10 +1335,10 @@ void dispatch(Kind k, dim3 grid, hipStream_t stream, const lpq_tensor* tab, cons
 
 void dispatch(Kind k, dim3 grid, hipStream_t stream, const lpq_requant_tensor* tab, const lpq_requant_tensor& one,
               const ChunkMap& map, const float* fa, float* fb) {
-    const dim3 flat(kThreads), tile(LPQ_RQT_THREADS);
+    const dim3 flat(kThreads), tile(256 * LPQ_RQT_TW);
     if (tab) {
         switch (k) {
-        case RQ_FP8: hipLaunchKernelGGL((k_requant_fp8blk<LPQ_RQT_THREADS, true>), grid, tile, 0, stream, tab, one, map); break;
+        case RQ_FP8: hipLaunchKernelGGL((k_requant_fp8blk<LPQ_RQT_TW, true>), grid, tile, 0, stream, tab, one, map); break;
         case RQ_MX: hipLaunchKernelGGL((k_requant_mxfp8<LPQ_RQM_U, true>), grid, flat, 0, stream, tab, one, map); break;
         case RQ_AMAX: hipLaunchKernelGGL((k_requant_amax<LPQ_RQA_U, true>), grid, flat, 0, stream, tab, one, map, fb); break;
         case RQ_NV: hipLaunchKernelGGL((k_requant_nvfp4<LPQ_RQN_U, true>), grid, flat, 0, stream, tab, one, map, fa, fb); break;
@@ -1306,7 +1346,7 @@ void dispatch(Kind k, dim3 grid, hipStream_t stream, const lpq_requant_tensor* t
         }
     } else {
         switch (k) {
-        case RQ_FP8: hipLaunchKernelGGL((k_requant_fp8blk<LPQ_RQT_THREADS, false>), grid, tile, 0, stream, tab, one, map); break;
+        case RQ_FP8: hipLaunchKernelGGL((k_requant_fp8blk<LPQ_RQT_TW, false>), grid, tile, 0, stream, tab, one, map); break;
         case RQ_MX: hipLaunchKernelGGL((k_requant_mxfp8<LPQ_RQM_U, false>), grid, flat, 0, stream, tab, one, map); break;
         case RQ_AMAX: hipLaunchKernelGGL((k_requant_amax<LPQ_RQA_U, false>), grid, flat, 0, stream, tab, one, map, fb); break;
         case RQ_NV: hipLaunchKernelGGL((k_requant_nvfp4<LPQ_RQN_U, false>), grid, flat, 0, stream, tab, one, map, fa, fb); break;
