@@ -291,15 +291,17 @@ struct GlobalScale {
     float g;       // the global scale
     float gd;      // divisor used for fl(t / g): g, or g * 2^64 when g is tiny
     float rg;      // RN(1 / gd)
-    float tpre;    // 1, or 2^64 when g is tiny (applied to t before the division)
+    bool tiny;     // g < 2^-90: t and g are pre-scaled by 2^64
+    bool large;    // g >= 2^-81: every nonzero block multiplier S = E4M3value * g
+                   // is at least 2^-9 * 2^-81 = 2^-90, so none is pre-scaled
 };
 
 __device__ __forceinline__ GlobalScale global_scale(float A, float gdiv) {
     GlobalScale G;
     G.g = A / gdiv;  // correctly rounded division (gdiv = 6 * E4M3 maximum)
-    const bool tiny = G.g < kTinyScale;
-    G.tpre = tiny ? kPreScale : 1.0f;
-    G.gd = tiny ? G.g * kPreScale : G.g;
+    G.tiny = G.g < kTinyScale;
+    G.large = G.g >= 0x1p-81f;
+    G.gd = G.tiny ? G.g * kPreScale : G.g;
     G.rg = G.g > 0.0f ? rcp_rn(G.gd) : 0.0f;
     return G;
 }
@@ -312,6 +314,7 @@ struct BlockScale {
     float Sd;      // divisor for the quotient: S, or S * 2^64 when S is tiny
     float r;       // RN(1 / Sd), or 0 when S == 0
     float xpre;    // 1, or 2^64 when S is tiny
+    bool maybe_tiny;   // wave-uniform: some S of the group could be tiny
 };
 
 __device__ __forceinline__ BlockScale block_scale(uint32_t bmax_bits, const GlobalScale& G) {
@@ -325,13 +328,20 @@ __device__ __forceinline__ BlockScale block_scale(uint32_t bmax_bits, const Glob
         __asm__ volatile("" : "+v"(bb));   // an empty barrier: keeps the long division inside the branch
         if (bb < 0x1p-100f) t6 = bb / 6.0f;
     }
-    const float t = t6 * G.tpre;                             // maybe pre-scaled by 2^64
+    const float t = G.tiny ? t6 * kPreScale : t6;           // group-uniform pre-scaling
     const float u = quot_rn(t, G.gd, G.rg);                  // fl(fl(b / 6) / g)
-    B.code = G.g > 0.0f ? (e4m3x2<false>(u, 0.0f, 0u) & 0xffu) : 0u;
+    const float uc = __builtin_amdgcn_fmed3f(u, -kE4M3Max, kE4M3Max);
+    B.code = G.g > 0.0f ? ((uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(uc, 0.0f, 0, false) & 0xffu) : 0u;
     B.S = e4m3_to_f32(B.code) * G.g;
-    const bool tiny = B.S > 0.0f && B.S < kTinyScale;
-    B.xpre = tiny ? kPreScale : 1.0f;
-    B.Sd = tiny ? B.S * kPreScale : B.S;
+    B.maybe_tiny = !G.large;
+    if (G.large) {   // group-uniform: no block multiplier is tiny
+        B.xpre = 1.0f;
+        B.Sd = B.S;
+    } else {
+        const bool tiny = B.S > 0.0f && B.S < kTinyScale;
+        B.xpre = tiny ? kPreScale : 1.0f;
+        B.Sd = tiny ? B.S * kPreScale : B.S;
+    }
     B.r = B.S > 0.0f ? rcp_rn(B.Sd) : 0.0f;
     return B;
 }
@@ -341,7 +351,7 @@ __device__ __forceinline__ uint32_t e2m1x8(const F8& f, const BlockScale& B) {
     float x[8];
 #pragma unroll
     for (int k = 0; k < 8; k++) x[k] = f.x[k];
-    if (any_lane(B.xpre != 1.0f)) {
+    if (B.maybe_tiny && any_lane(B.xpre != 1.0f)) {
 #pragma unroll
         for (int k = 0; k < 8; k++) x[k] *= B.xpre;
     }
