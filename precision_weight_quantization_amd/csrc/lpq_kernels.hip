@@ -19,7 +19,11 @@
 //    workgroup streams 16-byte BF16 vectors, 8 elements per lane, U vectors
 //    per lane; a 1x32 block is a quad of lanes and a 1x16 block a pair,
 //    reduced with DPP lane permutations.  U is 2 to 4 (16 for the read-only
-//    amax pass): enough bytes in flight per CU, short-lived workgroups.
+//    amax pass): enough bytes in flight per CU, short-lived workgroups.  A
+//    lane's U loads go out either all at once or one vector ahead of the
+//    work, chosen per kernel by measurement: the encoders and the MXFP8
+//    decoder run faster with fewer reads in flight per wave.  Full chunks
+//    (all but a tensor's last) take a body compiled without bounds checks.
 //  * Block-wise FP8 gives one workgroup a 128x128 tile: 16 lanes per 256-byte
 //    row segment, 2048/threads row passes, all values kept in registers
 //    between the tile-amax reduction (DPP + LDS across the waves) and the
@@ -75,6 +79,25 @@
 #ifndef LPQ_TILED_THREADS
 #define LPQ_TILED_THREADS 1024
 #endif
+// Load order of the flat kernels (1: one vector ahead, 0: all U up front).
+#ifndef LPQ_MXQ_AHEAD
+#define LPQ_MXQ_AHEAD 1
+#endif
+#ifndef LPQ_NVQ_AHEAD
+#define LPQ_NVQ_AHEAD 1
+#endif
+#ifndef LPQ_QDQ_AHEAD
+#define LPQ_QDQ_AHEAD 1
+#endif
+#ifndef LPQ_MXD_AHEAD
+#define LPQ_MXD_AHEAD 1
+#endif
+#ifndef LPQ_NVD_AHEAD
+#define LPQ_NVD_AHEAD 0
+#endif
+#ifndef LPQ_DQF_AHEAD
+#define LPQ_DQF_AHEAD 0
+#endif
 #ifndef LPQ_NTL
 #define LPQ_NTL 1
 #endif
@@ -98,19 +121,67 @@ constexpr int64_t chunk_elems() { return (int64_t)kThreads * 8 * U; }
 // Loads the lane's U vectors of a flat chunk: lane t of vector u holds the EV
 // elements starting at base + (u * kThreads + t) * EV.  A full chunk (the
 // common case) loads without per-lane bounds checks.
-template <int U, int EV = 8, typename T>
-__device__ __forceinline__ void load_chunk(T (&v)[U], const T* src, int64_t base, int64_t total, bool full) {
+template <int U, bool FULL, int EV = 8, typename T>
+__device__ __forceinline__ void load_chunk(T (&v)[U], const T* src, int64_t base, int64_t total) {
     const T* p = src + base / EV + threadIdx.x;
-    if (full) {
 #pragma unroll
-        for (int u = 0; u < U; u++) v[u] = load<kNTL>(p + u * kThreads);
-    } else {
+    for (int u = 0; u < U; u++) {
+        const bool in = FULL || base + (int64_t)(u * kThreads + threadIdx.x) * EV < total;
+        v[u] = in ? load<kNTL>(p + u * kThreads) : T{};
+    }
+}
+
+// Waits until the loads that produce x (and y) have arrived, and keeps every
+// later memory access behind that point: an empty asm that reads the values
+// (the compiler puts the memory-counter wait in front of it) and clobbers
+// memory.
+__device__ __forceinline__ void arrived(uint32_t x) { __asm__ volatile("" ::"v"(x) : "memory"); }
+__device__ __forceinline__ void arrived(uint32_t x, uint32_t y) { __asm__ volatile("" ::"v"(x), "v"(y) : "memory"); }
+
+// Issue order of a lane's U vectors, fetch(u) issuing the loads of vector u.
+// All U up front puts the most bytes in flight per wave; one ahead issues
+// vector u + 1 once vector u has arrived (step(u, ...) before the work on
+// vector u), so a wave holds at most two vectors in flight.  Which is faster
+// depends on the kernel's read / write mix and is measured per kernel.
+template <int U, bool ONE_AHEAD, typename Fetch>
+__device__ __forceinline__ void fetch_start(Fetch&& fetch) {
+    fetch(0);
+    if constexpr (!ONE_AHEAD) {
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            const int64_t e0 = base + (int64_t)(u * kThreads + threadIdx.x) * EV;
-            v[u] = e0 < total ? load<kNTL>(p + u * kThreads) : T{};
+        for (int u = 1; u < U; u++) fetch(u);
+    }
+}
+template <int U, bool ONE_AHEAD, typename Fetch, typename... X>
+__device__ __forceinline__ void fetch_step(int u, Fetch&& fetch, X... have) {
+    if constexpr (ONE_AHEAD) {
+        if (u + 1 < U) {
+            arrived(have...);
+            fetch(u + 1);
         }
     }
+}
+
+// Vector u of a lane in a flat chunk of EV-element vectors, zero past the end.
+template <bool FULL, int EV = 8, typename T>
+__device__ __forceinline__ T load_vec(const T* src, int64_t base, int64_t total, int u) {
+    const bool in = FULL || base + (int64_t)(u * kThreads + threadIdx.x) * EV < total;
+    return in ? load<kNTL>(src + base / EV + threadIdx.x + u * kThreads) : T{};
+}
+
+template <bool B>
+struct Full {
+    static constexpr bool value = B;
+};
+
+// Runs body(Full<true>) for a full chunk (every chunk of a tensor but its
+// last) and body(Full<false>) otherwise.  Fullness is uniform over the
+// workgroup; as a compile-time constant it gives full chunks a straight-line
+// body whose loads are all issued before the first wait, where a run-time
+// flag would let the compiler merge the two paths around per-lane branches.
+template <int64_t CHUNK, typename Body>
+__device__ __forceinline__ void by_fullness(int64_t base, int64_t total, Body&& body) {
+    if (base + CHUNK <= total) body(Full<true>{});
+    else body(Full<false>{});
 }
 
 // Dense work map of one launch.  Consecutive tensors with the same number of
@@ -172,17 +243,17 @@ __device__ __forceinline__ WorkT<D> locate(const D* table, const D& one, const C
     } else {
         const uint32_t b = blockIdx.x;
         // every table entry is read at a constant offset (one batch of scalar
-        // loads from the kernel arguments), then the segment is selected
+        // loads from the kernel arguments); the segment search stops at the
+        // first segment past b (a launch of one segment does no search)
         uint32_t f = 0, u = m.units[0], t0 = 0;
         double inv = m.inv_units[0];
 #pragma unroll
         for (int k = 1; k < kMaxSeg; k++) {
-            if (k < m.nseg && m.first[k] <= b) {
-                f = m.first[k];
-                u = m.units[k];
-                t0 = m.tensor0[k];
-                inv = m.inv_units[k];
-            }
+            if (k >= m.nseg || m.first[k] > b) break;
+            f = m.first[k];
+            u = m.units[k];
+            t0 = m.tensor0[k];
+            inv = m.inv_units[k];
         }
         const uint32_t x = b - f;
         // x / u from a double-precision estimate (off by at most one), corrected
@@ -212,7 +283,7 @@ __device__ __forceinline__ v2u mx_encode8(const F8& f, float X) {
 // FLOOR selects the shared-exponent rule of the OCP MX specification
 // (floor(log2 amax) - 8, elements beyond 448 saturate) instead of the default
 // no-saturation rule.
-template <int U, bool GROUPED, bool FLOOR = false>
+template <int U, bool GROUPED, bool FLOOR = false, bool AHEAD = LPQ_MXQ_AHEAD != 0>
 __global__ __launch_bounds__(kThreads) void k_mxfp8_quant(const lpq_tensor* table, lpq_tensor one, ChunkMap map) {
     const Work W = locate<GROUPED>(table, one, map);
     const lpq_tensor& d = W.d;
@@ -222,33 +293,35 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_quant(const lpq_tensor* tabl
     v2u* dst = reinterpret_cast<v2u*>(d.dst);
     uint8_t* esc = reinterpret_cast<uint8_t*>(d.scale);
     const int tid = threadIdx.x;
-
-    // every chunk but the last of a tensor is full: no per-lane bounds checks
-    const bool full = base + chunk_elems<U>() <= total;
-    v4u v[U];
-    load_chunk<U>(v, src, base, total, full);
+    by_fullness<chunk_elems<U>()>(base, total, [&](auto full) {
+        constexpr bool FULL = decltype(full)::value;
+        v4u v[U];
+        auto fetch = [&](int u) { v[u] = load_vec<FULL>(src, base, total, u); };
+        fetch_start<U, AHEAD>(fetch);
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-        const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
-        // a quad of lanes is one 32-element block; blocks never straddle the end
-        F8 f = widen8(v[u]);
-        const uint32_t amax = quad_max(absmax8_f32(f));
-        const uint32_t byte = FLOOR ? mx_floor_scale_byte(amax) : mx_scale_byte(amax);
-        if constexpr (FLOOR) {
-            // saturation: clamp to +-448 * 2^(byte-127) (exact; byte <= 246 keeps it finite)
-            const float L = __uint_as_float(((byte + 8u) << 23) | 0x600000u);
+        for (int u = 0; u < U; u++) {
+            fetch_step<U, AHEAD>(u, fetch, v[u].x);
+            const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+            // a quad of lanes is one 32-element block; blocks never straddle the end
+            F8 f = widen8(v[u]);
+            const uint32_t amax = quad_max(absmax8_f32(f));
+            const uint32_t byte = FLOOR ? mx_floor_scale_byte(amax) : mx_scale_byte(amax);
+            if constexpr (FLOOR) {
+                // saturation: clamp to +-448 * 2^(byte-127) (exact; byte <= 246 keeps it finite)
+                const float L = __uint_as_float(((byte + 8u) << 23) | 0x600000u);
 #pragma unroll
-            for (int k = 0; k < 8; k++) f.x[k] = __builtin_amdgcn_fmed3f(f.x[k], -L, L);
+                for (int k = 0; k < 8; k++) f.x[k] = __builtin_amdgcn_fmed3f(f.x[k], -L, L);
+            }
+            const v2u codes = mx_encode8(f, ue8m0_operand(byte));
+            if (FULL || e0 < total) {
+                store<kNTS>(dst + (e0 >> 3), codes);
+                if ((tid & 3) == 0) store_u8(esc + (e0 >> 5), byte);
+            }
         }
-        const v2u codes = mx_encode8(f, ue8m0_operand(byte));
-        if (full || e0 < total) {
-            store<kNTS>(dst + (e0 >> 3), codes);
-            if ((tid & 3) == 0) store_u8(esc + (e0 >> 5), byte);
-        }
-    }
+    });
 }
 
-template <int U, bool GROUPED>
+template <int U, bool GROUPED, bool AHEAD = LPQ_MXD_AHEAD != 0>
 __global__ __launch_bounds__(kThreads) void k_mxfp8_dequant(const lpq_tensor* table, lpq_tensor one, ChunkMap map) {
     const Work W = locate<GROUPED>(table, one, map);
     const lpq_tensor& d = W.d;
@@ -258,27 +331,29 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_dequant(const lpq_tensor* ta
     v4u* dst = reinterpret_cast<v4u*>(d.dst);
     const uint8_t* esc = reinterpret_cast<const uint8_t*>(d.scale);
     const int tid = threadIdx.x;
-
-    const bool full = base + chunk_elems<U>() <= total;
-    v2u c[U];
-    uint32_t b[U];
-    load_chunk<U>(c, src, base, total, full);
+    by_fullness<chunk_elems<U>()>(base, total, [&](auto full) {
+        constexpr bool FULL = decltype(full)::value;
+        v2u c[U];
+        uint32_t b[U];
+        auto fetch = [&](int u) {
+            const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+            c[u] = load_vec<FULL>(src, base, total, u);
+            b[u] = (FULL || e0 < total) ? load_u8(esc + (e0 >> 5)) : 127u;
+        };
+        fetch_start<U, AHEAD>(fetch);
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-        const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
-        b[u] = (full || e0 < total) ? load_u8(esc + (e0 >> 5)) : 127u;
-    }
-#pragma unroll
-    for (int u = 0; u < U; u++) {
-        const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
-        const float X = ue8m0_operand(b[u]);
-        v4u o;
-        o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[u].x, X, false));
-        o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[u].x, X, true));
-        o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[u].y, X, false));
-        o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[u].y, X, true));
-        if (full || e0 < total) store<kNTS>(dst + (e0 >> 3), o);
-    }
+        for (int u = 0; u < U; u++) {
+            fetch_step<U, AHEAD>(u, fetch, c[u].x, b[u]);
+            const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+            const float X = ue8m0_operand(b[u]);
+            v4u o;
+            o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[u].x, X, false));
+            o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[u].x, X, true));
+            o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[u].y, X, false));
+            o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[u].y, X, true));
+            if (FULL || e0 < total) store<kNTS>(dst + (e0 >> 3), o);
+        }
+    });
 }
 
 // ---------------------------------------------------------------------------
@@ -408,22 +483,24 @@ __global__ __launch_bounds__(kThreads) void k_minmax(lpq_tensor one, uint32_t* s
     const int64_t total = one.rows * one.cols;
     const int64_t base = (int64_t)blockIdx.x * chunk_elems<U>();
     const v4u* src = reinterpret_cast<const v4u*>(one.src);
-    const bool full = base + chunk_elems<U>() <= total;
-    v4u v[U];
-    load_chunk<U>(v, src, base, total, full);
     uint32_t lo = kKeyMinIdentity, hi = kKeyMaxIdentity;
+    by_fullness<chunk_elems<U>()>(base, total, [&](auto full) {
+        constexpr bool FULL = decltype(full)::value;
+        v4u v[U];
+        load_chunk<U, FULL>(v, src, base, total);
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-        const int64_t e0 = base + (int64_t)(u * kThreads + threadIdx.x) * 8;
-        if (!full && e0 >= total) continue;   // past the end (N % 8 == 0: vectors are whole)
-        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        for (int u = 0; u < U; u++) {
+            const int64_t e0 = base + (int64_t)(u * kThreads + threadIdx.x) * 8;
+            if (!FULL && e0 >= total) continue;   // past the end (N % 8 == 0: vectors are whole)
+            const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
-        for (int k = 0; k < 4; k++) {
-            const uint32_t a = order_key(w[k] << 16), b = order_key(w[k] & 0xffff0000u);
-            lo = umin(lo, umin(a, b));
-            hi = umax(hi, umax(a, b));
+            for (int k = 0; k < 4; k++) {
+                const uint32_t a = order_key(w[k] << 16), b = order_key(w[k] & 0xffff0000u);
+                lo = umin(lo, umin(a, b));
+                hi = umax(hi, umax(a, b));
+            }
         }
-    }
+    });
     lo = ~wave_max(~lo);   // min through the max reduction on complements
     hi = wave_max(hi);
     __shared__ uint32_t plo[kThreads / 64], phi[kThreads / 64];
@@ -499,13 +576,13 @@ __global__ __launch_bounds__(kThreads) void k_amax(const lpq_tensor* table, lpq_
     const int64_t base = W.unit * chunk_elems<U>();
     const v4u* src = reinterpret_cast<const v4u*>(d.src);
     const int tid = threadIdx.x;
-    // every chunk but the last of a tensor is full: no per-lane bounds checks
-    const bool full = base + chunk_elems<U>() <= total;
-    v4u v[U];
-    load_chunk<U>(v, src, base, total, full);
     uint32_t m = 0;
+    by_fullness<chunk_elems<U>()>(base, total, [&](auto full) {
+        v4u v[U];   // vectors past the end read as zero
+        load_chunk<U, decltype(full)::value>(v, src, base, total);
 #pragma unroll
-    for (int u = 0; u < U; u++) m = umax(m, absmax8_bits(v[u]));
+        for (int u = 0; u < U; u++) m = umax(m, absmax8_bits(v[u]));
+    });
     m = wave_max(m);
     __shared__ uint32_t part[kThreads / 64];
     if ((tid & 63) == 0) part[tid >> 6] = m;
@@ -516,7 +593,7 @@ __global__ __launch_bounds__(kThreads) void k_amax(const lpq_tensor* table, lpq_
     }
 }
 
-template <int U, bool GROUPED>
+template <int U, bool GROUPED, bool AHEAD = LPQ_NVQ_AHEAD != 0>
 __global__ __launch_bounds__(kThreads) void k_nvfp4_quant(const lpq_tensor* table, lpq_tensor one, ChunkMap map,
                                                           const float* group_amax, float* group_g) {
     const Work W = locate<GROUPED>(table, one, map);
@@ -531,24 +608,27 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_quant(const lpq_tensor* tabl
     uint32_t* dst = reinterpret_cast<uint32_t*>(d.dst);
     uint8_t* ssc = reinterpret_cast<uint8_t*>(d.scale);
 
-    // every chunk but the last of a tensor is full: no per-lane bounds checks
-    const bool full = base + chunk_elems<U>() <= total;
-    v4u v[U];
-    load_chunk<U>(v, src, base, total, full);
+    by_fullness<chunk_elems<U>()>(base, total, [&](auto full) {
+        constexpr bool FULL = decltype(full)::value;
+        v4u v[U];
+        auto fetch = [&](int u) { v[u] = load_vec<FULL>(src, base, total, u); };
+        fetch_start<U, AHEAD>(fetch);
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-        const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
-        const F8 f = widen8(v[u]);
-        const BlockScale B = block_scale(pair_max(absmax8_f32(f)), G);
-        const uint32_t p = e2m1x8(f, B);
-        if (full || e0 < total) {
-            store<kNTS>(dst + (e0 >> 3), p);
-            if ((tid & 1) == 0) store_u8(ssc + (e0 >> 4), B.code);
+        for (int u = 0; u < U; u++) {
+            fetch_step<U, AHEAD>(u, fetch, v[u].x);
+            const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+            const F8 f = widen8(v[u]);
+            const BlockScale B = block_scale(pair_max(absmax8_f32(f)), G);
+            const uint32_t p = e2m1x8(f, B);
+            if (FULL || e0 < total) {
+                store<kNTS>(dst + (e0 >> 3), p);
+                if ((tid & 1) == 0) store_u8(ssc + (e0 >> 4), B.code);
+            }
         }
-    }
+    });
 }
 
-template <int U, bool GROUPED>
+template <int U, bool GROUPED, bool AHEAD = LPQ_NVD_AHEAD != 0>
 __global__ __launch_bounds__(kThreads) void k_nvfp4_dequant(const lpq_tensor* table, lpq_tensor one, ChunkMap map,
                                                             const float* group_g) {
     const Work W = locate<GROUPED>(table, one, map);
@@ -561,24 +641,27 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_dequant(const lpq_tensor* ta
     v4u* dst = reinterpret_cast<v4u*>(d.dst);
     const int tid = threadIdx.x;
 
-    const bool full = base + chunk_elems<U>() <= total;
-    uint32_t p[U], sb[U];
-    load_chunk<U>(p, src, base, total, full);
+    by_fullness<chunk_elems<U>()>(base, total, [&](auto full) {
+        constexpr bool FULL = decltype(full)::value;
+        uint32_t p[U], sb[U];
+        auto fetch = [&](int u) {
+            const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+            p[u] = load_vec<FULL>(src, base, total, u);
+            sb[u] = (FULL || e0 < total) ? load_u8(ssc + (e0 >> 4)) : 0u;
+        };
+        fetch_start<U, AHEAD>(fetch);
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-        const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
-        sb[u] = (full || e0 < total) ? load_u8(ssc + (e0 >> 4)) : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < U; u++) {
-        const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
-        const float S = e4m3_to_f32(sb[u]) * g;
-        const v4u o = e2m1x8_to_bf16(p[u], S);
-        if (full || e0 < total) store<kNTS>(dst + (e0 >> 3), o);
-    }
+        for (int u = 0; u < U; u++) {
+            fetch_step<U, AHEAD>(u, fetch, p[u], sb[u]);
+            const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+            const float S = e4m3_to_f32(sb[u]) * g;
+            const v4u o = e2m1x8_to_bf16(p[u], S);
+            if (FULL || e0 < total) store<kNTS>(dst + (e0 >> 3), o);
+        }
+    });
 }
 
-template <int U, bool GROUPED>
+template <int U, bool GROUPED, bool AHEAD = LPQ_QDQ_AHEAD != 0>
 __global__ __launch_bounds__(kThreads) void k_nvfp4_qdq(const lpq_tensor* table, lpq_tensor one, ChunkMap map,
                                                         const float* group_amax) {
     const Work W = locate<GROUPED>(table, one, map);
@@ -590,18 +673,21 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_qdq(const lpq_tensor* table,
     v4u* dst = reinterpret_cast<v4u*>(d.dst);
     const int tid = threadIdx.x;
 
-    // every chunk but the last of a tensor is full: no per-lane bounds checks
-    const bool full = base + chunk_elems<U>() <= total;
-    v4u v[U];
-    load_chunk<U>(v, src, base, total, full);
+    by_fullness<chunk_elems<U>()>(base, total, [&](auto full) {
+        constexpr bool FULL = decltype(full)::value;
+        v4u v[U];
+        auto fetch = [&](int u) { v[u] = load_vec<FULL>(src, base, total, u); };
+        fetch_start<U, AHEAD>(fetch);
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-        const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
-        const F8 f = widen8(v[u]);
-        const BlockScale B = block_scale(pair_max(absmax8_f32(f)), G);
-        const v4u o = e2m1x8_to_bf16(e2m1x8(f, B), B.S);
-        if (full || e0 < total) store<kNTS>(dst + (e0 >> 3), o);
-    }
+        for (int u = 0; u < U; u++) {
+            fetch_step<U, AHEAD>(u, fetch, v[u].x);
+            const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+            const F8 f = widen8(v[u]);
+            const BlockScale B = block_scale(pair_max(absmax8_f32(f)), G);
+            const v4u o = e2m1x8_to_bf16(e2m1x8(f, B), B.S);
+            if (FULL || e0 < total) store<kNTS>(dst + (e0 >> 3), o);
+        }
+    });
 }
 
 // ---------------------------------------------------------------------------
@@ -1055,22 +1141,23 @@ __global__ __launch_bounds__(kThreads) void k_requant_nvfp4(const lpq_requant_te
 // arithmetic as k_fp8blk_dequant: y = BF16(fl(code * s_tile)).
 // A lane takes 8 codes (8 bytes) per step so that its 16 output bytes make
 // each store instruction one contiguous span across the wave.
-template <int U, bool FULL>
+template <int U, bool FULL, bool AHEAD>
 __device__ __forceinline__ void fp8blk_dequant_flat_body(const lpq_tensor& d, int64_t base, int64_t total) {
     const v2u* src = reinterpret_cast<const v2u*>(d.src) + base / 8 + threadIdx.x;
     v4u* dst = reinterpret_cast<v4u*>(d.dst);
     TileCursor<8> cur(reinterpret_cast<const float*>(d.scale), d.cols, base);
     v2u c[U];
     float s[U];
-#pragma unroll
-    for (int u = 0; u < U; u++) {
+    auto fetch = [&](int u) {   // called for u = 0, 1, ... in order: the cursor walks along
         const bool in = FULL || base + (int64_t)(u * kThreads + threadIdx.x) * 8 < total;
         c[u] = in ? load<kNTL>(src + u * kThreads) : v2u{0u, 0u};
         s[u] = in ? load<false>(cur.ptr()) : 0.0f;
         cur.next();
-    }
+    };
+    fetch_start<U, AHEAD>(fetch);
 #pragma unroll
     for (int u = 0; u < U; u++) {
+        fetch_step<U, AHEAD>(u, fetch, c[u].x, __float_as_uint(s[u]));
         const int64_t e0 = base + (int64_t)(u * kThreads + threadIdx.x) * 8;
         const float2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[u].x, false);
         const float2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[u].x, true);
@@ -1092,8 +1179,9 @@ __global__ __launch_bounds__(kThreads) void k_fp8blk_dequant_flat(const lpq_tens
     const Work W = locate<GROUPED>(table, one, map);
     const int64_t total = W.d.rows * W.d.cols;
     const int64_t base = W.unit * dqf_chunk_elems<U>();
-    if (base + dqf_chunk_elems<U>() <= total) fp8blk_dequant_flat_body<U, true>(W.d, base, total);
-    else fp8blk_dequant_flat_body<U, false>(W.d, base, total);
+    constexpr bool AHEAD = LPQ_DQF_AHEAD != 0;
+    if (base + dqf_chunk_elems<U>() <= total) fp8blk_dequant_flat_body<U, true, AHEAD>(W.d, base, total);
+    else fp8blk_dequant_flat_body<U, false, AHEAD>(W.d, base, total);
 }
 
 // Block-wise FP8 -> block-wise FP8, TW adjacent 128x128 tiles per workgroup:
