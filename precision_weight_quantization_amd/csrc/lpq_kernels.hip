@@ -73,6 +73,14 @@
 #ifndef LPQ_TILEQ_TW
 #define LPQ_TILEQ_TW 2
 #endif
+// Block-FP8 quantize launches with at least this many 4-tile strips take 4
+// tiles per workgroup instead of LPQ_TILEQ_TW.
+#ifndef LPQ_TILEQ_WIDE_TW
+#define LPQ_TILEQ_WIDE_TW 4
+#endif
+#ifndef LPQ_TILEQ_WIDE_MIN
+#define LPQ_TILEQ_WIDE_MIN 8192
+#endif
 #ifndef LPQ_TILEQ_WAVES_PER_SIMD
 #define LPQ_TILEQ_WAVES_PER_SIMD 4
 #endif
@@ -759,6 +767,29 @@ __device__ __forceinline__ uint32_t strip_reduce_max(uint32_t m, int sub) {
     return r;
 }
 
+// A raw buffer resource over the `bytes` bytes from p (at most 2^32 - 1; the
+// resource's third word is the gfx9 default).  Loads through it take a
+// 32-bit per-lane offset plus a uniform one in a scalar register, so the
+// addresses of a tile's row passes cost one vector register in all.
+// Stores do not go through buffers: a buffer store of more than 8 bytes with
+// a scalar-register offset gets no wait state before a following VALU write
+// of its data registers, and such a store was seen to write a stale first
+// dword.  Stores use global_store with a uniform 64-bit base and the 32-bit
+// lane offset (store_at), which costs no more vector registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* p, int64_t bytes) {
+    const int32_t n = bytes >= 0xffffffffLL ? -1 : (int32_t)(uint32_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, 0x00020000);
+}
+constexpr int kBufNT = 2;   // cache-policy bits of a non-temporal buffer access
+__device__ __forceinline__ v4u buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, kNTL ? kBufNT : 0);
+}
+// Stores x at byte offset lane_off from the uniform address base.
+template <typename T>
+__device__ __forceinline__ void store_at(uint8_t* base, uint32_t lane_off, T x) {
+    store<kNTS>(reinterpret_cast<T*>(base + lane_off), x);
+}
+
 template <int TW, bool GROUPED>
 __global__ __launch_bounds__(256 * TW, LPQ_TILEQ_WAVES_PER_SIMD) void k_fp8blk_quant(const lpq_tensor* table,
                                                                                       lpq_tensor one, ChunkMap map) {
@@ -771,69 +802,99 @@ __global__ __launch_bounds__(256 * TW, LPQ_TILEQ_WAVES_PER_SIMD) void k_fp8blk_q
     const int64_t r0 = tr * kTile, c0 = tcw * kTile * TW;
     const int64_t rows = M - r0 < kTile ? M - r0 : kTile;
     const int64_t cols = N - c0 < kTile * TW ? N - c0 : kTile * TW;   // columns of the strip inside the tensor
-    const bool fast = rows == kTile && cols == kTile * TW && (N & 7) == 0 &&
-                      ((reinterpret_cast<uintptr_t>(d.src) | reinterpret_cast<uintptr_t>(d.dst)) & 15) == 0;
     const uint16_t* w = reinterpret_cast<const uint16_t*>(d.src);
     uint8_t* q = reinterpret_cast<uint8_t*>(d.dst);
     const int tid = threadIdx.x;
     const int lr = tid / S::lanes_per_row;          // row inside a pass
     const int lc = (tid % S::lanes_per_row) * 8;    // first column of the lane's segment in the strip
     const int sub = lc / kTile;                     // the lane's tile within the strip
+    const int64_t origin = r0 * N + c0;             // element offset of the strip in the tensor
 
-    v4u v[S::passes];
-    if (fast) {
-#pragma unroll
-        for (int p = 0; p < S::passes; p++) {
-            const int64_t off = (r0 + S::rows_per_pass * p + lr) * N + c0 + lc;
-            v[p] = load<kNTL>(reinterpret_cast<const v4u*>(w + off));
-        }
-    } else {
-        for (int p = 0; p < S::passes; p++) {
+    // FAST: 16-byte aligned rows (N % 8 == 0, so a lane's 8 columns are all inside
+    // the tensor or all outside) whose buffer offsets (< 2 * 128 * N bytes) fit 32
+    // bits; edge strips included, lanes outside the tensor taking zeros and storing
+    // nothing.  It keeps the strip in registers between the amax and the encode.  The
+    // general body (any other tensor) reads the strip twice, the second time from
+    // cache, one pass at a time, so that its registers stay below the fast body's.
+    auto body = [&](auto fast_tag) {
+        constexpr bool FAST = decltype(fast_tag)::value;
+        const uint32_t lane_off = (uint32_t)lr * (uint32_t)N + (uint32_t)lc;   // elements, < 2^29 when FAST
+        const __amdgpu_buffer_rsrc_t rw = buffer_of(w + origin, (M * N - origin) * 2);
+        const bool in_c = lc < cols;   // the lane's columns are inside the tensor
+        auto in_r = [&](int p) { return S::rows_per_pass * p + lr < rows; };
+        auto gather = [&](int p) {   // general body: pass p of the lane, zero outside the tensor
             const int64_t r = S::rows_per_pass * p + lr;
             uint32_t h[8];
+#pragma unroll
             for (int k = 0; k < 8; k++) {
                 const bool in = r < rows && lc + k < cols;
                 h[k] = in ? w[(r0 + r) * N + c0 + lc + k] : 0u;
             }
-            v[p] = v4u{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-        }
-    }
-    uint32_t m = 0;
+            return v4u{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+        };
+        v4u v[FAST ? S::passes : 1];
+        uint32_t m = 0;
+        if constexpr (FAST) {
+            // lanes outside the columns read the strip's first element of their row
+            // (rows past the end of the tensor read as 0: buffer range check), then zero
+            const uint32_t ld_off = in_c ? lane_off * 2 : 0u;
 #pragma unroll
-    for (int p = 0; p < S::passes; p++) m = umax(m, absmax8_bits(v[p]));
-    const float amax = __uint_as_float(strip_reduce_max<16, TW, S::threads>(m, sub));
-    const float s = amax / kE4M3Max;   // correctly rounded division
-    if (lr == 0 && (lc & (kTile - 1)) == 0 && sub * kTile < cols)
-        reinterpret_cast<float*>(d.scale)[tr * tn + tcw * TW + sub] = s;
-    const bool tiny = s > 0.0f && s < kTinyScale;
-    const float sd = tiny ? s * kPreScale : s;
-    const float r = s > 0.0f ? rcp_rn(sd) : 0.0f;
-    const bool any_tiny = any_lane(tiny);
+            for (int p = 0; p < S::passes; p++)
+                v[p] = buffer_load16(rw, ld_off, (uint32_t)(S::rows_per_pass * p * N * 2));
+#pragma unroll
+            for (int p = 0; p < S::passes; p++) {
+                if (!(in_c && in_r(p))) v[p] = v4u{0u, 0u, 0u, 0u};
+                m = umax(m, absmax8_bits(v[p]));
+            }
+        } else {
+#pragma unroll 1
+            for (int p = 0; p < S::passes; p++) m = umax(m, absmax8_bits(gather(p)));
+        }
+        const float amax = __uint_as_float(strip_reduce_max<16, TW, S::threads>(m, sub));
+        const float s = amax / kE4M3Max;   // correctly rounded division
+        if (lr == 0 && (lc & (kTile - 1)) == 0 && sub * kTile < cols)
+            reinterpret_cast<float*>(d.scale)[tr * tn + tcw * TW + sub] = s;
+        const bool tiny = s > 0.0f && s < kTinyScale;
+        const float sd = tiny ? s * kPreScale : s;
+        const float r = s > 0.0f ? rcp_rn(sd) : 0.0f;
+        const bool any_tiny = any_lane(tiny);
 
+        auto encode = [&](int p, const v4u& x8) {
+            float x[8] = {bf16_lo(x8.x), bf16_hi(x8.x), bf16_lo(x8.y), bf16_hi(x8.y),
+                          bf16_lo(x8.z), bf16_hi(x8.z), bf16_lo(x8.w), bf16_hi(x8.w)};
+            if (any_tiny) {
 #pragma unroll
-    for (int p = 0; p < S::passes; p++) {
-        float x[8] = {bf16_lo(v[p].x), bf16_hi(v[p].x), bf16_lo(v[p].y), bf16_hi(v[p].y),
-                      bf16_lo(v[p].z), bf16_hi(v[p].z), bf16_lo(v[p].w), bf16_hi(v[p].w)};
-        if (any_tiny) {
+                for (int k = 0; k < 8; k++) x[k] *= tiny ? kPreScale : 1.0f;
+            }
+            float qq[8];
 #pragma unroll
-            for (int k = 0; k < 8; k++) x[k] *= tiny ? kPreScale : 1.0f;
+            for (int k = 0; k < 8; k++) qq[k] = quot_rn(x[k], sd, r);
+            uint32_t lo = e4m3x2<false>(qq[0], qq[1], 0u);
+            lo = e4m3x2<true>(qq[2], qq[3], lo);
+            uint32_t hi = e4m3x2<false>(qq[4], qq[5], 0u);
+            hi = e4m3x2<true>(qq[6], qq[7], hi);
+            const int64_t row = S::rows_per_pass * p + lr;
+            if constexpr (FAST) {
+                if (in_c && row < rows) store_at(q + origin + (int64_t)S::rows_per_pass * p * N, lane_off, v2u{lo, hi});
+            } else if (row < rows) {
+                const uint32_t c8[2] = {lo, hi};
+                for (int k = 0; k < 8; k++)
+                    if (lc + k < cols) q[(r0 + row) * N + c0 + lc + k] = (uint8_t)(c8[k >> 2] >> (8 * (k & 3)));
+            }
+        };
+        if constexpr (FAST) {
+#pragma unroll
+            for (int p = 0; p < S::passes; p++) encode(p, v[p]);
+        } else {
+#pragma unroll 1
+            for (int p = 0; p < S::passes; p++) encode(p, gather(p));
         }
-        float qq[8];
-#pragma unroll
-        for (int k = 0; k < 8; k++) qq[k] = quot_rn(x[k], sd, r);
-        uint32_t lo = e4m3x2<false>(qq[0], qq[1], 0u);
-        lo = e4m3x2<true>(qq[2], qq[3], lo);
-        uint32_t hi = e4m3x2<false>(qq[4], qq[5], 0u);
-        hi = e4m3x2<true>(qq[6], qq[7], hi);
-        const int64_t row = S::rows_per_pass * p + lr;
-        if (fast) {
-            store<kNTS>(reinterpret_cast<v2u*>(q + (r0 + row) * N + c0 + lc), v2u{lo, hi});
-        } else if (row < rows) {
-            const uint32_t c8[2] = {lo, hi};
-            for (int k = 0; k < 8; k++)
-                if (lc + k < cols) q[(r0 + row) * N + c0 + lc + k] = (uint8_t)(c8[k >> 2] >> (8 * (k & 3)));
-        }
-    }
+    };
+    if ((N & 7) == 0 && N <= (1 << 22) &&
+        ((reinterpret_cast<uintptr_t>(d.src) | reinterpret_cast<uintptr_t>(d.dst)) & 15) == 0)
+        body(Full<true>{});
+    else
+        body(Full<false>{});
 }
 
 template <int TT, bool GROUPED>
@@ -1209,8 +1270,6 @@ __global__ __launch_bounds__(256 * TW) void k_requant_fp8blk(const lpq_requant_t
     const int64_t r0 = tr * kTile, c0 = tcw * kTile * TW;
     const int64_t rows = M - r0 < kTile ? M - r0 : kTile;
     const int64_t cols = N - c0 < kTile * TW ? N - c0 : kTile * TW;
-    const bool fast = rows == kTile && cols == kTile * TW && (N & 15) == 0 &&
-                      ((reinterpret_cast<uintptr_t>(d.src) | reinterpret_cast<uintptr_t>(d.dst)) & 15) == 0;
     const uint8_t* q = d.src;
     uint8_t* qo = reinterpret_cast<uint8_t*>(d.dst);
     const int tid = threadIdx.x;
@@ -1219,71 +1278,107 @@ __global__ __launch_bounds__(256 * TW) void k_requant_fp8blk(const lpq_requant_t
     const int sub = lc / kTile;                     // the lane's tile within the strip
     const bool present = sub * kTile < cols;
     const float s = present ? d.src_scale[tr * tn + tcw * TW + sub] : 0.0f;
+    const int64_t origin = r0 * N + c0;             // offset of the strip in the tensor
 
-    v4u c[S::passes];
-    if (fast) {
-#pragma unroll
-        for (int p = 0; p < S::passes; p++)
-            c[p] = load<kNTL>(reinterpret_cast<const v4u*>(q + (r0 + S::rows_per_pass * p + lr) * N + c0 + lc));
-    } else {
-        for (int p = 0; p < S::passes; p++) {
+    // FAST: 16-byte aligned rows (N % 16 == 0, so a lane's 16 columns are all inside
+    // the tensor or all outside) whose buffer offsets (< 128 * N) fit 32 bits; edge
+    // strips included, lanes outside the tensor taking code 0 and storing nothing.
+    // It keeps the strip's codes in registers between the amax and the encode.  The
+    // general body (any other tensor) reads each pass twice, the second time from
+    // cache, so that its registers stay below the fast body's.
+    auto body = [&](auto fast_tag) {
+        constexpr bool FAST = decltype(fast_tag)::value;
+        const uint32_t lane_off = (uint32_t)lr * (uint32_t)N + (uint32_t)lc;   // < 2^27 when FAST
+        const __amdgpu_buffer_rsrc_t rs = buffer_of(q + origin, M * N - origin);
+        const bool in_c = lc < cols;   // the lane's columns are inside the tensor
+        auto in_r = [&](int p) { return S::rows_per_pass * p + lr < rows; };
+        auto gather = [&](int p) {   // general body: pass p of the lane, code 0 outside the tensor
             const int64_t r = S::rows_per_pass * p + lr;
             uint32_t w[4] = {0u, 0u, 0u, 0u};
             for (int k = 0; k < 16; k++)
                 if (r < rows && lc + k < cols) w[k >> 2] |= (uint32_t)q[(r0 + r) * N + c0 + lc + k] << (8 * (k & 3));
-            c[p] = v4u{w[0], w[1], w[2], w[3]};
-        }
-    }
-    // tile amax of y: BF16 rounding is monotone, so round fl(max|code| * |s|) once
-    float cm = 0.0f;
+            return v4u{w[0], w[1], w[2], w[3]};
+        };
+        // tile amax of y: BF16 rounding is monotone, so round fl(max|code| * |s|) once
+        auto code_max = [](const v4u& c, float cm) {
+            const uint32_t w[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
-    for (int p = 0; p < S::passes; p++) {
-        const uint32_t w[4] = {c[p].x, c[p].y, c[p].z, c[p].w};
+            for (int k = 0; k < 4; k++) {
+                const float2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
+                const float2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);
+                cm = fmaxf(fmaxf(cm, fabsf(a[0])), fabsf(a[1]));
+                cm = fmaxf(fmaxf(cm, fabsf(b[0])), fabsf(b[1]));
+            }
+            return cm;
+        };
+        v4u c[FAST ? S::passes : 1];
+        float cm = 0.0f;
+        if constexpr (FAST) {
+            // lanes outside the columns read the strip's first code of their row
+            // (rows past the end of the tensor read as 0: buffer range check), then zero
+            const uint32_t ld_off = in_c ? lane_off : 0u;
 #pragma unroll
-        for (int k = 0; k < 4; k++) {
-            const float2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
-            const float2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);
-            cm = fmaxf(fmaxf(cm, fabsf(a[0])), fabsf(a[1]));
-            cm = fmaxf(fmaxf(cm, fabsf(b[0])), fabsf(b[1]));
+            for (int p = 0; p < S::passes; p++) c[p] = buffer_load16(rs, ld_off, (uint32_t)(S::rows_per_pass * p * N));
+#pragma unroll
+            for (int p = 0; p < S::passes; p++) {
+                if (!(in_c && in_r(p))) c[p] = v4u{0u, 0u, 0u, 0u};
+                cm = code_max(c[p], cm);
+            }
+        } else {
+#pragma unroll 1
+            for (int p = 0; p < S::passes; p++) cm = code_max(gather(p), cm);
         }
-    }
-    const uint32_t mb = bf16_in_f32(cm * fabsf(s));   // codes outside the tensor read as 0
-    const float amax = __uint_as_float(strip_reduce_max<8, TW, S::threads>(mb, sub));
-    const float s2 = amax / kE4M3Max;   // correctly rounded division
-    if (lr == 0 && (lc & (kTile - 1)) == 0 && present) reinterpret_cast<float*>(d.dst_scale)[tr * tn + tcw * TW + sub] = s2;
-    const bool tiny = s2 > 0.0f && s2 < kTinyScale;
-    const float sd = tiny ? s2 * kPreScale : s2;
-    const float r = s2 > 0.0f ? rcp_rn(sd) : 0.0f;
-    const bool any_tiny = any_lane(tiny);
+        const uint32_t mb = bf16_in_f32(cm * fabsf(s));   // codes outside the tensor read as 0
+        const float amax = __uint_as_float(strip_reduce_max<8, TW, S::threads>(mb, sub));
+        const float s2 = amax / kE4M3Max;   // correctly rounded division
+        if (lr == 0 && (lc & (kTile - 1)) == 0 && present)
+            reinterpret_cast<float*>(d.dst_scale)[tr * tn + tcw * TW + sub] = s2;
+        const bool tiny = s2 > 0.0f && s2 < kTinyScale;
+        const float sd = tiny ? s2 * kPreScale : s2;
+        const float r = s2 > 0.0f ? rcp_rn(sd) : 0.0f;
+        const bool any_tiny = any_lane(tiny);
 
+        auto encode = [&](int p, const v4u& cp) {
+            const Y16 y = fp8blk_values16(cp, s);
+            float x[16];
 #pragma unroll
-    for (int p = 0; p < S::passes; p++) {
-        const Y16 y = fp8blk_values16(c[p], s);
-        float x[16];
+            for (int k = 0; k < 8; k++) {
+                x[k] = y.lo.x[k];
+                x[8 + k] = y.hi.x[k];
+            }
+            if (any_tiny) {
 #pragma unroll
-        for (int k = 0; k < 8; k++) {
-            x[k] = y.lo.x[k];
-            x[8 + k] = y.hi.x[k];
-        }
-        if (any_tiny) {
+                for (int k = 0; k < 16; k++) x[k] *= tiny ? kPreScale : 1.0f;
+            }
+            uint32_t o[4];
 #pragma unroll
-            for (int k = 0; k < 16; k++) x[k] *= tiny ? kPreScale : 1.0f;
-        }
-        uint32_t o[4];
+            for (int k = 0; k < 4; k++) {
+                const float q0 = quot_rn(x[4 * k + 0], sd, r), q1 = quot_rn(x[4 * k + 1], sd, r);
+                const float q2 = quot_rn(x[4 * k + 2], sd, r), q3 = quot_rn(x[4 * k + 3], sd, r);
+                o[k] = e4m3x2<true>(q2, q3, e4m3x2<false>(q0, q1, 0u));
+            }
+            const int64_t row = S::rows_per_pass * p + lr;
+            if constexpr (FAST) {
+                if (in_c && row < rows)
+                    store_at(qo + origin + (int64_t)S::rows_per_pass * p * N, lane_off, v4u{o[0], o[1], o[2], o[3]});
+            } else if (row < rows) {
+                for (int k = 0; k < 16; k++)
+                    if (lc + k < cols) qo[(r0 + row) * N + c0 + lc + k] = (uint8_t)(o[k >> 2] >> (8 * (k & 3)));
+            }
+        };
+        if constexpr (FAST) {
 #pragma unroll
-        for (int k = 0; k < 4; k++) {
-            const float q0 = quot_rn(x[4 * k + 0], sd, r), q1 = quot_rn(x[4 * k + 1], sd, r);
-            const float q2 = quot_rn(x[4 * k + 2], sd, r), q3 = quot_rn(x[4 * k + 3], sd, r);
-            o[k] = e4m3x2<true>(q2, q3, e4m3x2<false>(q0, q1, 0u));
+            for (int p = 0; p < S::passes; p++) encode(p, c[p]);
+        } else {
+#pragma unroll 1
+            for (int p = 0; p < S::passes; p++) encode(p, gather(p));
         }
-        const int64_t row = S::rows_per_pass * p + lr;
-        if (fast) {
-            store<kNTS>(reinterpret_cast<v4u*>(qo + (r0 + row) * N + c0 + lc), v4u{o[0], o[1], o[2], o[3]});
-        } else if (row < rows) {
-            for (int k = 0; k < 16; k++)
-                if (lc + k < cols) qo[(r0 + row) * N + c0 + lc + k] = (uint8_t)(o[k >> 2] >> (8 * (k & 3)));
-        }
-    }
+    };
+    if ((N & 15) == 0 && N <= (1 << 23) &&
+        ((reinterpret_cast<uintptr_t>(d.src) | reinterpret_cast<uintptr_t>(d.dst)) & 15) == 0)
+        body(Full<true>{});
+    else
+        body(Full<false>{});
 }
 
 }  // namespace
@@ -1307,7 +1402,7 @@ inline lpq_status launched() {
     return LPQ_OK;
 }
 
-enum Kind { FP8BLK_Q, FP8BLK_DQ, FP8BLK_DQF, MXFP8_Q, MXFP8_QF, MXFP8_DQ, NV_AMAX, NV_Q, NV_DQ, NV_QDQ, RQ_FP8, RQ_MX, RQ_AMAX, RQ_NV };
+enum Kind { FP8BLK_Q, FP8BLK_QW, FP8BLK_DQ, FP8BLK_DQF, MXFP8_Q, MXFP8_QF, MXFP8_DQ, NV_AMAX, NV_Q, NV_DQ, NV_QDQ, RQ_FP8, RQ_MX, RQ_AMAX, RQ_NV };
 
 // Shape and pointer checks of one tensor for one kind of call.
 lpq_status check_tensor(Kind k, const lpq_tensor& t, int32_t n_groups) {
@@ -1319,8 +1414,9 @@ lpq_status check_tensor(Kind k, const lpq_tensor& t, int32_t n_groups) {
     if (t.reserved != 0) return LPQ_ERR_ARG;
     switch (k) {
     case FP8BLK_Q:
+    case FP8BLK_QW:   // not a caller-visible kind: the wide-strip quantizer
     case FP8BLK_DQ:
-        if (!aligned(k == FP8BLK_Q ? t.src : t.dst, 2) || !aligned(t.scale, 4)) return LPQ_ERR_ALIGN;
+        if (!aligned(k == FP8BLK_DQ ? t.dst : t.src, 2) || !aligned(t.scale, 4)) return LPQ_ERR_ALIGN;
         break;
     case FP8BLK_DQF:   // not a caller-visible kind: the flat layout's extra conditions
         if (t.cols % 8 || t.rows >= (int64_t(1) << 31) || t.cols >= (int64_t(1) << 31) - kRqStep) return LPQ_ERR_SHAPE;
@@ -1371,6 +1467,8 @@ int64_t units(Kind k, const lpq_tensor& t) {
     const int64_t n = t.rows * t.cols;
     switch (k) {
     case FP8BLK_Q: return ((t.rows + kTile - 1) / kTile) * ((t.cols + kTile * LPQ_TILEQ_TW - 1) / (kTile * LPQ_TILEQ_TW));
+    case FP8BLK_QW:
+        return ((t.rows + kTile - 1) / kTile) * ((t.cols + kTile * LPQ_TILEQ_WIDE_TW - 1) / (kTile * LPQ_TILEQ_WIDE_TW));
     case FP8BLK_DQ: return ((t.rows + kTile - 1) / kTile) * ((t.cols + kTile - 1) / kTile);
     case FP8BLK_DQF: return (n + dqf_chunk_elems<LPQ_DQF_U>() - 1) / dqf_chunk_elems<LPQ_DQF_U>();
     case MXFP8_Q:
@@ -1399,10 +1497,13 @@ constexpr int64_t kMaxGridX = 0x7fffffffLL;
 
 void dispatch(Kind k, dim3 grid, hipStream_t stream, const lpq_tensor* tab, const lpq_tensor& one, const ChunkMap& map,
               const float* fa, float* fb) {
-    const dim3 flat(kThreads), tileq(256 * LPQ_TILEQ_TW), tiled(LPQ_TILED_THREADS);
+    const dim3 flat(kThreads), tileq(256 * LPQ_TILEQ_TW), tileqw(256 * LPQ_TILEQ_WIDE_TW), tiled(LPQ_TILED_THREADS);
     if (tab) {
         switch (k) {
         case FP8BLK_Q: hipLaunchKernelGGL((k_fp8blk_quant<LPQ_TILEQ_TW, true>), grid, tileq, 0, stream, tab, one, map); break;
+        case FP8BLK_QW:
+            hipLaunchKernelGGL((k_fp8blk_quant<LPQ_TILEQ_WIDE_TW, true>), grid, tileqw, 0, stream, tab, one, map);
+            break;
         case FP8BLK_DQ: hipLaunchKernelGGL((k_fp8blk_dequant<LPQ_TILED_THREADS, true>), grid, tiled, 0, stream, tab, one, map); break;
         case FP8BLK_DQF: hipLaunchKernelGGL((k_fp8blk_dequant_flat<LPQ_DQF_U, true>), grid, flat, 0, stream, tab, one, map); break;
         case MXFP8_Q: hipLaunchKernelGGL((k_mxfp8_quant<LPQ_MXQ_U, true>), grid, flat, 0, stream, tab, one, map); break;
@@ -1417,6 +1518,9 @@ void dispatch(Kind k, dim3 grid, hipStream_t stream, const lpq_tensor* tab, cons
     } else {
         switch (k) {
         case FP8BLK_Q: hipLaunchKernelGGL((k_fp8blk_quant<LPQ_TILEQ_TW, false>), grid, tileq, 0, stream, tab, one, map); break;
+        case FP8BLK_QW:
+            hipLaunchKernelGGL((k_fp8blk_quant<LPQ_TILEQ_WIDE_TW, false>), grid, tileqw, 0, stream, tab, one, map);
+            break;
         case FP8BLK_DQ: hipLaunchKernelGGL((k_fp8blk_dequant<LPQ_TILED_THREADS, false>), grid, tiled, 0, stream, tab, one, map); break;
         case FP8BLK_DQF: hipLaunchKernelGGL((k_fp8blk_dequant_flat<LPQ_DQF_U, false>), grid, flat, 0, stream, tab, one, map); break;
         case MXFP8_Q: hipLaunchKernelGGL((k_mxfp8_quant<LPQ_MXQ_U, false>), grid, flat, 0, stream, tab, one, map); break;
@@ -1453,6 +1557,47 @@ void dispatch(Kind k, dim3 grid, hipStream_t stream, const lpq_requant_tensor* t
     }
 }
 
+// Where the launch over tensors [i0, count) stops: the first tensor that would
+// exceed kMaxSeg segments (runs of equal work-unit counts) or 2^31-1 work units.
+// Fills map and total; returns -1 when one tensor alone is too large.
+template <typename D>
+int32_t slice_end(Kind k, const D* host, int32_t count, int32_t i0, const D& one, ChunkMap& map, int64_t& total) {
+    map = ChunkMap{};
+    total = 0;
+    int32_t nseg = 0, i = i0;
+    while (i < count) {
+        const int64_t u = units(k, host ? host[i] : one);
+        if (u > kMaxGridX) return -1;
+        if (total + u > kMaxGridX) break;
+        if (nseg == 0 || (int64_t)map.units[nseg - 1] != u) {
+            if (nseg == kMaxSeg) break;
+            map.first[nseg] = (uint32_t)total;
+            map.tensor0[nseg] = (uint32_t)(i - i0);
+            map.units[nseg] = (uint32_t)u;
+            map.inv_units[nseg] = 1.0 / (double)u;
+            nseg++;
+        }
+        total += u;
+        i++;
+    }
+    map.nseg = nseg;
+    return i;
+}
+
+// Number of launches a call of kind k over host[0, n) takes (-1: a tensor is too large).
+template <typename D>
+int64_t launch_count(Kind k, const D* host, int32_t n) {
+    int64_t launches = 0;
+    ChunkMap map;
+    int64_t total;
+    for (int32_t i0 = 0; i0 < n; launches++) {
+        const int32_t i = slice_end(k, host, n, i0, D{}, map, total);
+        if (i < 0) return -1;
+        i0 = i;
+    }
+    return launches;
+}
+
 // Launch kernel `k` over tensors [0, n) of `host`/`dev` (single tensor: dev ==
 // nullptr, `one` used), in slices of at most kMaxSeg segments and 2^31-1 work
 // units.
@@ -1462,25 +1607,10 @@ lpq_status launch(Kind k, const D* host, const D* dev, int32_t n, const D& one, 
     const int32_t count = dev ? n : 1;
     int32_t i0 = 0;
     while (i0 < count) {
-        ChunkMap map = {};
-        int64_t total = 0;
-        int32_t nseg = 0, i = i0;
-        while (i < count) {
-            const int64_t u = units(k, dev ? host[i] : one);
-            if (u > kMaxGridX) return LPQ_ERR_SHAPE;
-            if (total + u > kMaxGridX) break;
-            if (nseg == 0 || (int64_t)map.units[nseg - 1] != u) {
-                if (nseg == kMaxSeg) break;
-                map.first[nseg] = (uint32_t)total;
-                map.tensor0[nseg] = (uint32_t)(i - i0);
-                map.units[nseg] = (uint32_t)u;
-                map.inv_units[nseg] = 1.0 / (double)u;
-                nseg++;
-            }
-            total += u;
-            i++;
-        }
-        map.nseg = nseg;
+        ChunkMap map;
+        int64_t total;
+        const int32_t i = slice_end(k, dev ? host : nullptr, count, i0, one, map, total);
+        if (i < 0) return LPQ_ERR_SHAPE;
         map.gdiv = gdiv;
         dispatch(k, dim3((unsigned)total), stream, dev ? dev + i0 : nullptr, one, map, fa, fb);
         lpq_status st = launched();
@@ -1520,6 +1650,27 @@ lpq_status grouped(Kind k, const D* host, const D* dev, int32_t n, int32_t n_gro
         if (st != LPQ_OK) return st;
     }
     return launch<D>(k, host, dev, n, D{}, fa, fb, (hipStream_t)stream, gdiv);
+}
+
+// Strip width of a block-FP8 quantize call: 4 tiles per workgroup when the
+// call has at least LPQ_TILEQ_WIDE_MIN 4-tile strips and takes no more
+// launches that way, else LPQ_TILEQ_TW.  Measured: wide strips run faster on
+// large launches (longer contiguous row runs) and slower on short ones, where
+// fewer, longer workgroups leave more of the chip idle at the end.  The launch
+// count matters when the table alternates shapes: Qwen3-30B-A3B experts
+// (768x2048, 2048x768) have equal 2-tile strip counts, one run of equal work
+// units, but unequal 4-tile counts, a new run at every tensor.  Any tensor that
+// fails the checks keeps the narrow kind (the call is refused later).
+Kind fp8blk_quant_kind(const lpq_tensor* t, int32_t n) {
+    if (!t || n <= 0) return FP8BLK_Q;
+    int64_t strips = 0;
+    for (int32_t i = 0; i < n; i++) {
+        if (check_tensor(FP8BLK_QW, t[i], 0) != LPQ_OK) return FP8BLK_Q;
+        strips += units(FP8BLK_QW, t[i]);
+    }
+    if (strips < LPQ_TILEQ_WIDE_MIN) return FP8BLK_Q;
+    const int64_t wide = launch_count(FP8BLK_QW, t, n), narrow = launch_count(FP8BLK_Q, t, n);
+    return wide > 0 && wide <= narrow ? FP8BLK_QW : FP8BLK_Q;
 }
 
 // 6 * the E4M3 maximum of an NVFP4 call, or 0 for an unsupported maximum.
@@ -1566,7 +1717,8 @@ int lpq_last_hip_error(void) { return g_last_hip_error; }
 int lpq_version(void) { return 10000; }
 
 lpq_status lpq_quantize_fp8blk(const uint16_t* w, int64_t M, int64_t N, uint8_t* q, float* s, void* stream) {
-    return single(FP8BLK_Q, make_one(w, q, s, M, N), nullptr, nullptr, stream);
+    const lpq_tensor one = make_one(w, q, s, M, N);
+    return single(fp8blk_quant_kind(&one, 1), one, nullptr, nullptr, stream);
 }
 
 lpq_status lpq_dequantize_fp8blk(const uint8_t* q, const float* s, int64_t M, int64_t N, uint16_t* y, void* stream) {
@@ -1700,7 +1852,7 @@ lpq_status lpq_nvfp4_qdq_grouped_ex(const lpq_tensor* host, const lpq_tensor* de
 }
 
 lpq_status lpq_quantize_fp8blk_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, void* stream) {
-    return grouped(FP8BLK_Q, host, dev, n, 0, nullptr, nullptr, stream);
+    return grouped(fp8blk_quant_kind(host, n), host, dev, n, 0, nullptr, nullptr, stream);
 }
 
 lpq_status lpq_dequantize_fp8blk_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, void* stream) {

@@ -301,6 +301,39 @@ def test_bruteforce_fp8blk_grouped(lpq):
     assert bad == 0
 
 
+def test_fp8blk_wide_strips(lpq):
+    """Calls with at least 8192 strips of 4 tiles (the library's threshold) take the
+    4-tile-per-workgroup quantizer.  Tiles are independent, so bands of whole tiles
+    (edge bands included) are checked against the oracle run on the same band."""
+    from synth import gpu as sgpu
+    bad = 0
+    # one ragged tensor: 257 tile rows x 33 strips = 8481 strips
+    M, N = 32768 + 37, 16384 + 40
+    w = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    sgpu.fill(w, 92, 1, synth.DIST_MOE)
+    q, s = lpq.lpq_quantize_fp8blk(w)
+    for r0, r1, c0, c1 in [(0, 128, 0, N), (12800, 13056, 0, N), (32768, M, 0, N), (0, M, 16384, N)]:
+        oq, os_ = O.fp8blk_quantize(host_u16(w[r0:r1, c0:c1]))
+        bad += report(f"wide single codes rows {r0}:{r1} cols {c0}:{c1}", host_u8(q[r0:r1, c0:c1]), oq)
+        bad += report("  scales", s[r0 // 128:(r1 + 127) // 128, c0 // 128:(c1 + 127) // 128].cpu().numpy().view(np.uint32),
+                      os_.view(np.uint32))
+    del w, q, s
+    # grouped: 4 ragged shapes, 274 outputs each from one source per shape (8220 strips)
+    shapes = [(300, 1000), (256, 1536), (129, 2056), (512, 520)]
+    copies = 274
+    srcs = [to_dev_bf16(synth.generate(93, i, M, N, *synth.DIST_MOE)) for i, (M, N) in enumerate(shapes)]
+    qs = [torch.empty((copies, M, N), dtype=torch.uint8, device="cuda") for M, N in shapes]
+    ss = [torch.empty((copies, (M + 127) // 128, (N + 127) // 128), dtype=torch.float32, device="cuda") for M, N in shapes]
+    lpq.lpq_quantize_fp8blk_grouped(lpq.TensorTable(
+        [(srcs[k], qs[k][j], ss[k][j], M, N, 0) for k, (M, N) in enumerate(shapes) for j in range(copies)]))
+    for k, (M, N) in enumerate(shapes):
+        oq, os_ = O.fp8blk_quantize(host_u16(srcs[k]))
+        bad += report(f"wide grouped codes {M}x{N} (x{copies})", host_u8(qs[k]), np.broadcast_to(oq, (copies, M, N)))
+        bad += report("  scales", ss[k].cpu().numpy().view(np.uint32),
+                      np.broadcast_to(os_.view(np.uint32), (copies,) + os_.shape))
+    assert bad == 0
+
+
 # --------------------------------------------------------------------------- grouped calls
 
 def test_grouped_mixed_shapes_and_siblings(lpq):
