@@ -24,6 +24,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -38,12 +39,23 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+KERNEL_SOURCES = ("precision_weight_quantization_amd/csrc/lpq_kernels.hip",
+                  "precision_weight_quantization_amd/csrc/lpq_device.hpp")
+
+
+def code_text(src: str) -> str:
+    """C++ source without its comments and blank lines, spaces at line ends removed:
+    what the compiler sees, so that a comment-only edit keeps recorded counters valid."""
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return "\n".join(line.rstrip() for line in src.splitlines() if line.strip())
+
+
+def kernel_source_hash(root: str = ROOT) -> str:
     h = hashlib.sha256()
-    for rel in ("precision_weight_quantization_amd/csrc/lpq_kernels.hip",
-                "precision_weight_quantization_amd/csrc/lpq_device.hpp"):
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(root, rel)) as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

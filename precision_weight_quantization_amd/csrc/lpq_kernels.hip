@@ -24,10 +24,12 @@
 //    work, chosen per kernel by measurement: the encoders and the MXFP8
 //    decoder run faster with fewer reads in flight per wave.  Full chunks
 //    (all but a tensor's last) take a body compiled without bounds checks.
-//  * Block-wise FP8 gives one workgroup a 128x128 tile: 16 lanes per 256-byte
-//    row segment, 2048/threads row passes, all values kept in registers
-//    between the tile-amax reduction (DPP + LDS across the waves) and the
-//    encode, so HBM is read once.
+//  * Block-wise FP8 quantization gives one workgroup a strip of 2 or 4
+//    adjacent 128x128 tiles (one per 256 threads): 16 lanes per 256-byte row
+//    segment of a tile, 8 row passes, all values kept in registers between the
+//    per-tile amax reduction (DPP + LDS across the waves) and the encode, so
+//    HBM is read once.  Dequantization streams flat when the layout allows,
+//    else one tile per workgroup.
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
 #include <stdint.h>
@@ -734,8 +736,9 @@ __device__ __forceinline__ TileGeom tile_geom(const lpq_tensor& d, int64_t tile)
 // rows x 128*TW columns, 256*TW threads): each pass reads one 256*TW-byte run
 // per row instead of 256 bytes, which the memory system serves better (an
 // access-pattern probe with no arithmetic: 70-72% of HBM peak for one tile,
-// 75-79% for two).  Lane t covers columns 8*(t % (16 TW)) .. +8 of rows
-// 16*pass + t / (16 TW); its tile within the strip is (t % (16 TW)) / 16.
+// 75-79% for two).  TW is 2, or 4 for calls with many strips (the host's
+// choice, fp8blk_quant_kind).  Lane t covers columns 8*(t % (16 TW)) .. +8 of
+// rows 16*pass + t / (16 TW); its tile within the strip is (t % (16 TW)) / 16.
 template <int TW>
 struct WideShape {
     static constexpr int threads = 256 * TW;
