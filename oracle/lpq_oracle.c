@@ -1,6 +1,7 @@
 /*
  * lpq_oracle.c -- plain, slow CPU oracle for the BF16 -> low-precision weight
- * codecs (block-wise FP8, MXFP8, NVFP4) and the NVFP4 fake-quant (QDQ).
+ * codecs (block-wise FP8, MXFP8, NVFP4, group-wise INT4) and their fake-quant
+ * (QDQ).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
  * calls this file; only the test suite, the smoke check and the benchmark's
@@ -402,6 +403,90 @@ OC_API float oc_observer_update(int kind, float c, float* state, const uint16_t*
     state[2] = state[2] + 1.0f;
     float lo = fabsf(state[0]), hi = fabsf(state[1]);
     return lo > hi ? lo : hi;
+}
+
+/* ------------------------------------------------------------------------ */
+/* INT4, symmetric, one FP32 scale per group of G elements along a row        */
+/* ("低精度训练与 Rollout", "INT4 QAT 训练")                                  */
+/* ------------------------------------------------------------------------ */
+/* The page fixes only the group size (OPEN_TRAINING_INT4_GROUP_SIZE: 128 for
+ * Moonlight-16B-A3B, Qwen3-30B-A3B and Qwen3-235B-A22B, 32 for
+ * Kimi-K2-Thinking) and that QAT trains through a straight-through
+ * estimator, whose forward pass is quantize then dequantize.  Readings (the
+ * plainest ones, each listed in the design doc):
+ *  - groups run along a row (the GEMM reduction dimension), as the other
+ *    block formats' blocks do; N % G == 0;
+ *  - symmetric: s = fl(amax / 7), so the group's largest magnitude maps to
+ *    the largest positive code, 7;
+ *  - q = the integer nearest to fl(x / s), ties to even, clamped to [-8, 7]
+ *    (a finite input never reaches the clamp); a zero scale gives code 0;
+ *  - stored as two's-complement nibbles, element 2j in the low nibble of
+ *    byte j; s is FP32 [M, N / G];
+ *  - y = BF16(fl(q * s)).  An integer code has no sign of zero: -0 and
+ *    negative values that round to 0 come back as +0. */
+
+OC_API float oc_int4_scale(float amax) { return amax / 7.0f; }   /* fl(amax / 7) */
+
+static int oc_int4_code(float x, float s) {
+    if (s == 0.0f) return 0;
+    float t = nearbyintf(x / s);   /* fl(x / s), then the nearest integer, ties to even */
+    if (t > 7.0f) t = 7.0f;
+    if (t < -8.0f) t = -8.0f;
+    return (int)t;
+}
+
+static int oc_int4_decode(uint8_t nibble) { return (nibble & 8) ? (int)nibble - 16 : (int)nibble; }
+
+static float oc_int4_group_amax(const uint16_t* grp, int64_t G) {
+    float amax = 0.0f;
+    for (int64_t k = 0; k < G; k++) {
+        float a = fabsf(oc_bf16_to_f32(grp[k]));
+        if (a > amax) amax = a;
+    }
+    return amax;
+}
+
+/* N % G == 0.  p: [M, N/2] packed codes; s: [M, N/G] FP32 scales. */
+OC_API void oc_int4_quantize(const uint16_t* w, int64_t M, int64_t N, int64_t G, uint8_t* p, float* s) {
+    int64_t ng = N / G;
+    for (int64_t r = 0; r < M; r++)
+        for (int64_t gi = 0; gi < ng; gi++) {
+            const uint16_t* grp = w + r * N + gi * G;
+            float scale = oc_int4_scale(oc_int4_group_amax(grp, G));
+            s[r * ng + gi] = scale;
+            for (int64_t k = 0; k < G; k += 2) {
+                int lo = oc_int4_code(oc_bf16_to_f32(grp[k]), scale);
+                int hi = oc_int4_code(oc_bf16_to_f32(grp[k + 1]), scale);
+                p[(r * N + gi * G + k) / 2] = (uint8_t)((lo & 15) | ((hi & 15) << 4));
+            }
+        }
+}
+
+/* y = BF16(fl(q * s)). */
+OC_API void oc_int4_dequantize(const uint8_t* p, const float* s, int64_t M, int64_t N, int64_t G, uint16_t* y) {
+    int64_t ng = N / G;
+    for (int64_t r = 0; r < M; r++)
+        for (int64_t c = 0; c < N; c++) {
+            float scale = s[r * ng + c / G];
+            uint8_t byte = p[(r * N + c) / 2];
+            uint8_t nibble = (c & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+            y[r * N + c] = oc_f32_to_bf16((float)oc_int4_decode(nibble) * scale);
+        }
+}
+
+/* Fake quantization (the straight-through estimator's forward pass): each
+ * element's code, multiplied back by its group's scale; no codes stored. */
+OC_API void oc_int4_qdq(const uint16_t* x, int64_t M, int64_t N, int64_t G, uint16_t* y) {
+    int64_t ng = N / G;
+    for (int64_t r = 0; r < M; r++)
+        for (int64_t gi = 0; gi < ng; gi++) {
+            const uint16_t* grp = x + r * N + gi * G;
+            float scale = oc_int4_scale(oc_int4_group_amax(grp, G));
+            for (int64_t k = 0; k < G; k++) {
+                int q = oc_int4_code(oc_bf16_to_f32(grp[k]), scale);
+                y[r * N + gi * G + k] = oc_f32_to_bf16((float)q * scale);
+            }
+        }
 }
 
 /* Vectorised scalar entry points for the tests (n independent elements). */

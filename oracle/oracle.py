@@ -79,6 +79,10 @@ _SIG = {
     "oc_nvfp4_global_scale_reciprocal": (ctypes.c_float, [ctypes.c_float]),
     "oc_observer_update": (ctypes.c_float, [ctypes.c_int, ctypes.c_float, _f32p, _u16p, _i64]),
     "oc_nvfp4_global_scale_max": (ctypes.c_float, [ctypes.c_float, ctypes.c_int]),
+    "oc_int4_scale": (ctypes.c_float, [ctypes.c_float]),
+    "oc_int4_quantize": (None, [_u16p, _i64, _i64, _i64, _u8p, _f32p]),
+    "oc_int4_dequantize": (None, [_u8p, _f32p, _i64, _i64, _i64, _u16p]),
+    "oc_int4_qdq": (None, [_u16p, _i64, _i64, _i64, _u16p]),
 }
 
 
@@ -238,6 +242,39 @@ class Oracle:
         assert N % 16 == 0
         y = np.empty((M, N), np.uint16)
         self.L.oc_nvfp4_qdq(_p(x, _u16p), M, N, float(g), _p(y, _u16p))
+        return y
+
+    # ------------------------------------------------------------------ INT4, group-wise ("INT4 QAT 训练")
+    INT4_GROUPS = (32, 128)
+
+    def int4_scale(self, amax: float) -> float:
+        return float(self.L.oc_int4_scale(float(amax)))
+
+    def int4_quantize(self, w: np.ndarray, group: int):
+        """BF16 [M,N] (N % group == 0) -> (packed [M,N/2] two's-complement nibbles, FP32 scales [M,N/group])."""
+        w = _bf16(w)
+        M, N = w.shape
+        assert group in self.INT4_GROUPS and N % group == 0
+        p = np.empty((M, N // 2), np.uint8)
+        s = np.empty((M, N // group), np.float32)
+        self.L.oc_int4_quantize(_p(w, _u16p), M, N, group, _p(p, _u8p), _p(s, _f32p))
+        return p, s
+
+    def int4_dequantize(self, p: np.ndarray, s: np.ndarray, group: int) -> np.ndarray:
+        p = np.ascontiguousarray(p, dtype=np.uint8)
+        s = np.ascontiguousarray(s, dtype=np.float32)
+        M, N = p.shape[0], p.shape[1] * 2
+        assert group in self.INT4_GROUPS and s.shape == (M, N // group)
+        y = np.empty((M, N), np.uint16)
+        self.L.oc_int4_dequantize(_p(p, _u8p), _p(s, _f32p), M, N, group, _p(y, _u16p))
+        return y
+
+    def int4_qdq(self, x: np.ndarray, group: int) -> np.ndarray:
+        x = _bf16(x)
+        M, N = x.shape
+        assert group in self.INT4_GROUPS and N % group == 0
+        y = np.empty((M, N), np.uint16)
+        self.L.oc_int4_qdq(_p(x, _u16p), M, N, group, _p(y, _u16p))
         return y
 
     # ------------------------------------------------------------------ W4A4 activation observers

@@ -770,4 +770,110 @@ def pin_requant_nvfp4_round_trip(O):
         assert np.array_equal(O.nvfp4_dequantize(p, s, g), O.fp8blk_dequantize(q1, s1))
 
 
+# --------------------------------------------------------------------------- INT4, group-wise
+# "低精度训练与 Rollout", "INT4 QAT 训练": only the group sizes (128, 32) are on
+# the page; the readings (symmetric, s = amax / 7, nearest integer with ties to
+# even, two's-complement nibbles) are the oracle's and are pinned here from
+# independent routes: exact rationals, numpy's int8 bit patterns, and inputs
+# built to be exactly representable.
+
+def _int4_pack_numpy(q: np.ndarray) -> np.ndarray:
+    """Two's-complement nibbles from numpy's int8 bit patterns, element 2j low."""
+    nib = q.astype(np.int8).view(np.uint8) & 0x0F
+    return (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+
+
+def pin_int4_grid_round_trip(O):
+    """Integer codes times a power of two per group, with a +-7 in every group:
+    the scale is exactly that power, the codes come back packed as numpy's int8
+    nibbles, and dequantize and QDQ return the input bit for bit."""
+    rng = np.random.default_rng(41)
+    for G in (32, 128):
+        M, N = 6, 4 * G
+        q = rng.integers(-7, 8, (M, N)).astype(np.int64)
+        k = rng.integers(-30, 30, (M, N // G))
+        for r in range(M):
+            for gi in range(N // G):
+                q[r, gi * G + rng.integers(0, G)] = 7 if rng.integers(0, 2) else -7
+        scale = np.ldexp(1.0, np.repeat(k, G, axis=1))
+        w = f32_to_bf16_torch((q * scale).astype(np.float32))
+        assert np.array_equal(bf16_f32(w).astype(np.float64), q * scale)   # exact by construction
+        p, s = O.int4_quantize(w, G)
+        assert np.array_equal(s.astype(np.float64), np.ldexp(1.0, k)), G
+        assert np.array_equal(p, _int4_pack_numpy(q)), G
+        y = O.int4_dequantize(p, s, G)
+        assert np.array_equal(bf16_f32(y).astype(np.float64), q * scale), G
+        assert np.array_equal(O.int4_qdq(w, G), y), G
+
+
+def _int4_exact(xs: np.ndarray):
+    """Scale, codes and BF16 outputs of one group by exact rational arithmetic:
+    s = RN32(amax / 7), t = RN32(x / s), q = round-half-even(t) clamped to
+    [-8, 7], y = BF16(RN32(q * s))."""
+    vals = [Fraction(float(v)) for v in bf16_f32(xs)]
+    amax = max(abs(v) for v in vals)
+    s = rn_f32_of(amax / 7)
+    qs, ys = [], []
+    for v in vals:
+        if s == 0:
+            q = 0
+        else:
+            t = Fraction(float(rn_f32_of(v / Fraction(float(s)))))
+            q = min(7, max(-8, round(t)))          # Python rounds half to even
+        qs.append(q)
+        ys.append(rn_f32_of(Fraction(q) * Fraction(float(s))))
+    return s, np.array(qs, np.int64), f32_to_bf16_torch(np.array(ys, np.float32))
+
+
+def pin_int4_nearest_exact(O):
+    """Codes, scales and QDQ outputs against exact rationals, on MoE-like groups,
+    groups of subnormals, groups spanning wide exponent ranges, and groups whose
+    quotients land exactly on half-integers (ties to even)."""
+    rng = np.random.default_rng(42)
+    for G in (32, 128):
+        groups = []
+        for j in range(6):   # MoE-like values with outliers
+            v = rng.standard_normal(G) * 0.02
+            v[rng.integers(0, G)] *= 50
+            groups.append(v.astype(np.float32))
+        groups.append(random_f32(G, 43 + G, -133, -120))   # subnormal and tiny amax
+        groups.append(random_f32(G, 44 + G, -60, 60))      # wide exponent range
+        for k in (-12, 0, 9):                              # half-integer quotients under s = 2^k
+            t = np.resize(np.array([7, -7, 0.5, -0.5, 1.5, -1.5, 2.5, -2.5, 3.5, -3.5, 4.5, 5.5, 6.5, -6.5, 0, 3]),
+                          G)
+            groups.append(np.ldexp(t, k).astype(np.float32))
+        w = np.stack([f32_to_bf16_torch(g) for g in groups])
+        p, s = O.int4_quantize(w, G)
+        y = O.int4_qdq(w, G)
+        for r in range(w.shape[0]):
+            es, eq, ey = _int4_exact(w[r])
+            assert f32_bits(s[r, 0]) == f32_bits(es), (G, r)
+            assert np.array_equal(p[r], _int4_pack_numpy(eq[None])[0]), (G, r)
+            assert np.array_equal(y[r], ey), (G, r)
+
+
+def pin_int4_zero_and_layout(O):
+    """A zero group has scale 0, codes 0 and +0 outputs (integers carry no sign of
+    zero), a group's scale sits at [row, column / G], and QDQ is dequantize of
+    quantize on random data."""
+    for G in (32, 128):
+        M, N = 3, 3 * G
+        w = f32_to_bf16_torch(np.linspace(-1.0, 1.0, M * N, dtype=np.float32).reshape(M, N))
+        w[1, G:2 * G] = 0x8000            # -0 group
+        w[2, 0:G] = 0
+        p, s = O.int4_quantize(w, G)
+        assert s.shape == (M, N // G) and s[1, 1] == 0 and s[2, 0] == 0
+        assert np.all(p[1, G // 2:G] == 0) and np.all(p[2, :G // 2] == 0)
+        y = O.int4_dequantize(p, s, G)
+        assert np.all(y[1, G:2 * G] == 0) and np.all(y[2, :G] == 0)     # +0, not -0
+        # scale of group (r, gi) is the amax of exactly those G elements over 7
+        for r in range(M):
+            for gi in range(N // G):
+                amax = np.max(np.abs(bf16_f32(w[r, gi * G:(gi + 1) * G]).astype(np.float64)))
+                assert f32_bits(s[r, gi]) == f32_bits(rn_f32_of(Fraction(float(amax)) / 7)), (G, r, gi)
+        rng = np.random.default_rng(45)
+        x = f32_to_bf16_torch((rng.standard_normal((4, 2 * G)) * 0.03).astype(np.float32))
+        assert np.array_equal(O.int4_qdq(x, G), O.int4_dequantize(*O.int4_quantize(x, G), G))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

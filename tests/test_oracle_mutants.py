@@ -98,6 +98,30 @@ MUTANTS = [
     ("nvfp4 qdq does not multiply back by the global scale",
      "float S = oc_nvfp4_effective_scale(oc_nvfp4_block_scale(bmax, g), g);",
      "float S = oc_e4m3_decode(oc_nvfp4_block_scale(bmax, g)) * (g > 0.0f ? 1.0f : 0.0f);"),
+    ("int4 scale divisor 8",
+     "OC_API float oc_int4_scale(float amax) { return amax / 7.0f; }",
+     "OC_API float oc_int4_scale(float amax) { return amax / 8.0f; }"),
+    ("int4 rounds half away from zero",
+     "float t = nearbyintf(x / s);",
+     "float t = roundf(x / s);"),
+    ("int4 truncates the quotient",
+     "float t = nearbyintf(x / s);",
+     "float t = truncf(x / s);"),
+    ("int4 nibbles swapped",
+     "p[(r * N + gi * G + k) / 2] = (uint8_t)((lo & 15) | ((hi & 15) << 4));",
+     "p[(r * N + gi * G + k) / 2] = (uint8_t)((hi & 15) | ((lo & 15) << 4));"),
+    ("int4 decode without sign extension",
+     "static int oc_int4_decode(uint8_t nibble) { return (nibble & 8) ? (int)nibble - 16 : (int)nibble; }",
+     "static int oc_int4_decode(uint8_t nibble) { return (int)nibble; }"),
+    ("int4 dequant scale of the 32-element group",
+     "float scale = s[r * ng + c / G];",
+     "float scale = s[r * ng + (c / 32) % ng];"),
+    ("int4 group amax without abs",
+     "float a = fabsf(oc_bf16_to_f32(grp[k]));",
+     "float a = oc_bf16_to_f32(grp[k]);"),
+    ("int4 qdq keeps the quotient unrounded",
+     "y[r * N + gi * G + k] = oc_f32_to_bf16((float)q * scale);",
+     "y[r * N + gi * G + k] = oc_f32_to_bf16((scale == 0.0f ? 0.0f : oc_bf16_to_f32(grp[k]) / scale) * scale);"),
 ]
 
 
