@@ -340,6 +340,41 @@ lpq_status lpq_nvfp4_observe(const uint16_t* x, int64_t M, int64_t N, int observ
  * QAT" 3.3). */
 lpq_status lpq_nvfp4_global_scale(const float* amax, int32_t n, float* out, void* stream);
 
+/* ======================================================================== */
+/* Group-wise INT4.  "低精度训练与 Rollout" (vime and slime documentation),
+ * "INT4 QAT 训练": INT4 weights for rollout and INT4 fake-quant training
+ * through a straight-through estimator, with OPEN_TRAINING_INT4_GROUP_SIZE
+ * 128 (Moonlight-16B-A3B, Qwen3-30B-A3B, Qwen3-235B-A22B) or 32
+ * (Kimi-K2-Thinking).  The page fixes nothing else; readings:
+ *   group  G = 32 or 128 consecutive elements of a row, N % G == 0
+ *          (other group sizes: LPQ_ERR_ARG; N % G != 0: LPQ_ERR_SHAPE)
+ *   s      = fl(amax / 7), amax = max |w| over the group (symmetric)
+ *   code   = (s == 0) ? 0 : the integer nearest to fl(w / s), ties to even,
+ *            clamped to [-8, 7] (finite inputs never reach the clamp)
+ *   y      = BF16(fl(code * s))   (+0 for code 0: integers have no -0)
+ * Packed layout: two's-complement nibbles, element 2j in the low nibble of
+ * byte j.  p: [M, N/2] (4-byte aligned); s: [M, N/G] FP32 (4-byte aligned);
+ * w, x, y: [M, N] BF16, 16-byte aligned. */
+lpq_status lpq_quantize_int4(const uint16_t* w, int64_t M, int64_t N, int32_t group, uint8_t* p, float* s,
+                             void* stream);
+lpq_status lpq_dequantize_int4(const uint8_t* p, const float* s, int64_t M, int64_t N, int32_t group, uint16_t* y,
+                               void* stream);
+
+/* The straight-through estimator's forward pass: y = dequantize(quantize(x))
+ * bit for bit, no codes stored.  x and y may not overlap. */
+lpq_status lpq_int4_qdq(const uint16_t* x, int64_t M, int64_t N, int32_t group, uint16_t* y, void* stream);
+
+/* Grouped forms (descriptors as for the NVFP4 grouped
+ * calls: quantize {src = w, dst = p, scale = s}, dequantize {src = p, dst = y,
+ * scale = s}, QDQ {src = x, dst = y, scale unused}; the group field is
+ * ignored, reserved must be 0).  One group size per call. */
+lpq_status lpq_quantize_int4_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, int32_t group,
+                                     void* stream);
+lpq_status lpq_dequantize_int4_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, int32_t group,
+                                       void* stream);
+lpq_status lpq_int4_qdq_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, int32_t group,
+                                void* stream);
+
 #ifdef __cplusplus
 }
 #endif

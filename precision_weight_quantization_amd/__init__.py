@@ -99,6 +99,12 @@ _SIG = {
     "lpq_requantize_fp8blk_mxfp8_grouped": (_int, [_rp, _vp, _i32, _vp]),
     "lpq_fp8blk_amax_grouped": (_int, [_rp, _vp, _i32, _vp, _i32, _int, _vp]),
     "lpq_requantize_fp8blk_nvfp4_grouped": (_int, [_rp, _vp, _i32, _vp, _i32, _vp, _vp]),
+    "lpq_quantize_int4": (_int, [_vp, _i64, _i64, _i32, _vp, _vp, _vp]),
+    "lpq_dequantize_int4": (_int, [_vp, _vp, _i64, _i64, _i32, _vp, _vp]),
+    "lpq_int4_qdq": (_int, [_vp, _i64, _i64, _i32, _vp, _vp]),
+    "lpq_quantize_int4_grouped": (_int, [_tp, _vp, _i32, _i32, _vp]),
+    "lpq_dequantize_int4_grouped": (_int, [_tp, _vp, _i32, _i32, _vp]),
+    "lpq_int4_qdq_grouped": (_int, [_tp, _vp, _i32, _i32, _vp]),
 }
 for _name, (_res, _args) in _SIG.items():
     _fn = getattr(_L, _name)
@@ -295,6 +301,53 @@ def lpq_nvfp4_qdq(x, amax, y=None, stream=None):
     y = _empty((M, N), torch.bfloat16, x) if y is None else y
     _check(_L.lpq_nvfp4_qdq(x.data_ptr(), M, N, amax.data_ptr(), y.data_ptr(), _stream(stream)), "lpq_nvfp4_qdq")
     return y
+
+
+# --------------------------------------------------------------------------- INT4, group-wise
+
+INT4_GROUPS = (32, 128)
+
+
+def lpq_quantize_int4(w, group=128, p=None, s=None, stream=None):
+    """BF16 [M,N] (N % group == 0) -> (packed two's-complement nibbles [M,N/2] uint8,
+    FP32 group scales [M,N/group])."""
+    w = _bf16_in(w, "w")
+    M, N = w.shape
+    g = max(int(group), 1)
+    p = _empty((M, max(N // 2, 1)), torch.uint8, w) if p is None else p
+    s = _empty((M, max(N // g, 1)), torch.float32, w) if s is None else s
+    _check(_L.lpq_quantize_int4(w.data_ptr(), M, N, int(group), p.data_ptr(), s.data_ptr(), _stream(stream)),
+           "lpq_quantize_int4")
+    return p, s
+
+
+def lpq_dequantize_int4(p, s, group=128, y=None, stream=None):
+    M, N = p.shape[0], p.shape[1] * 2
+    y = _empty((M, N), torch.bfloat16, p) if y is None else y
+    _check(_L.lpq_dequantize_int4(p.data_ptr(), s.data_ptr(), M, N, int(group), y.data_ptr(), _stream(stream)),
+           "lpq_dequantize_int4")
+    return y
+
+
+def lpq_int4_qdq(x, group=128, y=None, stream=None):
+    """INT4 fake quantization (the straight-through estimator's forward pass) of BF16 [M,N]."""
+    x = _bf16_in(x, "x")
+    M, N = x.shape
+    y = _empty((M, N), torch.bfloat16, x) if y is None else y
+    _check(_L.lpq_int4_qdq(x.data_ptr(), M, N, int(group), y.data_ptr(), _stream(stream)), "lpq_int4_qdq")
+    return y
+
+
+def lpq_quantize_int4_grouped(table, group=128, stream=None):
+    _check(_L.lpq_quantize_int4_grouped(*table.args(), int(group), _stream(stream)), "lpq_quantize_int4_grouped")
+
+
+def lpq_dequantize_int4_grouped(table, group=128, stream=None):
+    _check(_L.lpq_dequantize_int4_grouped(*table.args(), int(group), _stream(stream)), "lpq_dequantize_int4_grouped")
+
+
+def lpq_int4_qdq_grouped(table, group=128, stream=None):
+    _check(_L.lpq_int4_qdq_grouped(*table.args(), int(group), _stream(stream)), "lpq_int4_qdq_grouped")
 
 
 # --------------------------------------------------------------------------- FP8 re-quantization

@@ -57,6 +57,15 @@
 #ifndef LPQ_AMAX_U
 #define LPQ_AMAX_U 32
 #endif
+#ifndef LPQ_I4Q_U
+#define LPQ_I4Q_U 4
+#endif
+#ifndef LPQ_I4D_U
+#define LPQ_I4D_U 2
+#endif
+#ifndef LPQ_I4QDQ_U
+#define LPQ_I4QDQ_U 2
+#endif
 #ifndef LPQ_RQM_U
 #define LPQ_RQM_U 2
 #endif
@@ -107,6 +116,15 @@
 #endif
 #ifndef LPQ_DQF_AHEAD
 #define LPQ_DQF_AHEAD 0
+#endif
+#ifndef LPQ_I4Q_AHEAD
+#define LPQ_I4Q_AHEAD 1
+#endif
+#ifndef LPQ_I4D_AHEAD
+#define LPQ_I4D_AHEAD 0
+#endif
+#ifndef LPQ_I4QDQ_AHEAD
+#define LPQ_I4QDQ_AHEAD 1
 #endif
 #ifndef LPQ_NTL
 #define LPQ_NTL 1
@@ -695,6 +713,186 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_qdq(const lpq_tensor* table,
             const F8 f = widen8(v[u]);
             const BlockScale B = block_scale(pair_max(absmax8_f32(f)), G);
             const v4u o = e2m1x8_to_bf16(e2m1x8(f, B), B.S);
+            if (FULL || e0 < total) store<kNTS>(dst + (e0 >> 3), o);
+        }
+    });
+}
+
+// ---------------------------------------------------------------------------
+// INT4: symmetric, one FP32 scale per group of G = 32 or 128 elements of a row
+// ---------------------------------------------------------------------------
+//
+// "低精度训练与 Rollout", "INT4 QAT 训练" fixes the group size (128, or 32 for
+// Kimi-K2) and a straight-through estimator, whose forward pass is QDQ.
+// Readings: s = fl(amax / 7); code = the integer nearest to fl(x / s), ties
+// to even, clamped to [-8, 7] (a zero scale gives 0); two's-complement
+// nibbles, element 2j low; y = BF16(fl(code * s)).  Flat layout as for
+// NVFP4: 8 elements per lane, a group is G / 8 consecutive lanes.
+
+constexpr float kRcp7 = 0x1.24924ap-3f;   // RN(1/7)
+constexpr float kRound = 0x1.8p23f;       // fl(t + 1.5 * 2^23) = 1.5 * 2^23 + RN_int(t) for |t| <= 2^22
+
+// Maximum over the G / 8 lanes of a group.
+template <int G>
+__device__ __forceinline__ uint32_t int4_group_max(uint32_t m) {
+    m = quad_max(m);
+    if constexpr (G == 128) {
+        m = umax(m, (uint32_t)__shfl_xor((int)m, 4));
+        m = umax(m, (uint32_t)__shfl_xor((int)m, 8));
+    }
+    return m;
+}
+
+struct Int4Scale {
+    float s;        // the group scale
+    float sd;       // divisor for the quotients: s, or s * 2^64 when s is tiny
+    float r;        // RN(1 / sd), or 0 when s == 0
+    float xpre;     // 1, or 2^64 when s is tiny
+    bool any_tiny;  // wave-uniform
+};
+
+__device__ __forceinline__ Int4Scale int4_scale(uint32_t amax_bits) {
+    Int4Scale I;
+    const float a = __uint_as_float(amax_bits);
+    // fl(a / 7): the short sequence is exact while the quotient is normal;
+    // tinier groups take the full correctly rounded division
+    float s = quot_rn(a, 7.0f, kRcp7);
+    if (any_lane(a < 0x1p-100f)) {
+        float aa = a;
+        __asm__ volatile("" : "+v"(aa));   // keeps the long division inside the branch
+        if (aa < 0x1p-100f) s = aa / 7.0f;
+    }
+    I.s = s;
+    const bool tiny = s > 0.0f && s < kTinyScale;
+    I.any_tiny = any_lane(tiny);
+    I.xpre = tiny ? kPreScale : 1.0f;
+    I.sd = tiny ? s * kPreScale : s;
+    I.r = s > 0.0f ? rcp_rn(I.sd) : 0.0f;
+    return I;
+}
+
+// fl(x / s) of the 8 values, clamped to [-8, 7] (so that rounding stays in range).
+__device__ __forceinline__ void int4_quotients(const F8& f, const Int4Scale& I, float (&t)[8]) {
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) x[k] = f.x[k];
+    if (I.any_tiny) {
+#pragma unroll
+        for (int k = 0; k < 8; k++) x[k] *= I.xpre;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; k++) t[k] = __builtin_amdgcn_fmed3f(quot_rn(x[k], I.sd, I.r), -8.0f, 7.0f);
+}
+
+// 8 values -> 8 nibbles (element 0 low).  The low four bits of fl(t + 1.5 *
+// 2^23) are RN_int(t) in two's complement.
+__device__ __forceinline__ uint32_t int4x8(const F8& f, const Int4Scale& I) {
+    float t[8];
+    int4_quotients(f, I, t);
+    uint32_t p = 0;
+#pragma unroll
+    for (int k = 0; k < 8; k++) p |= (__float_as_uint(t[k] + kRound) & 15u) << (4 * k);
+    return p;
+}
+
+// 8 values -> their fake-quantized BF16 values BF16(fl(RN_int(fl(x / s)) * s)).
+__device__ __forceinline__ v4u int4x8_qdq(const F8& f, const Int4Scale& I) {
+    float t[8], y[8];
+    int4_quotients(f, I, t);
+#pragma unroll
+    for (int k = 0; k < 8; k++) y[k] = ((t[k] + kRound) - kRound) * I.s;   // the integer, exactly, times s
+    return v4u{bf16x2(y[0], y[1]), bf16x2(y[2], y[3]), bf16x2(y[4], y[5]), bf16x2(y[6], y[7])};
+}
+
+// 8 nibbles (one word) times s -> 8 BF16 values.
+__device__ __forceinline__ v4u int4x8_to_bf16(uint32_t p, float s) {
+    float y[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) y[k] = (float)((int32_t)(p << (28 - 4 * k)) >> 28) * s;   // sign-extended nibble
+    return v4u{bf16x2(y[0], y[1]), bf16x2(y[2], y[3]), bf16x2(y[4], y[5]), bf16x2(y[6], y[7])};
+}
+
+template <int U, bool GROUPED, int G, bool AHEAD = LPQ_I4Q_AHEAD != 0>
+__global__ __launch_bounds__(kThreads) void k_int4_quant(const lpq_tensor* table, lpq_tensor one, ChunkMap map) {
+    const Work W = locate<GROUPED>(table, one, map);
+    const lpq_tensor& d = W.d;
+    const int64_t total = d.rows * d.cols;
+    const int64_t base = W.unit * chunk_elems<U>();
+    const v4u* src = reinterpret_cast<const v4u*>(d.src);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(d.dst);
+    float* scale = reinterpret_cast<float*>(d.scale);
+    const int tid = threadIdx.x;
+    by_fullness<chunk_elems<U>()>(base, total, [&](auto full) {
+        constexpr bool FULL = decltype(full)::value;
+        v4u v[U];
+        auto fetch = [&](int u) { v[u] = load_vec<FULL>(src, base, total, u); };
+        fetch_start<U, AHEAD>(fetch);
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            fetch_step<U, AHEAD>(u, fetch, v[u].x);
+            const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+            // G / 8 lanes are one group; groups never straddle the end (N % G == 0)
+            const F8 f = widen8(v[u]);
+            const Int4Scale I = int4_scale(int4_group_max<G>(absmax8_f32(f)));
+            const uint32_t p = int4x8(f, I);
+            if (FULL || e0 < total) {
+                store<kNTS>(dst + (e0 >> 3), p);
+                if ((tid & (G / 8 - 1)) == 0) store<false>(scale + e0 / G, I.s);
+            }
+        }
+    });
+}
+
+template <int U, bool GROUPED, int G, bool AHEAD = LPQ_I4D_AHEAD != 0>
+__global__ __launch_bounds__(kThreads) void k_int4_dequant(const lpq_tensor* table, lpq_tensor one, ChunkMap map) {
+    const Work W = locate<GROUPED>(table, one, map);
+    const lpq_tensor& d = W.d;
+    const int64_t total = d.rows * d.cols;
+    const int64_t base = W.unit * chunk_elems<U>();
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(d.src);
+    const float* scale = reinterpret_cast<const float*>(d.scale);
+    v4u* dst = reinterpret_cast<v4u*>(d.dst);
+    const int tid = threadIdx.x;
+    by_fullness<chunk_elems<U>()>(base, total, [&](auto full) {
+        constexpr bool FULL = decltype(full)::value;
+        uint32_t p[U];
+        float sc[U];
+        auto fetch = [&](int u) {
+            const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+            p[u] = load_vec<FULL>(src, base, total, u);
+            sc[u] = (FULL || e0 < total) ? load<false>(scale + e0 / G) : 0.0f;
+        };
+        fetch_start<U, AHEAD>(fetch);
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            fetch_step<U, AHEAD>(u, fetch, p[u], __float_as_uint(sc[u]));
+            const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+            const v4u o = int4x8_to_bf16(p[u], sc[u]);
+            if (FULL || e0 < total) store<kNTS>(dst + (e0 >> 3), o);
+        }
+    });
+}
+
+template <int U, bool GROUPED, int G, bool AHEAD = LPQ_I4QDQ_AHEAD != 0>
+__global__ __launch_bounds__(kThreads) void k_int4_qdq(const lpq_tensor* table, lpq_tensor one, ChunkMap map) {
+    const Work W = locate<GROUPED>(table, one, map);
+    const lpq_tensor& d = W.d;
+    const int64_t total = d.rows * d.cols;
+    const int64_t base = W.unit * chunk_elems<U>();
+    const v4u* src = reinterpret_cast<const v4u*>(d.src);
+    v4u* dst = reinterpret_cast<v4u*>(d.dst);
+    const int tid = threadIdx.x;
+    by_fullness<chunk_elems<U>()>(base, total, [&](auto full) {
+        constexpr bool FULL = decltype(full)::value;
+        v4u v[U];
+        auto fetch = [&](int u) { v[u] = load_vec<FULL>(src, base, total, u); };
+        fetch_start<U, AHEAD>(fetch);
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            fetch_step<U, AHEAD>(u, fetch, v[u].x);
+            const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+            const F8 f = widen8(v[u]);
+            const v4u o = int4x8_qdq(f, int4_scale(int4_group_max<G>(absmax8_f32(f))));
             if (FULL || e0 < total) store<kNTS>(dst + (e0 >> 3), o);
         }
     });
@@ -1405,7 +1603,16 @@ inline lpq_status launched() {
     return LPQ_OK;
 }
 
-enum Kind { FP8BLK_Q, FP8BLK_QW, FP8BLK_DQ, FP8BLK_DQF, MXFP8_Q, MXFP8_QF, MXFP8_DQ, NV_AMAX, NV_Q, NV_DQ, NV_QDQ, RQ_FP8, RQ_MX, RQ_AMAX, RQ_NV };
+enum Kind {
+    FP8BLK_Q, FP8BLK_QW, FP8BLK_DQ, FP8BLK_DQF, MXFP8_Q, MXFP8_QF, MXFP8_DQ, NV_AMAX, NV_Q, NV_DQ, NV_QDQ,
+    I4_Q32, I4_Q128, I4_DQ32, I4_DQ128, I4_QDQ32, I4_QDQ128,
+    RQ_FP8, RQ_MX, RQ_AMAX, RQ_NV
+};
+
+// The INT4 group size of an INT4 kind (0 for other kinds).
+constexpr int int4_group(Kind k) {
+    return (k == I4_Q32 || k == I4_DQ32 || k == I4_QDQ32) ? 32 : (k == I4_Q128 || k == I4_DQ128 || k == I4_QDQ128) ? 128 : 0;
+}
 
 // Shape and pointer checks of one tensor for one kind of call.
 lpq_status check_tensor(Kind k, const lpq_tensor& t, int32_t n_groups) {
@@ -1413,7 +1620,7 @@ lpq_status check_tensor(Kind k, const lpq_tensor& t, int32_t n_groups) {
     if (t.rows > (int64_t(1) << 40) / t.cols) return LPQ_ERR_SHAPE;   // element count overflow guard
     if (!t.src) return LPQ_ERR_NULL;
     if (k != NV_AMAX && !t.dst) return LPQ_ERR_NULL;
-    if (k != NV_AMAX && k != NV_QDQ && !t.scale) return LPQ_ERR_NULL;
+    if (k != NV_AMAX && k != NV_QDQ && k != I4_QDQ32 && k != I4_QDQ128 && !t.scale) return LPQ_ERR_NULL;
     if (t.reserved != 0) return LPQ_ERR_ARG;
     switch (k) {
     case FP8BLK_Q:
@@ -1443,6 +1650,21 @@ lpq_status check_tensor(Kind k, const lpq_tensor& t, int32_t n_groups) {
         if (k == NV_Q && !aligned(t.dst, 4)) return LPQ_ERR_ALIGN;
         if ((k == NV_DQ || k == NV_QDQ) && !aligned(t.dst, 16)) return LPQ_ERR_ALIGN;
         if (n_groups > 0 && (t.group < 0 || t.group >= n_groups)) return LPQ_ERR_GROUP;
+        break;
+    case I4_Q32:
+    case I4_Q128:
+        if (t.cols % int4_group(k)) return LPQ_ERR_SHAPE;
+        if (!aligned(t.src, 16) || !aligned(t.dst, 4) || !aligned(t.scale, 4)) return LPQ_ERR_ALIGN;
+        break;
+    case I4_DQ32:
+    case I4_DQ128:
+        if (t.cols % int4_group(k)) return LPQ_ERR_SHAPE;
+        if (!aligned(t.src, 4) || !aligned(t.dst, 16) || !aligned(t.scale, 4)) return LPQ_ERR_ALIGN;
+        break;
+    case I4_QDQ32:
+    case I4_QDQ128:
+        if (t.cols % int4_group(k)) return LPQ_ERR_SHAPE;
+        if (!aligned(t.src, 16) || !aligned(t.dst, 16)) return LPQ_ERR_ALIGN;
         break;
     default: return LPQ_ERR_ARG;
     }
@@ -1481,6 +1703,12 @@ int64_t units(Kind k, const lpq_tensor& t) {
     case NV_Q: return (n + chunk_elems<LPQ_NVQ_U>() - 1) / chunk_elems<LPQ_NVQ_U>();
     case NV_DQ: return (n + chunk_elems<LPQ_NVD_U>() - 1) / chunk_elems<LPQ_NVD_U>();
     case NV_QDQ: return (n + chunk_elems<LPQ_QDQ_U>() - 1) / chunk_elems<LPQ_QDQ_U>();
+    case I4_Q32:
+    case I4_Q128: return (n + chunk_elems<LPQ_I4Q_U>() - 1) / chunk_elems<LPQ_I4Q_U>();
+    case I4_DQ32:
+    case I4_DQ128: return (n + chunk_elems<LPQ_I4D_U>() - 1) / chunk_elems<LPQ_I4D_U>();
+    case I4_QDQ32:
+    case I4_QDQ128: return (n + chunk_elems<LPQ_I4QDQ_U>() - 1) / chunk_elems<LPQ_I4QDQ_U>();
     default: return 0;
     }
 }
@@ -1516,6 +1744,12 @@ void dispatch(Kind k, dim3 grid, hipStream_t stream, const lpq_tensor* tab, cons
         case NV_Q: hipLaunchKernelGGL((k_nvfp4_quant<LPQ_NVQ_U, true>), grid, flat, 0, stream, tab, one, map, fa, fb); break;
         case NV_DQ: hipLaunchKernelGGL((k_nvfp4_dequant<LPQ_NVD_U, true>), grid, flat, 0, stream, tab, one, map, fa); break;
         case NV_QDQ: hipLaunchKernelGGL((k_nvfp4_qdq<LPQ_QDQ_U, true>), grid, flat, 0, stream, tab, one, map, fa); break;
+        case I4_Q32: hipLaunchKernelGGL((k_int4_quant<LPQ_I4Q_U, true, 32>), grid, flat, 0, stream, tab, one, map); break;
+        case I4_Q128: hipLaunchKernelGGL((k_int4_quant<LPQ_I4Q_U, true, 128>), grid, flat, 0, stream, tab, one, map); break;
+        case I4_DQ32: hipLaunchKernelGGL((k_int4_dequant<LPQ_I4D_U, true, 32>), grid, flat, 0, stream, tab, one, map); break;
+        case I4_DQ128: hipLaunchKernelGGL((k_int4_dequant<LPQ_I4D_U, true, 128>), grid, flat, 0, stream, tab, one, map); break;
+        case I4_QDQ32: hipLaunchKernelGGL((k_int4_qdq<LPQ_I4QDQ_U, true, 32>), grid, flat, 0, stream, tab, one, map); break;
+        case I4_QDQ128: hipLaunchKernelGGL((k_int4_qdq<LPQ_I4QDQ_U, true, 128>), grid, flat, 0, stream, tab, one, map); break;
         default: break;
         }
     } else {
@@ -1533,6 +1767,12 @@ void dispatch(Kind k, dim3 grid, hipStream_t stream, const lpq_tensor* tab, cons
         case NV_Q: hipLaunchKernelGGL((k_nvfp4_quant<LPQ_NVQ_U, false>), grid, flat, 0, stream, tab, one, map, fa, fb); break;
         case NV_DQ: hipLaunchKernelGGL((k_nvfp4_dequant<LPQ_NVD_U, false>), grid, flat, 0, stream, tab, one, map, fa); break;
         case NV_QDQ: hipLaunchKernelGGL((k_nvfp4_qdq<LPQ_QDQ_U, false>), grid, flat, 0, stream, tab, one, map, fa); break;
+        case I4_Q32: hipLaunchKernelGGL((k_int4_quant<LPQ_I4Q_U, false, 32>), grid, flat, 0, stream, tab, one, map); break;
+        case I4_Q128: hipLaunchKernelGGL((k_int4_quant<LPQ_I4Q_U, false, 128>), grid, flat, 0, stream, tab, one, map); break;
+        case I4_DQ32: hipLaunchKernelGGL((k_int4_dequant<LPQ_I4D_U, false, 32>), grid, flat, 0, stream, tab, one, map); break;
+        case I4_DQ128: hipLaunchKernelGGL((k_int4_dequant<LPQ_I4D_U, false, 128>), grid, flat, 0, stream, tab, one, map); break;
+        case I4_QDQ32: hipLaunchKernelGGL((k_int4_qdq<LPQ_I4QDQ_U, false, 32>), grid, flat, 0, stream, tab, one, map); break;
+        case I4_QDQ128: hipLaunchKernelGGL((k_int4_qdq<LPQ_I4QDQ_U, false, 128>), grid, flat, 0, stream, tab, one, map); break;
         default: break;
         }
     }
@@ -1675,6 +1915,10 @@ Kind fp8blk_quant_kind(const lpq_tensor* t, int32_t n) {
     const int64_t wide = launch_count(FP8BLK_QW, t, n), narrow = launch_count(FP8BLK_Q, t, n);
     return wide > 0 && wide <= narrow ? FP8BLK_QW : FP8BLK_Q;
 }
+
+// The kind of an INT4 operation ("INT4 QAT 训练") for a group size of 32 or
+// 128; -1 for any other group size (the call returns LPQ_ERR_ARG).
+int int4_kind(Kind k32, Kind k128, int32_t group) { return group == 32 ? k32 : group == 128 ? k128 : -1; }
 
 // 6 * the E4M3 maximum of an NVFP4 call, or 0 for an unsupported maximum.
 float gdiv_of(int e4m3_max) { return e4m3_max == 448 ? 2688.0f : (e4m3_max == 256 ? 1536.0f : 0.0f); }
@@ -1978,6 +2222,47 @@ lpq_status lpq_requantize_fp8blk_nvfp4_grouped(const lpq_requant_tensor* host, c
     if (n_groups <= 0) return LPQ_ERR_SHAPE;
     if (!aligned(group_amax, 4) || !aligned(group_g, 4)) return LPQ_ERR_ALIGN;
     return grouped(RQ_NV, host, dev, n, n_groups, group_amax, group_g, stream);
+}
+
+lpq_status lpq_quantize_int4(const uint16_t* w, int64_t M, int64_t N, int32_t group, uint8_t* p, float* s,
+                             void* stream) {
+    const int k = int4_kind(I4_Q32, I4_Q128, group);
+    if (k < 0) return LPQ_ERR_ARG;
+    return single((Kind)k, make_one(w, p, s, M, N), nullptr, nullptr, stream);
+}
+
+lpq_status lpq_dequantize_int4(const uint8_t* p, const float* s, int64_t M, int64_t N, int32_t group, uint16_t* y,
+                               void* stream) {
+    const int k = int4_kind(I4_DQ32, I4_DQ128, group);
+    if (k < 0) return LPQ_ERR_ARG;
+    return single((Kind)k, make_one(p, y, const_cast<float*>(s), M, N), nullptr, nullptr, stream);
+}
+
+lpq_status lpq_int4_qdq(const uint16_t* x, int64_t M, int64_t N, int32_t group, uint16_t* y, void* stream) {
+    const int k = int4_kind(I4_QDQ32, I4_QDQ128, group);
+    if (k < 0) return LPQ_ERR_ARG;
+    return single((Kind)k, make_one(x, y, nullptr, M, N), nullptr, nullptr, stream);
+}
+
+lpq_status lpq_quantize_int4_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, int32_t group,
+                                     void* stream) {
+    const int k = int4_kind(I4_Q32, I4_Q128, group);
+    if (k < 0) return LPQ_ERR_ARG;
+    return grouped((Kind)k, host, dev, n, 0, nullptr, nullptr, stream);
+}
+
+lpq_status lpq_dequantize_int4_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, int32_t group,
+                                       void* stream) {
+    const int k = int4_kind(I4_DQ32, I4_DQ128, group);
+    if (k < 0) return LPQ_ERR_ARG;
+    return grouped((Kind)k, host, dev, n, 0, nullptr, nullptr, stream);
+}
+
+lpq_status lpq_int4_qdq_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, int32_t group,
+                                void* stream) {
+    const int k = int4_kind(I4_QDQ32, I4_QDQ128, group);
+    if (k < 0) return LPQ_ERR_ARG;
+    return grouped((Kind)k, host, dev, n, 0, nullptr, nullptr, stream);
 }
 
 }  // extern "C"

@@ -121,6 +121,40 @@ def test_grouped_validation(lib):
     assert L.lpq_last_hip_error() == 0
 
 
+def test_int4_validation(lib):
+    L = lib.raw()
+    assert L.lpq_quantize_int4(P, 4, 128, 64, P, P, None) == 6          # group 32 or 128 only
+    assert L.lpq_quantize_int4(P, 4, 128, 0, P, P, None) == 6
+    assert L.lpq_quantize_int4(None, 4, 128, 128, P, P, None) == 1
+    assert L.lpq_quantize_int4(P, 4, 128, 128, None, P, None) == 1
+    assert L.lpq_quantize_int4(P, 4, 128, 128, P, None, None) == 1
+    assert L.lpq_quantize_int4(P, 4, 96, 128, P, P, None) == 2          # N % group
+    assert L.lpq_quantize_int4(P, 0, 128, 128, P, P, None) == 2
+    assert L.lpq_quantize_int4(P + 8, 4, 128, 128, P, P, None) == 3      # BF16 input needs 16 bytes
+    assert L.lpq_quantize_int4(P, 4, 128, 128, P + 2, P, None) == 3      # packed needs 4
+    assert L.lpq_quantize_int4(P, 4, 128, 128, P, P + 2, None) == 3      # FP32 scales
+    assert L.lpq_dequantize_int4(P, P, 4, 96, 32, None, None) == 1
+    assert L.lpq_dequantize_int4(P, None, 4, 96, 32, P, None) == 1
+    assert L.lpq_dequantize_int4(P, P, 4, 80, 32, P, None) == 2
+    assert L.lpq_dequantize_int4(P, P, 4, 96, 32, P + 8, None) == 3      # BF16 output needs 16 bytes
+    assert L.lpq_dequantize_int4(P, P, 4, 96, 16, P, None) == 6
+    assert L.lpq_int4_qdq(P, 4, 96, 128, P, None) == 2
+    assert L.lpq_int4_qdq(P, 4, 96, 32, None, None) == 1
+    assert L.lpq_int4_qdq(P, 4, 96, 32, P + 8, None) == 3
+    assert L.lpq_int4_qdq(P, 4, 96, 33, P, None) == 6
+    good = (P, P, P, 8, 256, 0, 0)
+    t = _table(lib, [good, (P, P, P, 8, 160, 0, 0)])                      # 160 % 128 != 0, 160 % 32 == 0
+    assert L.lpq_quantize_int4_grouped(t, P, 2, 128, None) == 2
+    assert L.lpq_dequantize_int4_grouped(t, P, 2, 128, None) == 2
+    assert L.lpq_int4_qdq_grouped(t, P, 2, 128, None) == 2
+    assert L.lpq_quantize_int4_grouped(t, P, 2, 64, None) == 6
+    assert L.lpq_quantize_int4_grouped(None, P, 2, 32, None) == 1
+    assert L.lpq_quantize_int4_grouped(t, P, 0, 32, None) == 2
+    t2 = _table(lib, [good, (P, P, P, 8, 256, 0, 5)])                     # reserved != 0
+    assert L.lpq_int4_qdq_grouped(t2, P, 2, 32, None) == 6
+    assert L.lpq_last_hip_error() == 0
+
+
 def test_requant_validation(lib):
     L = lib.raw()
     assert L.lpq_requantize_fp8blk(None, P, 4, 5, P, P, None) == 1

@@ -10,7 +10,7 @@ import torch
 
 from oracle import oracle as O
 from synth import synth
-from tests.gpu_util import host_u8, host_u16, mismatches, report, to_dev_bf16
+from tests.gpu_util import brute_blocks, f2bf, finite_bf16, host_u8, host_u16, mismatches, report, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -138,39 +138,6 @@ def test_extreme_values(lpq):
 
 # --------------------------------------------------------------------------- brute force over BF16
 
-def _finite_bf16():
-    u = np.arange(65536, dtype=np.uint32).astype(np.uint16)
-    f = (u.astype(np.uint32) << 16).view(np.float32)
-    return u[np.isfinite(f)]
-
-
-def _f2bf(x):
-    x = np.asarray(x, np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
-
-
-def brute_blocks(width, seed):
-    """Two blocks per finite BF16 pattern p: {p alone with zeros} and {p with an
-    anchor a >= |p| and fillers inside [-|a|, |a|]}; p sits at a random position."""
-    rng = np.random.default_rng(seed)
-    pats = _finite_bf16()
-    n = pats.size
-    pf = (pats.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    A = np.zeros((n, width), np.uint16)
-    pos = rng.integers(0, width, n)
-    A[np.arange(n), pos] = pats
-    fac = rng.choice(np.array([1.0, 1.0000001, 1.5, 2.0, 3.0, 7.9, 100.0, 6.0, 448.0, 2688.0]), n)
-    a = np.minimum(np.abs(pf) * fac, 3.3e38)
-    a = np.where(a == 0, rng.choice(np.array([0.0, 1e-40, 1.0]), n), a)
-    fill = rng.uniform(-1, 1, (n, width)) * a[:, None]
-    B = _f2bf(fill.astype(np.float32))
-    apos = (pos + 1 + rng.integers(0, width - 1, n)) % width
-    B[np.arange(n), apos] = _f2bf((a * rng.choice([-1.0, 1.0], n)).astype(np.float32))
-    B[np.arange(n), pos] = pats
-    return np.concatenate([A, B])
-
-
 def test_bruteforce_mxfp8(lpq):
     w = brute_blocks(32, 1)
     check_mxfp8(lpq, w, "bruteforce")
@@ -272,7 +239,7 @@ def test_bruteforce_nvfp4_grouped(lpq, e4m3_max):
 
 def test_bruteforce_fp8blk_grouped(lpq):
     """Each 1x2 (ragged) tensor is its own tile: p with a zero, and p with an anchor."""
-    pats = _finite_bf16()
+    pats = finite_bf16()
     rng = np.random.default_rng(3)
     n = pats.size
     pf = (pats.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
@@ -280,7 +247,7 @@ def test_bruteforce_fp8blk_grouped(lpq):
     w_np = np.zeros((2 * n, 2), np.uint16)
     w_np[:n, 0] = pats
     w_np[n:, 1] = pats
-    w_np[n:, 0] = _f2bf(a.astype(np.float32))
+    w_np[n:, 0] = f2bf(a.astype(np.float32))
     N = 2 * n
     w = to_dev_bf16(w_np)
     q = torch.empty((N, 2), dtype=torch.uint8, device="cuda")
