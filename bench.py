@@ -11,10 +11,12 @@ region holds only the codec launches.
 value = algorithmic bytes of the step (each input and output byte counted
 once; the NVFP4 amax pre-passes are timed but not counted) / step time.
 
-The fp8train workload (fused re-quantization of block-wise FP8 weights into
-MXFP8 / NVFP4, next to the unfused sequences) is timed after the step, over
-the same number of iterations, and reported under "next_rows"; it is not part
-of value or ms_per_step.
+The widening rows -- the fp8train workload (fused re-quantization of
+block-wise FP8 weights into block-wise FP8 / MXFP8 / NVFP4, next to the
+unfused sequences), the OCP floor-rule MXFP8 quantizer, the W4A4 observer,
+and group-wise INT4 of the Qwen3-30B-A3B experts -- are timed after the
+step, over the same number of iterations, and reported under "next_rows";
+they are not part of value or ms_per_step.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -220,6 +222,25 @@ def next_rows_parity(bench, stride: int, threads: int):
             x, y = h16(a["x"]), h16(a["y"])
             jobs.append(lambda x=x, y=y: int((O.nvfp4_qdq(x, O.nvfp4_group_scale([x])[1]) != y).sum()))
             continue
+        if op.workload == "int4":
+            ws = bench.sets["moe_experts"]
+            out = bench.outputs["int4"]
+            G = out["group"]
+            for i in range(0, len(ws.specs), stride):
+                x = h16(ws.w[i])
+                if op.name.startswith("int4.quantize"):
+                    p, s = h8(out["p"][i]), out["s"][i].cpu().numpy()
+
+                    def job(x=x, p=p, s=s):
+                        op_, os_ = O.int4_quantize(x, G)
+                        return int((op_ != p).sum() + (os_.view(np.uint32) != s.view(np.uint32)).sum())
+                else:   # dequantize and QDQ both end in BF16(fl(code * s)) of the oracle's codes
+                    y = h16(out["y"][i])
+
+                    def job(x=x, y=y):
+                        return int((O.int4_dequantize(*O.int4_quantize(x, G), G) != y).sum())
+                jobs.append(job)
+            continue
         if op.workload != "fp8train" or op.name.startswith("requant.amax"):
             continue
         ws = bench.sets["moe"]
@@ -353,7 +374,8 @@ def time_next_rows(bench, steps: int):
                        "the Qwen3-30B-A3B weights held in block-wise FP8 (128x128 tiles, FP32 scales): the experts + "
                        "48 q/k/v (18,576 tensors) -> block-wise FP8; the 18,432 expert tensors -> MXFP8; the experts "
                        "+ q/k/v (12,336 sibling groups) -> NVFP4 with the model-wide amax pass; unfused = dequantize "
-                       "to BF16 in HBM, then quantize")
+                       "to BF16 in HBM, then quantize; the Qwen3-30B-A3B experts (18,432 tensors) -> group-wise INT4 "
+                       "(group 128) quantize, dequantize and QDQ")
     log(f"  fused speedup vs unfused: {sp}")
     return out
 
@@ -366,7 +388,7 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--bucket", choices=("layer", "all"), default="layer")
-    ap.add_argument("--workloads", default="dense,moe,nvfp4,dsv3,fp8train")
+    ap.add_argument("--workloads", default="dense,moe,nvfp4,dsv3,fp8train,int4")
     ap.add_argument("--cpu-stride", type=int, default=12)
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true")

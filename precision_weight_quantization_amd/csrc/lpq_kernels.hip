@@ -118,7 +118,7 @@
 #define LPQ_DQF_AHEAD 0
 #endif
 #ifndef LPQ_I4Q_AHEAD
-#define LPQ_I4Q_AHEAD 1
+#define LPQ_I4Q_AHEAD 0
 #endif
 #ifndef LPQ_I4D_AHEAD
 #define LPQ_I4D_AHEAD 0

@@ -2,8 +2,9 @@
 
 Builds every weight workload at its full size on the device (Qwen3-4B dense,
 Qwen3-30B-A3B experts with q/k/v sibling groups, DeepSeek-V3 MoE layer, W4A4
-activations, and the block-wise FP8 copy of the Qwen3-30B-A3B weights for
-re-quantization), runs each operation exactly as the benchmark does (grouped
+activations, the block-wise FP8 copy of the Qwen3-30B-A3B weights for
+re-quantization, and INT4 of its experts), runs each operation exactly as the
+benchmark does (grouped
 launches per layer), and compares sampled outputs -- every 48th tensor, every
 48th NVFP4 sibling group, and the whole activation QDQ -- with the oracle,
 bit for bit.  The sampled inputs are copied back from the device; the
@@ -42,7 +43,9 @@ def test_fullsize_sampled_parity(full_bench):
 
 
 def test_fullsize_requant_sampled_parity(full_bench):
-    """Fused and unfused FP8 re-quantization at full size, sampled, against the oracle."""
+    """The widening rows at full size, sampled, against the oracle: fused and unfused
+    FP8 re-quantization, floor-rule MXFP8, the observed activation QDQ and
+    group-wise INT4 of the Qwen3-30B-A3B experts."""
     import bench
     res = bench.next_rows_parity(full_bench, stride=48, threads=min(16, os.cpu_count() or 1))
     print(res, flush=True)

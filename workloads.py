@@ -24,6 +24,9 @@ distributions named for each workload.
           (experts) and NVFP4 (experts and q/k/v, sibling groups as above),
           each next to the unfused dequantize-then-quantize sequence on the
           same data.  Timed apart from the step.
+  int4    the moe workload's experts -> group-wise INT4 (group 128, the size
+          "INT4 QAT 训练" gives for Qwen3-30B-A3B) quantize, dequantize and
+          fake-quant.  Timed apart from the step.
 
 Buckets: one grouped launch per transformer layer (the unit a weight sync
 streams), or one launch over the whole workload.
@@ -218,6 +221,29 @@ def nvfp4_ops(tag: str, ws: WeightSet, packed: Slab, sbytes: Slab, out: Slab, bu
     return ops, dict(p=p, s=sb, y=y, amax=amax, g=g, n_groups=n_groups)
 
 
+INT4_GROUP = 128
+
+
+def int4_ops(tag: str, ws: WeightSet, packed: Slab, scales: Slab, out: Slab, bucket: str, group: int = INT4_GROUP):
+    specs = ws.specs
+    p = [packed.view(i, (s.M, s.N // 2), torch.uint8) for i, s in enumerate(specs)]
+    sc = [scales.view(i, (s.M, s.N // group), torch.float32) for i, s in enumerate(specs)]
+    y = [out.view(i, (s.M, s.N), torch.bfloat16) for i, s in enumerate(specs)]
+    tq, tdq, tqdq = [], [], []
+    for idx in _buckets(ws, bucket):
+        tq.append(lpq.TensorTable([(ws.w[i], p[i], sc[i], specs[i].M, specs[i].N, 0) for i in idx]))
+        tdq.append(lpq.TensorTable([(p[i], y[i], sc[i], specs[i].M, specs[i].N, 0) for i in idx]))
+        tqdq.append(lpq.TensorTable([(ws.w[i], y[i], None, specs[i].M, specs[i].N, 0) for i in idx]))
+    n = ws.numel
+    qbytes = 2 * n + n // 2 + 4 * (n // group)
+    ops = [
+        Op(f"int4.quantize[{tag}]", tag, qbytes, [lambda t=t: lpq.lpq_quantize_int4_grouped(t, group) for t in tq]),
+        Op(f"int4.dequantize[{tag}]", tag, qbytes, [lambda t=t: lpq.lpq_dequantize_int4_grouped(t, group) for t in tdq]),
+        Op(f"int4.qdq[{tag}]", tag, 4 * n, [lambda t=t: lpq.lpq_int4_qdq_grouped(t, group) for t in tqdq]),
+    ]
+    return ops, dict(p=p, s=sc, y=y, group=group)
+
+
 def tiles_of(s: TensorSpec) -> int:
     return ((s.M + 127) // 128) * ((s.N + 127) // 128)
 
@@ -330,7 +356,7 @@ def activation_ops(x: torch.Tensor, y: torch.Tensor):
 
 
 WORKLOADS = ("dense", "moe", "nvfp4", "dsv3")
-NEXT_WORKLOADS = ("fp8train",)
+NEXT_WORKLOADS = ("fp8train", "int4")
 
 
 def reslab(slab: Slab, specs, bytes_per_elem):
@@ -356,7 +382,7 @@ class Bench:
         self.outputs = {}
         self.sets = {}
         L = scale_layers
-        need_moe = "moe" in which or "nvfp4" in which or "fp8train" in which
+        need_moe = any(w in which for w in ("moe", "nvfp4", "fp8train", "int4"))
         if "dense" in which:
             self.sets["dense"] = WeightSet(2, dense_specs(L or 36), synth.DIST_DENSE, device)
             log(f"generated dense weights: {self.sets['dense'].numel * 2 / GB:.2f} GB")
@@ -419,6 +445,15 @@ class Bench:
             o["keep"] = keep
             self.next_ops += ops
             self.outputs["fp8train"] = o
+        if "int4" in which:
+            ws = self.sets.get("moe_experts") or self._experts_only(self.sets["moe"])
+            self.sets["moe_experts"] = ws
+            packed = self._reslab(self.codes, ws.specs, 0.5)
+            sc = Slab([4 * (s.numel // INT4_GROUP) for s in ws.specs], device)
+            out = self._reslab(self.out, ws.specs, 2)
+            ops, o = int4_ops("int4", ws, packed, sc, out, bucket)
+            self.next_ops += ops
+            self.outputs["int4"] = o
 
     _reslab = staticmethod(reslab)
 
