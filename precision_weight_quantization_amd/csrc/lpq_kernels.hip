@@ -489,7 +489,8 @@ __device__ __forceinline__ v4u e2m1x8_to_bf16(uint32_t p, float S) {
 //
 // Observer state (caller-owned device memory, 8 words): [0] min, [1] max,
 // [2] batches seen (FP32), [4] / [5] the current batch's min / max as
-// order-preserving keys.  Keys map binary32 bits to unsigned integers whose
+// order-preserving keys, [6] the number of workgroups of the current call
+// that have folded in their keys.  Keys map binary32 bits to unsigned integers whose
 // order is the values' order with -0 below +0: non-negative values get the
 // sign bit set, negative values have every bit flipped.
 
@@ -505,9 +506,42 @@ __global__ void k_observer_reset(uint32_t* state) {
     if (i < 8) state[i] = i == 4 ? kKeyMinIdentity : (i == 5 ? kKeyMaxIdentity : 0u);
 }
 
-// min / max of one BF16 tensor into the batch keys of the state.
+// Applies the observer rule to the batch extremes (one thread), writes the
+// activation amax and re-arms the batch keys.  Same operations, in the same
+// order, as the definition: m += c * (b - m) for the moving average.  The keys
+// were folded in by device-scope atomics of other workgroups: they are read
+// with device-scope atomic loads.
+__device__ void observer_apply(int kind, float c, uint32_t* state, float* amax) {
+    float* f = reinterpret_cast<float*>(state);
+    const uint32_t kmin = __hip_atomic_load(state + 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t kmax = __hip_atomic_load(state + 5, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float bmin = __uint_as_float(key_bits(kmin)), bmax = __uint_as_float(key_bits(kmax));
+    float mn = f[0], mx = f[1];
+    if (kind == LPQ_OBSERVER_MEMORYLESS_MINMAX || f[2] == 0.0f) {
+        mn = bmin;
+        mx = bmax;
+    } else if (kind == LPQ_OBSERVER_STATIC_MINMAX) {
+        if (kmin < order_key(__float_as_uint(mn))) mn = bmin;
+        if (kmax > order_key(__float_as_uint(mx))) mx = bmax;
+    } else {
+        mn = mn + c * (bmin - mn);
+        mx = mx + c * (bmax - mx);
+    }
+    f[0] = mn;
+    f[1] = mx;
+    f[2] = f[2] + 1.0f;
+    state[4] = kKeyMinIdentity;
+    state[5] = kKeyMaxIdentity;
+    *amax = fmaxf(fabsf(mn), fabsf(mx));
+}
+
+// min / max of one BF16 tensor into the batch keys of the state; the last
+// workgroup to fold in its keys applies the observer rule (no workgroup waits
+// for another: each counts its arrival after its keys are in, and the one
+// that arrives last finds every key there).
 template <int U>
-__global__ __launch_bounds__(kThreads) void k_minmax(lpq_tensor one, uint32_t* state) {
+__global__ __launch_bounds__(kThreads) void k_minmax(lpq_tensor one, int kind, float c, uint32_t* state,
+                                                     float* amax) {
     const int64_t total = one.rows * one.cols;
     const int64_t base = (int64_t)blockIdx.x * chunk_elems<U>();
     const v4u* src = reinterpret_cast<const v4u*>(one.src);
@@ -546,34 +580,13 @@ __global__ __launch_bounds__(kThreads) void k_minmax(lpq_tensor one, uint32_t* s
         }
         atomicMin(state + 4, l);
         atomicMax(state + 5, h);
+        __threadfence();   // this workgroup's keys before its arrival
+        if (atomicAdd(state + 6, 1u) == gridDim.x - 1) {
+            __threadfence();   // every other workgroup's keys before the rule reads them
+            observer_apply(kind, c, state, amax);
+            state[6] = 0u;     // re-armed for the next call
+        }
     }
-}
-
-// Applies the observer rule to the batch extremes (one thread), writes the
-// activation amax and re-arms the batch keys.  Same operations, in the same
-// order, as the definition: m += c * (b - m) for the moving average.
-__global__ void k_observer_update(int kind, float c, uint32_t* state, float* amax) {
-    if (threadIdx.x != 0) return;
-    float* f = reinterpret_cast<float*>(state);
-    const uint32_t kmin = state[4], kmax = state[5];
-    const float bmin = __uint_as_float(key_bits(kmin)), bmax = __uint_as_float(key_bits(kmax));
-    float mn = f[0], mx = f[1];
-    if (kind == LPQ_OBSERVER_MEMORYLESS_MINMAX || f[2] == 0.0f) {
-        mn = bmin;
-        mx = bmax;
-    } else if (kind == LPQ_OBSERVER_STATIC_MINMAX) {
-        if (kmin < order_key(__float_as_uint(mn))) mn = bmin;
-        if (kmax > order_key(__float_as_uint(mx))) mx = bmax;
-    } else {
-        mn = mn + c * (bmin - mn);
-        mx = mx + c * (bmax - mx);
-    }
-    f[0] = mn;
-    f[1] = mx;
-    f[2] = f[2] + 1.0f;
-    state[4] = kKeyMinIdentity;
-    state[5] = kKeyMaxIdentity;
-    *amax = fmaxf(fabsf(mn), fabsf(mx));
 }
 
 // fl(A / 2688) per entry: the multiplier form of a global scale.
@@ -2021,11 +2034,8 @@ lpq_status lpq_nvfp4_observe(const uint16_t* x, int64_t M, int64_t N, int observ
     if (st != LPQ_OK) return st;
     const int64_t units = (M * N + chunk_elems<LPQ_AMAX_U>() - 1) / chunk_elems<LPQ_AMAX_U>();
     if (units > kMaxGridX) return LPQ_ERR_SHAPE;
-    uint32_t* s = reinterpret_cast<uint32_t*>(state);
-    hipLaunchKernelGGL((k_minmax<LPQ_AMAX_U>), dim3((unsigned)units), dim3(kThreads), 0, (hipStream_t)stream, one, s);
-    if ((st = launched()) != LPQ_OK) return st;
-    hipLaunchKernelGGL(k_observer_update, dim3(1), dim3(64), 0, (hipStream_t)stream, observer, averaging_constant, s,
-                       amax);
+    hipLaunchKernelGGL((k_minmax<LPQ_AMAX_U>), dim3((unsigned)units), dim3(kThreads), 0, (hipStream_t)stream, one,
+                       observer, averaging_constant, reinterpret_cast<uint32_t*>(state), amax);
     return launched();
 }
 
