@@ -117,6 +117,12 @@
 #ifndef LPQ_DQF_AHEAD
 #define LPQ_DQF_AHEAD 0
 #endif
+#ifndef LPQ_RQM_AHEAD
+#define LPQ_RQM_AHEAD 1
+#endif
+#ifndef LPQ_RQN_AHEAD
+#define LPQ_RQN_AHEAD 0
+#endif
 #ifndef LPQ_I4Q_AHEAD
 #define LPQ_I4Q_AHEAD 0
 #endif
@@ -1296,18 +1302,38 @@ __device__ __forceinline__ void rq_load(v4u (&c)[U], float (&s)[U], const D& d, 
     }
 }
 
+// The code vectors and tile scales of a lane's U steps, issued in the order of
+// fetch_start / fetch_step (all up front, or one step ahead of the work);
+// body(u, codes, scale) runs on each step.  Steps past the end read as codes 0,
+// scale 0.
+template <int U, bool FULL, bool AHEAD, typename D, typename Body>
+__device__ __forceinline__ void rq_stream(const D& d, int64_t base, int64_t total, Body&& body) {
+    const v4u* src = reinterpret_cast<const v4u*>(codes_of(d)) + base / 16 + threadIdx.x;
+    TileCursor<16> cur(tile_scales_of(d), d.cols, base);
+    v4u c[U];
+    float s[U];
+    auto fetch = [&](int u) {   // called for u = 0, 1, ... in order: the cursor walks along
+        const bool in = FULL || base + (int64_t)(u * kThreads + threadIdx.x) * 16 < total;
+        c[u] = in ? load<kNTL>(src + u * kThreads) : v4u{0u, 0u, 0u, 0u};
+        s[u] = in ? load<false>(cur.ptr()) : 0.0f;
+        cur.next();
+    };
+    fetch_start<U, AHEAD>(fetch);
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        fetch_step<U, AHEAD>(u, fetch, c[u].x, __float_as_uint(s[u]));
+        body(u, c[u], s[u]);
+    }
+}
+
 template <int U, bool FULL>
 __device__ __forceinline__ void rq_mxfp8_body(const lpq_requant_tensor& d, int64_t base, int64_t total) {
     v4u* dst = reinterpret_cast<v4u*>(d.dst);
     uint8_t* esc = reinterpret_cast<uint8_t*>(d.dst_scale);
     const int tid = threadIdx.x;
-    v4u c[U];
-    float s[U];
-    rq_load<U, FULL>(c, s, d, base, total);
-#pragma unroll
-    for (int u = 0; u < U; u++) {
+    rq_stream<U, FULL, LPQ_RQM_AHEAD != 0>(d, base, total, [&](int u, const v4u& c, float s) {
         const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 16;
-        const Y16 y = fp8blk_values16(c[u], s[u]);
+        const Y16 y = fp8blk_values16(c, s);
         // a pair of lanes is one 32-element block
         const uint32_t byte = mx_scale_byte(pair_max(y.amax));
         const float X = ue8m0_operand(byte);
@@ -1317,7 +1343,7 @@ __device__ __forceinline__ void rq_mxfp8_body(const lpq_requant_tensor& d, int64
             store<kNTS>(dst + (e0 >> 4), v4u{q0.x, q0.y, q1.x, q1.y});
             if ((tid & 1) == 0) store_u8(esc + (e0 >> 5), byte);
         }
-    }
+    });
 }
 
 template <int U, bool GROUPED>
@@ -1380,13 +1406,9 @@ __device__ __forceinline__ void rq_nvfp4_body(const lpq_requant_tensor& d, int64
                                               const GlobalScale& G) {
     v2u* dst = reinterpret_cast<v2u*>(d.dst);
     uint8_t* ssc = reinterpret_cast<uint8_t*>(d.dst_scale);
-    v4u c[U];
-    float s[U];
-    rq_load<U, FULL>(c, s, d, base, total);
-#pragma unroll
-    for (int u = 0; u < U; u++) {
+    rq_stream<U, FULL, LPQ_RQN_AHEAD != 0>(d, base, total, [&](int u, const v4u& c, float s) {
         const int64_t e0 = base + (int64_t)(u * kThreads + threadIdx.x) * 16;
-        const Y16 y = fp8blk_values16(c[u], s[u]);
+        const Y16 y = fp8blk_values16(c, s);
         // one lane is one 16-element block
         const BlockScale B = block_scale(y.amax, G);
         const v2u p = v2u{e2m1x8(y.lo, B), e2m1x8(y.hi, B)};
@@ -1394,7 +1416,7 @@ __device__ __forceinline__ void rq_nvfp4_body(const lpq_requant_tensor& d, int64
             store<kNTS>(dst + (e0 >> 4), p);
             store_u8(ssc + (e0 >> 4), B.code);
         }
-    }
+    });
 }
 
 template <int U, bool GROUPED>
