@@ -15,9 +15,9 @@
 // from that table with scalar compares and one division, then reads the
 // descriptor into scalar registers.
 // No workgroup is launched without work.
-//  * MXFP8 / NVFP4 are flat in memory (N is a multiple of the block), so a
-//    workgroup streams 16-byte BF16 vectors, 8 elements per lane, U vectors
-//    per lane; a 1x32 block is a quad of lanes and a 1x16 block a pair,
+//  * MXFP8 / NVFP4 / INT4 are flat in memory (N is a multiple of the block),
+//    so a workgroup (128, 256 or 512 threads, chosen per kernel) streams
+//    16-byte BF16 vectors, 8 elements per lane, U vectors per lane; a 1x32 block is a quad of lanes and a 1x16 block a pair,
 //    reduced with DPP lane permutations.  U is 2 to 4 (16 for the read-only
 //    amax pass): enough bytes in flight per CU, short-lived workgroups.  A
 //    lane's U loads go out either all at once or one vector ahead of the
@@ -143,25 +143,70 @@ using namespace lpq;
 
 namespace {
 
-constexpr int kThreads = 256;            // flat kernels
+#ifndef LPQ_FLAT_THREADS
+#define LPQ_FLAT_THREADS 256
+#endif
+// Workgroup size of each flat kernel (64 to 512, a multiple of 64), measured
+// per kernel: the light encoders and the QDQs run best with 128 threads, the
+// NVFP4 and INT4 decoders and the INT4 encoder with 512, the rest with 256.
+#ifndef LPQ_MXQ_T
+#define LPQ_MXQ_T 128
+#endif
+#ifndef LPQ_MXD_T
+#define LPQ_MXD_T LPQ_FLAT_THREADS
+#endif
+#ifndef LPQ_AMAX_T
+#define LPQ_AMAX_T LPQ_FLAT_THREADS
+#endif
+#ifndef LPQ_NVQ_T
+#define LPQ_NVQ_T LPQ_FLAT_THREADS
+#endif
+#ifndef LPQ_NVD_T
+#define LPQ_NVD_T 512
+#endif
+#ifndef LPQ_QDQ_T
+#define LPQ_QDQ_T 128
+#endif
+#ifndef LPQ_I4Q_T
+#define LPQ_I4Q_T 512
+#endif
+#ifndef LPQ_I4D_T
+#define LPQ_I4D_T 512
+#endif
+#ifndef LPQ_I4QDQ_T
+#define LPQ_I4QDQ_T 128
+#endif
+#ifndef LPQ_DQF_T
+#define LPQ_DQF_T LPQ_FLAT_THREADS
+#endif
+#ifndef LPQ_RQM_T
+#define LPQ_RQM_T LPQ_FLAT_THREADS
+#endif
+#ifndef LPQ_RQA_T
+#define LPQ_RQA_T LPQ_FLAT_THREADS
+#endif
+#ifndef LPQ_RQN_T
+#define LPQ_RQN_T LPQ_FLAT_THREADS
+#endif
+constexpr int kThreads = LPQ_FLAT_THREADS;   // flat kernels
 constexpr int kTile = 128;
 constexpr bool kNTL = LPQ_NTL != 0;
 constexpr bool kNTS = LPQ_NTS != 0;
 constexpr int kMaxSeg = 8;               // segments per launch (longer lists are split)
 
-template <int U>
-constexpr int64_t chunk_elems() { return (int64_t)kThreads * 8 * U; }
+template <int U, int TH = kThreads>
+constexpr int64_t chunk_elems() { return (int64_t)TH * 8 * U; }
 
-// Loads the lane's U vectors of a flat chunk: lane t of vector u holds the EV
-// elements starting at base + (u * kThreads + t) * EV.  A full chunk (the
-// common case) loads without per-lane bounds checks.
-template <int U, bool FULL, int EV = 8, typename T>
+// Loads the lane's U vectors of a flat chunk of a TH-thread workgroup: lane t
+// of vector u holds the EV elements starting at base + (u * TH + t) * EV.  A
+// full chunk (the common case) loads without per-lane bounds checks.
+template <int U, bool FULL, int TH = kThreads, int EV = 8, typename T>
 __device__ __forceinline__ void load_chunk(T (&v)[U], const T* src, int64_t base, int64_t total) {
     const T* p = src + base / EV + threadIdx.x;
 #pragma unroll
     for (int u = 0; u < U; u++) {
-        const bool in = FULL || base + (int64_t)(u * kThreads + threadIdx.x) * EV < total;
-        v[u] = in ? load<kNTL>(p + u * kThreads) : T{};
+        const bool in = FULL || base + (int64_t)(u * TH + threadIdx.x) * EV < total;
+        v[u] = in ? load<kNTL>(p + u * TH) : T{};
     }
 }
 
@@ -195,11 +240,12 @@ __device__ __forceinline__ void fetch_step(int u, Fetch&& fetch, X... have) {
     }
 }
 
-// Vector u of a lane in a flat chunk of EV-element vectors, zero past the end.
-template <bool FULL, int EV = 8, typename T>
+// Vector u of a lane in a flat chunk of EV-element vectors (TH-thread
+// workgroup), zero past the end.
+template <int TH, bool FULL, int EV = 8, typename T>
 __device__ __forceinline__ T load_vec(const T* src, int64_t base, int64_t total, int u) {
-    const bool in = FULL || base + (int64_t)(u * kThreads + threadIdx.x) * EV < total;
-    return in ? load<kNTL>(src + base / EV + threadIdx.x + u * kThreads) : T{};
+    const bool in = FULL || base + (int64_t)(u * TH + threadIdx.x) * EV < total;
+    return in ? load<kNTL>(src + base / EV + threadIdx.x + u * TH) : T{};
 }
 
 template <bool B>
@@ -317,25 +363,25 @@ __device__ __forceinline__ v2u mx_encode8(const F8& f, float X) {
 // FLOOR selects the shared-exponent rule of the OCP MX specification
 // (floor(log2 amax) - 8, elements beyond 448 saturate) instead of the default
 // no-saturation rule.
-template <int U, bool GROUPED, bool FLOOR = false, bool AHEAD = LPQ_MXQ_AHEAD != 0>
-__global__ __launch_bounds__(kThreads) void k_mxfp8_quant(const lpq_tensor* table, lpq_tensor one, ChunkMap map) {
+template <int U, int TH, bool GROUPED, bool FLOOR = false, bool AHEAD = LPQ_MXQ_AHEAD != 0>
+__global__ __launch_bounds__(TH) void k_mxfp8_quant(const lpq_tensor* table, lpq_tensor one, ChunkMap map) {
     const Work W = locate<GROUPED>(table, one, map);
     const lpq_tensor& d = W.d;
     const int64_t total = d.rows * d.cols;
-    const int64_t base = W.unit * chunk_elems<U>();
+    const int64_t base = W.unit * chunk_elems<U, TH>();
     const v4u* src = reinterpret_cast<const v4u*>(d.src);
     v2u* dst = reinterpret_cast<v2u*>(d.dst);
     uint8_t* esc = reinterpret_cast<uint8_t*>(d.scale);
     const int tid = threadIdx.x;
-    by_fullness<chunk_elems<U>()>(base, total, [&](auto full) {
+    by_fullness<chunk_elems<U, TH>()>(base, total, [&](auto full) {
         constexpr bool FULL = decltype(full)::value;
         v4u v[U];
-        auto fetch = [&](int u) { v[u] = load_vec<FULL>(src, base, total, u); };
+        auto fetch = [&](int u) { v[u] = load_vec<TH, FULL>(src, base, total, u); };
         fetch_start<U, AHEAD>(fetch);
 #pragma unroll
         for (int u = 0; u < U; u++) {
             fetch_step<U, AHEAD>(u, fetch, v[u].x);
-            const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+            const int64_t e0 = base + (int64_t)(u * TH + tid) * 8;
             // a quad of lanes is one 32-element block; blocks never straddle the end
             F8 f = widen8(v[u]);
             const uint32_t amax = quad_max(absmax8_f32(f));
@@ -355,30 +401,30 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_quant(const lpq_tensor* tabl
     });
 }
 
-template <int U, bool GROUPED, bool AHEAD = LPQ_MXD_AHEAD != 0>
-__global__ __launch_bounds__(kThreads) void k_mxfp8_dequant(const lpq_tensor* table, lpq_tensor one, ChunkMap map) {
+template <int U, int TH, bool GROUPED, bool AHEAD = LPQ_MXD_AHEAD != 0>
+__global__ __launch_bounds__(TH) void k_mxfp8_dequant(const lpq_tensor* table, lpq_tensor one, ChunkMap map) {
     const Work W = locate<GROUPED>(table, one, map);
     const lpq_tensor& d = W.d;
     const int64_t total = d.rows * d.cols;
-    const int64_t base = W.unit * chunk_elems<U>();
+    const int64_t base = W.unit * chunk_elems<U, TH>();
     const v2u* src = reinterpret_cast<const v2u*>(d.src);
     v4u* dst = reinterpret_cast<v4u*>(d.dst);
     const uint8_t* esc = reinterpret_cast<const uint8_t*>(d.scale);
     const int tid = threadIdx.x;
-    by_fullness<chunk_elems<U>()>(base, total, [&](auto full) {
+    by_fullness<chunk_elems<U, TH>()>(base, total, [&](auto full) {
         constexpr bool FULL = decltype(full)::value;
         v2u c[U];
         uint32_t b[U];
         auto fetch = [&](int u) {
-            const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
-            c[u] = load_vec<FULL>(src, base, total, u);
+            const int64_t e0 = base + (int64_t)(u * TH + tid) * 8;
+            c[u] = load_vec<TH, FULL>(src, base, total, u);
             b[u] = (FULL || e0 < total) ? load_u8(esc + (e0 >> 5)) : 127u;
         };
         fetch_start<U, AHEAD>(fetch);
 #pragma unroll
         for (int u = 0; u < U; u++) {
             fetch_step<U, AHEAD>(u, fetch, c[u].x, b[u]);
-            const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+            const int64_t e0 = base + (int64_t)(u * TH + tid) * 8;
             const float X = ue8m0_operand(b[u]);
             v4u o;
             o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[u].x, X, false));
@@ -614,39 +660,41 @@ __global__ __launch_bounds__(kThreads) void k_fill_f32(float* p, int64_t n, floa
 
 // max |w| of each tensor, max-accumulated into its group slot (binary32 bits
 // of non-negative values order like unsigned integers).
-template <int U, bool GROUPED>
-__global__ __launch_bounds__(kThreads) void k_amax(const lpq_tensor* table, lpq_tensor one, ChunkMap map,
+template <int U, int TH, bool GROUPED>
+__global__ __launch_bounds__(TH) void k_amax(const lpq_tensor* table, lpq_tensor one, ChunkMap map,
                                                    float* group_amax) {
     const Work W = locate<GROUPED>(table, one, map);
     const lpq_tensor& d = W.d;
     const int64_t total = d.rows * d.cols;
-    const int64_t base = W.unit * chunk_elems<U>();
+    const int64_t base = W.unit * chunk_elems<U, TH>();
     const v4u* src = reinterpret_cast<const v4u*>(d.src);
     const int tid = threadIdx.x;
     uint32_t m = 0;
-    by_fullness<chunk_elems<U>()>(base, total, [&](auto full) {
+    by_fullness<chunk_elems<U, TH>()>(base, total, [&](auto full) {
         v4u v[U];   // vectors past the end read as zero
-        load_chunk<U, decltype(full)::value>(v, src, base, total);
+        load_chunk<U, decltype(full)::value, TH>(v, src, base, total);
 #pragma unroll
         for (int u = 0; u < U; u++) m = umax(m, absmax8_bits(v[u]));
     });
     m = wave_max(m);
-    __shared__ uint32_t part[kThreads / 64];
+    __shared__ uint32_t part[TH / 64];
     if ((tid & 63) == 0) part[tid >> 6] = m;
     __syncthreads();
     if (tid == 0) {
-        uint32_t w = umax(umax(part[0], part[1]), umax(part[2], part[3]));
+        uint32_t w = part[0];
+#pragma unroll
+        for (int k = 1; k < TH / 64; k++) w = umax(w, part[k]);
         atomicMax(reinterpret_cast<unsigned int*>(group_amax + (GROUPED ? d.group : 0)), w);
     }
 }
 
-template <int U, bool GROUPED, bool AHEAD = LPQ_NVQ_AHEAD != 0>
-__global__ __launch_bounds__(kThreads) void k_nvfp4_quant(const lpq_tensor* table, lpq_tensor one, ChunkMap map,
+template <int U, int TH, bool GROUPED, bool AHEAD = LPQ_NVQ_AHEAD != 0>
+__global__ __launch_bounds__(TH) void k_nvfp4_quant(const lpq_tensor* table, lpq_tensor one, ChunkMap map,
                                                           const float* group_amax, float* group_g) {
     const Work W = locate<GROUPED>(table, one, map);
     const lpq_tensor& d = W.d;
     const int64_t total = d.rows * d.cols;
-    const int64_t base = W.unit * chunk_elems<U>();
+    const int64_t base = W.unit * chunk_elems<U, TH>();
     const int gi = GROUPED ? d.group : 0;
     const GlobalScale G = global_scale(group_amax[gi], map.gdiv);
     const int tid = threadIdx.x;
@@ -655,15 +703,15 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_quant(const lpq_tensor* tabl
     uint32_t* dst = reinterpret_cast<uint32_t*>(d.dst);
     uint8_t* ssc = reinterpret_cast<uint8_t*>(d.scale);
 
-    by_fullness<chunk_elems<U>()>(base, total, [&](auto full) {
+    by_fullness<chunk_elems<U, TH>()>(base, total, [&](auto full) {
         constexpr bool FULL = decltype(full)::value;
         v4u v[U];
-        auto fetch = [&](int u) { v[u] = load_vec<FULL>(src, base, total, u); };
+        auto fetch = [&](int u) { v[u] = load_vec<TH, FULL>(src, base, total, u); };
         fetch_start<U, AHEAD>(fetch);
 #pragma unroll
         for (int u = 0; u < U; u++) {
             fetch_step<U, AHEAD>(u, fetch, v[u].x);
-            const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+            const int64_t e0 = base + (int64_t)(u * TH + tid) * 8;
             const F8 f = widen8(v[u]);
             const BlockScale B = block_scale(pair_max(absmax8_f32(f)), G);
             const uint32_t p = e2m1x8(f, B);
@@ -675,32 +723,32 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_quant(const lpq_tensor* tabl
     });
 }
 
-template <int U, bool GROUPED, bool AHEAD = LPQ_NVD_AHEAD != 0>
-__global__ __launch_bounds__(kThreads) void k_nvfp4_dequant(const lpq_tensor* table, lpq_tensor one, ChunkMap map,
+template <int U, int TH, bool GROUPED, bool AHEAD = LPQ_NVD_AHEAD != 0>
+__global__ __launch_bounds__(TH) void k_nvfp4_dequant(const lpq_tensor* table, lpq_tensor one, ChunkMap map,
                                                             const float* group_g) {
     const Work W = locate<GROUPED>(table, one, map);
     const lpq_tensor& d = W.d;
     const int64_t total = d.rows * d.cols;
-    const int64_t base = W.unit * chunk_elems<U>();
+    const int64_t base = W.unit * chunk_elems<U, TH>();
     const float g = group_g[GROUPED ? d.group : 0];
     const uint32_t* src = reinterpret_cast<const uint32_t*>(d.src);
     const uint8_t* ssc = reinterpret_cast<const uint8_t*>(d.scale);
     v4u* dst = reinterpret_cast<v4u*>(d.dst);
     const int tid = threadIdx.x;
 
-    by_fullness<chunk_elems<U>()>(base, total, [&](auto full) {
+    by_fullness<chunk_elems<U, TH>()>(base, total, [&](auto full) {
         constexpr bool FULL = decltype(full)::value;
         uint32_t p[U], sb[U];
         auto fetch = [&](int u) {
-            const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
-            p[u] = load_vec<FULL>(src, base, total, u);
+            const int64_t e0 = base + (int64_t)(u * TH + tid) * 8;
+            p[u] = load_vec<TH, FULL>(src, base, total, u);
             sb[u] = (FULL || e0 < total) ? load_u8(ssc + (e0 >> 4)) : 0u;
         };
         fetch_start<U, AHEAD>(fetch);
 #pragma unroll
         for (int u = 0; u < U; u++) {
             fetch_step<U, AHEAD>(u, fetch, p[u], sb[u]);
-            const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+            const int64_t e0 = base + (int64_t)(u * TH + tid) * 8;
             const float S = e4m3_to_f32(sb[u]) * g;
             const v4u o = e2m1x8_to_bf16(p[u], S);
             if (FULL || e0 < total) store<kNTS>(dst + (e0 >> 3), o);
@@ -708,27 +756,27 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_dequant(const lpq_tensor* ta
     });
 }
 
-template <int U, bool GROUPED, bool AHEAD = LPQ_QDQ_AHEAD != 0>
-__global__ __launch_bounds__(kThreads) void k_nvfp4_qdq(const lpq_tensor* table, lpq_tensor one, ChunkMap map,
+template <int U, int TH, bool GROUPED, bool AHEAD = LPQ_QDQ_AHEAD != 0>
+__global__ __launch_bounds__(TH) void k_nvfp4_qdq(const lpq_tensor* table, lpq_tensor one, ChunkMap map,
                                                         const float* group_amax) {
     const Work W = locate<GROUPED>(table, one, map);
     const lpq_tensor& d = W.d;
     const int64_t total = d.rows * d.cols;
-    const int64_t base = W.unit * chunk_elems<U>();
+    const int64_t base = W.unit * chunk_elems<U, TH>();
     const GlobalScale G = global_scale(group_amax[GROUPED ? d.group : 0], map.gdiv);
     const v4u* src = reinterpret_cast<const v4u*>(d.src);
     v4u* dst = reinterpret_cast<v4u*>(d.dst);
     const int tid = threadIdx.x;
 
-    by_fullness<chunk_elems<U>()>(base, total, [&](auto full) {
+    by_fullness<chunk_elems<U, TH>()>(base, total, [&](auto full) {
         constexpr bool FULL = decltype(full)::value;
         v4u v[U];
-        auto fetch = [&](int u) { v[u] = load_vec<FULL>(src, base, total, u); };
+        auto fetch = [&](int u) { v[u] = load_vec<TH, FULL>(src, base, total, u); };
         fetch_start<U, AHEAD>(fetch);
 #pragma unroll
         for (int u = 0; u < U; u++) {
             fetch_step<U, AHEAD>(u, fetch, v[u].x);
-            const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+            const int64_t e0 = base + (int64_t)(u * TH + tid) * 8;
             const F8 f = widen8(v[u]);
             const BlockScale B = block_scale(pair_max(absmax8_f32(f)), G);
             const v4u o = e2m1x8_to_bf16(e2m1x8(f, B), B.S);
@@ -831,25 +879,25 @@ __device__ __forceinline__ v4u int4x8_to_bf16(uint32_t p, float s) {
     return v4u{bf16x2(y[0], y[1]), bf16x2(y[2], y[3]), bf16x2(y[4], y[5]), bf16x2(y[6], y[7])};
 }
 
-template <int U, bool GROUPED, int G, bool AHEAD = LPQ_I4Q_AHEAD != 0>
-__global__ __launch_bounds__(kThreads) void k_int4_quant(const lpq_tensor* table, lpq_tensor one, ChunkMap map) {
+template <int U, int TH, bool GROUPED, int G, bool AHEAD = LPQ_I4Q_AHEAD != 0>
+__global__ __launch_bounds__(TH) void k_int4_quant(const lpq_tensor* table, lpq_tensor one, ChunkMap map) {
     const Work W = locate<GROUPED>(table, one, map);
     const lpq_tensor& d = W.d;
     const int64_t total = d.rows * d.cols;
-    const int64_t base = W.unit * chunk_elems<U>();
+    const int64_t base = W.unit * chunk_elems<U, TH>();
     const v4u* src = reinterpret_cast<const v4u*>(d.src);
     uint32_t* dst = reinterpret_cast<uint32_t*>(d.dst);
     float* scale = reinterpret_cast<float*>(d.scale);
     const int tid = threadIdx.x;
-    by_fullness<chunk_elems<U>()>(base, total, [&](auto full) {
+    by_fullness<chunk_elems<U, TH>()>(base, total, [&](auto full) {
         constexpr bool FULL = decltype(full)::value;
         v4u v[U];
-        auto fetch = [&](int u) { v[u] = load_vec<FULL>(src, base, total, u); };
+        auto fetch = [&](int u) { v[u] = load_vec<TH, FULL>(src, base, total, u); };
         fetch_start<U, AHEAD>(fetch);
 #pragma unroll
         for (int u = 0; u < U; u++) {
             fetch_step<U, AHEAD>(u, fetch, v[u].x);
-            const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+            const int64_t e0 = base + (int64_t)(u * TH + tid) * 8;
             // G / 8 lanes are one group; groups never straddle the end (N % G == 0)
             const F8 f = widen8(v[u]);
             const Int4Scale I = int4_scale(int4_group_max<G>(absmax8_f32(f)));
@@ -862,54 +910,54 @@ __global__ __launch_bounds__(kThreads) void k_int4_quant(const lpq_tensor* table
     });
 }
 
-template <int U, bool GROUPED, int G, bool AHEAD = LPQ_I4D_AHEAD != 0>
-__global__ __launch_bounds__(kThreads) void k_int4_dequant(const lpq_tensor* table, lpq_tensor one, ChunkMap map) {
+template <int U, int TH, bool GROUPED, int G, bool AHEAD = LPQ_I4D_AHEAD != 0>
+__global__ __launch_bounds__(TH) void k_int4_dequant(const lpq_tensor* table, lpq_tensor one, ChunkMap map) {
     const Work W = locate<GROUPED>(table, one, map);
     const lpq_tensor& d = W.d;
     const int64_t total = d.rows * d.cols;
-    const int64_t base = W.unit * chunk_elems<U>();
+    const int64_t base = W.unit * chunk_elems<U, TH>();
     const uint32_t* src = reinterpret_cast<const uint32_t*>(d.src);
     const float* scale = reinterpret_cast<const float*>(d.scale);
     v4u* dst = reinterpret_cast<v4u*>(d.dst);
     const int tid = threadIdx.x;
-    by_fullness<chunk_elems<U>()>(base, total, [&](auto full) {
+    by_fullness<chunk_elems<U, TH>()>(base, total, [&](auto full) {
         constexpr bool FULL = decltype(full)::value;
         uint32_t p[U];
         float sc[U];
         auto fetch = [&](int u) {
-            const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
-            p[u] = load_vec<FULL>(src, base, total, u);
+            const int64_t e0 = base + (int64_t)(u * TH + tid) * 8;
+            p[u] = load_vec<TH, FULL>(src, base, total, u);
             sc[u] = (FULL || e0 < total) ? load<false>(scale + e0 / G) : 0.0f;
         };
         fetch_start<U, AHEAD>(fetch);
 #pragma unroll
         for (int u = 0; u < U; u++) {
             fetch_step<U, AHEAD>(u, fetch, p[u], __float_as_uint(sc[u]));
-            const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+            const int64_t e0 = base + (int64_t)(u * TH + tid) * 8;
             const v4u o = int4x8_to_bf16(p[u], sc[u]);
             if (FULL || e0 < total) store<kNTS>(dst + (e0 >> 3), o);
         }
     });
 }
 
-template <int U, bool GROUPED, int G, bool AHEAD = LPQ_I4QDQ_AHEAD != 0>
-__global__ __launch_bounds__(kThreads) void k_int4_qdq(const lpq_tensor* table, lpq_tensor one, ChunkMap map) {
+template <int U, int TH, bool GROUPED, int G, bool AHEAD = LPQ_I4QDQ_AHEAD != 0>
+__global__ __launch_bounds__(TH) void k_int4_qdq(const lpq_tensor* table, lpq_tensor one, ChunkMap map) {
     const Work W = locate<GROUPED>(table, one, map);
     const lpq_tensor& d = W.d;
     const int64_t total = d.rows * d.cols;
-    const int64_t base = W.unit * chunk_elems<U>();
+    const int64_t base = W.unit * chunk_elems<U, TH>();
     const v4u* src = reinterpret_cast<const v4u*>(d.src);
     v4u* dst = reinterpret_cast<v4u*>(d.dst);
     const int tid = threadIdx.x;
-    by_fullness<chunk_elems<U>()>(base, total, [&](auto full) {
+    by_fullness<chunk_elems<U, TH>()>(base, total, [&](auto full) {
         constexpr bool FULL = decltype(full)::value;
         v4u v[U];
-        auto fetch = [&](int u) { v[u] = load_vec<FULL>(src, base, total, u); };
+        auto fetch = [&](int u) { v[u] = load_vec<TH, FULL>(src, base, total, u); };
         fetch_start<U, AHEAD>(fetch);
 #pragma unroll
         for (int u = 0; u < U; u++) {
             fetch_step<U, AHEAD>(u, fetch, v[u].x);
-            const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 8;
+            const int64_t e0 = base + (int64_t)(u * TH + tid) * 8;
             const F8 f = widen8(v[u]);
             const v4u o = int4x8_qdq(f, int4_scale(int4_group_max<G>(absmax8_f32(f))));
             if (FULL || e0 < total) store<kNTS>(dst + (e0 >> 3), o);
@@ -1182,15 +1230,17 @@ __global__ __launch_bounds__(TT) void k_fp8blk_dequant(const lpq_tensor* table, 
 // index work are kept to 32-bit integer steps (the host limits M and N to
 // below 2^31), and full chunks run a straight-line body.
 
-template <int U>
-constexpr int64_t rq_chunk_elems() { return (int64_t)kThreads * 16 * U; }
+template <int U, int TH = kThreads>
+constexpr int64_t rq_chunk_elems() { return (int64_t)TH * 16 * U; }
 
-constexpr uint32_t kRqStep = kThreads * 16;   // elements between a lane's consecutive vectors
+constexpr int kMaxFlatThreads = 512;                    // the largest flat workgroup
+constexpr uint32_t kRqStepMax = kMaxFlatThreads * 16;   // the largest step between a lane's vectors
 
-// Walks the (row, column) of a lane's vectors and looks up their tile scales.
-template <int EV>
+// Walks the (row, column) of a lane's vectors (TH-thread workgroup, EV
+// elements per vector) and looks up their tile scales.
+template <int EV, int TH = kThreads>
 struct TileCursor {
-    static constexpr uint32_t kStep = kThreads * EV;   // elements between a lane's consecutive vectors
+    static constexpr uint32_t kStep = TH * EV;   // elements between a lane's consecutive vectors
     const float* scale;   // tile scales of the tensor
     uint32_t N, tn;       // columns, tiles per row
     uint32_t sr, sc;      // kStep = sr * N + sc
@@ -1215,7 +1265,7 @@ struct TileCursor {
             c0 -= N;
         }
         // the lane's offset from the origin: t < N + kStep < 2^32 and
-        // t / N < 4097, so the single-precision estimate is within one
+        // t / N <= kStep <= 8192, so the single-precision estimate is within one
         const uint32_t t = (uint32_t)c0 + threadIdx.x * (uint32_t)EV;
         uint32_t q = (uint32_t)((float)t * __builtin_amdgcn_rcpf((float)N));
         if (q * N > t) q -= 1;
@@ -1284,18 +1334,18 @@ __device__ __forceinline__ const float* tile_scales_of(const lpq_tensor& d) { re
 
 // Loads of a lane's U code vectors and their tile scales; with FULL every
 // vector is in range, else vectors past the end read as codes 0, scale 0.
-template <int U, bool FULL, typename D>
+template <int U, bool FULL, int TH, typename D>
 __device__ __forceinline__ void rq_load(v4u (&c)[U], float (&s)[U], const D& d, int64_t base, int64_t total) {
     const v4u* src = reinterpret_cast<const v4u*>(codes_of(d)) + base / 16 + threadIdx.x;
-    TileCursor<16> cur(tile_scales_of(d), d.cols, base);
+    TileCursor<16, TH> cur(tile_scales_of(d), d.cols, base);
 #pragma unroll
     for (int u = 0; u < U; u++) {
         if (FULL) {
-            c[u] = load<kNTL>(src + u * kThreads);
+            c[u] = load<kNTL>(src + u * TH);
             s[u] = load<false>(cur.ptr());
         } else {
-            const bool in = base + (int64_t)(u * kThreads + threadIdx.x) * 16 < total;
-            c[u] = in ? load<kNTL>(src + u * kThreads) : v4u{0u, 0u, 0u, 0u};
+            const bool in = base + (int64_t)(u * TH + threadIdx.x) * 16 < total;
+            c[u] = in ? load<kNTL>(src + u * TH) : v4u{0u, 0u, 0u, 0u};
             s[u] = in ? load<false>(cur.ptr()) : 0.0f;
         }
         cur.next();
@@ -1306,15 +1356,15 @@ __device__ __forceinline__ void rq_load(v4u (&c)[U], float (&s)[U], const D& d, 
 // fetch_start / fetch_step (all up front, or one step ahead of the work);
 // body(u, codes, scale) runs on each step.  Steps past the end read as codes 0,
 // scale 0.
-template <int U, bool FULL, bool AHEAD, typename D, typename Body>
+template <int U, bool FULL, bool AHEAD, int TH, typename D, typename Body>
 __device__ __forceinline__ void rq_stream(const D& d, int64_t base, int64_t total, Body&& body) {
     const v4u* src = reinterpret_cast<const v4u*>(codes_of(d)) + base / 16 + threadIdx.x;
-    TileCursor<16> cur(tile_scales_of(d), d.cols, base);
+    TileCursor<16, TH> cur(tile_scales_of(d), d.cols, base);
     v4u c[U];
     float s[U];
     auto fetch = [&](int u) {   // called for u = 0, 1, ... in order: the cursor walks along
-        const bool in = FULL || base + (int64_t)(u * kThreads + threadIdx.x) * 16 < total;
-        c[u] = in ? load<kNTL>(src + u * kThreads) : v4u{0u, 0u, 0u, 0u};
+        const bool in = FULL || base + (int64_t)(u * TH + threadIdx.x) * 16 < total;
+        c[u] = in ? load<kNTL>(src + u * TH) : v4u{0u, 0u, 0u, 0u};
         s[u] = in ? load<false>(cur.ptr()) : 0.0f;
         cur.next();
     };
@@ -1326,13 +1376,13 @@ __device__ __forceinline__ void rq_stream(const D& d, int64_t base, int64_t tota
     }
 }
 
-template <int U, bool FULL>
+template <int U, bool FULL, int TH>
 __device__ __forceinline__ void rq_mxfp8_body(const lpq_requant_tensor& d, int64_t base, int64_t total) {
     v4u* dst = reinterpret_cast<v4u*>(d.dst);
     uint8_t* esc = reinterpret_cast<uint8_t*>(d.dst_scale);
     const int tid = threadIdx.x;
-    rq_stream<U, FULL, LPQ_RQM_AHEAD != 0>(d, base, total, [&](int u, const v4u& c, float s) {
-        const int64_t e0 = base + (int64_t)(u * kThreads + tid) * 16;
+    rq_stream<U, FULL, LPQ_RQM_AHEAD != 0, TH>(d, base, total, [&](int u, const v4u& c, float s) {
+        const int64_t e0 = base + (int64_t)(u * TH + tid) * 16;
         const Y16 y = fp8blk_values16(c, s);
         // a pair of lanes is one 32-element block
         const uint32_t byte = mx_scale_byte(pair_max(y.amax));
@@ -1346,24 +1396,24 @@ __device__ __forceinline__ void rq_mxfp8_body(const lpq_requant_tensor& d, int64
     });
 }
 
-template <int U, bool GROUPED>
-__global__ __launch_bounds__(kThreads) void k_requant_mxfp8(const lpq_requant_tensor* table, lpq_requant_tensor one,
+template <int U, int TH, bool GROUPED>
+__global__ __launch_bounds__(TH) void k_requant_mxfp8(const lpq_requant_tensor* table, lpq_requant_tensor one,
                                                             ChunkMap map) {
     const WorkT<lpq_requant_tensor> W = locate<GROUPED>(table, one, map);
     const int64_t total = W.d.rows * W.d.cols;
-    const int64_t base = W.unit * rq_chunk_elems<U>();
-    if (base + rq_chunk_elems<U>() <= total) rq_mxfp8_body<U, true>(W.d, base, total);
-    else rq_mxfp8_body<U, false>(W.d, base, total);
+    const int64_t base = W.unit * rq_chunk_elems<U, TH>();
+    if (base + rq_chunk_elems<U, TH>() <= total) rq_mxfp8_body<U, true, TH>(W.d, base, total);
+    else rq_mxfp8_body<U, false, TH>(W.d, base, total);
 }
 
 // max |y| of each tensor's dequantized values, max-accumulated into its group
 // slot.  |fl(code * s)| = fl(|code| * |s|) and BF16 rounding is monotone, so
 // the maximum is taken over fl(max|code| * |s|) and rounded once.
-template <int U, bool FULL>
+template <int U, bool FULL, int TH>
 __device__ __forceinline__ float rq_amax_body(const lpq_requant_tensor& d, int64_t base, int64_t total) {
     v4u c[U];
     float s[U];
-    rq_load<U, FULL>(c, s, d, base, total);
+    rq_load<U, FULL, TH>(c, s, d, base, total);
     float m = 0.0f;
 #pragma unroll
     for (int u = 0; u < U; u++) {
@@ -1381,33 +1431,35 @@ __device__ __forceinline__ float rq_amax_body(const lpq_requant_tensor& d, int64
     return m;
 }
 
-template <int U, bool GROUPED>
-__global__ __launch_bounds__(kThreads) void k_requant_amax(const lpq_requant_tensor* table, lpq_requant_tensor one,
+template <int U, int TH, bool GROUPED>
+__global__ __launch_bounds__(TH) void k_requant_amax(const lpq_requant_tensor* table, lpq_requant_tensor one,
                                                            ChunkMap map, float* group_amax) {
     const WorkT<lpq_requant_tensor> W = locate<GROUPED>(table, one, map);
     const int64_t total = W.d.rows * W.d.cols;
-    const int64_t base = W.unit * rq_chunk_elems<U>();
+    const int64_t base = W.unit * rq_chunk_elems<U, TH>();
     const int tid = threadIdx.x;
-    const float m = base + rq_chunk_elems<U>() <= total ? rq_amax_body<U, true>(W.d, base, total)
-                                                        : rq_amax_body<U, false>(W.d, base, total);
+    const float m = base + rq_chunk_elems<U, TH>() <= total ? rq_amax_body<U, true, TH>(W.d, base, total)
+                                                        : rq_amax_body<U, false, TH>(W.d, base, total);
     uint32_t mb = (bf16x2(m, 0.0f) & 0xffffu) << 16;
     mb = wave_max(mb);
-    __shared__ uint32_t part[kThreads / 64];
+    __shared__ uint32_t part[TH / 64];
     if ((tid & 63) == 0) part[tid >> 6] = mb;
     __syncthreads();
     if (tid == 0) {
-        const uint32_t r = umax(umax(part[0], part[1]), umax(part[2], part[3]));
+        uint32_t r = part[0];
+#pragma unroll
+        for (int k = 1; k < TH / 64; k++) r = umax(r, part[k]);
         atomicMax(reinterpret_cast<unsigned int*>(group_amax + (GROUPED ? W.d.group : 0)), r);
     }
 }
 
-template <int U, bool FULL>
+template <int U, bool FULL, int TH>
 __device__ __forceinline__ void rq_nvfp4_body(const lpq_requant_tensor& d, int64_t base, int64_t total,
                                               const GlobalScale& G) {
     v2u* dst = reinterpret_cast<v2u*>(d.dst);
     uint8_t* ssc = reinterpret_cast<uint8_t*>(d.dst_scale);
-    rq_stream<U, FULL, LPQ_RQN_AHEAD != 0>(d, base, total, [&](int u, const v4u& c, float s) {
-        const int64_t e0 = base + (int64_t)(u * kThreads + threadIdx.x) * 16;
+    rq_stream<U, FULL, LPQ_RQN_AHEAD != 0, TH>(d, base, total, [&](int u, const v4u& c, float s) {
+        const int64_t e0 = base + (int64_t)(u * TH + threadIdx.x) * 16;
         const Y16 y = fp8blk_values16(c, s);
         // one lane is one 16-element block
         const BlockScale B = block_scale(y.amax, G);
@@ -1419,17 +1471,17 @@ __device__ __forceinline__ void rq_nvfp4_body(const lpq_requant_tensor& d, int64
     });
 }
 
-template <int U, bool GROUPED>
-__global__ __launch_bounds__(kThreads) void k_requant_nvfp4(const lpq_requant_tensor* table, lpq_requant_tensor one,
+template <int U, int TH, bool GROUPED>
+__global__ __launch_bounds__(TH) void k_requant_nvfp4(const lpq_requant_tensor* table, lpq_requant_tensor one,
                                                             ChunkMap map, const float* group_amax, float* group_g) {
     const WorkT<lpq_requant_tensor> W = locate<GROUPED>(table, one, map);
     const int64_t total = W.d.rows * W.d.cols;
-    const int64_t base = W.unit * rq_chunk_elems<U>();
+    const int64_t base = W.unit * rq_chunk_elems<U, TH>();
     const int gi = GROUPED ? W.d.group : 0;
     const GlobalScale G = global_scale(group_amax[gi], map.gdiv);
     if (W.unit == 0 && threadIdx.x == 0) group_g[gi] = G.g;   // same value from every member
-    if (base + rq_chunk_elems<U>() <= total) rq_nvfp4_body<U, true>(W.d, base, total, G);
-    else rq_nvfp4_body<U, false>(W.d, base, total, G);
+    if (base + rq_chunk_elems<U, TH>() <= total) rq_nvfp4_body<U, true, TH>(W.d, base, total, G);
+    else rq_nvfp4_body<U, false, TH>(W.d, base, total, G);
 }
 
 // Block-wise FP8 dequantization in the flat layout: used when N % 16 == 0 and
@@ -1438,16 +1490,16 @@ __global__ __launch_bounds__(kThreads) void k_requant_nvfp4(const lpq_requant_te
 // arithmetic as k_fp8blk_dequant: y = BF16(fl(code * s_tile)).
 // A lane takes 8 codes (8 bytes) per step so that its 16 output bytes make
 // each store instruction one contiguous span across the wave.
-template <int U, bool FULL, bool AHEAD>
+template <int U, bool FULL, bool AHEAD, int TH>
 __device__ __forceinline__ void fp8blk_dequant_flat_body(const lpq_tensor& d, int64_t base, int64_t total) {
     const v2u* src = reinterpret_cast<const v2u*>(d.src) + base / 8 + threadIdx.x;
     v4u* dst = reinterpret_cast<v4u*>(d.dst);
-    TileCursor<8> cur(reinterpret_cast<const float*>(d.scale), d.cols, base);
+    TileCursor<8, TH> cur(reinterpret_cast<const float*>(d.scale), d.cols, base);
     v2u c[U];
     float s[U];
     auto fetch = [&](int u) {   // called for u = 0, 1, ... in order: the cursor walks along
-        const bool in = FULL || base + (int64_t)(u * kThreads + threadIdx.x) * 8 < total;
-        c[u] = in ? load<kNTL>(src + u * kThreads) : v2u{0u, 0u};
+        const bool in = FULL || base + (int64_t)(u * TH + threadIdx.x) * 8 < total;
+        c[u] = in ? load<kNTL>(src + u * TH) : v2u{0u, 0u};
         s[u] = in ? load<false>(cur.ptr()) : 0.0f;
         cur.next();
     };
@@ -1455,7 +1507,7 @@ __device__ __forceinline__ void fp8blk_dequant_flat_body(const lpq_tensor& d, in
 #pragma unroll
     for (int u = 0; u < U; u++) {
         fetch_step<U, AHEAD>(u, fetch, c[u].x, __float_as_uint(s[u]));
-        const int64_t e0 = base + (int64_t)(u * kThreads + threadIdx.x) * 8;
+        const int64_t e0 = base + (int64_t)(u * TH + threadIdx.x) * 8;
         const float2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[u].x, false);
         const float2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[u].x, true);
         const float2_t e = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[u].y, false);
@@ -1467,18 +1519,18 @@ __device__ __forceinline__ void fp8blk_dequant_flat_body(const lpq_tensor& d, in
     }
 }
 
-template <int U>
-constexpr int64_t dqf_chunk_elems() { return (int64_t)kThreads * 8 * U; }
+template <int U, int TH = kThreads>
+constexpr int64_t dqf_chunk_elems() { return (int64_t)TH * 8 * U; }
 
-template <int U, bool GROUPED>
-__global__ __launch_bounds__(kThreads) void k_fp8blk_dequant_flat(const lpq_tensor* table, lpq_tensor one,
+template <int U, int TH, bool GROUPED>
+__global__ __launch_bounds__(TH) void k_fp8blk_dequant_flat(const lpq_tensor* table, lpq_tensor one,
                                                                   ChunkMap map) {
     const Work W = locate<GROUPED>(table, one, map);
     const int64_t total = W.d.rows * W.d.cols;
-    const int64_t base = W.unit * dqf_chunk_elems<U>();
+    const int64_t base = W.unit * dqf_chunk_elems<U, TH>();
     constexpr bool AHEAD = LPQ_DQF_AHEAD != 0;
-    if (base + dqf_chunk_elems<U>() <= total) fp8blk_dequant_flat_body<U, true, AHEAD>(W.d, base, total);
-    else fp8blk_dequant_flat_body<U, false, AHEAD>(W.d, base, total);
+    if (base + dqf_chunk_elems<U, TH>() <= total) fp8blk_dequant_flat_body<U, true, AHEAD, TH>(W.d, base, total);
+    else fp8blk_dequant_flat_body<U, false, AHEAD, TH>(W.d, base, total);
 }
 
 // Block-wise FP8 -> block-wise FP8, TW adjacent 128x128 tiles per workgroup:
@@ -1664,7 +1716,7 @@ lpq_status check_tensor(Kind k, const lpq_tensor& t, int32_t n_groups) {
         if (!aligned(k == FP8BLK_DQ ? t.dst : t.src, 2) || !aligned(t.scale, 4)) return LPQ_ERR_ALIGN;
         break;
     case FP8BLK_DQF:   // not a caller-visible kind: the flat layout's extra conditions
-        if (t.cols % 8 || t.rows >= (int64_t(1) << 31) || t.cols >= (int64_t(1) << 31) - kRqStep) return LPQ_ERR_SHAPE;
+        if (t.cols % 8 || t.rows >= (int64_t(1) << 31) || t.cols >= (int64_t(1) << 31) - kRqStepMax) return LPQ_ERR_SHAPE;
         if (!aligned(t.src, 8) || !aligned(t.dst, 16) || !aligned(t.scale, 4)) return LPQ_ERR_ALIGN;
         break;
     case MXFP8_Q:
@@ -1714,7 +1766,7 @@ lpq_status check_tensor(Kind k, const lpq_requant_tensor& t, int32_t n_groups) {
     if (t.reserved != 0) return LPQ_ERR_ARG;
     if (k == RQ_FP8) return aligned(t.src_scale, 4) && aligned(t.dst_scale, 4) ? LPQ_OK : LPQ_ERR_ALIGN;
     if (t.cols % (k == RQ_MX ? 32 : 16)) return LPQ_ERR_SHAPE;
-    if (t.rows >= (int64_t(1) << 31) || t.cols >= (int64_t(1) << 31) - kRqStep) return LPQ_ERR_SHAPE;
+    if (t.rows >= (int64_t(1) << 31) || t.cols >= (int64_t(1) << 31) - kRqStepMax) return LPQ_ERR_SHAPE;
     if (!aligned(t.src, 16) || !aligned(t.src_scale, 4)) return LPQ_ERR_ALIGN;
     if (k == RQ_MX && !aligned(t.dst, 16)) return LPQ_ERR_ALIGN;
     if (k == RQ_NV && !aligned(t.dst, 8)) return LPQ_ERR_ALIGN;
@@ -1730,20 +1782,20 @@ int64_t units(Kind k, const lpq_tensor& t) {
     case FP8BLK_QW:
         return ((t.rows + kTile - 1) / kTile) * ((t.cols + kTile * LPQ_TILEQ_WIDE_TW - 1) / (kTile * LPQ_TILEQ_WIDE_TW));
     case FP8BLK_DQ: return ((t.rows + kTile - 1) / kTile) * ((t.cols + kTile - 1) / kTile);
-    case FP8BLK_DQF: return (n + dqf_chunk_elems<LPQ_DQF_U>() - 1) / dqf_chunk_elems<LPQ_DQF_U>();
+    case FP8BLK_DQF: return (n + dqf_chunk_elems<LPQ_DQF_U, LPQ_DQF_T>() - 1) / dqf_chunk_elems<LPQ_DQF_U, LPQ_DQF_T>();
     case MXFP8_Q:
-    case MXFP8_QF: return (n + chunk_elems<LPQ_MXQ_U>() - 1) / chunk_elems<LPQ_MXQ_U>();
-    case MXFP8_DQ: return (n + chunk_elems<LPQ_MXD_U>() - 1) / chunk_elems<LPQ_MXD_U>();
-    case NV_AMAX: return (n + chunk_elems<LPQ_AMAX_U>() - 1) / chunk_elems<LPQ_AMAX_U>();
-    case NV_Q: return (n + chunk_elems<LPQ_NVQ_U>() - 1) / chunk_elems<LPQ_NVQ_U>();
-    case NV_DQ: return (n + chunk_elems<LPQ_NVD_U>() - 1) / chunk_elems<LPQ_NVD_U>();
-    case NV_QDQ: return (n + chunk_elems<LPQ_QDQ_U>() - 1) / chunk_elems<LPQ_QDQ_U>();
+    case MXFP8_QF: return (n + chunk_elems<LPQ_MXQ_U, LPQ_MXQ_T>() - 1) / chunk_elems<LPQ_MXQ_U, LPQ_MXQ_T>();
+    case MXFP8_DQ: return (n + chunk_elems<LPQ_MXD_U, LPQ_MXD_T>() - 1) / chunk_elems<LPQ_MXD_U, LPQ_MXD_T>();
+    case NV_AMAX: return (n + chunk_elems<LPQ_AMAX_U, LPQ_AMAX_T>() - 1) / chunk_elems<LPQ_AMAX_U, LPQ_AMAX_T>();
+    case NV_Q: return (n + chunk_elems<LPQ_NVQ_U, LPQ_NVQ_T>() - 1) / chunk_elems<LPQ_NVQ_U, LPQ_NVQ_T>();
+    case NV_DQ: return (n + chunk_elems<LPQ_NVD_U, LPQ_NVD_T>() - 1) / chunk_elems<LPQ_NVD_U, LPQ_NVD_T>();
+    case NV_QDQ: return (n + chunk_elems<LPQ_QDQ_U, LPQ_QDQ_T>() - 1) / chunk_elems<LPQ_QDQ_U, LPQ_QDQ_T>();
     case I4_Q32:
-    case I4_Q128: return (n + chunk_elems<LPQ_I4Q_U>() - 1) / chunk_elems<LPQ_I4Q_U>();
+    case I4_Q128: return (n + chunk_elems<LPQ_I4Q_U, LPQ_I4Q_T>() - 1) / chunk_elems<LPQ_I4Q_U, LPQ_I4Q_T>();
     case I4_DQ32:
-    case I4_DQ128: return (n + chunk_elems<LPQ_I4D_U>() - 1) / chunk_elems<LPQ_I4D_U>();
+    case I4_DQ128: return (n + chunk_elems<LPQ_I4D_U, LPQ_I4D_T>() - 1) / chunk_elems<LPQ_I4D_U, LPQ_I4D_T>();
     case I4_QDQ32:
-    case I4_QDQ128: return (n + chunk_elems<LPQ_I4QDQ_U>() - 1) / chunk_elems<LPQ_I4QDQ_U>();
+    case I4_QDQ128: return (n + chunk_elems<LPQ_I4QDQ_U, LPQ_I4QDQ_T>() - 1) / chunk_elems<LPQ_I4QDQ_U, LPQ_I4QDQ_T>();
     default: return 0;
     }
 }
@@ -1752,9 +1804,9 @@ int64_t units(Kind k, const lpq_requant_tensor& t) {
     const int64_t n = t.rows * t.cols;
     switch (k) {
     case RQ_FP8: return ((t.rows + kTile - 1) / kTile) * ((t.cols + kTile * LPQ_RQT_TW - 1) / (kTile * LPQ_RQT_TW));
-    case RQ_MX: return (n + rq_chunk_elems<LPQ_RQM_U>() - 1) / rq_chunk_elems<LPQ_RQM_U>();
-    case RQ_AMAX: return (n + rq_chunk_elems<LPQ_RQA_U>() - 1) / rq_chunk_elems<LPQ_RQA_U>();
-    case RQ_NV: return (n + rq_chunk_elems<LPQ_RQN_U>() - 1) / rq_chunk_elems<LPQ_RQN_U>();
+    case RQ_MX: return (n + rq_chunk_elems<LPQ_RQM_U, LPQ_RQM_T>() - 1) / rq_chunk_elems<LPQ_RQM_U, LPQ_RQM_T>();
+    case RQ_AMAX: return (n + rq_chunk_elems<LPQ_RQA_U, LPQ_RQA_T>() - 1) / rq_chunk_elems<LPQ_RQA_U, LPQ_RQA_T>();
+    case RQ_NV: return (n + rq_chunk_elems<LPQ_RQN_U, LPQ_RQN_T>() - 1) / rq_chunk_elems<LPQ_RQN_U, LPQ_RQN_T>();
     default: return 0;
     }
 }
@@ -1763,7 +1815,7 @@ constexpr int64_t kMaxGridX = 0x7fffffffLL;
 
 void dispatch(Kind k, dim3 grid, hipStream_t stream, const lpq_tensor* tab, const lpq_tensor& one, const ChunkMap& map,
               const float* fa, float* fb) {
-    const dim3 flat(kThreads), tileq(256 * LPQ_TILEQ_TW), tileqw(256 * LPQ_TILEQ_WIDE_TW), tiled(LPQ_TILED_THREADS);
+    const dim3 tileq(256 * LPQ_TILEQ_TW), tileqw(256 * LPQ_TILEQ_WIDE_TW), tiled(LPQ_TILED_THREADS);
     if (tab) {
         switch (k) {
         case FP8BLK_Q: hipLaunchKernelGGL((k_fp8blk_quant<LPQ_TILEQ_TW, true>), grid, tileq, 0, stream, tab, one, map); break;
@@ -1771,20 +1823,20 @@ void dispatch(Kind k, dim3 grid, hipStream_t stream, const lpq_tensor* tab, cons
             hipLaunchKernelGGL((k_fp8blk_quant<LPQ_TILEQ_WIDE_TW, true>), grid, tileqw, 0, stream, tab, one, map);
             break;
         case FP8BLK_DQ: hipLaunchKernelGGL((k_fp8blk_dequant<LPQ_TILED_THREADS, true>), grid, tiled, 0, stream, tab, one, map); break;
-        case FP8BLK_DQF: hipLaunchKernelGGL((k_fp8blk_dequant_flat<LPQ_DQF_U, true>), grid, flat, 0, stream, tab, one, map); break;
-        case MXFP8_Q: hipLaunchKernelGGL((k_mxfp8_quant<LPQ_MXQ_U, true>), grid, flat, 0, stream, tab, one, map); break;
-        case MXFP8_QF: hipLaunchKernelGGL((k_mxfp8_quant<LPQ_MXQ_U, true, true>), grid, flat, 0, stream, tab, one, map); break;
-        case MXFP8_DQ: hipLaunchKernelGGL((k_mxfp8_dequant<LPQ_MXD_U, true>), grid, flat, 0, stream, tab, one, map); break;
-        case NV_AMAX: hipLaunchKernelGGL((k_amax<LPQ_AMAX_U, true>), grid, flat, 0, stream, tab, one, map, fb); break;
-        case NV_Q: hipLaunchKernelGGL((k_nvfp4_quant<LPQ_NVQ_U, true>), grid, flat, 0, stream, tab, one, map, fa, fb); break;
-        case NV_DQ: hipLaunchKernelGGL((k_nvfp4_dequant<LPQ_NVD_U, true>), grid, flat, 0, stream, tab, one, map, fa); break;
-        case NV_QDQ: hipLaunchKernelGGL((k_nvfp4_qdq<LPQ_QDQ_U, true>), grid, flat, 0, stream, tab, one, map, fa); break;
-        case I4_Q32: hipLaunchKernelGGL((k_int4_quant<LPQ_I4Q_U, true, 32>), grid, flat, 0, stream, tab, one, map); break;
-        case I4_Q128: hipLaunchKernelGGL((k_int4_quant<LPQ_I4Q_U, true, 128>), grid, flat, 0, stream, tab, one, map); break;
-        case I4_DQ32: hipLaunchKernelGGL((k_int4_dequant<LPQ_I4D_U, true, 32>), grid, flat, 0, stream, tab, one, map); break;
-        case I4_DQ128: hipLaunchKernelGGL((k_int4_dequant<LPQ_I4D_U, true, 128>), grid, flat, 0, stream, tab, one, map); break;
-        case I4_QDQ32: hipLaunchKernelGGL((k_int4_qdq<LPQ_I4QDQ_U, true, 32>), grid, flat, 0, stream, tab, one, map); break;
-        case I4_QDQ128: hipLaunchKernelGGL((k_int4_qdq<LPQ_I4QDQ_U, true, 128>), grid, flat, 0, stream, tab, one, map); break;
+        case FP8BLK_DQF: hipLaunchKernelGGL((k_fp8blk_dequant_flat<LPQ_DQF_U, LPQ_DQF_T, true>), grid, dim3(LPQ_DQF_T), 0, stream, tab, one, map); break;
+        case MXFP8_Q: hipLaunchKernelGGL((k_mxfp8_quant<LPQ_MXQ_U, LPQ_MXQ_T, true>), grid, dim3(LPQ_MXQ_T), 0, stream, tab, one, map); break;
+        case MXFP8_QF: hipLaunchKernelGGL((k_mxfp8_quant<LPQ_MXQ_U, LPQ_MXQ_T, true, true>), grid, dim3(LPQ_MXQ_T), 0, stream, tab, one, map); break;
+        case MXFP8_DQ: hipLaunchKernelGGL((k_mxfp8_dequant<LPQ_MXD_U, LPQ_MXD_T, true>), grid, dim3(LPQ_MXD_T), 0, stream, tab, one, map); break;
+        case NV_AMAX: hipLaunchKernelGGL((k_amax<LPQ_AMAX_U, LPQ_AMAX_T, true>), grid, dim3(LPQ_AMAX_T), 0, stream, tab, one, map, fb); break;
+        case NV_Q: hipLaunchKernelGGL((k_nvfp4_quant<LPQ_NVQ_U, LPQ_NVQ_T, true>), grid, dim3(LPQ_NVQ_T), 0, stream, tab, one, map, fa, fb); break;
+        case NV_DQ: hipLaunchKernelGGL((k_nvfp4_dequant<LPQ_NVD_U, LPQ_NVD_T, true>), grid, dim3(LPQ_NVD_T), 0, stream, tab, one, map, fa); break;
+        case NV_QDQ: hipLaunchKernelGGL((k_nvfp4_qdq<LPQ_QDQ_U, LPQ_QDQ_T, true>), grid, dim3(LPQ_QDQ_T), 0, stream, tab, one, map, fa); break;
+        case I4_Q32: hipLaunchKernelGGL((k_int4_quant<LPQ_I4Q_U, LPQ_I4Q_T, true, 32>), grid, dim3(LPQ_I4Q_T), 0, stream, tab, one, map); break;
+        case I4_Q128: hipLaunchKernelGGL((k_int4_quant<LPQ_I4Q_U, LPQ_I4Q_T, true, 128>), grid, dim3(LPQ_I4Q_T), 0, stream, tab, one, map); break;
+        case I4_DQ32: hipLaunchKernelGGL((k_int4_dequant<LPQ_I4D_U, LPQ_I4D_T, true, 32>), grid, dim3(LPQ_I4D_T), 0, stream, tab, one, map); break;
+        case I4_DQ128: hipLaunchKernelGGL((k_int4_dequant<LPQ_I4D_U, LPQ_I4D_T, true, 128>), grid, dim3(LPQ_I4D_T), 0, stream, tab, one, map); break;
+        case I4_QDQ32: hipLaunchKernelGGL((k_int4_qdq<LPQ_I4QDQ_U, LPQ_I4QDQ_T, true, 32>), grid, dim3(LPQ_I4QDQ_T), 0, stream, tab, one, map); break;
+        case I4_QDQ128: hipLaunchKernelGGL((k_int4_qdq<LPQ_I4QDQ_U, LPQ_I4QDQ_T, true, 128>), grid, dim3(LPQ_I4QDQ_T), 0, stream, tab, one, map); break;
         default: break;
         }
     } else {
@@ -1794,20 +1846,20 @@ void dispatch(Kind k, dim3 grid, hipStream_t stream, const lpq_tensor* tab, cons
             hipLaunchKernelGGL((k_fp8blk_quant<LPQ_TILEQ_WIDE_TW, false>), grid, tileqw, 0, stream, tab, one, map);
             break;
         case FP8BLK_DQ: hipLaunchKernelGGL((k_fp8blk_dequant<LPQ_TILED_THREADS, false>), grid, tiled, 0, stream, tab, one, map); break;
-        case FP8BLK_DQF: hipLaunchKernelGGL((k_fp8blk_dequant_flat<LPQ_DQF_U, false>), grid, flat, 0, stream, tab, one, map); break;
-        case MXFP8_Q: hipLaunchKernelGGL((k_mxfp8_quant<LPQ_MXQ_U, false>), grid, flat, 0, stream, tab, one, map); break;
-        case MXFP8_QF: hipLaunchKernelGGL((k_mxfp8_quant<LPQ_MXQ_U, false, true>), grid, flat, 0, stream, tab, one, map); break;
-        case MXFP8_DQ: hipLaunchKernelGGL((k_mxfp8_dequant<LPQ_MXD_U, false>), grid, flat, 0, stream, tab, one, map); break;
-        case NV_AMAX: hipLaunchKernelGGL((k_amax<LPQ_AMAX_U, false>), grid, flat, 0, stream, tab, one, map, fb); break;
-        case NV_Q: hipLaunchKernelGGL((k_nvfp4_quant<LPQ_NVQ_U, false>), grid, flat, 0, stream, tab, one, map, fa, fb); break;
-        case NV_DQ: hipLaunchKernelGGL((k_nvfp4_dequant<LPQ_NVD_U, false>), grid, flat, 0, stream, tab, one, map, fa); break;
-        case NV_QDQ: hipLaunchKernelGGL((k_nvfp4_qdq<LPQ_QDQ_U, false>), grid, flat, 0, stream, tab, one, map, fa); break;
-        case I4_Q32: hipLaunchKernelGGL((k_int4_quant<LPQ_I4Q_U, false, 32>), grid, flat, 0, stream, tab, one, map); break;
-        case I4_Q128: hipLaunchKernelGGL((k_int4_quant<LPQ_I4Q_U, false, 128>), grid, flat, 0, stream, tab, one, map); break;
-        case I4_DQ32: hipLaunchKernelGGL((k_int4_dequant<LPQ_I4D_U, false, 32>), grid, flat, 0, stream, tab, one, map); break;
-        case I4_DQ128: hipLaunchKernelGGL((k_int4_dequant<LPQ_I4D_U, false, 128>), grid, flat, 0, stream, tab, one, map); break;
-        case I4_QDQ32: hipLaunchKernelGGL((k_int4_qdq<LPQ_I4QDQ_U, false, 32>), grid, flat, 0, stream, tab, one, map); break;
-        case I4_QDQ128: hipLaunchKernelGGL((k_int4_qdq<LPQ_I4QDQ_U, false, 128>), grid, flat, 0, stream, tab, one, map); break;
+        case FP8BLK_DQF: hipLaunchKernelGGL((k_fp8blk_dequant_flat<LPQ_DQF_U, LPQ_DQF_T, false>), grid, dim3(LPQ_DQF_T), 0, stream, tab, one, map); break;
+        case MXFP8_Q: hipLaunchKernelGGL((k_mxfp8_quant<LPQ_MXQ_U, LPQ_MXQ_T, false>), grid, dim3(LPQ_MXQ_T), 0, stream, tab, one, map); break;
+        case MXFP8_QF: hipLaunchKernelGGL((k_mxfp8_quant<LPQ_MXQ_U, LPQ_MXQ_T, false, true>), grid, dim3(LPQ_MXQ_T), 0, stream, tab, one, map); break;
+        case MXFP8_DQ: hipLaunchKernelGGL((k_mxfp8_dequant<LPQ_MXD_U, LPQ_MXD_T, false>), grid, dim3(LPQ_MXD_T), 0, stream, tab, one, map); break;
+        case NV_AMAX: hipLaunchKernelGGL((k_amax<LPQ_AMAX_U, LPQ_AMAX_T, false>), grid, dim3(LPQ_AMAX_T), 0, stream, tab, one, map, fb); break;
+        case NV_Q: hipLaunchKernelGGL((k_nvfp4_quant<LPQ_NVQ_U, LPQ_NVQ_T, false>), grid, dim3(LPQ_NVQ_T), 0, stream, tab, one, map, fa, fb); break;
+        case NV_DQ: hipLaunchKernelGGL((k_nvfp4_dequant<LPQ_NVD_U, LPQ_NVD_T, false>), grid, dim3(LPQ_NVD_T), 0, stream, tab, one, map, fa); break;
+        case NV_QDQ: hipLaunchKernelGGL((k_nvfp4_qdq<LPQ_QDQ_U, LPQ_QDQ_T, false>), grid, dim3(LPQ_QDQ_T), 0, stream, tab, one, map, fa); break;
+        case I4_Q32: hipLaunchKernelGGL((k_int4_quant<LPQ_I4Q_U, LPQ_I4Q_T, false, 32>), grid, dim3(LPQ_I4Q_T), 0, stream, tab, one, map); break;
+        case I4_Q128: hipLaunchKernelGGL((k_int4_quant<LPQ_I4Q_U, LPQ_I4Q_T, false, 128>), grid, dim3(LPQ_I4Q_T), 0, stream, tab, one, map); break;
+        case I4_DQ32: hipLaunchKernelGGL((k_int4_dequant<LPQ_I4D_U, LPQ_I4D_T, false, 32>), grid, dim3(LPQ_I4D_T), 0, stream, tab, one, map); break;
+        case I4_DQ128: hipLaunchKernelGGL((k_int4_dequant<LPQ_I4D_U, LPQ_I4D_T, false, 128>), grid, dim3(LPQ_I4D_T), 0, stream, tab, one, map); break;
+        case I4_QDQ32: hipLaunchKernelGGL((k_int4_qdq<LPQ_I4QDQ_U, LPQ_I4QDQ_T, false, 32>), grid, dim3(LPQ_I4QDQ_T), 0, stream, tab, one, map); break;
+        case I4_QDQ128: hipLaunchKernelGGL((k_int4_qdq<LPQ_I4QDQ_U, LPQ_I4QDQ_T, false, 128>), grid, dim3(LPQ_I4QDQ_T), 0, stream, tab, one, map); break;
         default: break;
         }
     }
@@ -1815,21 +1867,21 @@ void dispatch(Kind k, dim3 grid, hipStream_t stream, const lpq_tensor* tab, cons
 
 void dispatch(Kind k, dim3 grid, hipStream_t stream, const lpq_requant_tensor* tab, const lpq_requant_tensor& one,
               const ChunkMap& map, const float* fa, float* fb) {
-    const dim3 flat(kThreads), tile(256 * LPQ_RQT_TW);
+    const dim3 tile(256 * LPQ_RQT_TW);
     if (tab) {
         switch (k) {
         case RQ_FP8: hipLaunchKernelGGL((k_requant_fp8blk<LPQ_RQT_TW, true>), grid, tile, 0, stream, tab, one, map); break;
-        case RQ_MX: hipLaunchKernelGGL((k_requant_mxfp8<LPQ_RQM_U, true>), grid, flat, 0, stream, tab, one, map); break;
-        case RQ_AMAX: hipLaunchKernelGGL((k_requant_amax<LPQ_RQA_U, true>), grid, flat, 0, stream, tab, one, map, fb); break;
-        case RQ_NV: hipLaunchKernelGGL((k_requant_nvfp4<LPQ_RQN_U, true>), grid, flat, 0, stream, tab, one, map, fa, fb); break;
+        case RQ_MX: hipLaunchKernelGGL((k_requant_mxfp8<LPQ_RQM_U, LPQ_RQM_T, true>), grid, dim3(LPQ_RQM_T), 0, stream, tab, one, map); break;
+        case RQ_AMAX: hipLaunchKernelGGL((k_requant_amax<LPQ_RQA_U, LPQ_RQA_T, true>), grid, dim3(LPQ_RQA_T), 0, stream, tab, one, map, fb); break;
+        case RQ_NV: hipLaunchKernelGGL((k_requant_nvfp4<LPQ_RQN_U, LPQ_RQN_T, true>), grid, dim3(LPQ_RQN_T), 0, stream, tab, one, map, fa, fb); break;
         default: break;
         }
     } else {
         switch (k) {
         case RQ_FP8: hipLaunchKernelGGL((k_requant_fp8blk<LPQ_RQT_TW, false>), grid, tile, 0, stream, tab, one, map); break;
-        case RQ_MX: hipLaunchKernelGGL((k_requant_mxfp8<LPQ_RQM_U, false>), grid, flat, 0, stream, tab, one, map); break;
-        case RQ_AMAX: hipLaunchKernelGGL((k_requant_amax<LPQ_RQA_U, false>), grid, flat, 0, stream, tab, one, map, fb); break;
-        case RQ_NV: hipLaunchKernelGGL((k_requant_nvfp4<LPQ_RQN_U, false>), grid, flat, 0, stream, tab, one, map, fa, fb); break;
+        case RQ_MX: hipLaunchKernelGGL((k_requant_mxfp8<LPQ_RQM_U, LPQ_RQM_T, false>), grid, dim3(LPQ_RQM_T), 0, stream, tab, one, map); break;
+        case RQ_AMAX: hipLaunchKernelGGL((k_requant_amax<LPQ_RQA_U, LPQ_RQA_T, false>), grid, dim3(LPQ_RQA_T), 0, stream, tab, one, map, fb); break;
+        case RQ_NV: hipLaunchKernelGGL((k_requant_nvfp4<LPQ_RQN_U, LPQ_RQN_T, false>), grid, dim3(LPQ_RQN_T), 0, stream, tab, one, map, fa, fb); break;
         default: break;
         }
     }
