@@ -403,7 +403,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the codecs need no cross-GPU exchange on this path "
-              "(sharding is described in DESIGN.md); run it with --gpus 1.", file=sys.stderr)
+              "(each GPU would run the same kernels on its own share of the tensors); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -31,7 +31,7 @@
  *  [PR503] vime pull request 503 review: fake QAT requires exact
  *          round-to-nearest numerics (no fast math).
  *
- * Readings where the pages are silent (each is listed in the design doc):
+ * Readings where the pages are silent:
  *  - every rounding is round-to-nearest, ties-to-even (the "exact RN" rule);
  *  - FP8 block scale s = fl(amax / 448), stored as the dequant multiplier;
  *  - MXFP8 exponent: smallest e with amax <= 448 * 2^e, clamped to e >= -127;
@@ -413,7 +413,7 @@ OC_API float oc_observer_update(int kind, float c, float* state, const uint16_t*
  * Moonlight-16B-A3B, Qwen3-30B-A3B and Qwen3-235B-A22B, 32 for
  * Kimi-K2-Thinking) and that QAT trains through a straight-through
  * estimator, whose forward pass is quantize then dequantize.  Readings (the
- * plainest ones, each listed in the design doc):
+ * plainest ones):
  *  - groups run along a row (the GEMM reduction dimension), as the other
  *    block formats' blocks do; N % G == 0;
  *  - symmetric: s = fl(amax / 7), so the group's largest magnitude maps to
