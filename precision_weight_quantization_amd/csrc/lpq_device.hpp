@@ -111,6 +111,17 @@ __device__ __forceinline__ uint32_t bf16x2(float a, float b) {
 // condition for rare slow paths).
 __device__ __forceinline__ bool any_lane(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
+// A pointer the caller knows to be wave-uniform, pinned to scalar registers:
+// lane addresses formed from it are the scalar base plus a 32-bit lane offset
+// (global_load's saddr form) instead of a 64-bit address per lane.
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    return (T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Maximum of two non-negative binary32 values through their bit patterns.
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 

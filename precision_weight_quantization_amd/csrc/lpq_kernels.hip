@@ -147,8 +147,9 @@ namespace {
 #define LPQ_FLAT_THREADS 256
 #endif
 // Workgroup size of each flat kernel (64 to 512, a multiple of 64), measured
-// per kernel: the light encoders and the QDQs run best with 128 threads, the
-// NVFP4 and INT4 decoders and the INT4 encoder with 512, the rest with 256.
+// per kernel: the NVFP4 encoder runs best with one wave, MXFP8 encoding and the
+// QDQs with 128 threads, the NVFP4 and INT4 decoders and the INT4 encoder with
+// 512, the rest with 256.
 #ifndef LPQ_MXQ_T
 #define LPQ_MXQ_T 128
 #endif
@@ -159,7 +160,7 @@ namespace {
 #define LPQ_AMAX_T LPQ_FLAT_THREADS
 #endif
 #ifndef LPQ_NVQ_T
-#define LPQ_NVQ_T LPQ_FLAT_THREADS
+#define LPQ_NVQ_T 64
 #endif
 #ifndef LPQ_NVD_T
 #define LPQ_NVD_T 512
@@ -194,8 +195,16 @@ constexpr bool kNTL = LPQ_NTL != 0;
 constexpr bool kNTS = LPQ_NTS != 0;
 constexpr int kMaxSeg = 8;               // segments per launch (longer lists are split)
 
+constexpr int kMaxFlatThreads = 512;   // the largest flat workgroup
+
+// Elements of one flat work unit.  Whole waves per workgroup keep every chunk
+// origin a multiple of 512 elements, which the kernels' split of a lane's
+// address into a uniform chunk origin plus a lane offset relies on.
 template <int U, int TH = kThreads>
-constexpr int64_t chunk_elems() { return (int64_t)TH * 8 * U; }
+constexpr int64_t chunk_elems() {
+    static_assert(TH % 64 == 0 && TH >= 64 && TH <= kMaxFlatThreads, "whole waves, at most kMaxFlatThreads");
+    return (int64_t)TH * 8 * U;
+}
 
 // Loads the lane's U vectors of a flat chunk of a TH-thread workgroup: lane t
 // of vector u holds the EV elements starting at base + (u * TH + t) * EV.  A
@@ -472,6 +481,10 @@ struct BlockScale {
     bool maybe_tiny;   // wave-uniform: some S of the group could be tiny
 };
 
+// LARGE: the caller has established G.large (a group-uniform fact), so neither g
+// nor any block multiplier is pre-scaled and the pre-scaling selects drop out.
+// LARGE = false is correct for every G.
+template <bool LARGE = false>
 __device__ __forceinline__ BlockScale block_scale(uint32_t bmax_bits, const GlobalScale& G) {
     BlockScale B;
     const float b = __uint_as_float(bmax_bits);
@@ -483,13 +496,16 @@ __device__ __forceinline__ BlockScale block_scale(uint32_t bmax_bits, const Glob
         __asm__ volatile("" : "+v"(bb));   // an empty barrier: keeps the long division inside the branch
         if (bb < 0x1p-100f) t6 = bb / 6.0f;
     }
-    const float t = G.tiny ? t6 * kPreScale : t6;           // group-uniform pre-scaling
-    const float u = quot_rn(t, G.gd, G.rg);                  // fl(fl(b / 6) / g)
+    const float t = (!LARGE && G.tiny) ? t6 * kPreScale : t6;   // group-uniform pre-scaling
+    const float u = quot_rn(t, G.gd, G.rg);                      // fl(fl(b / 6) / g)
     const float uc = __builtin_amdgcn_fmed3f(u, -kE4M3Max, kE4M3Max);
-    B.code = G.g > 0.0f ? ((uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(uc, 0.0f, 0, false) & 0xffu) : 0u;
+    // the conversion writes the low 16 bits (the code, then E4M3(0) = 0) and keeps
+    // the rest of its last operand, here the dead bits of b
+    const uint32_t c8 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(uc, 0.0f, (int)bmax_bits, false) & 0xffu;
+    B.code = (LARGE || G.g > 0.0f) ? c8 : 0u;
     B.S = e4m3_to_f32(B.code) * G.g;
-    B.maybe_tiny = !G.large;
-    if (G.large) {   // group-uniform: no block multiplier is tiny
+    B.maybe_tiny = !LARGE && !G.large;
+    if (LARGE || G.large) {   // group-uniform: no block multiplier is tiny
         B.xpre = 1.0f;
         B.Sd = B.S;
     } else {
@@ -699,28 +715,42 @@ __global__ __launch_bounds__(TH) void k_nvfp4_quant(const lpq_tensor* table, lpq
     const GlobalScale G = global_scale(group_amax[gi], map.gdiv);
     const int tid = threadIdx.x;
     if (W.unit == 0 && tid == 0) group_g[gi] = G.g;   // same value from every member
-    const v4u* src = reinterpret_cast<const v4u*>(d.src);
-    uint32_t* dst = reinterpret_cast<uint32_t*>(d.dst);
-    uint8_t* ssc = reinterpret_cast<uint8_t*>(d.scale);
+    // the chunk's origins (uniform); a lane's vector i = u * TH + tid is addressed
+    // with a 32-bit offset from them
+    const v4u* src = reinterpret_cast<const v4u*>(d.src) + base / 8;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(d.dst) + base / 8;
+    uint8_t* ssc = reinterpret_cast<uint8_t*>(d.scale) + base / 16;
+    const int64_t left = total - base;   // elements from the chunk origin to the end
 
-    by_fullness<chunk_elems<U, TH>()>(base, total, [&](auto full) {
-        constexpr bool FULL = decltype(full)::value;
+    auto run = [&](auto full, auto large) {
+        constexpr bool FULL = decltype(full)::value, LARGE = decltype(large)::value;
+        auto in = [&](int i) { return FULL || (int64_t)i * 8 < left; };
         v4u v[U];
-        auto fetch = [&](int u) { v[u] = load_vec<TH, FULL>(src, base, total, u); };
+        auto fetch = [&](int u) {
+            const int i = u * TH + tid;
+            v[u] = in(i) ? load<kNTL>(uniform_ptr(src + u * TH) + tid) : v4u{};
+        };
         fetch_start<U, AHEAD>(fetch);
 #pragma unroll
         for (int u = 0; u < U; u++) {
             fetch_step<U, AHEAD>(u, fetch, v[u].x);
-            const int64_t e0 = base + (int64_t)(u * TH + tid) * 8;
+            const int i = u * TH + tid;
             const F8 f = widen8(v[u]);
-            const BlockScale B = block_scale(pair_max(absmax8_f32(f)), G);
+            const BlockScale B = block_scale<LARGE>(pair_max(absmax8_f32(f)), G);
             const uint32_t p = e2m1x8(f, B);
-            if (FULL || e0 < total) {
-                store<kNTS>(dst + (e0 >> 3), p);
-                if ((tid & 1) == 0) store_u8(ssc + (e0 >> 4), B.code);
+            if (in(i)) {
+                store<kNTS>(dst + i, p);
+                if ((tid & 1) == 0) store_u8(ssc + u * (TH / 2) + (tid >> 1), B.code);
             }
         }
-    });
+    };
+    const bool full = base + chunk_elems<U, TH>() <= total;   // uniform, as is G.large
+    if (full) {
+        if (G.large) run(Full<true>{}, Full<true>{});
+        else run(Full<true>{}, Full<false>{});
+    } else {
+        run(Full<false>{}, Full<false>{});
+    }
 }
 
 template <int U, int TH, bool GROUPED, bool AHEAD = LPQ_NVD_AHEAD != 0>
@@ -764,25 +794,39 @@ __global__ __launch_bounds__(TH) void k_nvfp4_qdq(const lpq_tensor* table, lpq_t
     const int64_t total = d.rows * d.cols;
     const int64_t base = W.unit * chunk_elems<U, TH>();
     const GlobalScale G = global_scale(group_amax[GROUPED ? d.group : 0], map.gdiv);
-    const v4u* src = reinterpret_cast<const v4u*>(d.src);
-    v4u* dst = reinterpret_cast<v4u*>(d.dst);
     const int tid = threadIdx.x;
+    // the chunk's origins (uniform); a lane's vector i = u * TH + tid is addressed
+    // with a 32-bit offset from them
+    const v4u* src = reinterpret_cast<const v4u*>(d.src) + base / 8;
+    v4u* dst = reinterpret_cast<v4u*>(d.dst) + base / 8;
+    const int64_t left = total - base;   // elements from the chunk origin to the end
 
-    by_fullness<chunk_elems<U, TH>()>(base, total, [&](auto full) {
-        constexpr bool FULL = decltype(full)::value;
+    auto run = [&](auto full, auto large) {
+        constexpr bool FULL = decltype(full)::value, LARGE = decltype(large)::value;
+        auto in = [&](int i) { return FULL || (int64_t)i * 8 < left; };
         v4u v[U];
-        auto fetch = [&](int u) { v[u] = load_vec<TH, FULL>(src, base, total, u); };
+        auto fetch = [&](int u) {
+            const int i = u * TH + tid;
+            v[u] = in(i) ? load<kNTL>(uniform_ptr(src + u * TH) + tid) : v4u{};
+        };
         fetch_start<U, AHEAD>(fetch);
 #pragma unroll
         for (int u = 0; u < U; u++) {
             fetch_step<U, AHEAD>(u, fetch, v[u].x);
-            const int64_t e0 = base + (int64_t)(u * TH + tid) * 8;
+            const int i = u * TH + tid;
             const F8 f = widen8(v[u]);
-            const BlockScale B = block_scale(pair_max(absmax8_f32(f)), G);
+            const BlockScale B = block_scale<LARGE>(pair_max(absmax8_f32(f)), G);
             const v4u o = e2m1x8_to_bf16(e2m1x8(f, B), B.S);
-            if (FULL || e0 < total) store<kNTS>(dst + (e0 >> 3), o);
+            if (in(i)) store<kNTS>(uniform_ptr(dst + u * TH) + tid, o);
         }
-    });
+    };
+    const bool full = base + chunk_elems<U, TH>() <= total;   // uniform, as is G.large
+    if (full) {
+        if (G.large) run(Full<true>{}, Full<true>{});
+        else run(Full<true>{}, Full<false>{});
+    } else {
+        run(Full<false>{}, Full<false>{});
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1231,9 +1275,11 @@ __global__ __launch_bounds__(TT) void k_fp8blk_dequant(const lpq_tensor* table, 
 // below 2^31), and full chunks run a straight-line body.
 
 template <int U, int TH = kThreads>
-constexpr int64_t rq_chunk_elems() { return (int64_t)TH * 16 * U; }
+constexpr int64_t rq_chunk_elems() {
+    static_assert(TH % 64 == 0 && TH >= 64 && TH <= kMaxFlatThreads, "whole waves, at most kMaxFlatThreads");
+    return (int64_t)TH * 16 * U;
+}
 
-constexpr int kMaxFlatThreads = 512;                    // the largest flat workgroup
 constexpr uint32_t kRqStepMax = kMaxFlatThreads * 16;   // the largest step between a lane's vectors
 
 // Walks the (row, column) of a lane's vectors (TH-thread workgroup, EV
@@ -1453,20 +1499,21 @@ __global__ __launch_bounds__(TH) void k_requant_amax(const lpq_requant_tensor* t
     }
 }
 
-template <int U, bool FULL, int TH>
+template <int U, bool FULL, bool LARGE, int TH>
 __device__ __forceinline__ void rq_nvfp4_body(const lpq_requant_tensor& d, int64_t base, int64_t total,
                                               const GlobalScale& G) {
-    v2u* dst = reinterpret_cast<v2u*>(d.dst);
-    uint8_t* ssc = reinterpret_cast<uint8_t*>(d.dst_scale);
+    // the chunk's origins (uniform): one 8-byte code word and one scale byte per lane and step
+    v2u* dst = reinterpret_cast<v2u*>(d.dst) + base / 16;
+    uint8_t* ssc = reinterpret_cast<uint8_t*>(d.dst_scale) + base / 16;
     rq_stream<U, FULL, LPQ_RQN_AHEAD != 0, TH>(d, base, total, [&](int u, const v4u& c, float s) {
-        const int64_t e0 = base + (int64_t)(u * TH + threadIdx.x) * 16;
+        const int i = u * TH + threadIdx.x;
         const Y16 y = fp8blk_values16(c, s);
         // one lane is one 16-element block
-        const BlockScale B = block_scale(y.amax, G);
+        const BlockScale B = block_scale<LARGE>(y.amax, G);
         const v2u p = v2u{e2m1x8(y.lo, B), e2m1x8(y.hi, B)};
-        if (FULL || e0 < total) {
-            store<kNTS>(dst + (e0 >> 4), p);
-            store_u8(ssc + (e0 >> 4), B.code);
+        if (FULL || base + (int64_t)i * 16 < total) {
+            store<kNTS>(dst + i, p);
+            store_u8(ssc + i, B.code);
         }
     });
 }
@@ -1480,8 +1527,12 @@ __global__ __launch_bounds__(TH) void k_requant_nvfp4(const lpq_requant_tensor* 
     const int gi = GROUPED ? W.d.group : 0;
     const GlobalScale G = global_scale(group_amax[gi], map.gdiv);
     if (W.unit == 0 && threadIdx.x == 0) group_g[gi] = G.g;   // same value from every member
-    if (base + rq_chunk_elems<U, TH>() <= total) rq_nvfp4_body<U, true, TH>(W.d, base, total, G);
-    else rq_nvfp4_body<U, false, TH>(W.d, base, total, G);
+    if (base + rq_chunk_elems<U, TH>() <= total) {   // uniform, as is G.large
+        if (G.large) rq_nvfp4_body<U, true, true, TH>(W.d, base, total, G);
+        else rq_nvfp4_body<U, true, false, TH>(W.d, base, total, G);
+    } else {
+        rq_nvfp4_body<U, false, false, TH>(W.d, base, total, G);
+    }
 }
 
 // Block-wise FP8 dequantization in the flat layout: used when N % 16 == 0 and
@@ -1520,7 +1571,10 @@ __device__ __forceinline__ void fp8blk_dequant_flat_body(const lpq_tensor& d, in
 }
 
 template <int U, int TH = kThreads>
-constexpr int64_t dqf_chunk_elems() { return (int64_t)TH * 8 * U; }
+constexpr int64_t dqf_chunk_elems() {
+    static_assert(TH % 64 == 0 && TH >= 64 && TH <= kMaxFlatThreads, "whole waves, at most kMaxFlatThreads");
+    return (int64_t)TH * 8 * U;
+}
 
 template <int U, int TH, bool GROUPED>
 __global__ __launch_bounds__(TH) void k_fp8blk_dequant_flat(const lpq_tensor* table, lpq_tensor one,
