@@ -122,9 +122,11 @@ def test_fp8blk_unaligned_pointers(lpq):
 
 
 def test_extreme_values(lpq):
-    """Tiny (subnormal-scale), huge (near the BF16 maximum) and mixed-magnitude tensors."""
+    """Tiny (subnormal-scale), huge (near the BF16 maximum) and mixed-magnitude tensors.
+    1e-22 puts the NVFP4 global scale g between 2^-90 and 2^-81: g itself is not
+    pre-scaled but block multipliers can be, in full chunks as well as the tail."""
     rng = np.random.default_rng(5)
-    for scale in (1e-38, 1e-30, 1e-12, 1.0, 1e30, 3e38):
+    for scale in (1e-38, 1e-30, 1e-22, 1e-12, 1.0, 1e30, 3e38):
         x = (rng.standard_normal((64, 256)) * scale / 4).astype(np.float32)
         x = np.clip(x, -3.38e38, 3.38e38)
         w = (((x.view(np.uint32).astype(np.uint64) + 0x7FFF + ((x.view(np.uint32) >> 16) & 1)) >> 16)

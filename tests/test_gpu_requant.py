@@ -109,11 +109,12 @@ def test_requant_nvfp4_random(lpq, M, N):
 
 
 @pytest.mark.parametrize("lo,hi,signed", [(-126, -100, False), (100, 118, False), (-126, 118, True),
-                                          (-30, 30, True)])
+                                          (-30, 30, True), (-84, -80, False)])
 def test_requant_scale_extremes(lpq, lo, hi, signed):
     """Tile scales from the bottom of the normal range (dequantized values in BF16's
     subnormal range or flushed to zero by rounding) to the top (values near BF16's
-    largest finite), and negative scales."""
+    largest finite), and negative scales.  [-84, -80] puts the NVFP4 global scale
+    between 2^-90 and 2^-81 (some block multipliers pre-scaled, g not)."""
     M, N = 300, 544
     q, s = random_case(M, N, 300 + lo + hi, lo, hi, signed)
     bad = check_mx(lpq, q, s, f"[{lo},{hi}] signed={signed}")
