@@ -1,6 +1,7 @@
 """Seeded random shapes and magnitudes through every format, bit for bit against
 the oracle: block-wise FP8, MXFP8, NVFP4 (quantize, dequantize, QDQ) and INT4
-with groups of 32 and, where N allows, 128.
+with groups of 32 and, where N allows, 128; and 12 more shapes through the fused
+FP8 re-quantizers (tile scales 2^lo .. 2^hi of both signs, lo from -60 to 19).
 
 24 shapes are drawn once from a fixed seed: M from 1 to 1500, N a multiple of
 32 from 32 to 8192, so that most shapes end in a ragged chunk, tile or row band.
@@ -53,3 +54,28 @@ def test_random_shape_all_formats(lpq, i, M, N, sigma):
     check_int4(lpq, w, 32, name)
     if N % 128 == 0:
         check_int4(lpq, w, 128, name)
+
+
+def _requant_cases():
+    rng = np.random.default_rng(20261204)
+    out = []
+    for i in range(12):
+        M = int(rng.integers(1, 1501))
+        N = 32 * int(rng.integers(1, 257))
+        lo = int(rng.integers(-60, 20))
+        out.append((i, M, N, lo, lo + int(rng.integers(0, 30))))
+    return out
+
+
+RQ_CASES = _requant_cases()
+
+
+@pytest.mark.parametrize("i,M,N,lo,hi", RQ_CASES, ids=[f"{M}x{N}" for _, M, N, _, _ in RQ_CASES])
+def test_random_shape_requant(lpq, i, M, N, lo, hi):
+    """Seeded E4M3 codes and tile scales 2^lo .. 2^hi of both signs, through the
+    three fused FP8 re-quantizers."""
+    from tests.test_gpu_requant import check_fp8, check_mx, check_nv, random_case
+    q, s = random_case(M, N, 400 + i, lo, hi, signed=True)
+    name = f"{M}x{N} scales 2^[{lo},{hi}]"
+    print(f"  requant case {i}: {name}", flush=True)
+    assert check_fp8(lpq, q, s, name) + check_mx(lpq, q, s, name) + check_nv(lpq, q, s, name) == 0
