@@ -843,13 +843,14 @@ __global__ __launch_bounds__(TH) void k_nvfp4_qdq(const lpq_tensor* table, lpq_t
 constexpr float kRcp7 = 0x1.24924ap-3f;   // RN(1/7)
 constexpr float kRound = 0x1.8p23f;       // fl(t + 1.5 * 2^23) = 1.5 * 2^23 + RN_int(t) for |t| <= 2^22
 
-// Maximum over the G / 8 lanes of a group.
+// Maximum over the G / 8 lanes of a group: a quad, or a DPP row of 16 lanes
+// (rotations by 4 and 8 lanes inside the row: no LDS round trip).
 template <int G>
 __device__ __forceinline__ uint32_t int4_group_max(uint32_t m) {
     m = quad_max(m);
     if constexpr (G == 128) {
-        m = umax(m, (uint32_t)__shfl_xor((int)m, 4));
-        m = umax(m, (uint32_t)__shfl_xor((int)m, 8));
+        m = umax(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x124, 0xF, 0xF, false));   // row_ror:4
+        m = umax(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x128, 0xF, 0xF, false));   // row_ror:8
     }
     return m;
 }
@@ -874,10 +875,16 @@ __device__ __forceinline__ Int4Scale int4_scale(uint32_t amax_bits) {
         if (aa < 0x1p-100f) s = aa / 7.0f;
     }
     I.s = s;
-    const bool tiny = s > 0.0f && s < kTinyScale;
-    I.any_tiny = any_lane(tiny);
-    I.xpre = tiny ? kPreScale : 1.0f;
-    I.sd = tiny ? s * kPreScale : s;
+    I.any_tiny = any_lane(s > 0.0f && s < kTinyScale);
+    I.xpre = 1.0f;
+    I.sd = s;
+    if (I.any_tiny) {   // wave-uniform and rare: the pre-scaling selects stay inside the branch
+        float ss = s;
+        __asm__ volatile("" : "+v"(ss));
+        const bool tiny = ss > 0.0f && ss < kTinyScale;
+        I.xpre = tiny ? kPreScale : 1.0f;
+        I.sd = tiny ? ss * kPreScale : ss;
+    }
     I.r = s > 0.0f ? rcp_rn(I.sd) : 0.0f;
     return I;
 }
@@ -900,10 +907,15 @@ __device__ __forceinline__ void int4_quotients(const F8& f, const Int4Scale& I, 
 __device__ __forceinline__ uint32_t int4x8(const F8& f, const Int4Scale& I) {
     float t[8];
     int4_quotients(f, I, t);
-    uint32_t p = 0;
+    // byte j = nibbles 2j, 2j+1 (the bits above the byte are don't-cares), then
+    // the four low bytes gathered with byte permutes
+    uint32_t b[4];
 #pragma unroll
-    for (int k = 0; k < 8; k++) p |= (__float_as_uint(t[k] + kRound) & 15u) << (4 * k);
-    return p;
+    for (int j = 0; j < 4; j++)
+        b[j] = (__float_as_uint(t[2 * j] + kRound) & 15u) | (__float_as_uint(t[2 * j + 1] + kRound) << 4);
+    const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u);   // b0.byte0, b1.byte0
+    const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x0C0C0400u);   // b2.byte0, b3.byte0
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);                    // lo.bytes 0-1, hi.bytes 0-1
 }
 
 // 8 values -> their fake-quantized BF16 values BF16(fl(RN_int(fl(x / s)) * s)).
@@ -929,26 +941,34 @@ __global__ __launch_bounds__(TH) void k_int4_quant(const lpq_tensor* table, lpq_
     const lpq_tensor& d = W.d;
     const int64_t total = d.rows * d.cols;
     const int64_t base = W.unit * chunk_elems<U, TH>();
-    const v4u* src = reinterpret_cast<const v4u*>(d.src);
-    uint32_t* dst = reinterpret_cast<uint32_t*>(d.dst);
-    float* scale = reinterpret_cast<float*>(d.scale);
     const int tid = threadIdx.x;
+    // the chunk's origins (uniform); a lane's vector i = u * TH + tid, and its
+    // group's scale, are addressed with 32-bit offsets from them
+    const v4u* src = reinterpret_cast<const v4u*>(d.src) + base / 8;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(d.dst) + base / 8;
+    float* scale = reinterpret_cast<float*>(d.scale) + base / G;
+    const int64_t left = total - base;   // elements from the chunk origin to the end
+    const bool leader = (tid & (G / 8 - 1)) == 0;   // the first lane of its group
     by_fullness<chunk_elems<U, TH>()>(base, total, [&](auto full) {
         constexpr bool FULL = decltype(full)::value;
+        auto in = [&](int i) { return FULL || (int64_t)i * 8 < left; };
         v4u v[U];
-        auto fetch = [&](int u) { v[u] = load_vec<TH, FULL>(src, base, total, u); };
+        auto fetch = [&](int u) {
+            const int i = u * TH + tid;
+            v[u] = in(i) ? load<kNTL>(uniform_ptr(src + u * TH) + tid) : v4u{};
+        };
         fetch_start<U, AHEAD>(fetch);
 #pragma unroll
         for (int u = 0; u < U; u++) {
             fetch_step<U, AHEAD>(u, fetch, v[u].x);
-            const int64_t e0 = base + (int64_t)(u * TH + tid) * 8;
+            const int i = u * TH + tid;
             // G / 8 lanes are one group; groups never straddle the end (N % G == 0)
             const F8 f = widen8(v[u]);
             const Int4Scale I = int4_scale(int4_group_max<G>(absmax8_f32(f)));
             const uint32_t p = int4x8(f, I);
-            if (FULL || e0 < total) {
-                store<kNTS>(dst + (e0 >> 3), p);
-                if ((tid & (G / 8 - 1)) == 0) store<false>(scale + e0 / G, I.s);
+            if (in(i)) {
+                store<kNTS>(uniform_ptr(dst + u * TH) + tid, p);
+                if (leader) store<false>(uniform_ptr(scale + u * (TH * 8 / G)) + tid / (G / 8), I.s);
             }
         }
     });
