@@ -29,7 +29,11 @@
  *    is safe to call from several host threads.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Work is enqueued asynchronously; a kernel fault surfaces at the caller's
- *    next synchronization.
+ *    next synchronization.  A call enqueues kernels only (no memset, copy or
+ *    allocation), so it can be recorded by stream capture into a HIP graph
+ *    and replayed; the host-side table of a grouped call is read when the
+ *    call is made, and the device-side table must hold the same descriptors
+ *    at every replay.
  *  - Tensors are row-major and contiguous: M rows (out_features) by N
  *    columns (in_features); blocks run along N.  BF16 values travel as
  *    uint16_t bit patterns, E4M3 codes as uint8_t (float8_e4m3fn).
