@@ -39,7 +39,19 @@
  *    S = fl(E4M3value * g);
  *  - E4M3 and E2M1 casts saturate to +-448 / +-6 and keep the sign of zero;
  *  - a zero scale encodes every element as a zero of the element's sign;
- *  - packed E2M1: element 2j in the low nibble of byte j.
+ *  - packed E2M1: element 2j in the low nibble of byte j;
+ *  - group-wise INT4 (the page gives only the group sizes 32 and 128):
+ *    s = fl(amax / 7) per group of a row, code = the nearest integer of
+ *    fl(x / s), ties to even, clamped to [-8, 7], two's-complement nibbles
+ *    with element 2j low, y = BF16(fl(code * s));
+ *  - activation observers (the page names them): the latest batch's extremes,
+ *    the running extremes, or the moving average m + c * (b - m).
+ *
+ * Parity unpinned against the pages: they fix no value for the multiplier
+ * form of the scales, the MXFP8 exponent rule, the FP32 evaluation order, the
+ * observer rules, the E4M3 maximum of 256 or the INT4 convention.  The tests
+ * pin each function to its stated definition instead (closed forms, exact
+ * rational arithmetic, brute force over BF16 patterns).
  */
 #include <math.h>
 #include <stdint.h>
