@@ -23,6 +23,7 @@ Prints one JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
@@ -41,8 +42,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-KERNEL_SOURCES = ("precision_weight_quantization_amd/csrc/lpq_kernels.hip",
-                  "precision_weight_quantization_amd/csrc/lpq_device.hpp")
+# every source of the kernel library (the .hip translation unit and the parts it includes), in a fixed order
+KERNEL_SOURCES = tuple(sorted(os.path.relpath(f, ROOT) for ext in ("*.hip", "*.hpp")
+                              for f in glob.glob(os.path.join(ROOT, "precision_weight_quantization_amd", "csrc", ext))))
 
 
 def code_text(src: str) -> str:

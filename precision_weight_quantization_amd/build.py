@@ -6,6 +6,7 @@ to build.
 """
 from __future__ import annotations
 
+import glob
 import os
 import subprocess
 import sys
@@ -15,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "liblpq.so")
 SOURCES = [os.path.join(CSRC, "lpq_kernels.hip")]
-HEADERS = [os.path.join(ROOT, "include", "lpq.h"), os.path.join(CSRC, "lpq_device.hpp")]
+# lpq_kernels.hip includes the public header and every .hpp beside it (one translation unit)
+HEADERS = [os.path.join(ROOT, "include", "lpq.h")] + sorted(glob.glob(os.path.join(CSRC, "*.hpp")))
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -ffp-contract=off: every multiply/add written separately stays separately
