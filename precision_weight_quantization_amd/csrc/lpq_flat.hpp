@@ -1,4 +1,5 @@
-// Shared device-side machinery: constants, flat work units, the dense work map and its lookup, load order.
+// Shared device-side machinery: constants, flat work units, the dense work map
+// and its lookup, load order.
 //
 // Part of lpq_kernels.hip, which includes each part once, in this order: one
 // translation unit.

@@ -1,4 +1,5 @@
-// Block-wise FP8: the tile quantizer (strips of 2 or 4 tiles) and the tile dequantizer.
+// Block-wise FP8: the tile quantizer (strips of 2 or 4 tiles) and the tile
+// dequantizer.
 //
 // Part of lpq_kernels.hip, which includes each part once, in this order: one
 // translation unit.

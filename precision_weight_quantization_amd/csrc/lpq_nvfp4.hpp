@@ -1,4 +1,5 @@
-// NVFP4: global and block scales, E2M1 encode/decode, the W4A4 observers, the amax pass, quantize, dequantize and QDQ.
+// NVFP4: global and block scales, E2M1 encode/decode, the W4A4 observers, the
+// amax pass, quantize, dequantize and QDQ.
 //
 // Part of lpq_kernels.hip, which includes each part once, in this order: one
 // translation unit.

@@ -1,4 +1,6 @@
-// Fused re-quantization of block-wise FP8 weights (to block FP8, MXFP8, NVFP4, and their amax) and the flat block-FP8 dequantizer, which shares their tile-scale walk.
+// Fused re-quantization of block-wise FP8 weights (to block FP8, MXFP8, NVFP4,
+// and their amax) and the flat block-FP8 dequantizer, which shares their tile-
+// scale walk.
 //
 // Part of lpq_kernels.hip, which includes each part once, in this order: one
 // translation unit.

@@ -1,4 +1,5 @@
-// Launch parameters of the kernels (compile-time; each can be overridden with -D).
+// Launch parameters of the kernels (compile-time; each can be overridden with
+// -D).
 //
 // Part of lpq_kernels.hip, which includes each part once, in this order: one
 // translation unit.
