@@ -20,6 +20,7 @@ Independent routes used here (none re-types the oracle's own arithmetic):
 """
 from __future__ import annotations
 
+import math
 import os
 from fractions import Fraction
 
@@ -514,6 +515,342 @@ def pin_round_trip_nvfp4(O):
         assert np.array_equal(O.nvfp4_dequantize(p, s, g), w1)
 
 
+# --------------------------------------------------------------------------- exact quotients
+
+# The oracle's divisions (the block-FP8 tile scale and element quotient, the NVFP4
+# global scale, block scale and element quotient) are each one correctly rounded
+# binary32 operation.  The pins below recompute every such quotient from the exact
+# rational value of its operands with integer arithmetic alone, and check the
+# oracle's codes and scale bits against it.  Power-of-two scales would hide a
+# reciprocal-multiply mistake (x * (1/s) is exact there), so the inputs use scales
+# that are not powers of two, including quotients that land exactly on a rounding
+# midpoint of the E4M3 or E2M1 grid, where only a correctly rounded quotient gives
+# the tie (ties go to the even code).
+
+_F32_EMIN_Q = -149          # exponent of binary32's smallest subnormal step
+
+
+def rn_f32_ratio(n: int, d: int) -> float:
+    """The binary32 value nearest to the rational n / d (d != 0), ties to the even
+    significand, returned as a Python float; overflow gives +-inf, and a nonzero
+    quotient that rounds to zero keeps its sign.  Integer arithmetic only: the
+    24-bit significand is the integer part of n / (d * 2^e) for the right e, and
+    the remainder decides the rounding."""
+    if d < 0:
+        n, d = -n, -d
+    neg = n < 0
+    n = -n if neg else n
+    if n == 0:
+        return -0.0 if neg else 0.0
+
+    def split(e):
+        num, den = (n, d << e) if e >= 0 else (n << -e, d)
+        q, r = divmod(num, den)
+        return q, r, den
+
+    e = n.bit_length() - d.bit_length() - 24     # n / (d 2^e) lies in [2^23, 2^25)
+    q, r, den = split(e)
+    if q >= 1 << 24:
+        e += 1
+        q, r, den = split(e)
+    if e < _F32_EMIN_Q:                          # subnormal result: fixed quantum
+        e = _F32_EMIN_Q
+        q, r, den = split(e)
+    if 2 * r > den or (2 * r == den and q & 1):
+        q += 1
+    if e > 104 or (e == 104 and q >= 1 << 24):   # at or beyond 2^128
+        val = float("inf")
+    else:
+        val = math.ldexp(q, e)                   # exact: q <= 2^24, e >= -149
+    return -val if neg else val
+
+
+def _ratio(v: float):
+    n, d = float(v).as_integer_ratio()
+    return n, d
+
+
+def rn_div_f32(a, b) -> np.ndarray:
+    """Elementwise RN32(a / b) of binary32 operands, exactly (b != 0).  The sign of a
+    zero quotient is the XOR of the operands' signs, as in IEEE division."""
+    a, b = (v.ravel() for v in np.broadcast_arrays(np.asarray(a, np.float64), np.asarray(b, np.float64)))
+    out = np.empty(a.size, np.float64)
+    for i in range(a.size):
+        x, y = float(a[i]), float(b[i])
+        if x == 0.0:
+            out[i] = math.copysign(0.0, math.copysign(1.0, x) * math.copysign(1.0, y))
+            continue
+        nx, dx = _ratio(x)
+        ny, dy = _ratio(y)
+        out[i] = rn_f32_ratio(nx * dy, dx * ny)
+    return out.astype(np.float32)
+
+
+def rn_mul_f32(a, b) -> np.ndarray:
+    """Elementwise RN32(a * b) of binary32 operands, exactly."""
+    a, b = (v.ravel() for v in np.broadcast_arrays(np.asarray(a, np.float64), np.asarray(b, np.float64)))
+    out = np.empty(a.size, np.float64)
+    for i in range(a.size):
+        x, y = float(a[i]), float(b[i])
+        if x == 0.0 or y == 0.0:
+            out[i] = math.copysign(0.0, math.copysign(1.0, x) * math.copysign(1.0, y))
+            continue
+        nx, dx = _ratio(x)
+        ny, dy = _ratio(y)
+        out[i] = rn_f32_ratio(nx * ny, dx * dy)
+    return out.astype(np.float32)
+
+
+def _e4m3_nearest(t) -> np.ndarray:
+    """Saturating nearest-even E4M3 code of binary32 values (sign of zero kept)."""
+    grid, codes = e4m3_positive_grid()
+    t = np.asarray(t, np.float32)
+    return (nearest_even_codes(t, grid, codes) | (sign_bit(t) << 7)).astype(np.uint8)
+
+
+def _e2m1_nearest(t) -> np.ndarray:
+    t = np.asarray(t, np.float32)
+    return (nearest_even_codes(t, read_grid_file(), np.arange(8, dtype=np.int64)) | (sign_bit(t) << 3)).astype(np.uint8)
+
+
+def _short_significands(max_bits: int) -> list:
+    """Significands in (1, 2) with at most ``max_bits`` bits after the leading one."""
+    return [1.0 + k / 2.0 ** max_bits for k in range(1, 1 << max_bits)]
+
+
+def _bf16_exact(v) -> bool:
+    v = np.float32(v)
+    return bool(np.isfinite(v)) and (int(v.view(np.uint32)) & 0xFFFF) == 0
+
+
+def exact_fp8blk(w: np.ndarray):
+    """Block-wise FP8 of a BF16 [M, N] tensor by exact rationals: per tile
+    s = RN32(amax / 448); code = E4M3(RN32(x / s)), a signed zero when s = 0;
+    y = BF16(RN32(E4M3value * s))."""
+    M, N = w.shape
+    x = bf16_f32(w)
+    tm, tn = (M + 127) // 128, (N + 127) // 128
+    pad = np.zeros((tm * 128, tn * 128), np.float32)
+    pad[:M, :N] = np.abs(x)
+    amax = pad.reshape(tm, 128, tn, 128).max(axis=(1, 3))
+    s = rn_div_f32(amax, 448.0).reshape(tm, tn)
+    sf = np.repeat(np.repeat(s, 128, 0), 128, 1)[:M, :N]
+    nz = sf != 0
+    t = np.zeros((M, N), np.float32)
+    t[nz] = rn_div_f32(x[nz], sf[nz])
+    t[~nz] = np.copysign(np.float32(0), x[~nz])
+    q = _e4m3_nearest(t).reshape(M, N)
+    y = f32_to_bf16_torch(rn_mul_f32(e4m3_table()[q], sf)).reshape(M, N)
+    return q, s, y
+
+
+def exact_nvfp4(w: np.ndarray, g: float, e4m3_max: int = 448):
+    """NVFP4 of a BF16 [M, N] tensor under global scale g by exact rationals: per
+    1x16 block with amax b, scode = E4M3(RN32(RN32(b / 6) / g)) (0 when g = 0),
+    S = RN32(E4M3value * g), code = E2M1(RN32(x / S)) (a signed zero when S = 0),
+    y = BF16(RN32(E2M1value * S)).  Returns (codes [M, N], scodes [M, N/16], y)."""
+    M, N = w.shape
+    x = bf16_f32(w)
+    b = np.abs(x).reshape(M, N // 16, 16).max(-1).ravel()
+    if g == 0.0:
+        sc = np.zeros(b.size, np.uint8)
+    else:
+        sc = _e4m3_nearest(rn_div_f32(rn_div_f32(b, 6.0), g))
+    S = rn_mul_f32(e4m3_table()[sc], g).reshape(M, N // 16)
+    Sf = np.repeat(S, 16, 1)
+    nz = Sf != 0
+    t = np.zeros((M, N), np.float32)
+    t[nz] = rn_div_f32(x[nz], Sf[nz])
+    t[~nz] = np.copysign(np.float32(0), x[~nz])
+    codes = _e2m1_nearest(t).reshape(M, N)
+    grid = read_grid_file()
+    val = (grid[codes & 7] * np.where(codes & 8, -1.0, 1.0)).astype(np.float32)
+    y = f32_to_bf16_torch(rn_mul_f32(val, Sf)).reshape(M, N)
+    return codes, sc.reshape(M, N // 16), y
+
+
+def _unpack_e2m1(p: np.ndarray) -> np.ndarray:
+    codes = np.empty((p.shape[0], p.shape[1] * 2), np.uint8)
+    codes[:, 0::2] = p & 15
+    codes[:, 1::2] = p >> 4
+    return codes
+
+
+def pin_exact_global_scale(O):
+    """g = RN32(A / 2688) on every positive finite BF16 amax (the amax of BF16 weights
+    is a BF16 value) and on 20,000 random binary32 A (a caller-supplied or observed
+    amax), against the exact rational quotient; likewise A / 1536 (E4M3 maximum 256)
+    and the reciprocal export RN32(2688 / A).  Then 2,000 random tensors, whose A is
+    recomputed with numpy: the group call reports that A and its exact quotient
+    ("verl NVFP4 QAT" 2.3 and 3.3: amax / (6.0 * 448.0))."""
+    u = all_finite_bf16()
+    A = np.concatenate([bf16_f32(u[(u > 0) & (u < 0x8000)]), np.abs(random_f32(20000, 60, -140, 127))])
+    A = A[A > 0]
+    got = np.array([O.nvfp4_global_scale(float(a)) for a in A], np.float32)
+    assert np.array_equal(f32_bits(got), f32_bits(rn_div_f32(A, 2688.0)))
+    got256 = np.array([O.nvfp4_global_scale(float(a), 256) for a in A[::4]], np.float32)
+    assert np.array_equal(f32_bits(got256), f32_bits(rn_div_f32(A[::4], 1536.0)))
+    rec = np.array([O.nvfp4_global_scale_reciprocal(float(a)) for a in A[::4]], np.float32)
+    want = np.array([rn_f32_ratio(2688 * _ratio(a)[1], _ratio(a)[0]) for a in A[::4]], np.float32)
+    assert np.array_equal(f32_bits(rec), f32_bits(want))
+    rng = np.random.default_rng(61)
+    for _ in range(2000):
+        m = int(rng.integers(1, 4))
+        w = _moe_like(rng, m, 16, float(np.exp(rng.uniform(-60, 60))), 0.05)
+        Ar = float(np.abs(bf16_f32(w).astype(np.float64)).max())
+        A2, g2 = O.nvfp4_group_scale([w])
+        assert A2 == Ar and f32_bits(np.float32(g2)) == f32_bits(rn_div_f32([Ar], 2688.0)[0])
+
+
+def pin_exact_fp8blk(O):
+    """Block-wise FP8 tile scales, codes and dequantized values against exact rationals:
+    (1) one 1x128 tile per positive finite BF16 amax (32,640 tiles), scale bits only;
+    (2) tiles whose scale s = sigma * 2^k is not a power of two, holding every
+    BF16-representable x = m * s for m an E4M3 rounding midpoint (an exact tie that
+    only a correctly rounded x / s produces), plus the other grid points times s;
+    (3) a MoE-like ragged tensor (0.1% outliers x 50) and tiles of subnormal and
+    huge magnitudes, every element."""
+    u = all_finite_bf16()
+    amax = u[(u > 0) & (u < 0x8000)]
+    w = np.zeros((1, 128 * amax.size), np.uint16)
+    w[0, ::128] = amax
+    w[0, 1::128] = amax | 0x8000          # a negative element of the same magnitude
+    _, s = O.fp8blk_quantize(w)
+    assert np.array_equal(f32_bits(s[0]), f32_bits(rn_div_f32(bf16_f32(amax), 448.0)))
+
+    grid, _ = e4m3_positive_grid()
+    mids = (grid[1:] + grid[:-1]) / 2.0
+    rows = []
+    rng = np.random.default_rng(62)
+    for sigma in _short_significands(3):
+        for k in (-20, -3, 0, 5):
+            sc = np.ldexp(sigma, k)
+            if not _bf16_exact(448.0 * sc):
+                continue
+            rest = [m * sc for m in mids if _bf16_exact(m * sc)]
+            rest += [v * sc for v in grid[1:-1] if _bf16_exact(v * sc)]
+            for j in range(0, len(rest), 127):       # every tile holds its amax 448 * s
+                vals = np.array([448.0 * sc] + rest[j:j + 127])
+                vals *= np.where(rng.integers(0, 2, len(vals)) == 1, -1.0, 1.0)
+                rows.append(vals[rng.permutation(len(vals))])
+    tiles = np.zeros((len(rows), 128), np.float32)
+    for i, r in enumerate(rows):
+        tiles[i, :len(r)] = r
+    # each row is its own 1 x 128 tile: lay the rows side by side in one row
+    wt = f32_to_bf16_torch(tiles.reshape(1, -1)).reshape(1, -1)
+    assert np.array_equal(bf16_f32(wt).ravel(), tiles.ravel()), "tie construction must be BF16-exact"
+    cases = [wt]
+    cases.append(_moe_like(np.random.default_rng(63), 200, 296, 0.02, 0.001))
+    cases.append(_moe_like(np.random.default_rng(64), 130, 136, 1e-39, 0.01))
+    cases.append(_moe_like(np.random.default_rng(65), 130, 136, 1e34, 0.01))
+    for w in cases:
+        q, s = O.fp8blk_quantize(w)
+        eq, es, ey = exact_fp8blk(w)
+        assert np.array_equal(f32_bits(s), f32_bits(es))
+        bad = np.nonzero(q != eq)
+        assert bad[0].size == 0, f"{bad[0].size} codes differ from the exact quotient"
+        assert np.array_equal(O.fp8blk_dequantize(q, s), ey)
+
+
+def pin_exact_nvfp4(O):
+    """NVFP4 block-scale codes, element codes and dequantized values against exact
+    rationals, RN32(RN32(b / 6) / g) and RN32(x / S):
+    (1) groups whose g = gamma * 2^k is not a power of two, with blocks whose
+    RN32(b / 6) / g is an E4M3 rounding midpoint, or whose elements x / S are E2M1
+    midpoints (0.25, 0.75, ..., 5): exact ties;
+    (2) block scales of (b, g) pairs built so that RN32(b / 6) / g is an E4M3 midpoint;
+    (3) a 1-in-4 sample of positive finite BF16 patterns, each in a block with a larger
+    anchor and 14 random elements below it;
+    (4) MoE-like tensors, tiny and huge magnitudes; the E4M3-256 form on one of them."""
+    rng = np.random.default_rng(66)
+    grid, _ = e4m3_positive_grid()
+    e4_mids = (grid[1:] + grid[:-1]) / 2.0
+    e4_normal = grid[grid >= 2.0 ** -6]
+    e2 = read_grid_file()
+    e2_mids = (e2[1:] + e2[:-1]) / 2.0
+
+    def check(members, e4m3_max=448):
+        A, g, outs = O.nvfp4_quantize_group(members, e4m3_max)
+        assert A == max(float(np.abs(bf16_f32(m)).max()) for m in members)
+        assert f32_bits(np.float32(g)) == f32_bits(rn_div_f32([A], 6.0 * e4m3_max)[0])
+        for m, (p, s) in zip(members, outs):
+            ec, es, ey = exact_nvfp4(m, g, e4m3_max)
+            assert np.array_equal(s, es), f"{np.count_nonzero(s != es)} block scales differ"
+            codes = _unpack_e2m1(p)
+            assert np.array_equal(codes, ec), f"{np.count_nonzero(codes != ec)} codes differ"
+            assert np.array_equal(O.nvfp4_dequantize(p, s, g), ey)
+            assert np.array_equal(O.nvfp4_qdq(m, g), ey)
+
+    # (1) exact ties under g = gamma * 2^k
+    for gamma in _short_significands(3):
+        for k in (-24, -7, 0):
+            gk = np.ldexp(gamma, k)
+            if not _bf16_exact(2688.0 * gk):
+                continue
+            blocks = []
+            for m in e4_mids[40:]:                  # block-scale ties: b = 6 * m * g
+                b = 6.0 * m * gk
+                if _bf16_exact(b):
+                    blocks.append([b] + [0.0] * 15)
+            for v in e4_normal[::3]:                # element ties: x = mu * v * g
+                S = v * gk
+                if not _bf16_exact(6.0 * S):
+                    continue
+                xs = [6.0 * S] + [mu * S for mu in e2_mids if _bf16_exact(mu * S)]
+                xs += [mu * S for mu in e2[1:7] if _bf16_exact(mu * S)]
+                blocks.append((xs + [0.0] * 16)[:16])
+            if not blocks:
+                continue
+            x = np.array(blocks, np.float64)
+            x *= np.where(rng.integers(0, 2, x.shape) == 1, -1.0, 1.0)
+            w = f32_to_bf16_torch(x.astype(np.float32)).reshape(x.shape)
+            assert np.array_equal(bf16_f32(w), x.astype(np.float32)), "tie construction must be BF16-exact"
+            anchor = np.zeros((1, 16), np.float32)
+            anchor[0, 3] = 2688.0 * gk
+            check([w, f32_to_bf16_torch(anchor).reshape(1, 16)])
+
+    # (2) block-scale ties from the first division: b is any BF16 value whose RN32(b / 6)
+    # has an integer significand divisible by the odd part o of an E4M3 midpoint m;
+    # then g = RN32(b / 6) / m is exact and RN32(b / 6) / g = m, a tie only when both
+    # divisions are correctly rounded in this order.
+    u = all_finite_bf16()
+    bs = bf16_f32(u[(u > 0) & (u < 0x8000)])
+    bs = bs[(bs > 2.0 ** -100) & (bs < 2.0 ** 100)]
+    t1 = rn_div_f32(bs[::7], 6.0)
+    pairs = []
+    for b, t in zip(bs[::7], t1):
+        n, d = _ratio(float(t))
+        for m in e4_mids[40:120:3]:
+            mn, md = _ratio(float(m))
+            if n % mn == 0:
+                g = np.float32(float(t) / float(m))
+                if float(g) * float(m) == float(t):
+                    pairs.append((float(b), float(g)))
+    assert len(pairs) > 500
+    pb = np.array([p_[0] for p_ in pairs], np.float32)
+    pg = np.array([p_[1] for p_ in pairs], np.float32)
+    got = np.array([O.nvfp4_block_scale(float(b), float(g)) for b, g in pairs], np.uint8)
+    want = _e4m3_nearest(rn_div_f32(rn_div_f32(pb, 6.0), pg))
+    assert np.array_equal(got, want), f"{np.count_nonzero(got != want)} block-scale codes differ"
+
+    # (3) a sample of positive finite BF16 patterns p, each in a block with a seeded
+    # larger anchor and 14 random elements below it; blocks sorted by anchor and
+    # quantized 256 to a group, so that every group spans a few binades
+    pats = bf16_f32(u[(u > 0) & (u < 0x7B00)][::4]).astype(np.float64)      # anchors stay below 2^126
+    a = pats * rng.uniform(1.0, 64.0, pats.size)
+    rows = np.concatenate([a[:, None], pats[:, None], rng.uniform(-1.0, 1.0, (pats.size, 14)) * a[:, None]], 1)
+    rows *= np.where(rng.integers(0, 2, rows.shape) == 1, -1.0, 1.0)
+    rows = rows[np.argsort(a)].astype(np.float32)
+    for j in range(0, rows.shape[0], 256):
+        check([f32_to_bf16_torch(rows[j:j + 256]).reshape(-1, 16)])
+
+    # (4) MoE-like tensors and extreme magnitudes
+    check([_moe_like(np.random.default_rng(67), 96, 512, 0.02, 0.001)])
+    check([_moe_like(np.random.default_rng(68), 32, 256, 1e-38, 0.01)])
+    check([_moe_like(np.random.default_rng(69), 32, 256, 1e34, 0.01)])
+    check([_moe_like(np.random.default_rng(70), 32, 256, 0.02, 0.001)], 256)
+
+
 # --------------------------------------------------------------------------- invariants on random data
 
 def _moe_like(rng, M, N, scale=0.02, p_out=0.01, factor=50.0):
@@ -828,7 +1165,9 @@ def _int4_exact(xs: np.ndarray):
 def pin_int4_nearest_exact(O):
     """Codes, scales and QDQ outputs against exact rationals, on MoE-like groups,
     groups of subnormals, groups spanning wide exponent ranges, and groups whose
-    quotients land exactly on half-integers (ties to even)."""
+    quotients land exactly on half-integers (ties to even) under power-of-two scales
+    and under scales sigma * 2^k that are not (only a correctly rounded x / s gives
+    the tie there)."""
     rng = np.random.default_rng(42)
     for G in (32, 128):
         groups = []
@@ -838,10 +1177,13 @@ def pin_int4_nearest_exact(O):
             groups.append(v.astype(np.float32))
         groups.append(random_f32(G, 43 + G, -133, -120))   # subnormal and tiny amax
         groups.append(random_f32(G, 44 + G, -60, 60))      # wide exponent range
+        halves = np.array([7, -7, 0.5, -0.5, 1.5, -1.5, 2.5, -2.5, 3.5, -3.5, 4.5, 5.5, 6.5, -6.5, 0, 3])
         for k in (-12, 0, 9):                              # half-integer quotients under s = 2^k
-            t = np.resize(np.array([7, -7, 0.5, -0.5, 1.5, -1.5, 2.5, -2.5, 3.5, -3.5, 4.5, 5.5, 6.5, -6.5, 0, 3]),
-                          G)
-            groups.append(np.ldexp(t, k).astype(np.float32))
+            groups.append(np.ldexp(np.resize(halves, G), k).astype(np.float32))
+        for sigma in _short_significands(3):               # the same ties under s = sigma * 2^k
+            t = np.resize(halves, G) * sigma
+            if all(_bf16_exact(v) for v in t):
+                groups.append(np.ldexp(t, -5).astype(np.float32))
         w = np.stack([f32_to_bf16_torch(g) for g in groups])
         p, s = O.int4_quantize(w, G)
         y = O.int4_qdq(w, G)
@@ -876,4 +1218,8 @@ def pin_int4_zero_and_layout(O):
         assert np.array_equal(O.int4_qdq(x, G), O.int4_dequantize(*O.int4_quantize(x, G), G))
 
 
-ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
+# The exact-quotient pins take seconds each; they run last, so that a planted mistake
+# that a cheaper pin catches never waits for them.
+_SLOW_PINS = ("pin_exact_global_scale", "pin_exact_fp8blk", "pin_exact_nvfp4")
+ALL_PINS = ([v for k, v in sorted(globals().items()) if k.startswith("pin_") and k not in _SLOW_PINS]
+            + [globals()[k] for k in _SLOW_PINS])
