@@ -67,8 +67,9 @@ typedef enum lpq_status {
     LPQ_ERR_ARG = 6     /* any other invalid argument (reserved field not 0, ...)      */
 } lpq_status;
 
-/* Static, NUL-terminated description of a status code. */
-const char* lpq_status_string(int status);
+/* Static, NUL-terminated description of a status code ("unknown status" for a
+ * value outside the enumeration). */
+const char* lpq_status_string(lpq_status status);
 
 /* hipError_t of the most recent LPQ_ERR_HIP on the calling thread (0 if none). */
 int lpq_last_hip_error(void);
@@ -135,8 +136,12 @@ lpq_status lpq_quantize_mxfp8_floor(const uint16_t* w, int64_t M, int64_t N, uin
 lpq_status lpq_nvfp4_amax(const uint16_t* w, int64_t M, int64_t N, float* amax,
                           int accumulate, void* stream);
 
-/* amax: 1 FP32 (device) holding A.  p: [M, N/2] packed codes.  s: [M, N/16]
- * E4M3 codes.  g: 1 FP32 (device), receives the global scale. */
+/* amax: 1 FP32 (device) holding A (e.g. a cached amax, "verl NVFP4 QAT" 2.4,
+ * or the group maximum of lpq_nvfp4_amax), or NULL: then A is this tensor's
+ * own max |w| (a tensor of its own is a group of one), computed by the call
+ * itself -- it reads w twice, and uses the caller's g word to hold A until g
+ * is written.  p: [M, N/2] packed codes.  s: [M, N/16] E4M3 codes.  g: 1 FP32
+ * (device), receives the global scale. */
 lpq_status lpq_quantize_nvfp4(const uint16_t* w, int64_t M, int64_t N, const float* amax,
                               uint8_t* p, uint8_t* s, float* g, void* stream);
 
@@ -146,7 +151,12 @@ lpq_status lpq_dequantize_nvfp4(const uint8_t* p, const uint8_t* s, const float*
 
 /* Fake quantization ("verl NVFP4 QAT" 2.3, also used on W4A4 activations):
  * y = dequantize(quantize(x)) bit for bit, without storing codes.
- * amax: 1 FP32 (device) holding A.  x, y: [M, N] BF16 (may not overlap). */
+ * amax: 1 FP32 (device) holding A; required (NULL: LPQ_ERR_NULL).  Unlike the
+ * quantizer, this call has no FP32 output in which an amax it computed could
+ * be held between the amax pass and the encode, and the library allocates
+ * nothing: a caller without a cached amax runs lpq_nvfp4_amax into a word of
+ * its own first (or lpq_nvfp4_observe for W4A4 activations).
+ * x, y: [M, N] BF16 (may not overlap). */
 lpq_status lpq_nvfp4_qdq(const uint16_t* x, int64_t M, int64_t N, const float* amax,
                          uint16_t* y, void* stream);
 
@@ -196,20 +206,26 @@ lpq_status lpq_dequantize_mxfp8_grouped(const lpq_tensor* host, const lpq_tensor
 lpq_status lpq_nvfp4_amax_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n,
                                   float* group_amax, int32_t n_groups, int accumulate, void* stream);
 
-/* group_amax: n_groups FP32 (device, the A of each group, e.g. from
- * lpq_nvfp4_amax_grouped or a cached value).  group_g: n_groups FP32
- * (device, out): g of every group that has at least one member. */
+/* group_amax: n_groups FP32 (device), the A of each group.  amax_valid != 0:
+ * group_amax already holds them (from lpq_nvfp4_amax_grouped, an observer or
+ * a cached value, "verl NVFP4 QAT" 2.4) and is only read.  amax_valid == 0:
+ * the call fills it first -- every slot set to 0, then each member's max |w|
+ * max-folded into its group's slot (the group maximum) -- and then encodes;
+ * the filled values stay there for the caller (e.g. to cache).  group_g:
+ * n_groups FP32 (device, out): g of every group that has at least one
+ * member. */
 lpq_status lpq_quantize_nvfp4_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n,
-                                      const float* group_amax, int32_t n_groups, float* group_g,
+                                      float* group_amax, int32_t n_groups, int amax_valid, float* group_g,
                                       void* stream);
 
 /* group_g: n_groups FP32 (device), the global scales written by the quantizer. */
 lpq_status lpq_dequantize_nvfp4_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n,
                                         const float* group_g, int32_t n_groups, void* stream);
 
-/* group_amax: n_groups FP32 (device).  src and dst of a descriptor may not overlap. */
+/* group_amax, amax_valid: as for lpq_quantize_nvfp4_grouped.  src and dst of a
+ * descriptor may not overlap. */
 lpq_status lpq_nvfp4_qdq_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n,
-                                 const float* group_amax, int32_t n_groups, void* stream);
+                                 float* group_amax, int32_t n_groups, int amax_valid, void* stream);
 
 /* ======================================================================== */
 /* Re-quantization of block-wise FP8 weights, for the FP8-training weight
@@ -295,18 +311,18 @@ lpq_status lpq_nvfp4_global_scale_reciprocal(const float* group_amax, int32_t n_
  * "4over6" switch with its "E4M3 use 256" flag sets the E4M3 maximum to 256;
  * the global scale of "verl NVFP4 QAT" 2.3 divides amax by FP4 max x FP8 max.
  * Everything else is as for lpq_quantize_nvfp4 / lpq_nvfp4_qdq (and their
- * grouped forms); lpq_dequantize_nvfp4* decode the output with the g it
- * wrote.  The per-block choice between two scalings that gives "4over6" its
+ * grouped forms: amax NULL, amax_valid); lpq_dequantize_nvfp4* decode the
+ * output with the g it wrote.  The per-block choice between two scalings that gives "4over6" its
  * name is not described on the pages and is not implemented. */
 lpq_status lpq_quantize_nvfp4_ex(const uint16_t* w, int64_t M, int64_t N, const float* amax, int e4m3_max,
                                  uint8_t* p, uint8_t* s, float* g, void* stream);
 lpq_status lpq_nvfp4_qdq_ex(const uint16_t* x, int64_t M, int64_t N, const float* amax, int e4m3_max, uint16_t* y,
                             void* stream);
 lpq_status lpq_quantize_nvfp4_grouped_ex(const lpq_tensor* host, const lpq_tensor* dev, int32_t n,
-                                         const float* group_amax, int32_t n_groups, int e4m3_max, float* group_g,
-                                         void* stream);
-lpq_status lpq_nvfp4_qdq_grouped_ex(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, const float* group_amax,
-                                    int32_t n_groups, int e4m3_max, void* stream);
+                                         float* group_amax, int32_t n_groups, int amax_valid, int e4m3_max,
+                                         float* group_g, void* stream);
+lpq_status lpq_nvfp4_qdq_grouped_ex(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, float* group_amax,
+                                    int32_t n_groups, int amax_valid, int e4m3_max, void* stream);
 
 /* ======================================================================== */
 /* W4A4 activation observers.  "verl NVFP4 QAT" 2.2 (activation_observer,

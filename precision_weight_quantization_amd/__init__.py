@@ -75,8 +75,8 @@ _SIG = {
     "lpq_nvfp4_global_scale": (_int, [_vp, _i32, _vp, _vp]),
     "lpq_quantize_nvfp4_ex": (_int, [_vp, _i64, _i64, _vp, _int, _vp, _vp, _vp, _vp]),
     "lpq_nvfp4_qdq_ex": (_int, [_vp, _i64, _i64, _vp, _int, _vp, _vp]),
-    "lpq_quantize_nvfp4_grouped_ex": (_int, [_tp, _vp, _i32, _vp, _i32, _int, _vp, _vp]),
-    "lpq_nvfp4_qdq_grouped_ex": (_int, [_tp, _vp, _i32, _vp, _i32, _int, _vp]),
+    "lpq_quantize_nvfp4_grouped_ex": (_int, [_tp, _vp, _i32, _vp, _i32, _int, _int, _vp, _vp]),
+    "lpq_nvfp4_qdq_grouped_ex": (_int, [_tp, _vp, _i32, _vp, _i32, _int, _int, _vp]),
     "lpq_observer_reset": (_int, [_vp, _vp]),
     "lpq_nvfp4_observe": (_int, [_vp, _i64, _i64, _int, ctypes.c_float, _vp, _vp, _vp]),
     "lpq_nvfp4_amax": (_int, [_vp, _i64, _i64, _vp, _int, _vp]),
@@ -88,9 +88,9 @@ _SIG = {
     "lpq_quantize_mxfp8_grouped": (_int, [_tp, _vp, _i32, _vp]),
     "lpq_dequantize_mxfp8_grouped": (_int, [_tp, _vp, _i32, _vp]),
     "lpq_nvfp4_amax_grouped": (_int, [_tp, _vp, _i32, _vp, _i32, _int, _vp]),
-    "lpq_quantize_nvfp4_grouped": (_int, [_tp, _vp, _i32, _vp, _i32, _vp, _vp]),
+    "lpq_quantize_nvfp4_grouped": (_int, [_tp, _vp, _i32, _vp, _i32, _int, _vp, _vp]),
     "lpq_dequantize_nvfp4_grouped": (_int, [_tp, _vp, _i32, _vp, _i32, _vp]),
-    "lpq_nvfp4_qdq_grouped": (_int, [_tp, _vp, _i32, _vp, _i32, _vp]),
+    "lpq_nvfp4_qdq_grouped": (_int, [_tp, _vp, _i32, _vp, _i32, _int, _vp]),
     "lpq_requantize_fp8blk": (_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
     "lpq_requantize_fp8blk_grouped": (_int, [_rp, _vp, _i32, _vp]),
     "lpq_requantize_fp8blk_mxfp8": (_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
@@ -129,18 +129,67 @@ def _ptr(t) -> int:
     return 0 if t is None else t.data_ptr()
 
 
-def _bf16_in(x: torch.Tensor, name: str) -> torch.Tensor:
-    if x.dim() != 2:
-        raise ValueError(f"{name} must be 2-D [M, N]")
-    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
-        raise TypeError(f"{name} must be bfloat16 (or its 16-bit view), got {x.dtype}")
-    if not x.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
-    return x.contiguous()
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _arg(t, name: str, like=None, nbytes: int = 0, esize=None, dtypes=None, dims=None):
+    """Check a tensor argument before its address reaches a kernel: a device
+    tensor, on the device of ``like`` (the call's data), contiguous, of the
+    given element size or dtypes and rank, holding at least ``nbytes`` bytes.
+    Raises TypeError or ValueError; nothing has been launched then."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor, got one on {t.device}")
+    if like is not None and t.device != like.device:
+        raise ValueError(f"{name} is on {t.device}, the call's data on {like.device}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} must be one of {[str(d) for d in dtypes]}, got {t.dtype}")
+    if esize is not None and t.element_size() != esize:
+        raise TypeError(f"{name} must have {esize}-byte elements, got {t.dtype}")
+    if dims is not None and t.dim() != dims:
+        raise ValueError(f"{name} must be {dims}-D, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name} holds {have} bytes; the call accesses {nbytes}")
+    return t
+
+
+def _bf16_in(x, name: str):
+    """A BF16 [M, N] device tensor (or its 16-bit integer view)."""
+    return _arg(x, name, dtypes=_BF16, dims=2)
+
+
+def _out(t, name: str, like, nbytes: int, shape, dtype, esize):
+    """A caller-supplied output, checked; or a new one of ``shape`` and ``dtype``."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    return _arg(t, name, like, nbytes, esize=esize)
+
+
+def _outs(like, *specs):
+    """Several outputs, each (tensor or None, name, nbytes, shape, dtype, esize):
+    every tensor the caller gave is checked before any missing one is allocated."""
+    for t, name, nbytes, _, _, esize in specs:
+        if t is not None:
+            _arg(t, name, like, nbytes, esize=esize)
+    return [t if t is not None else torch.empty(shape, dtype=dtype, device=like.device)
+            for t, _, _, shape, dtype, _ in specs]
+
+
+def _f32_words(t, name: str, like, n: int = 1):
+    """``n`` FP32 words on the device (an amax, a global scale, ...)."""
+    return _arg(t, name, like, 4 * n, dtypes=(torch.float32,))
 
 
 def _empty(shape, dtype, like: torch.Tensor) -> torch.Tensor:
     return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+def _tiles(M: int, N: int) -> int:
+    return ((M + 127) // 128) * ((N + 127) // 128)
 
 
 # --------------------------------------------------------------------------- block-wise FP8
@@ -149,20 +198,27 @@ def fp8blk_scale_shape(M: int, N: int):
     return ((M + 127) // 128, (N + 127) // 128)
 
 
+def _codes_in(q, name: str):
+    """A 2-D device tensor of 1-byte codes (E4M3 or packed FP4/INT4)."""
+    return _arg(q, name, esize=1, dims=2)
+
+
 def lpq_quantize_fp8blk(w, q=None, s=None, stream=None):
     """BF16 [M,N] -> (codes [M,N] float8_e4m3fn, FP32 tile scales [ceil(M/128), ceil(N/128)])."""
     w = _bf16_in(w, "w")
     M, N = w.shape
-    q = _empty((M, N), torch.float8_e4m3fn, w) if q is None else q
-    s = _empty(fp8blk_scale_shape(M, N), torch.float32, w) if s is None else s
+    q, s = _outs(w, (q, "q", M * N, (M, N), torch.float8_e4m3fn, 1),
+                 (s, "s", 4 * _tiles(M, N), fp8blk_scale_shape(M, N), torch.float32, 4))
     _check(_L.lpq_quantize_fp8blk(w.data_ptr(), M, N, q.data_ptr(), s.data_ptr(), _stream(stream)),
            "lpq_quantize_fp8blk")
     return q, s
 
 
 def lpq_dequantize_fp8blk(q, s, y=None, stream=None):
+    q = _codes_in(q, "q")
     M, N = q.shape
-    y = _empty((M, N), torch.bfloat16, q) if y is None else y
+    _arg(s, "s", q, 4 * _tiles(M, N), esize=4)
+    y = _out(y, "y", q, 2 * M * N, (M, N), torch.bfloat16, 2)
     _check(_L.lpq_dequantize_fp8blk(q.data_ptr(), s.data_ptr(), M, N, y.data_ptr(), _stream(stream)),
            "lpq_dequantize_fp8blk")
     return y
@@ -170,31 +226,30 @@ def lpq_dequantize_fp8blk(q, s, y=None, stream=None):
 
 # --------------------------------------------------------------------------- MXFP8
 
-def lpq_quantize_mxfp8(w, q=None, e=None, stream=None):
-    """BF16 [M,N] (N % 32 == 0) -> (codes [M,N] float8_e4m3fn, UE8M0 bytes [M,N/32] uint8)."""
+def _mxfp8_quantize(fn, where, w, q, e, stream):
     w = _bf16_in(w, "w")
     M, N = w.shape
-    q = _empty((M, N), torch.float8_e4m3fn, w) if q is None else q
-    e = _empty((M, max(N // 32, 1)), torch.uint8, w) if e is None else e
-    _check(_L.lpq_quantize_mxfp8(w.data_ptr(), M, N, q.data_ptr(), e.data_ptr(), _stream(stream)),
-           "lpq_quantize_mxfp8")
+    q, e = _outs(w, (q, "q", M * N, (M, N), torch.float8_e4m3fn, 1),
+                 (e, "e", M * (N // 32), (M, max(N // 32, 1)), torch.uint8, 1))
+    _check(fn(w.data_ptr(), M, N, q.data_ptr(), e.data_ptr(), _stream(stream)), where)
     return q, e
+
+
+def lpq_quantize_mxfp8(w, q=None, e=None, stream=None):
+    """BF16 [M,N] (N % 32 == 0) -> (codes [M,N] float8_e4m3fn, UE8M0 bytes [M,N/32] uint8)."""
+    return _mxfp8_quantize(_L.lpq_quantize_mxfp8, "lpq_quantize_mxfp8", w, q, e, stream)
 
 
 def lpq_quantize_mxfp8_floor(w, q=None, e=None, stream=None):
     """As lpq_quantize_mxfp8, with the OCP MX floor exponent rule (saturating)."""
-    w = _bf16_in(w, "w")
-    M, N = w.shape
-    q = _empty((M, N), torch.float8_e4m3fn, w) if q is None else q
-    e = _empty((M, max(N // 32, 1)), torch.uint8, w) if e is None else e
-    _check(_L.lpq_quantize_mxfp8_floor(w.data_ptr(), M, N, q.data_ptr(), e.data_ptr(), _stream(stream)),
-           "lpq_quantize_mxfp8_floor")
-    return q, e
+    return _mxfp8_quantize(_L.lpq_quantize_mxfp8_floor, "lpq_quantize_mxfp8_floor", w, q, e, stream)
 
 
 def lpq_dequantize_mxfp8(q, e, y=None, stream=None):
+    q = _codes_in(q, "q")
     M, N = q.shape
-    y = _empty((M, N), torch.bfloat16, q) if y is None else y
+    _arg(e, "e", q, M * (N // 32), esize=1)
+    y = _out(y, "y", q, 2 * M * N, (M, N), torch.bfloat16, 2)
     _check(_L.lpq_dequantize_mxfp8(q.data_ptr(), e.data_ptr(), M, N, y.data_ptr(), _stream(stream)),
            "lpq_dequantize_mxfp8")
     return y
@@ -206,49 +261,59 @@ def lpq_nvfp4_amax(w, amax=None, accumulate=False, stream=None):
     """max |w| into a 1-element FP32 device tensor (max-accumulated when accumulate)."""
     w = _bf16_in(w, "w")
     M, N = w.shape
-    amax = _empty((1,), torch.float32, w) if amax is None else amax
+    amax = _empty((1,), torch.float32, w) if amax is None else _f32_words(amax, "amax", w)
     _check(_L.lpq_nvfp4_amax(w.data_ptr(), M, N, amax.data_ptr(), int(bool(accumulate)), _stream(stream)),
            "lpq_nvfp4_amax")
     return amax
 
 
-def lpq_quantize_nvfp4_ex(w, amax, e4m3_max=448, p=None, s=None, g=None, stream=None):
-    """lpq_quantize_nvfp4 with the global scale fl(A / (6 * e4m3_max)), e4m3_max 448 or 256."""
+def lpq_quantize_nvfp4_ex(w, amax=None, e4m3_max=448, p=None, s=None, g=None, stream=None):
+    """BF16 [M,N] (N % 16 == 0) -> (packed [M,N/2] uint8, E4M3 block scales [M,N/16]
+    float8_e4m3fn, global scale [1] FP32 = fl(A / (6 * e4m3_max))), e4m3_max 448 or 256.
+    amax: 1-element FP32 device tensor holding the group amax A, or None for the
+    tensor's own (computed by the call)."""
     w = _bf16_in(w, "w")
     M, N = w.shape
-    p = _empty((M, max(N // 2, 1)), torch.uint8, w) if p is None else p
-    s = _empty((M, max(N // 16, 1)), torch.float8_e4m3fn, w) if s is None else s
-    g = _empty((1,), torch.float32, w) if g is None else g
-    _check(_L.lpq_quantize_nvfp4_ex(w.data_ptr(), M, N, amax.data_ptr(), int(e4m3_max), p.data_ptr(), s.data_ptr(),
+    if amax is not None:
+        _f32_words(amax, "amax", w)
+    p, s, g = _outs(w, (p, "p", M * (N // 2), (M, max(N // 2, 1)), torch.uint8, 1),
+                    (s, "s", M * (N // 16), (M, max(N // 16, 1)), torch.float8_e4m3fn, 1),
+                    (g, "g", 4, (1,), torch.float32, 4))
+    _check(_L.lpq_quantize_nvfp4_ex(w.data_ptr(), M, N, _ptr(amax), int(e4m3_max), p.data_ptr(), s.data_ptr(),
                                     g.data_ptr(), _stream(stream)), "lpq_quantize_nvfp4_ex")
+    return p, s, g
+
+
+def lpq_quantize_nvfp4(w, amax=None, p=None, s=None, g=None, stream=None):
+    """BF16 [M,N] (N % 16 == 0) with group amax (1-element FP32 device tensor, or None
+    for the tensor's own, computed by the call) -> (packed [M,N/2] uint8, E4M3 block
+    scales [M,N/16] float8_e4m3fn, global scale [1] FP32)."""
+    w = _bf16_in(w, "w")
+    M, N = w.shape
+    if amax is not None:
+        _f32_words(amax, "amax", w)
+    p, s, g = _outs(w, (p, "p", M * (N // 2), (M, max(N // 2, 1)), torch.uint8, 1),
+                    (s, "s", M * (N // 16), (M, max(N // 16, 1)), torch.float8_e4m3fn, 1),
+                    (g, "g", 4, (1,), torch.float32, 4))
+    _check(_L.lpq_quantize_nvfp4(w.data_ptr(), M, N, _ptr(amax), p.data_ptr(), s.data_ptr(), g.data_ptr(),
+                                 _stream(stream)), "lpq_quantize_nvfp4")
     return p, s, g
 
 
 def lpq_nvfp4_qdq_ex(x, amax, e4m3_max=448, y=None, stream=None):
     x = _bf16_in(x, "x")
     M, N = x.shape
-    y = _empty((M, N), torch.bfloat16, x) if y is None else y
+    _f32_words(amax, "amax", x)
+    y = _out(y, "y", x, 2 * M * N, (M, N), torch.bfloat16, 2)
     _check(_L.lpq_nvfp4_qdq_ex(x.data_ptr(), M, N, amax.data_ptr(), int(e4m3_max), y.data_ptr(), _stream(stream)),
            "lpq_nvfp4_qdq_ex")
     return y
 
 
-def lpq_quantize_nvfp4(w, amax, p=None, s=None, g=None, stream=None):
-    """BF16 [M,N] (N % 16 == 0) with group amax (1-element FP32 device tensor) ->
-    (packed [M,N/2] uint8, E4M3 block scales [M,N/16] float8_e4m3fn, global scale [1] FP32)."""
-    w = _bf16_in(w, "w")
-    M, N = w.shape
-    p = _empty((M, max(N // 2, 1)), torch.uint8, w) if p is None else p
-    s = _empty((M, max(N // 16, 1)), torch.float8_e4m3fn, w) if s is None else s
-    g = _empty((1,), torch.float32, w) if g is None else g
-    _check(_L.lpq_quantize_nvfp4(w.data_ptr(), M, N, amax.data_ptr(), p.data_ptr(), s.data_ptr(), g.data_ptr(),
-                                 _stream(stream)), "lpq_quantize_nvfp4")
-    return p, s, g
-
-
 def lpq_nvfp4_global_scale_reciprocal(group_amax, out=None, stream=None):
     """fl(2688 / A) per group (the reciprocal export form of the global scale)."""
-    out = torch.empty_like(group_amax) if out is None else out
+    _f32_words(group_amax, "group_amax", None, group_amax.numel() if isinstance(group_amax, torch.Tensor) else 1)
+    out = torch.empty_like(group_amax) if out is None else _f32_words(out, "out", group_amax, group_amax.numel())
     _check(_L.lpq_nvfp4_global_scale_reciprocal(group_amax.data_ptr(), group_amax.numel(), out.data_ptr(),
                                                 _stream(stream)), "lpq_nvfp4_global_scale_reciprocal")
     return out
@@ -256,7 +321,8 @@ def lpq_nvfp4_global_scale_reciprocal(group_amax, out=None, stream=None):
 
 def lpq_nvfp4_global_scale(amax, out=None, stream=None):
     """fl(A / 2688) per entry (the multiplier form of a global scale)."""
-    out = torch.empty_like(amax) if out is None else out
+    _f32_words(amax, "amax", None, amax.numel() if isinstance(amax, torch.Tensor) else 1)
+    out = torch.empty_like(amax) if out is None else _f32_words(out, "out", amax, amax.numel())
     _check(_L.lpq_nvfp4_global_scale(amax.data_ptr(), amax.numel(), out.data_ptr(), _stream(stream)),
            "lpq_nvfp4_global_scale")
     return out
@@ -271,6 +337,8 @@ def lpq_observer_reset(state=None, device=None, stream=None):
     """A reset observer state (8 FP32 words on the device; allocated when not given)."""
     if state is None:
         state = torch.empty(OBSERVER_STATE_FLOATS, dtype=torch.float32, device=device or "cuda")
+    else:
+        _f32_words(state, "state", None, OBSERVER_STATE_FLOATS)
     _check(_L.lpq_observer_reset(state.data_ptr(), _stream(stream)), "lpq_observer_reset")
     return state
 
@@ -279,7 +347,8 @@ def lpq_nvfp4_observe(x, state, observer="static_minmax", averaging_constant=0.0
     """Update the observer state with the BF16 batch x; returns the activation amax (1 FP32, device)."""
     x = _bf16_in(x, "x")
     M, N = x.shape
-    amax = _empty((1,), torch.float32, x) if amax is None else amax
+    _f32_words(state, "state", x, OBSERVER_STATE_FLOATS)
+    amax = _empty((1,), torch.float32, x) if amax is None else _f32_words(amax, "amax", x)
     kind = OBSERVERS[observer] if isinstance(observer, str) else int(observer)
     _check(_L.lpq_nvfp4_observe(x.data_ptr(), M, N, kind, float(averaging_constant), state.data_ptr(),
                                 amax.data_ptr(), _stream(stream)), "lpq_nvfp4_observe")
@@ -287,18 +356,26 @@ def lpq_nvfp4_observe(x, state, observer="static_minmax", averaging_constant=0.0
 
 
 def lpq_dequantize_nvfp4(p, s, g, y=None, stream=None):
+    p = _codes_in(p, "p")
     M, N = p.shape[0], p.shape[1] * 2
-    y = _empty((M, N), torch.bfloat16, p) if y is None else y
+    _arg(s, "s", p, M * (N // 16), esize=1)
+    _f32_words(g, "g", p)
+    y = _out(y, "y", p, 2 * M * N, (M, N), torch.bfloat16, 2)
     _check(_L.lpq_dequantize_nvfp4(p.data_ptr(), s.data_ptr(), g.data_ptr(), M, N, y.data_ptr(), _stream(stream)),
            "lpq_dequantize_nvfp4")
     return y
 
 
-def lpq_nvfp4_qdq(x, amax, y=None, stream=None):
-    """NVFP4 fake quantization of BF16 [M,N] under the group amax; returns BF16 [M,N]."""
+def lpq_nvfp4_qdq(x, amax=None, y=None, stream=None):
+    """NVFP4 fake quantization of BF16 [M,N] under the group amax (1-element FP32 device
+    tensor); returns BF16 [M,N].  amax None: the tensor's own, from lpq_nvfp4_amax into a
+    new word first (the C call itself requires an amax)."""
     x = _bf16_in(x, "x")
     M, N = x.shape
-    y = _empty((M, N), torch.bfloat16, x) if y is None else y
+    if amax is None:
+        amax = lpq_nvfp4_amax(x, stream=stream)
+    _f32_words(amax, "amax", x)
+    y = _out(y, "y", x, 2 * M * N, (M, N), torch.bfloat16, 2)
     _check(_L.lpq_nvfp4_qdq(x.data_ptr(), M, N, amax.data_ptr(), y.data_ptr(), _stream(stream)), "lpq_nvfp4_qdq")
     return y
 
@@ -308,22 +385,28 @@ def lpq_nvfp4_qdq(x, amax, y=None, stream=None):
 INT4_GROUPS = (32, 128)
 
 
+def _int4_group(group) -> int:
+    return max(int(group), 1)
+
+
 def lpq_quantize_int4(w, group=128, p=None, s=None, stream=None):
     """BF16 [M,N] (N % group == 0) -> (packed two's-complement nibbles [M,N/2] uint8,
     FP32 group scales [M,N/group])."""
     w = _bf16_in(w, "w")
     M, N = w.shape
-    g = max(int(group), 1)
-    p = _empty((M, max(N // 2, 1)), torch.uint8, w) if p is None else p
-    s = _empty((M, max(N // g, 1)), torch.float32, w) if s is None else s
+    G = _int4_group(group)
+    p, s = _outs(w, (p, "p", M * (N // 2), (M, max(N // 2, 1)), torch.uint8, 1),
+                 (s, "s", 4 * M * (N // G), (M, max(N // G, 1)), torch.float32, 4))
     _check(_L.lpq_quantize_int4(w.data_ptr(), M, N, int(group), p.data_ptr(), s.data_ptr(), _stream(stream)),
            "lpq_quantize_int4")
     return p, s
 
 
 def lpq_dequantize_int4(p, s, group=128, y=None, stream=None):
+    p = _codes_in(p, "p")
     M, N = p.shape[0], p.shape[1] * 2
-    y = _empty((M, N), torch.bfloat16, p) if y is None else y
+    _arg(s, "s", p, 4 * M * (N // _int4_group(group)), esize=4)
+    y = _out(y, "y", p, 2 * M * N, (M, N), torch.bfloat16, 2)
     _check(_L.lpq_dequantize_int4(p.data_ptr(), s.data_ptr(), M, N, int(group), y.data_ptr(), _stream(stream)),
            "lpq_dequantize_int4")
     return y
@@ -333,42 +416,21 @@ def lpq_int4_qdq(x, group=128, y=None, stream=None):
     """INT4 fake quantization (the straight-through estimator's forward pass) of BF16 [M,N]."""
     x = _bf16_in(x, "x")
     M, N = x.shape
-    y = _empty((M, N), torch.bfloat16, x) if y is None else y
+    y = _out(y, "y", x, 2 * M * N, (M, N), torch.bfloat16, 2)
     _check(_L.lpq_int4_qdq(x.data_ptr(), M, N, int(group), y.data_ptr(), _stream(stream)), "lpq_int4_qdq")
     return y
 
 
-def lpq_quantize_int4_grouped(table, group=128, stream=None):
-    _check(_L.lpq_quantize_int4_grouped(*table.args(), int(group), _stream(stream)), "lpq_quantize_int4_grouped")
-
-
-def lpq_dequantize_int4_grouped(table, group=128, stream=None):
-    _check(_L.lpq_dequantize_int4_grouped(*table.args(), int(group), _stream(stream)), "lpq_dequantize_int4_grouped")
-
-
-def lpq_int4_qdq_grouped(table, group=128, stream=None):
-    _check(_L.lpq_int4_qdq_grouped(*table.args(), int(group), _stream(stream)), "lpq_int4_qdq_grouped")
-
-
 # --------------------------------------------------------------------------- FP8 re-quantization
-
-def _codes_in(q, name: str):
-    if q.dim() != 2:
-        raise ValueError(f"{name} must be 2-D [M, N]")
-    if q.element_size() != 1:
-        raise TypeError(f"{name} must hold 1-byte E4M3 codes, got {q.dtype}")
-    if not q.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
-    return q.contiguous()
-
 
 def lpq_requantize_fp8blk(q, s, q_out=None, s_out=None, stream=None):
     """Block-wise FP8 (codes [M,N], FP32 tile scales) -> block-wise FP8 of the dequantized
     BF16 values (codes [M,N] float8_e4m3fn, new FP32 tile scales), in one pass."""
     q = _codes_in(q, "q")
     M, N = q.shape
-    q_out = _empty((M, N), torch.float8_e4m3fn, q) if q_out is None else q_out
-    s_out = _empty(fp8blk_scale_shape(M, N), torch.float32, q) if s_out is None else s_out
+    _arg(s, "s", q, 4 * _tiles(M, N), esize=4)
+    q_out, s_out = _outs(q, (q_out, "q_out", M * N, (M, N), torch.float8_e4m3fn, 1),
+                         (s_out, "s_out", 4 * _tiles(M, N), fp8blk_scale_shape(M, N), torch.float32, 4))
     _check(_L.lpq_requantize_fp8blk(q.data_ptr(), s.data_ptr(), M, N, q_out.data_ptr(), s_out.data_ptr(),
                                     _stream(stream)), "lpq_requantize_fp8blk")
     return q_out, s_out
@@ -379,8 +441,9 @@ def lpq_requantize_fp8blk_mxfp8(q, s, q_out=None, e_out=None, stream=None):
     UE8M0 bytes [M,N/32] uint8) of the dequantized BF16 values, in one pass."""
     q = _codes_in(q, "q")
     M, N = q.shape
-    q_out = _empty((M, N), torch.float8_e4m3fn, q) if q_out is None else q_out
-    e_out = _empty((M, max(N // 32, 1)), torch.uint8, q) if e_out is None else e_out
+    _arg(s, "s", q, 4 * _tiles(M, N), esize=4)
+    q_out, e_out = _outs(q, (q_out, "q_out", M * N, (M, N), torch.float8_e4m3fn, 1),
+                         (e_out, "e_out", M * (N // 32), (M, max(N // 32, 1)), torch.uint8, 1))
     _check(_L.lpq_requantize_fp8blk_mxfp8(q.data_ptr(), s.data_ptr(), M, N, q_out.data_ptr(), e_out.data_ptr(),
                                           _stream(stream)), "lpq_requantize_fp8blk_mxfp8")
     return q_out, e_out
@@ -390,7 +453,8 @@ def lpq_fp8blk_amax(q, s, amax=None, accumulate=False, stream=None):
     """max |y| of the dequantized BF16 values into a 1-element FP32 device tensor."""
     q = _codes_in(q, "q")
     M, N = q.shape
-    amax = _empty((1,), torch.float32, q) if amax is None else amax
+    _arg(s, "s", q, 4 * _tiles(M, N), esize=4)
+    amax = _empty((1,), torch.float32, q) if amax is None else _f32_words(amax, "amax", q)
     _check(_L.lpq_fp8blk_amax(q.data_ptr(), s.data_ptr(), M, N, amax.data_ptr(), int(bool(accumulate)),
                               _stream(stream)), "lpq_fp8blk_amax")
     return amax
@@ -401,9 +465,11 @@ def lpq_requantize_fp8blk_nvfp4(q, s, amax, p=None, sb=None, g=None, stream=None
     of the dequantized BF16 values under the group amax (1-element FP32 device tensor)."""
     q = _codes_in(q, "q")
     M, N = q.shape
-    p = _empty((M, max(N // 2, 1)), torch.uint8, q) if p is None else p
-    sb = _empty((M, max(N // 16, 1)), torch.float8_e4m3fn, q) if sb is None else sb
-    g = _empty((1,), torch.float32, q) if g is None else g
+    _arg(s, "s", q, 4 * _tiles(M, N), esize=4)
+    _f32_words(amax, "amax", q)
+    p, sb, g = _outs(q, (p, "p", M * (N // 2), (M, max(N // 2, 1)), torch.uint8, 1),
+                     (sb, "sb", M * (N // 16), (M, max(N // 16, 1)), torch.float8_e4m3fn, 1),
+                     (g, "g", 4, (1,), torch.float32, 4))
     _check(_L.lpq_requantize_fp8blk_nvfp4(q.data_ptr(), s.data_ptr(), M, N, amax.data_ptr(), p.data_ptr(),
                                           sb.data_ptr(), g.data_ptr(), _stream(stream)),
            "lpq_requantize_fp8blk_nvfp4")
@@ -412,129 +478,226 @@ def lpq_requantize_fp8blk_nvfp4(q, s, amax, p=None, sb=None, g=None, stream=None
 
 # --------------------------------------------------------------------------- grouped
 
-class TensorTable:
-    """The n descriptors of a grouped call, in host memory and on the device.
+# Bytes each descriptor array of a grouped call accesses, per operation, for a
+# tensor of M x N elements: (src, dst, scale) of lpq_tensor, or (src,
+# src_scale, dst, dst_scale) of lpq_requant_tensor; None = not accessed.
+def _grouped_bytes(op: str, M: int, N: int, G: int = 128):
+    MN, t = M * N, 4 * _tiles(M, N)
+    return _GROUPED_BYTES[op](MN, t, G)
 
-    ``entries`` is a list of (src, dst, scale, rows, cols, group): torch tensors
-    (dst / scale may be None where the call ignores them), the logical shape
-    M x N of the BF16 tensor, and the NVFP4 sibling group.  The tensors must
-    stay alive while the table is used."""
+
+_GROUPED_BYTES = {
+    "fp8blk_q": lambda MN, t, G: (2 * MN, MN, t),
+    "fp8blk_dq": lambda MN, t, G: (MN, 2 * MN, t),
+    "mxfp8_q": lambda MN, t, G: (2 * MN, MN, MN // 32),
+    "mxfp8_dq": lambda MN, t, G: (MN, 2 * MN, MN // 32),
+    "nvfp4_amax": lambda MN, t, G: (2 * MN, None, None),
+    "nvfp4_q": lambda MN, t, G: (2 * MN, MN // 2, MN // 16),
+    "nvfp4_dq": lambda MN, t, G: (MN // 2, 2 * MN, MN // 16),
+    "nvfp4_qdq": lambda MN, t, G: (2 * MN, 2 * MN, None),
+    "int4_q": lambda MN, t, G: (2 * MN, MN // 2, 4 * (MN // G)),
+    "int4_dq": lambda MN, t, G: (MN // 2, 2 * MN, 4 * (MN // G)),
+    "int4_qdq": lambda MN, t, G: (2 * MN, 2 * MN, None),
+    "rq_fp8": lambda MN, t, G: (MN, t, MN, t),
+    "rq_mx": lambda MN, t, G: (MN, t, MN, MN // 32),
+    "rq_amax": lambda MN, t, G: (MN, t, None, None),
+    "rq_nv": lambda MN, t, G: (MN, t, MN // 2, MN // 16),
+}
+
+
+class _Table:
+    """Descriptors of a grouped call in host memory and, copied once, on the device.
+
+    The device copy is a blocking host-to-device copy: it has completed when the
+    constructor returns, so the table serves calls on any stream.  The tensors
+    named by the entries must stay alive while the table is used."""
+
+    _CTYPE = None
+    _FIELDS = ()
 
     def __init__(self, entries, device=None):
         n = len(entries)
-        self.host = (lpq_tensor * n)()
+        if n == 0:
+            raise ValueError("a grouped call needs at least one tensor")
+        first = entries[0][0]
+        _arg(first, f"entry 0 {self._FIELDS[0]}")
+        dev = torch.device(device) if device is not None else first.device
+        if dev.type == "cuda" and dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        self.host = (self._CTYPE * n)()
         self.keep = []
-        for i, (src, dst, scale, rows, cols, group) in enumerate(entries):
-            self.host[i].src = _ptr(src)
-            self.host[i].dst = _ptr(dst)
-            self.host[i].scale = _ptr(scale)
-            self.host[i].rows = int(rows)
-            self.host[i].cols = int(cols)
-            self.host[i].group = int(group)
-            self.host[i].reserved = 0
-            self.keep.append((src, dst, scale))
+        for i, e in enumerate(entries):
+            tensors, (rows, cols, group) = e[:-3], e[-3:]
+            for name, t in zip(self._FIELDS, tensors):
+                if t is not None and (not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != dev
+                                      or not t.is_contiguous()):
+                    raise ValueError(f"entry {i} {name}: a contiguous tensor on {dev} is required")
+            h = self.host[i]
+            for name, t in zip(self._FIELDS, tensors):
+                setattr(h, name, _ptr(t))
+            h.rows, h.cols, h.group, h.reserved = int(rows), int(cols), int(group), 0
+            self.keep.append(tuple(tensors))
         raw = torch.frombuffer(bytearray(bytes(self.host)), dtype=torch.uint8)
-        dev = device if device is not None else entries[0][0].device
-        self.dev = raw.to(dev)
+        self.dev = torch.empty(raw.numel(), dtype=torch.uint8, device=dev)
+        self.dev.copy_(raw, non_blocking=False)
+        self.device = dev
         self.n = n
+        self._checked = set()
+
+    def check(self, op: str, G: int = 128):
+        """Raise ValueError unless every tensor an operation accesses is large enough
+        (checked once per operation and group size: the entries do not change)."""
+        if (op, G) in self._checked:
+            return self
+        for i, tensors in enumerate(self.keep):
+            h = self.host[i]
+            for name, t, need in zip(self._FIELDS, tensors, _grouped_bytes(op, h.rows, h.cols, G)):
+                if need is None:
+                    continue
+                if t is None:
+                    raise ValueError(f"entry {i}: {op} needs {name}")
+                have = t.numel() * t.element_size()
+                if have < need:
+                    raise ValueError(f"entry {i} {name} holds {have} bytes; {op} accesses {need}")
+        self._checked.add((op, G))
+        return self
 
     def args(self):
         return self.host, self.dev.data_ptr(), self.n
 
 
-class RequantTable:
+class TensorTable(_Table):
+    """The n descriptors of a grouped call.  ``entries`` is a list of (src, dst,
+    scale, rows, cols, group): device tensors (dst / scale may be None where the
+    call ignores them), the logical shape M x N of the BF16 tensor, and the
+    NVFP4 sibling group."""
+
+    _CTYPE = lpq_tensor
+    _FIELDS = ("src", "dst", "scale")
+
+
+class RequantTable(_Table):
     """Descriptors of a grouped re-quantization call: ``entries`` is a list of
     (src codes, src tile scales, dst, dst scales, rows, cols, group)."""
 
-    def __init__(self, entries, device=None):
-        n = len(entries)
-        self.host = (lpq_requant_tensor * n)()
-        self.keep = []
-        for i, (src, src_scale, dst, dst_scale, rows, cols, group) in enumerate(entries):
-            h = self.host[i]
-            h.src, h.src_scale, h.dst, h.dst_scale = _ptr(src), _ptr(src_scale), _ptr(dst), _ptr(dst_scale)
-            h.rows, h.cols, h.group, h.reserved = int(rows), int(cols), int(group), 0
-            self.keep.append((src, src_scale, dst, dst_scale))
-        raw = torch.frombuffer(bytearray(bytes(self.host)), dtype=torch.uint8)
-        dev = device if device is not None else entries[0][0].device
-        self.dev = raw.to(dev)
-        self.n = n
+    _CTYPE = lpq_requant_tensor
+    _FIELDS = ("src", "src_scale", "dst", "dst_scale")
 
-    def args(self):
-        return self.host, self.dev.data_ptr(), self.n
+
+def _group_words(t, name, table, n=None):
+    return _f32_words(t, name, table.dev, t.numel() if n is None and isinstance(t, torch.Tensor) else (n or 1))
 
 
 def lpq_quantize_fp8blk_grouped(table: TensorTable, stream=None):
-    _check(_L.lpq_quantize_fp8blk_grouped(*table.args(), _stream(stream)), "lpq_quantize_fp8blk_grouped")
+    _check(_L.lpq_quantize_fp8blk_grouped(*table.check("fp8blk_q").args(), _stream(stream)),
+           "lpq_quantize_fp8blk_grouped")
 
 
 def lpq_dequantize_fp8blk_grouped(table: TensorTable, stream=None):
-    _check(_L.lpq_dequantize_fp8blk_grouped(*table.args(), _stream(stream)), "lpq_dequantize_fp8blk_grouped")
+    _check(_L.lpq_dequantize_fp8blk_grouped(*table.check("fp8blk_dq").args(), _stream(stream)),
+           "lpq_dequantize_fp8blk_grouped")
 
 
 def lpq_quantize_mxfp8_grouped(table: TensorTable, stream=None):
-    _check(_L.lpq_quantize_mxfp8_grouped(*table.args(), _stream(stream)), "lpq_quantize_mxfp8_grouped")
+    _check(_L.lpq_quantize_mxfp8_grouped(*table.check("mxfp8_q").args(), _stream(stream)),
+           "lpq_quantize_mxfp8_grouped")
 
 
 def lpq_quantize_mxfp8_floor_grouped(table: TensorTable, stream=None):
-    _check(_L.lpq_quantize_mxfp8_floor_grouped(*table.args(), _stream(stream)), "lpq_quantize_mxfp8_floor_grouped")
+    _check(_L.lpq_quantize_mxfp8_floor_grouped(*table.check("mxfp8_q").args(), _stream(stream)),
+           "lpq_quantize_mxfp8_floor_grouped")
 
 
 def lpq_dequantize_mxfp8_grouped(table: TensorTable, stream=None):
-    _check(_L.lpq_dequantize_mxfp8_grouped(*table.args(), _stream(stream)), "lpq_dequantize_mxfp8_grouped")
+    _check(_L.lpq_dequantize_mxfp8_grouped(*table.check("mxfp8_dq").args(), _stream(stream)),
+           "lpq_dequantize_mxfp8_grouped")
 
 
 def lpq_nvfp4_amax_grouped(table: TensorTable, group_amax, accumulate=False, stream=None):
-    _check(_L.lpq_nvfp4_amax_grouped(*table.args(), group_amax.data_ptr(), group_amax.numel(),
+    _group_words(group_amax, "group_amax", table)
+    _check(_L.lpq_nvfp4_amax_grouped(*table.check("nvfp4_amax").args(), group_amax.data_ptr(), group_amax.numel(),
                                      int(bool(accumulate)), _stream(stream)), "lpq_nvfp4_amax_grouped")
     return group_amax
 
 
-def lpq_quantize_nvfp4_grouped(table: TensorTable, group_amax, group_g, stream=None):
-    _check(_L.lpq_quantize_nvfp4_grouped(*table.args(), group_amax.data_ptr(), group_amax.numel(),
-                                         group_g.data_ptr(), _stream(stream)), "lpq_quantize_nvfp4_grouped")
+def lpq_quantize_nvfp4_grouped(table: TensorTable, group_amax, group_g, amax_valid=True, stream=None):
+    """amax_valid False: the call fills group_amax (every member's max |w| folded into
+    its group's slot) before it encodes."""
+    _group_words(group_amax, "group_amax", table)
+    _group_words(group_g, "group_g", table, group_amax.numel())
+    _check(_L.lpq_quantize_nvfp4_grouped(*table.check("nvfp4_q").args(), group_amax.data_ptr(), group_amax.numel(),
+                                         int(bool(amax_valid)), group_g.data_ptr(), _stream(stream)),
+           "lpq_quantize_nvfp4_grouped")
     return group_g
 
 
-def lpq_quantize_nvfp4_grouped_ex(table: TensorTable, group_amax, group_g, e4m3_max=448, stream=None):
-    _check(_L.lpq_quantize_nvfp4_grouped_ex(*table.args(), group_amax.data_ptr(), group_amax.numel(), int(e4m3_max),
-                                            group_g.data_ptr(), _stream(stream)), "lpq_quantize_nvfp4_grouped_ex")
+def lpq_quantize_nvfp4_grouped_ex(table: TensorTable, group_amax, group_g, e4m3_max=448, amax_valid=True,
+                                  stream=None):
+    _group_words(group_amax, "group_amax", table)
+    _group_words(group_g, "group_g", table, group_amax.numel())
+    _check(_L.lpq_quantize_nvfp4_grouped_ex(*table.check("nvfp4_q").args(), group_amax.data_ptr(), group_amax.numel(),
+                                            int(bool(amax_valid)), int(e4m3_max), group_g.data_ptr(),
+                                            _stream(stream)), "lpq_quantize_nvfp4_grouped_ex")
     return group_g
 
 
-def lpq_nvfp4_qdq_grouped_ex(table: TensorTable, group_amax, e4m3_max=448, stream=None):
-    _check(_L.lpq_nvfp4_qdq_grouped_ex(*table.args(), group_amax.data_ptr(), group_amax.numel(), int(e4m3_max),
-                                       _stream(stream)), "lpq_nvfp4_qdq_grouped_ex")
+def lpq_nvfp4_qdq_grouped_ex(table: TensorTable, group_amax, e4m3_max=448, amax_valid=True, stream=None):
+    _group_words(group_amax, "group_amax", table)
+    _check(_L.lpq_nvfp4_qdq_grouped_ex(*table.check("nvfp4_qdq").args(), group_amax.data_ptr(), group_amax.numel(),
+                                       int(bool(amax_valid)), int(e4m3_max), _stream(stream)),
+           "lpq_nvfp4_qdq_grouped_ex")
 
 
 def lpq_dequantize_nvfp4_grouped(table: TensorTable, group_g, stream=None):
-    _check(_L.lpq_dequantize_nvfp4_grouped(*table.args(), group_g.data_ptr(), group_g.numel(), _stream(stream)),
-           "lpq_dequantize_nvfp4_grouped")
+    _group_words(group_g, "group_g", table)
+    _check(_L.lpq_dequantize_nvfp4_grouped(*table.check("nvfp4_dq").args(), group_g.data_ptr(), group_g.numel(),
+                                           _stream(stream)), "lpq_dequantize_nvfp4_grouped")
 
 
-def lpq_nvfp4_qdq_grouped(table: TensorTable, group_amax, stream=None):
-    _check(_L.lpq_nvfp4_qdq_grouped(*table.args(), group_amax.data_ptr(), group_amax.numel(), _stream(stream)),
-           "lpq_nvfp4_qdq_grouped")
+def lpq_nvfp4_qdq_grouped(table: TensorTable, group_amax, amax_valid=True, stream=None):
+    """amax_valid False: the call fills group_amax before it encodes."""
+    _group_words(group_amax, "group_amax", table)
+    _check(_L.lpq_nvfp4_qdq_grouped(*table.check("nvfp4_qdq").args(), group_amax.data_ptr(), group_amax.numel(),
+                                    int(bool(amax_valid)), _stream(stream)), "lpq_nvfp4_qdq_grouped")
+
+
+def lpq_quantize_int4_grouped(table: TensorTable, group=128, stream=None):
+    _check(_L.lpq_quantize_int4_grouped(*table.check("int4_q", _int4_group(group)).args(), int(group),
+                                        _stream(stream)), "lpq_quantize_int4_grouped")
+
+
+def lpq_dequantize_int4_grouped(table: TensorTable, group=128, stream=None):
+    _check(_L.lpq_dequantize_int4_grouped(*table.check("int4_dq", _int4_group(group)).args(), int(group),
+                                          _stream(stream)), "lpq_dequantize_int4_grouped")
+
+
+def lpq_int4_qdq_grouped(table: TensorTable, group=128, stream=None):
+    _check(_L.lpq_int4_qdq_grouped(*table.check("int4_qdq").args(), int(group), _stream(stream)),
+           "lpq_int4_qdq_grouped")
 
 
 def lpq_requantize_fp8blk_grouped(table: RequantTable, stream=None):
-    _check(_L.lpq_requantize_fp8blk_grouped(*table.args(), _stream(stream)), "lpq_requantize_fp8blk_grouped")
+    _check(_L.lpq_requantize_fp8blk_grouped(*table.check("rq_fp8").args(), _stream(stream)),
+           "lpq_requantize_fp8blk_grouped")
 
 
 def lpq_requantize_fp8blk_mxfp8_grouped(table: RequantTable, stream=None):
-    _check(_L.lpq_requantize_fp8blk_mxfp8_grouped(*table.args(), _stream(stream)),
+    _check(_L.lpq_requantize_fp8blk_mxfp8_grouped(*table.check("rq_mx").args(), _stream(stream)),
            "lpq_requantize_fp8blk_mxfp8_grouped")
 
 
 def lpq_fp8blk_amax_grouped(table: RequantTable, group_amax, accumulate=False, stream=None):
-    _check(_L.lpq_fp8blk_amax_grouped(*table.args(), group_amax.data_ptr(), group_amax.numel(),
+    _group_words(group_amax, "group_amax", table)
+    _check(_L.lpq_fp8blk_amax_grouped(*table.check("rq_amax").args(), group_amax.data_ptr(), group_amax.numel(),
                                       int(bool(accumulate)), _stream(stream)), "lpq_fp8blk_amax_grouped")
     return group_amax
 
 
 def lpq_requantize_fp8blk_nvfp4_grouped(table: RequantTable, group_amax, group_g, stream=None):
-    _check(_L.lpq_requantize_fp8blk_nvfp4_grouped(*table.args(), group_amax.data_ptr(), group_amax.numel(),
-                                                  group_g.data_ptr(), _stream(stream)),
+    _group_words(group_amax, "group_amax", table)
+    _group_words(group_g, "group_g", table, group_amax.numel())
+    _check(_L.lpq_requantize_fp8blk_nvfp4_grouped(*table.check("rq_nv").args(), group_amax.data_ptr(),
+                                                  group_amax.numel(), group_g.data_ptr(), _stream(stream)),
            "lpq_requantize_fp8blk_nvfp4_grouped")
     return group_g
 

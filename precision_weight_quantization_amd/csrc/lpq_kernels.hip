@@ -348,9 +348,9 @@ lpq_status single(Kind k, const D& one, const float* fa, float* fb, void* stream
     return launch<D>(k, nullptr, nullptr, 0, one, fa, fb, (hipStream_t)stream, gdiv);
 }
 
+// Checks of a grouped call's tables and of every descriptor for kind k.
 template <typename D>
-lpq_status grouped(Kind k, const D* host, const D* dev, int32_t n, int32_t n_groups, const float* fa, float* fb,
-                   void* stream, float gdiv = 2688.0f) {
+lpq_status check_grouped(Kind k, const D* host, const D* dev, int32_t n, int32_t n_groups) {
     if (!host || !dev) return LPQ_ERR_NULL;
     if (n <= 0) return LPQ_ERR_SHAPE;
     if (!aligned(dev, 8)) return LPQ_ERR_ALIGN;
@@ -358,6 +358,14 @@ lpq_status grouped(Kind k, const D* host, const D* dev, int32_t n, int32_t n_gro
         lpq_status st = check_tensor(k, host[i], n_groups);
         if (st != LPQ_OK) return st;
     }
+    return LPQ_OK;
+}
+
+template <typename D>
+lpq_status grouped(Kind k, const D* host, const D* dev, int32_t n, int32_t n_groups, const float* fa, float* fb,
+                   void* stream, float gdiv = 2688.0f) {
+    lpq_status st = check_grouped(k, host, dev, n, n_groups);
+    if (st != LPQ_OK) return st;
     return launch<D>(k, host, dev, n, D{}, fa, fb, (hipStream_t)stream, gdiv);
 }
 
@@ -408,11 +416,63 @@ lpq_status fill(float* p, int64_t n, float v, void* stream) {
     return launched();
 }
 
+lpq_status global_scale(const float* amax, int32_t n, float* out, float gdiv, void* stream) {
+    hipLaunchKernelGGL(k_global_scale, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                       (hipStream_t)stream, amax, n, out, gdiv);
+    return launched();
+}
+
+// NVFP4 quantize (k = NV_Q) or QDQ (k = NV_QDQ) of one tensor.  With amax ==
+// NULL (quantize only) the tensor's own amax is the group amax ("verl NVFP4
+// QAT" 2.3: a tensor of its own is a group of one): the caller's g word is
+// cleared, receives max |w| from the amax pass, is read as A by the encode
+// (which then leaves it alone), and is finally turned into fl(A / gdiv).  All
+// four launches are on the caller's stream, so each sees the previous one's
+// result.
+lpq_status nvfp4_single(Kind k, const uint16_t* w, int64_t M, int64_t N, const float* amax, int e4m3_max, void* dst,
+                        void* scale, float* g, void* stream) {
+    if ((k == NV_Q && !g) || (k == NV_QDQ && !amax)) return LPQ_ERR_NULL;
+    if ((amax && !aligned(amax, 4)) || (g && !aligned(g, 4))) return LPQ_ERR_ALIGN;
+    const float gdiv = gdiv_of(e4m3_max);
+    if (gdiv == 0.0f) return LPQ_ERR_ARG;
+    const lpq_tensor one = make_one(w, dst, scale, M, N);
+    lpq_status st = check_tensor(k, one, 0);
+    if (st != LPQ_OK) return st;
+    const hipStream_t s = (hipStream_t)stream;
+    if (amax) return launch<lpq_tensor>(k, nullptr, nullptr, 0, one, amax, k == NV_Q ? g : nullptr, s, gdiv);
+    if ((st = fill(g, 1, 0.0f, stream)) != LPQ_OK) return st;
+    if ((st = launch<lpq_tensor>(NV_AMAX, nullptr, nullptr, 0, one, nullptr, g, s)) != LPQ_OK) return st;
+    if ((st = launch<lpq_tensor>(NV_Q, nullptr, nullptr, 0, one, g, nullptr, s, gdiv)) != LPQ_OK) return st;
+    return global_scale(g, 1, g, gdiv, stream);
+}
+
+// Grouped NVFP4 quantize (NV_Q) or QDQ (NV_QDQ).  amax_valid != 0: group_amax
+// holds each group's A (a cached or observed value, or lpq_nvfp4_amax_grouped's
+// result) and is only read.  amax_valid == 0: the call fills it first -- the
+// slots are cleared and the amax pass folds every member's max |w| into its
+// group's slot (the group maximum, "verl NVFP4 QAT" 2.4) -- then encodes.
+lpq_status nvfp4_grouped(Kind k, const lpq_tensor* host, const lpq_tensor* dev, int32_t n, float* group_amax,
+                         int32_t n_groups, int amax_valid, int e4m3_max, float* group_g, void* stream) {
+    if (!group_amax || (k == NV_Q && !group_g)) return LPQ_ERR_NULL;
+    if (n_groups <= 0) return LPQ_ERR_SHAPE;
+    if (!aligned(group_amax, 4) || (group_g && !aligned(group_g, 4))) return LPQ_ERR_ALIGN;
+    const float gdiv = gdiv_of(e4m3_max);
+    if (gdiv == 0.0f) return LPQ_ERR_ARG;
+    lpq_status st = check_grouped(k, host, dev, n, n_groups);   // every amax-pass condition included
+    if (st != LPQ_OK) return st;
+    const hipStream_t s = (hipStream_t)stream;
+    if (!amax_valid) {
+        if ((st = fill(group_amax, n_groups, 0.0f, stream)) != LPQ_OK) return st;
+        if ((st = launch<lpq_tensor>(NV_AMAX, host, dev, n, lpq_tensor{}, nullptr, group_amax, s)) != LPQ_OK) return st;
+    }
+    return launch<lpq_tensor>(k, host, dev, n, lpq_tensor{}, group_amax, k == NV_Q ? group_g : nullptr, s, gdiv);
+}
+
 }  // namespace
 
 extern "C" {
 
-const char* lpq_status_string(int status) {
+const char* lpq_status_string(lpq_status status) {
     switch (status) {
     case LPQ_OK: return "ok";
     case LPQ_ERR_NULL: return "a required pointer is NULL";
@@ -465,9 +525,7 @@ lpq_status lpq_nvfp4_global_scale(const float* amax, int32_t n, float* out, void
     if (!amax || !out) return LPQ_ERR_NULL;
     if (n <= 0) return LPQ_ERR_SHAPE;
     if (!aligned(amax, 4) || !aligned(out, 4)) return LPQ_ERR_ALIGN;
-    hipLaunchKernelGGL(k_global_scale, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                       (hipStream_t)stream, amax, n, out);
-    return launched();
+    return global_scale(amax, n, out, 2688.0f, stream);
 }
 
 lpq_status lpq_observer_reset(float* state, void* stream) {
@@ -508,9 +566,7 @@ lpq_status lpq_nvfp4_amax(const uint16_t* w, int64_t M, int64_t N, float* amax, 
 
 lpq_status lpq_quantize_nvfp4(const uint16_t* w, int64_t M, int64_t N, const float* amax, uint8_t* p, uint8_t* s,
                               float* g, void* stream) {
-    if (!amax || !g) return LPQ_ERR_NULL;
-    if (!aligned(amax, 4) || !aligned(g, 4)) return LPQ_ERR_ALIGN;
-    return single(NV_Q, make_one(w, p, s, M, N), amax, g, stream);
+    return nvfp4_single(NV_Q, w, M, N, amax, 448, p, s, g, stream);
 }
 
 lpq_status lpq_dequantize_nvfp4(const uint8_t* p, const uint8_t* s, const float* g, int64_t M, int64_t N, uint16_t* y,
@@ -521,44 +577,28 @@ lpq_status lpq_dequantize_nvfp4(const uint8_t* p, const uint8_t* s, const float*
 }
 
 lpq_status lpq_nvfp4_qdq(const uint16_t* x, int64_t M, int64_t N, const float* amax, uint16_t* y, void* stream) {
-    if (!amax) return LPQ_ERR_NULL;
-    if (!aligned(amax, 4)) return LPQ_ERR_ALIGN;
-    return single(NV_QDQ, make_one(x, y, nullptr, M, N), amax, nullptr, stream);
+    return nvfp4_single(NV_QDQ, x, M, N, amax, 448, y, nullptr, nullptr, stream);
 }
 
 lpq_status lpq_quantize_nvfp4_ex(const uint16_t* w, int64_t M, int64_t N, const float* amax, int e4m3_max, uint8_t* p,
                                  uint8_t* s, float* g, void* stream) {
-    if (!amax || !g) return LPQ_ERR_NULL;
-    if (!aligned(amax, 4) || !aligned(g, 4)) return LPQ_ERR_ALIGN;
-    if (gdiv_of(e4m3_max) == 0.0f) return LPQ_ERR_ARG;
-    return single(NV_Q, make_one(w, p, s, M, N), amax, g, stream, gdiv_of(e4m3_max));
+    return nvfp4_single(NV_Q, w, M, N, amax, e4m3_max, p, s, g, stream);
 }
 
 lpq_status lpq_nvfp4_qdq_ex(const uint16_t* x, int64_t M, int64_t N, const float* amax, int e4m3_max, uint16_t* y,
                             void* stream) {
-    if (!amax) return LPQ_ERR_NULL;
-    if (!aligned(amax, 4)) return LPQ_ERR_ALIGN;
-    if (gdiv_of(e4m3_max) == 0.0f) return LPQ_ERR_ARG;
-    return single(NV_QDQ, make_one(x, y, nullptr, M, N), amax, nullptr, stream, gdiv_of(e4m3_max));
+    return nvfp4_single(NV_QDQ, x, M, N, amax, e4m3_max, y, nullptr, nullptr, stream);
 }
 
-lpq_status lpq_quantize_nvfp4_grouped_ex(const lpq_tensor* host, const lpq_tensor* dev, int32_t n,
-                                         const float* group_amax, int32_t n_groups, int e4m3_max, float* group_g,
+lpq_status lpq_quantize_nvfp4_grouped_ex(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, float* group_amax,
+                                         int32_t n_groups, int amax_valid, int e4m3_max, float* group_g,
                                          void* stream) {
-    if (!group_amax || !group_g) return LPQ_ERR_NULL;
-    if (n_groups <= 0) return LPQ_ERR_SHAPE;
-    if (!aligned(group_amax, 4) || !aligned(group_g, 4)) return LPQ_ERR_ALIGN;
-    if (gdiv_of(e4m3_max) == 0.0f) return LPQ_ERR_ARG;
-    return grouped(NV_Q, host, dev, n, n_groups, group_amax, group_g, stream, gdiv_of(e4m3_max));
+    return nvfp4_grouped(NV_Q, host, dev, n, group_amax, n_groups, amax_valid, e4m3_max, group_g, stream);
 }
 
-lpq_status lpq_nvfp4_qdq_grouped_ex(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, const float* group_amax,
-                                    int32_t n_groups, int e4m3_max, void* stream) {
-    if (!group_amax) return LPQ_ERR_NULL;
-    if (n_groups <= 0) return LPQ_ERR_SHAPE;
-    if (!aligned(group_amax, 4)) return LPQ_ERR_ALIGN;
-    if (gdiv_of(e4m3_max) == 0.0f) return LPQ_ERR_ARG;
-    return grouped(NV_QDQ, host, dev, n, n_groups, group_amax, nullptr, stream, gdiv_of(e4m3_max));
+lpq_status lpq_nvfp4_qdq_grouped_ex(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, float* group_amax,
+                                    int32_t n_groups, int amax_valid, int e4m3_max, void* stream) {
+    return nvfp4_grouped(NV_QDQ, host, dev, n, group_amax, n_groups, amax_valid, e4m3_max, nullptr, stream);
 }
 
 lpq_status lpq_quantize_fp8blk_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, void* stream) {
@@ -598,12 +638,9 @@ lpq_status lpq_nvfp4_amax_grouped(const lpq_tensor* host, const lpq_tensor* dev,
     return grouped(NV_AMAX, host, dev, n, n_groups, nullptr, group_amax, stream);
 }
 
-lpq_status lpq_quantize_nvfp4_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n,
-                                      const float* group_amax, int32_t n_groups, float* group_g, void* stream) {
-    if (!group_amax || !group_g) return LPQ_ERR_NULL;
-    if (n_groups <= 0) return LPQ_ERR_SHAPE;
-    if (!aligned(group_amax, 4) || !aligned(group_g, 4)) return LPQ_ERR_ALIGN;
-    return grouped(NV_Q, host, dev, n, n_groups, group_amax, group_g, stream);
+lpq_status lpq_quantize_nvfp4_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, float* group_amax,
+                                      int32_t n_groups, int amax_valid, float* group_g, void* stream) {
+    return nvfp4_grouped(NV_Q, host, dev, n, group_amax, n_groups, amax_valid, 448, group_g, stream);
 }
 
 lpq_status lpq_dequantize_nvfp4_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n,
@@ -614,12 +651,9 @@ lpq_status lpq_dequantize_nvfp4_grouped(const lpq_tensor* host, const lpq_tensor
     return grouped(NV_DQ, host, dev, n, n_groups, group_g, nullptr, stream);
 }
 
-lpq_status lpq_nvfp4_qdq_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, const float* group_amax,
-                                 int32_t n_groups, void* stream) {
-    if (!group_amax) return LPQ_ERR_NULL;
-    if (n_groups <= 0) return LPQ_ERR_SHAPE;
-    if (!aligned(group_amax, 4)) return LPQ_ERR_ALIGN;
-    return grouped(NV_QDQ, host, dev, n, n_groups, group_amax, nullptr, stream);
+lpq_status lpq_nvfp4_qdq_grouped(const lpq_tensor* host, const lpq_tensor* dev, int32_t n, float* group_amax,
+                                 int32_t n_groups, int amax_valid, void* stream) {
+    return nvfp4_grouped(NV_QDQ, host, dev, n, group_amax, n_groups, amax_valid, 448, nullptr, stream);
 }
 
 lpq_status lpq_requantize_fp8blk(const uint8_t* q, const float* s, int64_t M, int64_t N, uint8_t* q_out, float* s_out,

@@ -219,10 +219,12 @@ __global__ __launch_bounds__(kThreads) void k_minmax(lpq_tensor one, int kind, f
     }
 }
 
-// fl(A / 2688) per entry: the multiplier form of a global scale.
-__global__ __launch_bounds__(kThreads) void k_global_scale(const float* amax, int32_t n, float* out) {
+// fl(A / gdiv) per entry, gdiv = 6 * the E4M3 maximum (2688 or 1536): the
+// multiplier form of a global scale.  out may be amax itself (each entry is
+// read, then written, by one thread).
+__global__ __launch_bounds__(kThreads) void k_global_scale(const float* amax, int32_t n, float* out, float gdiv) {
     const int32_t i = blockIdx.x * kThreads + threadIdx.x;
-    if (i < n) out[i] = amax[i] / 2688.0f;   // correctly rounded division
+    if (i < n) out[i] = amax[i] / gdiv;   // correctly rounded division
 }
 
 // fl(2688 / A) per group: the reciprocal form of the global scale.
@@ -276,7 +278,9 @@ __global__ __launch_bounds__(TH) void k_nvfp4_quant(const lpq_tensor* table, lpq
     const int gi = GROUPED ? d.group : 0;
     const GlobalScale G = global_scale(group_amax[gi], map.gdiv);
     const int tid = threadIdx.x;
-    if (W.unit == 0 && tid == 0) group_g[gi] = G.g;   // same value from every member
+    // same value from every member; no g pointer: the amax slot is turned into g
+    // by a later launch (the call whose amax the library computes)
+    if (group_g != nullptr && W.unit == 0 && tid == 0) group_g[gi] = G.g;
     // the chunk's origins (uniform); a lane's vector i = u * TH + tid is addressed
     // with a 32-bit offset from them
     const v4u* src = reinterpret_cast<const v4u*>(d.src) + base / 8;

@@ -140,6 +140,17 @@ int main(void) {
     HIP_OK(hipDeviceSynchronize());
     oc_nvfp4_qdq(w, M, N, g, y);
     check("nvfp4 qdq", dy, y, n * 2);
+    /* no amax given: the call computes the tensor's own (in the g word) */
+    HIP_OK(hipMemset(dq, 0, n / 2));
+    lpq_ok(lpq_quantize_nvfp4(dw, M, N, NULL, dq, de, dg, NULL), "lpq_quantize_nvfp4 (amax NULL)");
+    HIP_OK(hipDeviceSynchronize());
+    check("nvfp4 global scale, own amax", dg, &g, 4);
+    check("nvfp4 packed, own amax", dq, q, n / 2);
+    check("nvfp4 block scales, own amax", de, e, n / 16);
+    if (lpq_nvfp4_qdq(dw, M, N, NULL, dy, NULL) != LPQ_ERR_NULL) {   /* QDQ needs its amax */
+        printf("lpq_nvfp4_qdq with amax NULL was not refused with LPQ_ERR_NULL\n");
+        failures++;
+    }
 
     /* group-wise INT4, group 128 */
     lpq_ok(lpq_quantize_int4(dw, M, N, 128, dq, ds4, NULL), "lpq_quantize_int4");

@@ -20,6 +20,18 @@ def host_u16(t: torch.Tensor) -> np.ndarray:
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+def bits32(x) -> np.ndarray:
+    """binary32 bit patterns of a device tensor, a numpy array or a Python float:
+    FP32 results are compared as bits (a -0 / +0 or NaN-payload difference counts)."""
+    if isinstance(x, torch.Tensor):
+        x = x.detach().cpu().numpy()
+    return np.atleast_1d(np.asarray(x, np.float32)).view(np.uint32)
+
+
+def same_bits(a, b) -> bool:
+    return np.array_equal(bits32(a), bits32(b))
+
+
 def mismatches(a: np.ndarray, b: np.ndarray) -> int:
     assert a.shape == b.shape, (a.shape, b.shape)
     return int(np.count_nonzero(a != b))

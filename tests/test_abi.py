@@ -5,6 +5,7 @@ import os
 import re
 
 import pytest
+import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "lpq.h")
@@ -70,14 +71,19 @@ def test_single_call_validation(lib):
     assert L.lpq_dequantize_mxfp8(P, P, 4, 33, P, None) == 2
     assert L.lpq_dequantize_mxfp8(P + 4, P, 4, 32, P, None) == 3
     assert L.lpq_quantize_nvfp4(P, 4, 24, P, P, P, P, None) == 2
-    assert L.lpq_quantize_nvfp4(P, 4, 32, None, P, P, P, None) == 1
     assert L.lpq_quantize_nvfp4(P, 4, 32, P, P, P, None, None) == 1
+    # amax NULL: the call computes the tensor's own amax into g, so g stays required
+    assert L.lpq_quantize_nvfp4(P, 4, 32, None, P, P, None, None) == 1
+    assert L.lpq_quantize_nvfp4(P, 4, 24, None, P, P, P, None) == 2
+    assert L.lpq_quantize_nvfp4(P, 4, 32, None, P, P, P + 2, None) == 3
+    assert L.lpq_quantize_nvfp4_ex(P, 4, 32, None, 256, P, P, None, None) == 1
     assert L.lpq_quantize_nvfp4(P, 4, 32, P + 1, P, P, P, None) == 3
     assert L.lpq_quantize_nvfp4(P + 8, 4, 32, P, P, P, P, None) == 3
     assert L.lpq_quantize_nvfp4(P, 4, 32, P, P + 2, P, P, None) == 3
     assert L.lpq_dequantize_nvfp4(P, P, None, 4, 32, P, None) == 1
     assert L.lpq_dequantize_nvfp4(P, P, P, 4, 32, P + 8, None) == 3
-    assert L.lpq_nvfp4_qdq(P, 4, 32, None, P, None) == 1
+    assert L.lpq_nvfp4_qdq(P, 4, 32, None, P, None) == 1      # QDQ has no word to hold an amax it computed
+    assert L.lpq_nvfp4_qdq_ex(P, 4, 32, None, 448, P, None) == 1
     assert L.lpq_nvfp4_qdq(P, 4, 32, P, None, None) == 1
     assert L.lpq_nvfp4_amax(P, 4, 32, None, 0, None) == 1
     assert L.lpq_nvfp4_amax(P, 4, 8, P, 0, None) == 2
@@ -101,12 +107,23 @@ def test_grouped_validation(lib):
     L = lib.raw()
     good = (P, P, P, 8, 64, 0, 0)
     t = _table(lib, [good, (P, P, P, 8, 64, 3, 0)])
-    assert L.lpq_quantize_nvfp4_grouped(t, P, 2, P, 2, P, None) == 4        # group 3 >= n_groups 2
-    assert L.lpq_quantize_nvfp4_grouped(t, P, 2, P, 4, None, None) == 1
-    assert L.lpq_quantize_nvfp4_grouped(t, P, 0, P, 4, P, None) == 2
-    assert L.lpq_quantize_nvfp4_grouped(None, P, 2, P, 4, P, None) == 1
-    assert L.lpq_quantize_nvfp4_grouped(t, None, 2, P, 4, P, None) == 1
-    assert L.lpq_quantize_nvfp4_grouped(t, P + 4, 2, P, 4, P, None) == 3
+    for valid in (1, 0):   # amax_valid 0 (the call fills group_amax): the same checks, before anything runs
+        assert L.lpq_quantize_nvfp4_grouped(t, P, 2, P, 2, valid, P, None) == 4     # group 3 >= n_groups 2
+        assert L.lpq_quantize_nvfp4_grouped(t, P, 2, P, 4, valid, None, None) == 1
+        assert L.lpq_quantize_nvfp4_grouped(t, P, 2, None, 4, valid, P, None) == 1
+        assert L.lpq_quantize_nvfp4_grouped(t, P, 2, P + 2, 4, valid, P, None) == 3
+        assert L.lpq_quantize_nvfp4_grouped(t, P, 0, P, 4, valid, P, None) == 2
+        assert L.lpq_quantize_nvfp4_grouped(None, P, 2, P, 4, valid, P, None) == 1
+        assert L.lpq_quantize_nvfp4_grouped(t, None, 2, P, 4, valid, P, None) == 1
+        assert L.lpq_quantize_nvfp4_grouped(t, P + 4, 2, P, 4, valid, P, None) == 3
+        assert L.lpq_nvfp4_qdq_grouped(t, P, 2, P, 2, valid, None) == 4
+        assert L.lpq_nvfp4_qdq_grouped(t, P, 2, P, 0, valid, None) == 2
+        assert L.lpq_nvfp4_qdq_grouped(t, P, 2, None, 4, valid, None) == 1
+        assert L.lpq_nvfp4_qdq_grouped(t, P, 2, P + 2, 4, valid, None) == 3
+        assert L.lpq_quantize_nvfp4_grouped_ex(t, P, 2, P, 4, valid, 300, P, None) == 6
+        assert L.lpq_quantize_nvfp4_grouped_ex(t, P, 2, P, 2, valid, 256, P, None) == 4
+        assert L.lpq_nvfp4_qdq_grouped_ex(t, P, 2, P, 4, valid, 100, None) == 6
+        assert L.lpq_nvfp4_qdq_grouped_ex(t, P, 2, P, 2, valid, 256, None) == 4
     t2 = _table(lib, [good, (P, P, P, 8, 63, 0, 0)])
     assert L.lpq_quantize_mxfp8_grouped(t2, P, 2, None) == 2
     assert L.lpq_quantize_mxfp8_floor_grouped(t2, P, 2, None) == 2
@@ -116,7 +133,6 @@ def test_grouped_validation(lib):
     assert L.lpq_quantize_fp8blk_grouped(t4, P, 2, None) == 1
     assert L.lpq_nvfp4_amax_grouped(t, P, 2, P, 2, 0, None) == 4
     assert L.lpq_nvfp4_amax_grouped(t, P, 2, None, 4, 0, None) == 1
-    assert L.lpq_nvfp4_qdq_grouped(t, P, 2, P, 0, None) == 2
     assert L.lpq_dequantize_nvfp4_grouped(t, P, 2, None, 4, None) == 1
     assert L.lpq_last_hip_error() == 0
 
@@ -204,3 +220,107 @@ def test_product_path_has_no_oracle_or_fallback():
             if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f
+
+
+# --------------------------------------------------------------------------- the Python binding's checks
+
+class _FakeDevice(torch.Tensor):
+    """A host tensor that reports itself as a device tensor on ``FAKE_DEVICE``:
+    enough to drive the binding's argument checks without a GPU."""
+
+    FAKE_DEVICE = torch.device("cuda", 0)
+
+    @property
+    def is_cuda(self):
+        return True
+
+    @property
+    def device(self):
+        return self.FAKE_DEVICE
+
+
+def fake(t):
+    return torch.Tensor._make_subclass(_FakeDevice, t)
+
+
+class _OtherDevice(_FakeDevice):
+    FAKE_DEVICE = torch.device("cuda", 1)
+
+
+class _Recorder:
+    """Stands in for the C library: records any call (none may happen)."""
+
+    def __init__(self):
+        self.calls = []
+
+    def __getattr__(self, name):
+        def fn(*args):
+            self.calls.append(name)
+            return 0
+        return fn
+
+
+@pytest.fixture
+def recorder(lib, monkeypatch):
+    r = _Recorder()
+    monkeypatch.setattr(lib, "_L", r)
+    return r
+
+
+def test_binding_refuses_bad_tensors_before_any_call(lib, recorder):
+    bf = lambda *shape: fake(torch.zeros(shape, dtype=torch.bfloat16))
+    u8 = lambda *shape: fake(torch.zeros(shape, dtype=torch.uint8))
+    f32 = lambda *shape: fake(torch.zeros(shape, dtype=torch.float32))
+    w = bf(4, 64)
+    cases = [
+        (ValueError, lambda: lib.lpq_quantize_mxfp8(torch.zeros(4, 64, dtype=torch.bfloat16))),    # host tensor
+        (TypeError, lambda: lib.lpq_quantize_mxfp8(fake(torch.zeros(4, 64)))),                     # FP32, not BF16
+        (ValueError, lambda: lib.lpq_quantize_mxfp8(bf(4, 64, 1))),                                 # not 2-D
+        (ValueError, lambda: lib.lpq_quantize_mxfp8(fake(torch.zeros(64, 4, dtype=torch.bfloat16).t()))),
+        (ValueError, lambda: lib.lpq_quantize_mxfp8(w, q=u8(4, 63))),                               # too small
+        (ValueError, lambda: lib.lpq_quantize_mxfp8(w, e=u8(4, 1))),
+        (ValueError, lambda: lib.lpq_quantize_mxfp8(w, q=u8(64, 4).t())),                           # strided out
+        (TypeError, lambda: lib.lpq_quantize_fp8blk(w, s=fake(torch.zeros(1, 1, dtype=torch.float16)))),
+        (ValueError, lambda: lib.lpq_dequantize_fp8blk(u8(4, 64), f32(1, 1), y=bf(4, 63))),
+        (ValueError, lambda: lib.lpq_dequantize_fp8blk(u8(200, 64), f32(1, 1))),                    # 2 tiles
+        (ValueError, lambda: lib.lpq_dequantize_mxfp8(u8(4, 64), u8(4, 1))),
+        (ValueError, lambda: lib.lpq_quantize_nvfp4(w, amax=torch.zeros(1))),                       # host amax
+        (ValueError, lambda: lib.lpq_quantize_nvfp4(w, amax=torch.Tensor._make_subclass(_OtherDevice,
+                                                                                         torch.zeros(1)))),
+        (TypeError, lambda: lib.lpq_quantize_nvfp4(w, amax=fake(torch.zeros(1, dtype=torch.float64)))),
+        (ValueError, lambda: lib.lpq_quantize_nvfp4(w, p=u8(4, 31))),
+        (ValueError, lambda: lib.lpq_quantize_nvfp4(w, g=f32(0))),
+        (ValueError, lambda: lib.lpq_dequantize_nvfp4(u8(4, 32), u8(4, 3), f32(1))),
+        (ValueError, lambda: lib.lpq_nvfp4_qdq(w, f32(1), y=bf(4, 32))),
+        (ValueError, lambda: lib.lpq_quantize_int4(w, 32, s=f32(4, 1))),
+        (ValueError, lambda: lib.lpq_dequantize_int4(u8(4, 32), f32(4, 1), 32)),
+        (ValueError, lambda: lib.lpq_requantize_fp8blk_nvfp4(u8(4, 64), f32(1, 1), f32(1), sb=u8(4, 3))),
+        (ValueError, lambda: lib.lpq_nvfp4_observe(w, f32(4))),                                     # state: 8 words
+        (ValueError, lambda: lib.lpq_nvfp4_global_scale(f32(4), out=f32(3))),
+    ]
+    for exc, call in cases:
+        with pytest.raises(exc):
+            call()
+    assert recorder.calls == []
+
+
+def test_tensor_table_checks(lib, recorder):
+    with pytest.raises(ValueError):   # a host tensor in an entry: refused before the table is copied anywhere
+        lib.TensorTable([(fake(torch.zeros(4, 64, dtype=torch.bfloat16)), torch.zeros(4, 64, dtype=torch.uint8),
+                          None, 4, 64, 0)])
+    with pytest.raises(ValueError):
+        lib.TensorTable([])
+    # the per-operation size check, on a table whose device copy is skipped
+    t = lib.TensorTable.__new__(lib.TensorTable)
+    src = fake(torch.zeros(4, 64, dtype=torch.bfloat16))
+    t.host = (lib.lpq_tensor * 1)()
+    t.host[0].rows, t.host[0].cols = 4, 64
+    t.keep = [(src, fake(torch.zeros(4 * 32 - 1, dtype=torch.uint8)), fake(torch.zeros(16, dtype=torch.uint8)))]
+    t._checked = set()
+    with pytest.raises(ValueError):
+        t.check("nvfp4_q")           # packed output one byte short
+    t.check("nvfp4_amax")            # the amax pass reads src only
+    t.keep = [(src, None, None)]
+    with pytest.raises(ValueError):
+        t.check("nvfp4_qdq")         # QDQ needs dst
+    assert recorder.calls == []

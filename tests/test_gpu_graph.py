@@ -17,7 +17,7 @@ import torch
 
 from oracle import oracle as O
 from synth import synth
-from tests.gpu_util import host_u8, host_u16, report, to_dev_bf16
+from tests.gpu_util import host_u8, host_u16, report, same_bits, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -127,7 +127,7 @@ def test_grouped_calls_in_a_graph(lpq):
         for gid in range(NG):
             members = [i for i in range(len(SHAPES)) if GROUPS[i] == gid]
             A, og, res = O.nvfp4_quantize_group([ws[i] for i in members])
-            assert float(amax[gid].item()) == A and float(g[gid].item()) == og, (rep, gid)
+            assert same_bits(amax[gid], A) and same_bits(g[gid], og), (rep, gid)
             for i, (op, os_) in zip(members, res):
                 oy = O.nvfp4_dequantize(op, os_, og)
                 bad += report(f"graph {rep} nvfp4 packed {i}", host_u8(np_[i]), op)

@@ -12,7 +12,7 @@ import torch
 
 from oracle import oracle as O
 from synth import synth
-from tests.gpu_util import host_u8, host_u16, report, to_dev_bf16
+from tests.gpu_util import host_u8, host_u16, report, same_bits, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -92,7 +92,7 @@ def test_split_nvfp4_siblings(lpq, weights):
     bad = 0
     for gid, idx in sorted(members.items()):
         A, og, res = O.nvfp4_quantize_group([ws[i] for i in idx])
-        assert float(amax[gid].item()) == A and float(g[gid].item()) == og, gid
+        assert same_bits(amax[gid], A) and same_bits(g[gid], og), gid
         for i, (op, os_) in zip(idx, res):
             oy = O.nvfp4_dequantize(op, os_, og)
             bad += report(f"nvfp4 packed {i}", host_u8(ps[i]), op) + report("  scales", host_u8(ss[i]), os_)

@@ -10,7 +10,8 @@ import torch
 
 from oracle import oracle as O
 from synth import synth
-from tests.gpu_util import brute_blocks, f2bf, finite_bf16, host_u8, host_u16, mismatches, report, to_dev_bf16
+from tests.gpu_util import (bits32, brute_blocks, f2bf, finite_bf16, host_u8, host_u16, mismatches, report,
+                            same_bits, to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -57,9 +58,14 @@ def check_nvfp4(lpq, w_np, name=""):
     yq = lpq.lpq_nvfp4_qdq(w, amax)
     A, og, [(op, os_)] = O.nvfp4_quantize_group([w_np])
     oy = O.nvfp4_dequantize(op, os_, og)
-    assert float(amax.item()) == A, (float(amax.item()), A)
-    assert np.float32(g.item()).view(np.uint32) == np.float32(og).view(np.uint32)
-    bad = report(f"nvfp4 packed {name}", host_u8(p), op)
+    assert same_bits(amax, A), (float(amax.item()), A)
+    assert same_bits(g, og)
+    # the same call with no amax given: the library computes the tensor's own
+    p2, s2, g2 = lpq.lpq_quantize_nvfp4(w)
+    assert same_bits(g2, og)
+    bad = report(f"nvfp4 packed, amax computed by the call {name}", host_u8(p2), op)
+    bad += report(f"nvfp4 block scales, amax computed by the call {name}", host_u8(s2), os_)
+    bad += report(f"nvfp4 packed {name}", host_u8(p), op)
     bad += report(f"nvfp4 block scales {name}", host_u8(s), os_)
     bad += report(f"nvfp4 dequant {name}", host_u16(y), oy)
     bad += report(f"nvfp4 qdq {name}", host_u16(yq), O.nvfp4_qdq(w_np, og))
@@ -118,7 +124,7 @@ def test_fp8blk_unaligned_pointers(lpq):
     st = raw.lpq_quantize_fp8blk(w.data_ptr(), M, N, q.data_ptr(), s.data_ptr(), torch.cuda.current_stream().cuda_stream)
     assert st == 0
     oq, os_ = O.fp8blk_quantize(w_np)
-    assert mismatches(host_u8(q), oq) == 0 and mismatches(s.cpu().numpy(), os_) == 0
+    assert mismatches(host_u8(q), oq) == 0 and mismatches(bits32(s), bits32(os_)) == 0
 
 
 def test_extreme_values(lpq):
@@ -181,7 +187,9 @@ def test_nvfp4_e4m3_max_256_single(lpq, M, N):
     p, s, g = lpq.lpq_quantize_nvfp4_ex(w, amax, 256)
     yq = lpq.lpq_nvfp4_qdq_ex(w, amax, 256)
     A, og, [(op, os_)] = O.nvfp4_quantize_group([w_np], 256)
-    bad = int(np.float32(g.item()).view(np.uint32) != np.float32(og).view(np.uint32))
+    bad = int(not same_bits(g, og))
+    p2, s2, g2 = lpq.lpq_quantize_nvfp4_ex(w, None, 256)     # amax computed by the call
+    bad += int(not same_bits(g2, og)) + report("packed, own amax", host_u8(p2), op) + report("scales", host_u8(s2), os_)
     bad += report(f"nvfp4/256 packed {M}x{N}", host_u8(p), op) + report("scales", host_u8(s), os_)
     bad += report("qdq", host_u16(yq), O.nvfp4_qdq(w_np, og))
     assert int(host_u8(s).max()) <= 0x78   # block-scale codes stay at or below 256 (0x78)
@@ -225,6 +233,15 @@ def test_bruteforce_nvfp4_grouped(lpq, e4m3_max):
     lpq.lpq_dequantize_nvfp4_grouped(tdq, g)
     hp, hs, hy, hyq = host_u8(p), host_u8(s), host_u16(y), host_u16(yq)
     hg = g.cpu().numpy()
+    # the same calls with amax_valid False: each call fills the group amax itself
+    # (slots start as NaN here: the call must overwrite every one)
+    amax2 = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    amax3 = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    g2 = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    lpq.lpq_quantize_nvfp4_grouped_ex(tq, amax2, g2, e4m3_max, amax_valid=False)
+    hp2, hs2 = host_u8(p), host_u8(s)
+    lpq.lpq_nvfp4_qdq_grouped_ex(tqdq, amax3, e4m3_max, amax_valid=False)
+    hyq2 = host_u16(yq)
     op = np.empty_like(hp); os_ = np.empty_like(hs); oy = np.empty_like(hy); og = np.empty(n, np.float32)
     for i in range(n):
         A, og[i], [(a, b)] = O.nvfp4_quantize_group([w_np[i:i + 1]], e4m3_max)
@@ -236,6 +253,12 @@ def test_bruteforce_nvfp4_grouped(lpq, e4m3_max):
     bad += report("bruteforce nvfp4 scales", hs, os_)
     bad += report("bruteforce nvfp4 dequant", hy, oy)
     bad += report("bruteforce nvfp4 qdq", hyq, oy)
+    bad += report("bruteforce nvfp4 amax filled by quantize", bits32(amax2), bits32(amax))
+    bad += report("bruteforce nvfp4 amax filled by qdq", bits32(amax3), bits32(amax))
+    bad += report("bruteforce nvfp4 g, amax filled", bits32(g2), og.view(np.uint32))
+    bad += report("bruteforce nvfp4 packed, amax filled", hp2, op)
+    bad += report("bruteforce nvfp4 scales, amax filled", hs2, os_)
+    bad += report("bruteforce nvfp4 qdq, amax filled", hyq2, oy)
     assert bad == 0
 
 
@@ -327,10 +350,27 @@ def test_grouped_mixed_shapes_and_siblings(lpq):
     lpq.lpq_dequantize_nvfp4_grouped(tdq, g)
     lpq.lpq_nvfp4_qdq_grouped(tqdq, amax)
     bad = 0
+    # amax_valid False: quantize and QDQ fill their group amax themselves (from NaN)
+    ps2 = [torch.empty_like(t) for t in ps]
+    ss2 = [torch.empty_like(t) for t in ss]
+    yq2 = [torch.empty_like(t) for t in yq]
+    amax2 = torch.full((4,), float("nan"), dtype=torch.float32, device="cuda")
+    amax3 = torch.full((4,), float("nan"), dtype=torch.float32, device="cuda")
+    g2 = torch.full((4,), float("nan"), dtype=torch.float32, device="cuda")
+    lpq.lpq_quantize_nvfp4_grouped(lpq.TensorTable([(dw[i], ps2[i], ss2[i], M, N, groups[nm])
+                                                    for i, (nm, M, N) in enumerate(shapes)]), amax2, g2,
+                                   amax_valid=False)
+    lpq.lpq_nvfp4_qdq_grouped(lpq.TensorTable([(dw[i], yq2[i], None, M, N, groups[nm])
+                                               for i, (nm, M, N) in enumerate(shapes)]), amax3, amax_valid=False)
+    bad += mismatches(bits32(amax2), bits32(amax)) + mismatches(bits32(amax3), bits32(amax))
+    bad += mismatches(bits32(g2), bits32(g))
+    for i in range(len(shapes)):
+        bad += mismatches(host_u8(ps2[i]), host_u8(ps[i])) + mismatches(host_u8(ss2[i]), host_u8(ss[i]))
+        bad += mismatches(host_u16(yq2[i]), host_u16(yq[i]))
     for gid in range(4):
         members = [i for i, (nm, _, _) in enumerate(shapes) if groups[nm] == gid]
         A, og, outs = O.nvfp4_quantize_group([ws[i] for i in members])
-        assert float(amax[gid].item()) == A and float(g[gid].item()) == og
+        assert same_bits(amax[gid], A) and same_bits(g[gid], og)
         for i, (op, os_) in zip(members, outs):
             bad += mismatches(host_u8(ps[i]), op) + mismatches(host_u8(ss[i]), os_)
             oy = O.nvfp4_dequantize(op, os_, og)
@@ -349,7 +389,7 @@ def test_grouped_mixed_shapes_and_siblings(lpq):
     lpq.lpq_dequantize_fp8blk_grouped(lpq.TensorTable([(qs[i], ys[i], sc[i], M, N, 0) for i, (_, M, N) in enumerate(shapes)]))
     for i in range(len(shapes)):
         oq, os_ = O.fp8blk_quantize(ws[i])
-        bad += mismatches(host_u8(qs[i]), oq) + mismatches(sc[i].cpu().numpy(), os_)
+        bad += mismatches(host_u8(qs[i]), oq) + mismatches(bits32(sc[i]), bits32(os_))
         bad += mismatches(host_u16(ys[i]), O.fp8blk_dequantize(oq, os_))
     assert bad == 0
 
@@ -369,4 +409,24 @@ def test_amax_accumulate(lpq):
     m = lpq.lpq_nvfp4_amax(a)
     lpq.lpq_nvfp4_amax(b, m, accumulate=True)
     want = max(O.amax(host_u16(a)), O.amax(host_u16(b)))
-    assert float(m.item()) == want
+    assert same_bits(m, want)
+
+
+def test_binding_refuses_undersized_and_host_tensors(lpq):
+    """The Python binding checks every tensor before its address reaches a kernel."""
+    w = to_dev_bf16(synth.generate(94, 1, 64, 256, *synth.DIST_MOE))
+    with pytest.raises(ValueError):
+        lpq.lpq_quantize_mxfp8(w, q=torch.empty((64, 255), dtype=torch.uint8, device="cuda"))
+    with pytest.raises(ValueError):
+        lpq.lpq_quantize_nvfp4(w, amax=torch.zeros(1))                       # host amax
+    with pytest.raises(ValueError):
+        lpq.lpq_dequantize_nvfp4(torch.empty((64, 128), dtype=torch.uint8, device="cuda"),
+                                 torch.empty((64, 15), dtype=torch.uint8, device="cuda"), torch.ones(1, device="cuda"))
+    with pytest.raises(ValueError):
+        lpq.lpq_nvfp4_qdq(w, lpq.lpq_nvfp4_amax(w), y=torch.empty((64, 256), dtype=torch.bfloat16,
+                                                                  device="cuda").t().contiguous().t())
+    short = torch.empty((64, 100), dtype=torch.uint8, device="cuda")
+    t = lpq.TensorTable([(w, short, short, 64, 256, 0)])
+    with pytest.raises(ValueError):
+        lpq.lpq_quantize_mxfp8_grouped(t)
+    torch.cuda.synchronize()
