@@ -389,7 +389,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--bucket", choices=("layer", "all"), default="layer")
+    ap.add_argument("--bucket", choices=("sync", "layer", "all"), default="sync")
     ap.add_argument("--workloads", default="dense,moe,nvfp4,dsv3,fp8train,int4")
     ap.add_argument("--cpu-stride", type=int, default=12)
     ap.add_argument("--cpu-threads", type=int, default=0)

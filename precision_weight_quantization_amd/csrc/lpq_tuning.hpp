@@ -83,7 +83,7 @@
 #define LPQ_NVD_AHEAD 0
 #endif
 #ifndef LPQ_DQF_AHEAD
-#define LPQ_DQF_AHEAD 0
+#define LPQ_DQF_AHEAD 1
 #endif
 #ifndef LPQ_RQM_AHEAD
 #define LPQ_RQM_AHEAD 1
@@ -113,9 +113,9 @@
 #define LPQ_FLAT_THREADS 256
 #endif
 // Workgroup size of each flat kernel (64 to 512, a multiple of 64), measured
-// per kernel: the NVFP4 encoder runs best with one wave, MXFP8 encoding and the
-// QDQs with 128 threads, the NVFP4 and INT4 decoders and the INT4 encoder with
-// 512, the rest with 256.
+// per kernel: the NVFP4 encoder runs best with one wave, MXFP8 encoding, the
+// QDQs and the flat block-FP8 decoder with 128 threads, the NVFP4 and INT4
+// decoders and the INT4 encoder with 512, the rest with 256.
 #ifndef LPQ_MXQ_T
 #define LPQ_MXQ_T 128
 #endif
@@ -144,7 +144,7 @@
 #define LPQ_I4QDQ_T 128
 #endif
 #ifndef LPQ_DQF_T
-#define LPQ_DQF_T LPQ_FLAT_THREADS
+#define LPQ_DQF_T 128
 #endif
 #ifndef LPQ_RQM_T
 #define LPQ_RQM_T LPQ_FLAT_THREADS

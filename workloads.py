@@ -28,8 +28,9 @@ distributions named for each workload.
           "INT4 QAT 训练" gives for Qwen3-30B-A3B) quantize, dequantize and
           fake-quant.  Timed apart from the step.
 
-Buckets: one grouped launch per transformer layer (the unit a weight sync
-streams), or one launch over the whole workload.
+Buckets: one grouped launch per weight-sync bucket of about 1-3 GB (a
+Qwen3-30B-A3B layer, four Qwen3-4B layers, one DeepSeek-V3 expert-parallel
+rank's 32 experts), per transformer layer, or over the whole workload.
 """
 from __future__ import annotations
 
@@ -153,8 +154,33 @@ class Op:
             f()
 
 
+# Weight-sync buckets: the tensors one grouped launch covers.  A weight sync
+# streams its buckets one after another; "sync" (the default) keeps each at
+# about 1-3 GB of BF16: a Qwen3-30B-A3B layer (384 expert tensors, 1.2 GB), four
+# Qwen3-4B layers (28 tensors, 1.2 GB), one DeepSeek-V3 expert-parallel rank's
+# share (32 of 256 experts, 96 tensors, 2.8 GB).  Measured on the DeepSeek-V3
+# layer: block-FP8 quantize 73% of HBM peak as one 22.5 GB launch against 78%
+# in such buckets (MXFP8 quantize on the same tensors: 77% against 82%); on
+# Qwen3-4B, 70% per layer against 75% for four layers.  "layer" and "all" are
+# one launch per transformer layer and one launch over everything.
+DENSE_LAYERS_PER_BUCKET = 4
+EP_RANK_EXPERTS = 32
+
+
 def _buckets(ws: WeightSet, bucket: str):
-    return ws.layers() if bucket == "layer" else [list(range(len(ws.specs)))]
+    if bucket == "all":
+        return [list(range(len(ws.specs)))]
+    if bucket == "layer":
+        return ws.layers()
+    if ws.config == 2:      # Qwen3-4B dense
+        layers = ws.layers()
+        return [sum(layers[i:i + DENSE_LAYERS_PER_BUCKET], []) for i in range(0, len(layers), DENSE_LAYERS_PER_BUCKET)]
+    if ws.config == 5:      # DeepSeek-V3 MoE layer: per expert-parallel rank
+        out = {}
+        for i, s in enumerate(ws.specs):
+            out.setdefault(s.expert // EP_RANK_EXPERTS, []).append(i)
+        return [out[k] for k in sorted(out)]
+    return ws.layers()
 
 
 def fp8blk_ops(tag: str, ws: WeightSet, codes: Slab, scales: Slab, out: Slab, bucket: str):
@@ -376,7 +402,7 @@ def reslab(slab: Slab, specs, bytes_per_elem):
 class Bench:
     """All workloads' tensors and operations, buffers shared where the order allows."""
 
-    def __init__(self, which=WORKLOADS, bucket="layer", device="cuda", log=print, scale_layers=None):
+    def __init__(self, which=WORKLOADS, bucket="sync", device="cuda", log=print, scale_layers=None):
         self.ops = []
         self.next_ops = []      # widening rows: timed apart from the step
         self.outputs = {}
