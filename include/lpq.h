@@ -56,7 +56,13 @@
 extern "C" {
 #endif
 
+/* C++ sees a fixed 32-bit int underlying type, so that any int a C caller
+ * passes (lpq_status_string of an unknown code) is a valid value there too. */
+#ifdef __cplusplus
+typedef enum lpq_status : int {
+#else
 typedef enum lpq_status {
+#endif
     LPQ_OK = 0,
     LPQ_ERR_NULL = 1,   /* a required pointer is NULL                                   */
     LPQ_ERR_SHAPE = 2,  /* M or N <= 0, N not a multiple of the block (32 MXFP8, 16
