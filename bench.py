@@ -176,6 +176,7 @@ def cpu_baseline(bench, stride: int, threads: int):
     t1 = time.perf_counter()
     bad1 = sum(j[0]() for j in one)
     dt1 = time.perf_counter() - t1
+    lin = linear_single_thread()
     return {
         "value": round(total / dt / GB, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
         "sample": f"every {stride}th tensor (NVFP4: every {stride}th sibling group) of each workload op, plus the "
@@ -183,9 +184,45 @@ def cpu_baseline(bench, stride: int, threads: int):
         "seconds": round(dt, 2),
         "parity_mismatches": int(sum(res)) + int(bad1),
         "single_thread": {"value": round(one_bytes / dt1 / GB, 3), "unit": "GB/s", "cores": 1,
+                          "workload": "Qwen3-4B dense block-FP8 quantize",
                           "sample": f"the first {len(one)} of those calls ({one_bytes / GB:.2f} GB algorithmic), "
                                     f"{dt1:.1f} s"},
+        "single_thread_linear": lin,
     }
+
+
+def linear_single_thread(min_seconds: float = 1.0):
+    """One host thread on the 256x512 single-Linear case: block-FP8, MXFP8 and
+    NVFP4 quantize + dequantize and the NVFP4 QDQ, repeated for `min_seconds`."""
+    from oracle import oracle as O
+    from synth import synth
+
+    w = synth.single_linear()
+    n, M, N = w.size, w.shape[0], w.shape[1]
+    tiles = -(-M // 128) * -(-N // 128)
+    per_pass = (2 * (3 * n + 4 * tiles) + 2 * (3 * n + n // 32) + 2 * (2 * n + n // 2 + n // 16 + 4) + 4 * n)
+    orc = O.default()
+
+    def one_pass():
+        q, s = orc.fp8blk_quantize(w)
+        orc.fp8blk_dequantize(q, s)
+        q, e = orc.mxfp8_quantize(w)
+        orc.mxfp8_dequantize(q, e)
+        _, g, ((p, sb),) = orc.nvfp4_quantize_group([w])
+        orc.nvfp4_dequantize(p, sb, g)
+        orc.nvfp4_qdq(w, g)
+
+    one_pass()
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        one_pass()
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {"value": round(passes * per_pass / dt / GB, 3), "unit": "GB/s", "cores": 1,
+            "workload": f"single Linear {M}x{N}, all formats quantize + dequantize + NVFP4 QDQ",
+            "sample": f"{passes} passes of {per_pass} algorithmic bytes, {dt:.2f} s"}
 
 
 def next_rows_parity(bench, stride: int, threads: int):
@@ -486,7 +523,8 @@ def main():
         log(f"cpu baseline: oracle on a 1/{args.cpu_stride} sample with {threads} threads")
         cpu = cpu_baseline(bench, args.cpu_stride, threads)
         log(f"cpu baseline: {cpu['value']} GB/s, {cpu['parity_mismatches']} mismatches vs GPU, {cpu['seconds']} s; "
-            f"one thread: {cpu['single_thread']['value']} GB/s ({cpu['single_thread']['sample']})")
+            f"one thread: {cpu['single_thread']['value']} GB/s ({cpu['single_thread']['sample']}); "
+            f"one thread on the single Linear: {cpu['single_thread_linear']['value']} GB/s")
 
     result = {
         "metric": "quantize+dequant GB/s (bytes in+out) and % of HBM peak, per format, 1 GPU",

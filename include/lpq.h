@@ -344,14 +344,15 @@ lpq_status lpq_nvfp4_qdq_grouped_ex(const lpq_tensor* host, const lpq_tensor* de
  *
  * state: LPQ_OBSERVER_STATE_FLOATS words of caller-owned device memory, 4-byte
  * aligned, one per observed tensor: [0] min, [1] max, [2] batches seen (FP32),
- * the rest scratch of the calls below.  Reset it once before first use; calls
+ * the rest scratch of the calls below (on cache lines of their own: 512
+ * bytes in all).  Reset it once before first use; calls
  * on one state must not overlap.  The amax feeds lpq_nvfp4_qdq (the W4A4
  * activation fake-quant) or lpq_nvfp4_global_scale[_reciprocal] (the exported
  * input_scale / input_global_scale). */
 #define LPQ_OBSERVER_MEMORYLESS_MINMAX 0
 #define LPQ_OBSERVER_STATIC_MINMAX 1
 #define LPQ_OBSERVER_MINMAX 2
-#define LPQ_OBSERVER_STATE_FLOATS 8
+#define LPQ_OBSERVER_STATE_FLOATS 128
 
 lpq_status lpq_observer_reset(float* state, void* stream);
 

@@ -330,7 +330,7 @@ def lpq_nvfp4_global_scale(amax, out=None, stream=None):
 
 # W4A4 activation observers (the C constants of the same names)
 OBSERVERS = {"memoryless_minmax": 0, "static_minmax": 1, "minmax": 2}
-OBSERVER_STATE_FLOATS = 8
+OBSERVER_STATE_FLOATS = 128
 
 
 def lpq_observer_reset(state=None, device=None, stream=None):

@@ -70,7 +70,7 @@ inline lpq_status launched() {
 }
 
 enum Kind {
-    FP8BLK_Q, FP8BLK_QW, FP8BLK_DQ, FP8BLK_DQF, MXFP8_Q, MXFP8_QF, MXFP8_DQ, NV_AMAX, NV_Q, NV_DQ, NV_QDQ,
+    FP8BLK_Q, FP8BLK_QW, FP8BLK_DQ, FP8BLK_DQF, MXFP8_Q, MXFP8_QF, MXFP8_DQ, NV_AMAX, NV_Q, NV_DQ, NV_QDQ, NV_QDQ_W,
     I4_Q32, I4_Q128, I4_DQ32, I4_DQ128, I4_QDQ32, I4_QDQ128,
     RQ_FP8, RQ_MX, RQ_AMAX, RQ_NV
 };
@@ -169,6 +169,7 @@ int64_t units(Kind k, const lpq_tensor& t) {
     case NV_Q: return (n + chunk_elems<LPQ_NVQ_U, LPQ_NVQ_T>() - 1) / chunk_elems<LPQ_NVQ_U, LPQ_NVQ_T>();
     case NV_DQ: return (n + chunk_elems<LPQ_NVD_U, LPQ_NVD_T>() - 1) / chunk_elems<LPQ_NVD_U, LPQ_NVD_T>();
     case NV_QDQ: return (n + chunk_elems<LPQ_QDQ_U, LPQ_QDQ_T>() - 1) / chunk_elems<LPQ_QDQ_U, LPQ_QDQ_T>();
+    case NV_QDQ_W: return (n + chunk_elems<LPQ_QDQW_U, LPQ_QDQW_T>() - 1) / chunk_elems<LPQ_QDQW_U, LPQ_QDQW_T>();
     case I4_Q32:
     case I4_Q128: return (n + chunk_elems<LPQ_I4Q_U, LPQ_I4Q_T>() - 1) / chunk_elems<LPQ_I4Q_U, LPQ_I4Q_T>();
     case I4_DQ32:
@@ -233,6 +234,10 @@ void dispatch(Kind k, dim3 grid, hipStream_t stream, const lpq_tensor* tab, cons
         case NV_Q: hipLaunchKernelGGL((k_nvfp4_quant<LPQ_NVQ_U, LPQ_NVQ_T, false>), grid, dim3(LPQ_NVQ_T), 0, stream, tab, one, map, fa, fb); break;
         case NV_DQ: hipLaunchKernelGGL((k_nvfp4_dequant<LPQ_NVD_U, LPQ_NVD_T, false>), grid, dim3(LPQ_NVD_T), 0, stream, tab, one, map, fa); break;
         case NV_QDQ: hipLaunchKernelGGL((k_nvfp4_qdq<LPQ_QDQ_U, LPQ_QDQ_T, false>), grid, dim3(LPQ_QDQ_T), 0, stream, tab, one, map, fa); break;
+        case NV_QDQ_W:
+            hipLaunchKernelGGL((k_nvfp4_qdq<LPQ_QDQW_U, LPQ_QDQW_T, false, LPQ_QDQW_AHEAD != 0>), grid, dim3(LPQ_QDQW_T), 0,
+                               stream, tab, one, map, fa);
+            break;
         case I4_Q32: hipLaunchKernelGGL((k_int4_quant<LPQ_I4Q_U, LPQ_I4Q_T, false, 32>), grid, dim3(LPQ_I4Q_T), 0, stream, tab, one, map); break;
         case I4_Q128: hipLaunchKernelGGL((k_int4_quant<LPQ_I4Q_U, LPQ_I4Q_T, false, 128>), grid, dim3(LPQ_I4Q_T), 0, stream, tab, one, map); break;
         case I4_DQ32: hipLaunchKernelGGL((k_int4_dequant<LPQ_I4D_U, LPQ_I4D_T, false, 32>), grid, dim3(LPQ_I4D_T), 0, stream, tab, one, map); break;
@@ -439,6 +444,9 @@ lpq_status nvfp4_single(Kind k, const uint16_t* w, int64_t M, int64_t N, const f
     lpq_status st = check_tensor(k, one, 0);
     if (st != LPQ_OK) return st;
     const hipStream_t s = (hipStream_t)stream;
+    // a QDQ tensor of at most a few waves of full-CU workgroups takes the wide
+    // shape (every load of a lane issued up front); larger ones stream
+    if (k == NV_QDQ && M * N <= LPQ_QDQW_MAX_ELEMS) k = NV_QDQ_W;
     if (amax) return launch<lpq_tensor>(k, nullptr, nullptr, 0, one, amax, k == NV_Q ? g : nullptr, s, gdiv);
     if ((st = fill(g, 1, 0.0f, stream)) != LPQ_OK) return st;
     if ((st = launch<lpq_tensor>(NV_AMAX, nullptr, nullptr, 0, one, nullptr, g, s)) != LPQ_OK) return st;

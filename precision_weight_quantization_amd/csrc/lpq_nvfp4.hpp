@@ -117,12 +117,15 @@ __device__ __forceinline__ v4u e2m1x8_to_bf16(uint32_t p, float S) {
 // W4A4 activation observers
 // ---------------------------------------------------------------------------
 //
-// Observer state (caller-owned device memory, 8 words): [0] min, [1] max,
-// [2] batches seen (FP32), [4] / [5] the current batch's min / max as
-// order-preserving keys, [6] the number of workgroups of the current call
-// that have folded in their keys.  Keys map binary32 bits to unsigned integers whose
-// order is the values' order with -0 below +0: non-negative values get the
-// sign bit set, negative values have every bit flipped.
+// Observer state (caller-owned device memory, LPQ_OBSERVER_STATE_FLOATS
+// words): [0] min, [1] max, [2] batches seen (FP32); then, each on a cache
+// line of its own so that the workgroups' atomics on them do not queue behind
+// one another, [32] / [64] the current batch's min / max as order-preserving
+// keys and [96] the number of workgroups of the current call that have folded
+// in their keys.  Keys map binary32 bits to unsigned integers whose order is
+// the values' order with -0 below +0: non-negative values get the sign bit
+// set, negative values have every bit flipped.
+constexpr int kObsKeyMin = 32, kObsKeyMax = 64, kObsArrived = 96;
 
 __device__ __forceinline__ uint32_t order_key(uint32_t u) { return (u >> 31) ? ~u : (u | 0x80000000u); }
 __device__ __forceinline__ uint32_t key_bits(uint32_t k) { return (k >> 31) ? (k & 0x7fffffffu) : ~k; }
@@ -133,18 +136,27 @@ constexpr uint32_t kKeyMaxIdentity = 0u;
 
 __global__ void k_observer_reset(uint32_t* state) {
     const int i = threadIdx.x;
-    if (i < 8) state[i] = i == 4 ? kKeyMinIdentity : (i == 5 ? kKeyMaxIdentity : 0u);
+    if (i < 3) state[i] = 0u;
+    if (i == 0) {
+        state[kObsKeyMin] = kKeyMinIdentity;
+        state[kObsKeyMax] = kKeyMaxIdentity;
+        state[kObsArrived] = 0u;
+    }
+}
+
+__device__ __forceinline__ uint32_t dev_atomic_xchg(uint32_t* p, uint32_t v) {
+    return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Applies the observer rule to the batch extremes (one thread), writes the
 // activation amax and re-arms the batch keys.  Same operations, in the same
 // order, as the definition: m += c * (b - m) for the moving average.  The keys
-// were folded in by device-scope atomics of other workgroups: they are read
-// with device-scope atomic loads.
+// are taken (and reset to their identities) with device-scope atomic
+// exchanges, performed where the other workgroups' key atomics were.
 __device__ void observer_apply(int kind, float c, uint32_t* state, float* amax) {
     float* f = reinterpret_cast<float*>(state);
-    const uint32_t kmin = __hip_atomic_load(state + 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t kmax = __hip_atomic_load(state + 5, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t kmin = dev_atomic_xchg(state + kObsKeyMin, kKeyMinIdentity);
+    const uint32_t kmax = dev_atomic_xchg(state + kObsKeyMax, kKeyMaxIdentity);
     const float bmin = __uint_as_float(key_bits(kmin)), bmax = __uint_as_float(key_bits(kmax));
     float mn = f[0], mx = f[1];
     if (kind == LPQ_OBSERVER_MEMORYLESS_MINMAX || f[2] == 0.0f) {
@@ -160,8 +172,6 @@ __device__ void observer_apply(int kind, float c, uint32_t* state, float* amax) 
     f[0] = mn;
     f[1] = mx;
     f[2] = f[2] + 1.0f;
-    state[4] = kKeyMinIdentity;
-    state[5] = kKeyMaxIdentity;
     *amax = fmaxf(fabsf(mn), fabsf(mx));
 }
 
@@ -208,13 +218,13 @@ __global__ __launch_bounds__(kThreads) void k_minmax(lpq_tensor one, int kind, f
             l = umin(l, plo[k]);
             h = umax(h, phi[k]);
         }
-        atomicMin(state + 4, l);
-        atomicMax(state + 5, h);
-        __threadfence();   // this workgroup's keys before its arrival
-        if (atomicAdd(state + 6, 1u) == gridDim.x - 1) {
-            __threadfence();   // every other workgroup's keys before the rule reads them
+        atomicMin(state + kObsKeyMin, l);
+        atomicMax(state + kObsKeyMax, h);
+        // this workgroup's keys before its arrival; the last arriver's reads after every arrival
+        if (__hip_atomic_fetch_add(state + kObsArrived, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+            gridDim.x - 1) {
             observer_apply(kind, c, state, amax);
-            state[6] = 0u;     // re-armed for the next call
+            __hip_atomic_store(state + kObsArrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // re-armed
         }
     }
 }

@@ -22,6 +22,21 @@
 #ifndef LPQ_QDQ_U
 #define LPQ_QDQ_U 2
 #endif
+// The single-tensor QDQ of at most LPQ_QDQW_MAX_ELEMS elements (the W4A4
+// activation case): 512-thread workgroups of 16 vectors per lane, all loaded
+// up front, so that a 8192 x 2048 activation is one pass of 256 workgroups.
+#ifndef LPQ_QDQW_U
+#define LPQ_QDQW_U 16
+#endif
+#ifndef LPQ_QDQW_T
+#define LPQ_QDQW_T 512
+#endif
+#ifndef LPQ_QDQW_AHEAD
+#define LPQ_QDQW_AHEAD 0
+#endif
+#ifndef LPQ_QDQW_MAX_ELEMS
+#define LPQ_QDQW_MAX_ELEMS (int64_t(1) << 25)
+#endif
 #ifndef LPQ_AMAX_U
 #define LPQ_AMAX_U 32
 #endif

@@ -1,4 +1,4 @@
-"""The amax and observer passes on large single tensors, against the oracle.
+"""The amax, observer and QDQ passes on large single tensors, against the oracle.
 
 8177 x 16384 and 8192 x 16384 BF16 tensors (268 MB each, about 2,000 workgroups,
 each folding its maximum into one slot with an atomic) go through the
@@ -81,3 +81,25 @@ def test_observer_large(lpq, tensors, name):
         st = state.cpu().numpy()[:3]
         assert np.array_equal(bits(st), bits(ost)), (name, batch, st, ost)
         assert bits(amax.item()) == bits(a), (name, batch)
+
+
+@pytest.mark.parametrize("M,N", [(8192, 2048), (2048, 16384), (2049, 16384), (8177, 16384)])
+def test_qdq_single_both_shapes(lpq, M, N):
+    """Single-tensor QDQ on both sides of the switch between the wide launch
+    shape (at most 2^25 elements: the 8192 x 2048 activation, 2048 x 16384)
+    and the streaming one (2049 x 16384, 8177 x 16384 with a ragged last
+    chunk).  The global scale comes from the whole tensor; the QDQ output is
+    compared on every 61st row and the last row."""
+    from synth import gpu as sgpu
+    x = sgpu.generate(142, M, M, N, synth.DIST_ACT)
+    amax = lpq.lpq_nvfp4_amax(x)
+    y = lpq.lpq_nvfp4_qdq(x, amax)
+    A = O.amax(host_u16(x))
+    assert bits(amax.item()) == bits(A)
+    rows = np.unique(np.concatenate([np.arange(0, M, 61), [M - 1]]))
+    idx = torch.as_tensor(rows, device=x.device)
+    want = O.nvfp4_qdq(host_u16(x[idx]), O.nvfp4_global_scale(A))
+    got = host_u16(y[idx])
+    bad = int((got != want).sum())
+    print(f"  qdq {M}x{N}: {len(rows)} rows, {bad} mismatches", flush=True)
+    assert bad == 0
