@@ -374,6 +374,38 @@ def summarize_pmc(path: str) -> None:
         print(f"| {name} | {grid} | {ctr} | {len(disp)} | {tot / max(len(disp), 1):.1f} |")
 
 
+# --------------------------------------------------------------------------- launch floor
+
+def launch_floor_us(reps: int = 50) -> float:
+    """Median time between two events around one launch of the library's
+    smallest kernel (one workgroup: the multiplier form of one global scale),
+    with the pairs queued back to back behind a long fill so that the GPU, not
+    the host, paces them, as the ops of a step are paced: the fixed cost of
+    any single launch timed this way, which bounds the small activation ops
+    from below."""
+    import statistics
+
+    import torch
+
+    import precision_weight_quantization_amd as lpq
+    a = torch.full((1,), 2688.0, dtype=torch.float32, device="cuda")
+    out = torch.empty_like(a)
+    block = torch.empty(1 << 29, dtype=torch.float32, device="cuda")   # 2 GiB
+    for _ in range(5):
+        lpq.lpq_nvfp4_global_scale(a, out)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for _ in range(4):
+        block.fill_(1.0)
+    for e0, e1 in ev:
+        e0.record()
+        lpq.lpq_nvfp4_global_scale(a, out)
+        e1.record()
+    torch.cuda.synchronize()
+    del block
+    return round(statistics.median(e0.elapsed_time(e1) for e0, e1 in ev) * 1e3, 2)
+
+
 # --------------------------------------------------------------------------- widening rows
 
 def time_next_rows(bench, steps: int):
@@ -502,6 +534,8 @@ def main():
         log(f"  {op.name:32s} {ms:8.3f} ms  {gbs:8.1f} GB/s  {100 * gbs / HBM_PEAK_GBS:5.1f}% of peak")
 
     next_rows = time_next_rows(bench, args.steps) if bench.next_ops else None
+    floor_us = launch_floor_us()
+    log(f"launch floor (one-workgroup kernel between two events): {floor_us} us")
 
     roofline = None
     if nops:
@@ -551,6 +585,7 @@ def main():
             "algorithmic_GB_per_step": round(counted / GB, 3),
         },
         "per_op": per_op,
+        "launch_floor_us": floor_us,
         "roofline": roofline,
         "next_rows": next_rows,
         "cpu_baseline": cpu,
