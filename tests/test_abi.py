@@ -295,7 +295,7 @@ def test_binding_refuses_bad_tensors_before_any_call(lib, recorder):
         (ValueError, lambda: lib.lpq_quantize_int4(w, 32, s=f32(4, 1))),
         (ValueError, lambda: lib.lpq_dequantize_int4(u8(4, 32), f32(4, 1), 32)),
         (ValueError, lambda: lib.lpq_requantize_fp8blk_nvfp4(u8(4, 64), f32(1, 1), f32(1), sb=u8(4, 3))),
-        (ValueError, lambda: lib.lpq_nvfp4_observe(w, f32(4))),                                     # state: 8 words
+        (ValueError, lambda: lib.lpq_nvfp4_observe(w, f32(lib.OBSERVER_STATE_FLOATS - 1))),         # state too short
         (ValueError, lambda: lib.lpq_nvfp4_global_scale(f32(4), out=f32(3))),
     ]
     for exc, call in cases:
@@ -324,3 +324,16 @@ def test_tensor_table_checks(lib, recorder):
     with pytest.raises(ValueError):
         t.check("nvfp4_qdq")         # QDQ needs dst
     assert recorder.calls == []
+
+
+def test_header_constants_match_binding(lib):
+    """The binding's copies of the header's constants (status codes, observer
+    kinds and the observer state size) are the header's values."""
+    import re
+    text = open(os.path.join(ROOT, "include", "lpq.h")).read()
+    defs = {k: int(v) for k, v in re.findall(r"#define (LPQ_\w+) (\d+)", text)}
+    assert defs["LPQ_OBSERVER_STATE_FLOATS"] == lib.OBSERVER_STATE_FLOATS
+    assert {k: defs["LPQ_OBSERVER_" + k.upper()] for k in lib.OBSERVERS} == lib.OBSERVERS
+    enum = dict((k, int(v)) for k, v in re.findall(r"(LPQ_(?:OK|ERR_\w+)) = (\d+)", text))
+    assert enum["LPQ_OK"] == lib.LPQ_OK
+    assert lib.STATUS_NAMES == {v: k for k, v in enum.items()}
