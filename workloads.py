@@ -161,8 +161,11 @@ class Op:
 # share (32 of 256 experts, 96 tensors, 2.8 GB).  Measured on the DeepSeek-V3
 # layer: block-FP8 quantize 73% of HBM peak as one 22.5 GB launch against 78%
 # in such buckets (MXFP8 quantize on the same tensors: 77% against 82%); on
-# Qwen3-4B, 70% per layer against 75% for four layers.  "layer" and "all" are
-# one launch per transformer layer and one launch over everything.
+# Qwen3-4B, 70% per layer against 75% for four layers.  A Qwen3-4B bucket lists
+# its tensors by shape (q and o, then k and v, then gate, up and down: three runs
+# of equal work-unit counts), so that it is one launch rather than two of at
+# most 8 runs each: about one more point for quantize and dequantize.  "layer"
+# and "all" are one launch per transformer layer and one launch over everything.
 DENSE_LAYERS_PER_BUCKET = 4
 EP_RANK_EXPERTS = 32
 
@@ -174,7 +177,9 @@ def _buckets(ws: WeightSet, bucket: str):
         return ws.layers()
     if ws.config == 2:      # Qwen3-4B dense
         layers = ws.layers()
-        return [sum(layers[i:i + DENSE_LAYERS_PER_BUCKET], []) for i in range(0, len(layers), DENSE_LAYERS_PER_BUCKET)]
+        buckets = [sum(layers[i:i + DENSE_LAYERS_PER_BUCKET], [])
+                   for i in range(0, len(layers), DENSE_LAYERS_PER_BUCKET)]
+        return [sorted(b, key=lambda i: (ws.specs[i].numel, ws.specs[i].M, i)) for b in buckets]
     if ws.config == 5:      # DeepSeek-V3 MoE layer: per expert-parallel rank
         out = {}
         for i, s in enumerate(ws.specs):
