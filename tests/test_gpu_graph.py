@@ -141,3 +141,37 @@ def test_grouped_calls_in_a_graph(lpq):
             assert np.array_equal(a, b), (rep, k)
         del junk
     assert bad == 0
+
+
+def test_w4a4_activation_path_in_a_graph(lpq):
+    """The W4A4 activation forward, the static min/max observer then the QDQ under
+    its amax, captured once and replayed over a sequence of batches: between
+    replays a new batch is copied into the captured input, with eager work and a
+    synchronisation. After every replay the observer state, the amax and the
+    QDQ output must equal the oracle's sequence, bit for bit; the observer's
+    batch keys and arrival counter re-arm themselves inside the replay."""
+    M, N = 2048, 2048
+    x = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    amax = torch.empty(1, dtype=torch.float32, device="cuda")
+    state = lpq.lpq_observer_reset(device="cuda")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        lpq.lpq_nvfp4_observe(x, state, "static_minmax", amax=amax)
+        lpq.lpq_nvfp4_qdq(x, amax, y)
+    lpq.lpq_observer_reset(state)   # capture ran nothing; start the sequence from a reset state
+    ost = np.zeros(3, np.float32)
+    bad = 0
+    for t in range(4):
+        sigma = float(np.ldexp(1.0, t - 1)) * (1.0 + 0.3 * t)
+        x_np = synth.generate(777, t, M, N, sigma, 0.0, 1e-4, 100.0)
+        x.copy_(to_dev_bf16(x_np))
+        torch.zeros(1024, device="cuda").sum().item()   # other eager work and a synchronisation
+        graph.replay()
+        torch.cuda.synchronize()
+        a = O.observer_update("static_minmax", ost, x_np)
+        bad += int(not same_bits(state[:3], ost))
+        bad += int(not same_bits(amax, np.float32(a)))
+        bad += report(f"graph W4A4 replay {t}", host_u16(y), O.nvfp4_qdq(x_np, O.nvfp4_global_scale(a)))
+        print(f"  replay {t}: amax {a!r}", flush=True)
+    assert bad == 0
