@@ -157,12 +157,13 @@ lpq_status lpq_dequantize_nvfp4(const uint8_t* p, const uint8_t* s, const float*
 
 /* Fake quantization ("verl NVFP4 QAT" 2.3, also used on W4A4 activations):
  * y = dequantize(quantize(x)) bit for bit, without storing codes.
- * amax: 1 FP32 (device) holding A; required (NULL: LPQ_ERR_NULL).  Unlike the
- * quantizer, this call has no FP32 output in which an amax it computed could
- * be held between the amax pass and the encode, and the library allocates
- * nothing: a caller without a cached amax runs lpq_nvfp4_amax into a word of
- * its own first (or lpq_nvfp4_observe for W4A4 activations).
- * x, y: [M, N] BF16 (may not overlap). */
+ * amax: 1 FP32 (device) holding A, or NULL: the tensor's own amax, computed
+ * by the call.  The library allocates nothing, so between the amax pass and
+ * the encode A is held in the first 4 bytes of y, which the last of the
+ * call's four launches (the first 16-element block) overwrites with its
+ * result; y is complete when the call's work on the stream is.
+ * x, y: [M, N] BF16, and may not overlap (with amax NULL an overlap is
+ * refused: LPQ_ERR_ARG). */
 lpq_status lpq_nvfp4_qdq(const uint16_t* x, int64_t M, int64_t N, const float* amax,
                          uint16_t* y, void* stream);
 

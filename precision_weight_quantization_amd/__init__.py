@@ -303,9 +303,10 @@ def lpq_quantize_nvfp4(w, amax=None, p=None, s=None, g=None, stream=None):
 def lpq_nvfp4_qdq_ex(x, amax, e4m3_max=448, y=None, stream=None):
     x = _bf16_in(x, "x")
     M, N = x.shape
-    _f32_words(amax, "amax", x)
+    if amax is not None:
+        _f32_words(amax, "amax", x)
     y = _out(y, "y", x, 2 * M * N, (M, N), torch.bfloat16, 2)
-    _check(_L.lpq_nvfp4_qdq_ex(x.data_ptr(), M, N, amax.data_ptr(), int(e4m3_max), y.data_ptr(), _stream(stream)),
+    _check(_L.lpq_nvfp4_qdq_ex(x.data_ptr(), M, N, _ptr(amax), int(e4m3_max), y.data_ptr(), _stream(stream)),
            "lpq_nvfp4_qdq_ex")
     return y
 
@@ -368,15 +369,13 @@ def lpq_dequantize_nvfp4(p, s, g, y=None, stream=None):
 
 def lpq_nvfp4_qdq(x, amax=None, y=None, stream=None):
     """NVFP4 fake quantization of BF16 [M,N] under the group amax (1-element FP32 device
-    tensor); returns BF16 [M,N].  amax None: the tensor's own, from lpq_nvfp4_amax into a
-    new word first (the C call itself requires an amax)."""
+    tensor); returns BF16 [M,N].  amax None: the tensor's own, computed by the library."""
     x = _bf16_in(x, "x")
     M, N = x.shape
-    if amax is None:
-        amax = lpq_nvfp4_amax(x, stream=stream)
-    _f32_words(amax, "amax", x)
+    if amax is not None:
+        _f32_words(amax, "amax", x)
     y = _out(y, "y", x, 2 * M * N, (M, N), torch.bfloat16, 2)
-    _check(_L.lpq_nvfp4_qdq(x.data_ptr(), M, N, amax.data_ptr(), y.data_ptr(), _stream(stream)), "lpq_nvfp4_qdq")
+    _check(_L.lpq_nvfp4_qdq(x.data_ptr(), M, N, _ptr(amax), y.data_ptr(), _stream(stream)), "lpq_nvfp4_qdq")
     return y
 
 

@@ -427,16 +427,27 @@ lpq_status global_scale(const float* amax, int32_t n, float* out, float gdiv, vo
     return launched();
 }
 
+// The single-tensor QDQ kind for n elements: a tensor of at most a few waves
+// of full-CU workgroups takes the wide shape (every load of a lane issued up
+// front); larger ones stream.
+Kind qdq_kind(int64_t n) { return n <= LPQ_QDQW_MAX_ELEMS ? NV_QDQ_W : NV_QDQ; }
+
 // NVFP4 quantize (k = NV_Q) or QDQ (k = NV_QDQ) of one tensor.  With amax ==
-// NULL (quantize only) the tensor's own amax is the group amax ("verl NVFP4
-// QAT" 2.3: a tensor of its own is a group of one): the caller's g word is
-// cleared, receives max |w| from the amax pass, is read as A by the encode
-// (which then leaves it alone), and is finally turned into fl(A / gdiv).  All
-// four launches are on the caller's stream, so each sees the previous one's
-// result.
+// NULL the tensor's own amax is the group amax ("verl NVFP4 QAT" 2.3: a tensor
+// of its own is a group of one), computed by the call into a word the caller
+// already owns, and every launch goes on the caller's stream, so each sees the
+// previous one's result:
+//   quantize: the g word is cleared, receives max |w| from the amax pass, is
+//     read as A by the encode (which then leaves it alone), and is finally
+//     turned into fl(A / gdiv);
+//   QDQ: the first word of y is cleared and receives max |x|; the QDQ of every
+//     element but the first 16-element block reads A from it; the QDQ of that
+//     block runs last, reading A before it writes the block over the word
+//     (only its first wave holds elements, and each lane reads A before its
+//     store).  x and y must not overlap.
 lpq_status nvfp4_single(Kind k, const uint16_t* w, int64_t M, int64_t N, const float* amax, int e4m3_max, void* dst,
                         void* scale, float* g, void* stream) {
-    if ((k == NV_Q && !g) || (k == NV_QDQ && !amax)) return LPQ_ERR_NULL;
+    if (k == NV_Q && !g) return LPQ_ERR_NULL;
     if ((amax && !aligned(amax, 4)) || (g && !aligned(g, 4))) return LPQ_ERR_ALIGN;
     const float gdiv = gdiv_of(e4m3_max);
     if (gdiv == 0.0f) return LPQ_ERR_ARG;
@@ -444,14 +455,30 @@ lpq_status nvfp4_single(Kind k, const uint16_t* w, int64_t M, int64_t N, const f
     lpq_status st = check_tensor(k, one, 0);
     if (st != LPQ_OK) return st;
     const hipStream_t s = (hipStream_t)stream;
-    // a QDQ tensor of at most a few waves of full-CU workgroups takes the wide
-    // shape (every load of a lane issued up front); larger ones stream
-    if (k == NV_QDQ && M * N <= LPQ_QDQW_MAX_ELEMS) k = NV_QDQ_W;
-    if (amax) return launch<lpq_tensor>(k, nullptr, nullptr, 0, one, amax, k == NV_Q ? g : nullptr, s, gdiv);
-    if ((st = fill(g, 1, 0.0f, stream)) != LPQ_OK) return st;
-    if ((st = launch<lpq_tensor>(NV_AMAX, nullptr, nullptr, 0, one, nullptr, g, s)) != LPQ_OK) return st;
-    if ((st = launch<lpq_tensor>(NV_Q, nullptr, nullptr, 0, one, g, nullptr, s, gdiv)) != LPQ_OK) return st;
-    return global_scale(g, 1, g, gdiv, stream);
+    const int64_t n = M * N;
+    if (amax) {
+        const Kind kk = k == NV_QDQ ? qdq_kind(n) : k;
+        return launch<lpq_tensor>(kk, nullptr, nullptr, 0, one, amax, k == NV_Q ? g : nullptr, s, gdiv);
+    }
+    if (k == NV_Q) {
+        if ((st = fill(g, 1, 0.0f, stream)) != LPQ_OK) return st;
+        if ((st = launch<lpq_tensor>(NV_AMAX, nullptr, nullptr, 0, one, nullptr, g, s)) != LPQ_OK) return st;
+        if ((st = launch<lpq_tensor>(NV_Q, nullptr, nullptr, 0, one, g, nullptr, s, gdiv)) != LPQ_OK) return st;
+        return global_scale(g, 1, g, gdiv, stream);
+    }
+    uint16_t* y = static_cast<uint16_t*>(dst);
+    const uintptr_t xa = reinterpret_cast<uintptr_t>(w), ya = reinterpret_cast<uintptr_t>(y);
+    if (xa < ya + 2 * (uint64_t)n && ya < xa + 2 * (uint64_t)n) return LPQ_ERR_ARG;   // overlapping x and y
+    float* a = reinterpret_cast<float*>(y);
+    if ((st = fill(a, 1, 0.0f, stream)) != LPQ_OK) return st;
+    if ((st = launch<lpq_tensor>(NV_AMAX, nullptr, nullptr, 0, one, nullptr, a, s)) != LPQ_OK) return st;
+    if (n > 16) {
+        const lpq_tensor tail = make_one(w + 16, y + 16, nullptr, 1, n - 16);
+        if ((st = launch<lpq_tensor>(qdq_kind(n - 16), nullptr, nullptr, 0, tail, a, nullptr, s, gdiv)) != LPQ_OK)
+            return st;
+    }
+    const lpq_tensor head = make_one(w, y, nullptr, 1, 16);
+    return launch<lpq_tensor>(NV_QDQ_W, nullptr, nullptr, 0, head, a, nullptr, s, gdiv);
 }
 
 // Grouped NVFP4 quantize (NV_Q) or QDQ (NV_QDQ).  amax_valid != 0: group_amax

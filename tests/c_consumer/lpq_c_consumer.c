@@ -147,8 +147,13 @@ int main(void) {
     check("nvfp4 global scale, own amax", dg, &g, 4);
     check("nvfp4 packed, own amax", dq, q, n / 2);
     check("nvfp4 block scales, own amax", de, e, n / 16);
-    if (lpq_nvfp4_qdq(dw, M, N, NULL, dy, NULL) != LPQ_ERR_NULL) {   /* QDQ needs its amax */
-        printf("lpq_nvfp4_qdq with amax NULL was not refused with LPQ_ERR_NULL\n");
+    HIP_OK(hipMemset(dy, 0xff, n * 2));
+    lpq_ok(lpq_nvfp4_qdq(dw, M, N, NULL, dy, NULL), "lpq_nvfp4_qdq (amax NULL)");   /* A held in y meanwhile */
+    HIP_OK(hipDeviceSynchronize());
+    oc_nvfp4_qdq(w, M, N, g, y);
+    check("nvfp4 qdq, own amax", dy, y, n * 2);
+    if (lpq_nvfp4_qdq(dw, M, N, NULL, (uint16_t*)dw + 8, NULL) != LPQ_ERR_ARG) {   /* y overlapping x */
+        printf("lpq_nvfp4_qdq with amax NULL and overlapping x, y was not refused with LPQ_ERR_ARG\n");
         failures++;
     }
 

@@ -38,7 +38,7 @@ int main(void) {
     EXPECT(lpq_dequantize_fp8blk(B, F, 5, 5, NULL, NULL), LPQ_ERR_NULL);
     EXPECT(lpq_quantize_nvfp4(W, 4, 24, F, B, B, F, NULL), LPQ_ERR_SHAPE);
     EXPECT(lpq_quantize_nvfp4(W, 4, 32, NULL, B, B, NULL, NULL), LPQ_ERR_NULL);
-    EXPECT(lpq_nvfp4_qdq(W, 4, 32, NULL, H, NULL), LPQ_ERR_NULL);
+    EXPECT(lpq_nvfp4_qdq(W, 4, 32, NULL, H, NULL), LPQ_ERR_ARG);   /* amax computed into y: x, y overlap */
     EXPECT(lpq_quantize_nvfp4_ex(W, 4, 32, F, 300, B, B, F, NULL), LPQ_ERR_ARG);
     EXPECT(lpq_nvfp4_observe(W, 4, 32, 7, 0.5f, F, F, NULL), LPQ_ERR_ARG);
     EXPECT(lpq_quantize_int4(W, 4, 128, 64, B, F, NULL), LPQ_ERR_ARG);

@@ -82,8 +82,11 @@ def test_single_call_validation(lib):
     assert L.lpq_quantize_nvfp4(P, 4, 32, P, P + 2, P, P, None) == 3
     assert L.lpq_dequantize_nvfp4(P, P, None, 4, 32, P, None) == 1
     assert L.lpq_dequantize_nvfp4(P, P, P, 4, 32, P + 8, None) == 3
-    assert L.lpq_nvfp4_qdq(P, 4, 32, None, P, None) == 1      # QDQ has no word to hold an amax it computed
-    assert L.lpq_nvfp4_qdq_ex(P, 4, 32, None, 448, P, None) == 1
+    assert L.lpq_nvfp4_qdq(P, 4, 32, None, P, None) == 6      # amax computed into y: x and y may not overlap
+    assert L.lpq_nvfp4_qdq(P, 4, 32, None, P + 240, None) == 6
+    assert L.lpq_nvfp4_qdq(P + 240, 4, 32, None, P, None) == 6
+    assert L.lpq_nvfp4_qdq_ex(P, 4, 32, None, 448, P, None) == 6
+    assert L.lpq_nvfp4_qdq_ex(P, 4, 32, None, 100, P + 4096, None) == 6   # bad maximum before anything else
     assert L.lpq_nvfp4_qdq(P, 4, 32, P, None, None) == 1
     assert L.lpq_nvfp4_amax(P, 4, 32, None, 0, None) == 1
     assert L.lpq_nvfp4_amax(P, 4, 8, P, 0, None) == 2

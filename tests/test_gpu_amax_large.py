@@ -101,5 +101,7 @@ def test_qdq_single_both_shapes(lpq, M, N):
     want = O.nvfp4_qdq(host_u16(x[idx]), O.nvfp4_global_scale(A))
     got = host_u16(y[idx])
     bad = int((got != want).sum())
+    y2 = lpq.lpq_nvfp4_qdq(x)   # amax computed by the call (held in y's first word meanwhile)
+    bad += int((host_u16(y2[idx]) != want).sum())
     print(f"  qdq {M}x{N}: {len(rows)} rows, {bad} mismatches", flush=True)
     assert bad == 0

@@ -70,6 +70,10 @@ def check_nvfp4(lpq, w_np, name=""):
     bad += report(f"nvfp4 dequant {name}", host_u16(y), oy)
     bad += report(f"nvfp4 qdq {name}", host_u16(yq), O.nvfp4_qdq(w_np, og))
     bad += report(f"nvfp4 qdq vs dequant(quant) {name}", host_u16(yq), host_u16(y))
+    # QDQ with no amax given: the library computes it, holding A in y's first word meanwhile
+    yq2 = torch.full_like(w, -7.0)
+    lpq.lpq_nvfp4_qdq(w, None, yq2)
+    bad += report(f"nvfp4 qdq, amax computed by the call {name}", host_u16(yq2), O.nvfp4_qdq(w_np, og))
     assert bad == 0
 
 
@@ -192,6 +196,7 @@ def test_nvfp4_e4m3_max_256_single(lpq, M, N):
     bad += int(not same_bits(g2, og)) + report("packed, own amax", host_u8(p2), op) + report("scales", host_u8(s2), os_)
     bad += report(f"nvfp4/256 packed {M}x{N}", host_u8(p), op) + report("scales", host_u8(s), os_)
     bad += report("qdq", host_u16(yq), O.nvfp4_qdq(w_np, og))
+    bad += report("qdq, own amax", host_u16(lpq.lpq_nvfp4_qdq_ex(w, None, 256)), O.nvfp4_qdq(w_np, og))
     assert int(host_u8(s).max()) <= 0x78   # block-scale codes stay at or below 256 (0x78)
     assert bad == 0
 
