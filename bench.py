@@ -232,6 +232,7 @@ def next_rows_parity(bench, stride: int, threads: int):
     import numpy as np
     import torch
 
+    import workloads as W
     from oracle import oracle as O
 
     def h8(t):
@@ -280,24 +281,30 @@ def next_rows_parity(bench, stride: int, threads: int):
                         return int((O.int4_dequantize(*O.int4_quantize(x, G), G) != y).sum())
                 jobs.append(job)
             continue
-        if op.workload != "fp8train" or op.name.startswith("requant.amax"):
+        if op.workload not in ("fp8train", "fp8train-pow2") or op.name.startswith("requant.amax"):
             continue
         ws = bench.sets["moe"]
-        out = bench.outputs["fp8train"]
+        out = bench.outputs[op.workload]
+        if op.workload == "fp8train-pow2":   # the oracle's own block-FP8 copy, scales cut to powers of two
+            def fp8_of(x):
+                q, s = O.fp8blk_quantize(x)
+                return q, (s.view(np.uint32) & np.uint32(W.POW2_MASK)).view(np.float32)
+        else:
+            fp8_of = O.fp8blk_quantize
         if op.name.startswith("requant.fp8blk"):
             for i in range(0, len(ws.specs), stride):
                 x, q, s8 = h16(ws.w[i]), h8(out["fq"][i]), out["fs"][i].cpu().numpy()
 
-                def job(x=x, q=q, s8=s8):
-                    oq, os_ = O.fp8blk_requantize_fp8blk(*O.fp8blk_quantize(x))
+                def job(x=x, q=q, s8=s8, fp8_of=fp8_of):
+                    oq, os_ = O.fp8blk_requantize_fp8blk(*fp8_of(x))
                     return int((oq != q).sum() + (os_.view(np.uint32) != s8.view(np.uint32)).sum())
                 jobs.append(job)
         elif op.name.startswith("requant.mxfp8"):
             for i in out["ex"][::stride]:
                 x, q, e = h16(ws.w[i]), h8(out["mq"][i]), h8(out["me"][i])
 
-                def job(x=x, q=q, e=e):
-                    oq, oe = O.fp8blk_requantize_mxfp8(*O.fp8blk_quantize(x))
+                def job(x=x, q=q, e=e, fp8_of=fp8_of):
+                    oq, oe = O.fp8blk_requantize_mxfp8(*fp8_of(x))
                     return int((oq != q).sum() + (oe != e).sum())
                 jobs.append(job)
         elif op.name.startswith("requant.nvfp4"):
@@ -311,8 +318,8 @@ def next_rows_parity(bench, stride: int, threads: int):
                 ps, ss = [h8(out["p"][i]) for i in idx], [h8(out["sb"][i]) for i in idx]
                 A_d, gg_d = np.float32(amax_d[gid]), np.float32(g_d[gid])
 
-                def job(xs=xs, ps=ps, ss=ss, A_d=A_d, gg_d=gg_d):
-                    A, g, res = O.fp8blk_requantize_nvfp4_group([O.fp8blk_quantize(x) for x in xs])
+                def job(xs=xs, ps=ps, ss=ss, A_d=A_d, gg_d=gg_d, fp8_of=fp8_of):
+                    A, g, res = O.fp8blk_requantize_nvfp4_group([fp8_of(x) for x in xs])
                     bad = int(np.float32(A) != A_d) + int(np.float32(g) != gg_d)
                     for (p, s), pp, sg in zip(res, ps, ss):
                         bad += int((p != pp).sum() + (s != sg).sum())

@@ -95,28 +95,55 @@ struct Y16 {
     uint32_t amax;
 };
 
+// POW2: the tile scale is 2^k with -121 <= k <= 119 (positive, significand bits
+// clear, biased exponent 6 to 246).  A code
+// has at most 4 significant bits and |code| lies in {0} or [2^-9, 448], so
+// code * 2^k is then exact in binary32 and in BF16 (|y| in [2^-130, 1.75 * 2^127]
+// keeps the 4 bits above BF16's last place, subnormal range included): y is
+// the product itself, which the scaled convert forms from the scale's exponent
+// (measured equal to the correctly rounded product for every code and every
+// k from -126 to 127), with no multiply and no BF16 rounding.
+template <bool POW2 = false>
 __device__ __forceinline__ Y16 fp8blk_values16(const v4u& c, float s) {
     float p[16];
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
     for (int k = 0; k < 4; k++) {
-        const float2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
-        const float2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);
-        p[4 * k + 0] = a[0] * s;
-        p[4 * k + 1] = a[1] * s;
-        p[4 * k + 2] = b[0] * s;
-        p[4 * k + 3] = b[1] * s;
+        if constexpr (POW2) {
+            const float2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)w[k], s, false);
+            const float2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)w[k], s, true);
+            p[4 * k + 0] = a[0];
+            p[4 * k + 1] = a[1];
+            p[4 * k + 2] = b[0];
+            p[4 * k + 3] = b[1];
+        } else {
+            const float2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
+            const float2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);
+            p[4 * k + 0] = a[0] * s;
+            p[4 * k + 1] = a[1] * s;
+            p[4 * k + 2] = b[0] * s;
+            p[4 * k + 3] = b[1] * s;
+        }
     }
     float m = fmaxf(fmaxf(fabsf(p[0]), fabsf(p[1])), fabsf(p[2]));
 #pragma unroll
     for (int k = 3; k < 15; k += 2) m = fmaxf(fmaxf(m, fabsf(p[k])), fabsf(p[k + 1]));
     m = fmaxf(m, fabsf(p[15]));
     Y16 y;
-    y.amax = bf16_in_f32(m);
+    if constexpr (POW2) {
+        y.amax = __float_as_uint(m);
 #pragma unroll
-    for (int k = 0; k < 8; k++) {
-        y.lo.x[k] = __uint_as_float(bf16_in_f32(p[k]));
-        y.hi.x[k] = __uint_as_float(bf16_in_f32(p[8 + k]));
+        for (int k = 0; k < 8; k++) {
+            y.lo.x[k] = p[k];
+            y.hi.x[k] = p[8 + k];
+        }
+    } else {
+        y.amax = bf16_in_f32(m);
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            y.lo.x[k] = __uint_as_float(bf16_in_f32(p[k]));
+            y.hi.x[k] = __uint_as_float(bf16_in_f32(p[8 + k]));
+        }
     }
     return y;
 }
@@ -248,15 +275,16 @@ __global__ __launch_bounds__(TH) void k_requant_amax(const lpq_requant_tensor* t
     }
 }
 
-template <int U, bool FULL, bool LARGE, int TH>
-__device__ __forceinline__ void rq_nvfp4_body(const lpq_requant_tensor& d, int64_t base, int64_t total,
-                                              const GlobalScale& G) {
+template <int U, bool FULL, bool LARGE, bool POW2, int TH>
+__device__ __forceinline__ void rq_nvfp4_steps(const lpq_requant_tensor& d, int64_t base, int64_t total,
+                                               const GlobalScale& G, const v4u (&c)[U], const float (&s)[U]) {
     // the chunk's origins (uniform): one 8-byte code word and one scale byte per lane and step
     v2u* dst = reinterpret_cast<v2u*>(d.dst) + base / 16;
     uint8_t* ssc = reinterpret_cast<uint8_t*>(d.dst_scale) + base / 16;
-    rq_stream<U, FULL, LPQ_RQN_AHEAD != 0, TH>(d, base, total, [&](int u, const v4u& c, float s) {
+#pragma unroll
+    for (int u = 0; u < U; u++) {
         const int i = u * TH + threadIdx.x;
-        const Y16 y = fp8blk_values16(c, s);
+        const Y16 y = fp8blk_values16<POW2>(c[u], s[u]);
         // one lane is one 16-element block
         const BlockScale B = block_scale<LARGE>(y.amax, G);
         const v2u p = v2u{e2m1x8(y.lo, B), e2m1x8(y.hi, B)};
@@ -264,7 +292,49 @@ __device__ __forceinline__ void rq_nvfp4_body(const lpq_requant_tensor& d, int64
             store<kNTS>(dst + i, p);
             store_u8(ssc + i, B.code);
         }
-    });
+    }
+}
+
+// Every load of a lane issued up front, its U tile scales first: the wave then
+// learns from the scales alone (without waiting for its codes) whether all its
+// tiles have power-of-two scales, and runs the steps with the exact
+// scaled-convert dequantization if so (the block scales a trainer writes
+// unless FP32 block scales are asked for), else with multiply and rounding.
+template <int U, bool FULL, bool LARGE, int TH>
+__device__ __forceinline__ void rq_nvfp4_body(const lpq_requant_tensor& d, int64_t base, int64_t total,
+                                              const GlobalScale& G) {
+    const v4u* src = reinterpret_cast<const v4u*>(d.src) + base / 16 + threadIdx.x;
+    TileCursor<16, TH> cur(d.src_scale, d.cols, base);
+    v4u c[U];
+    float s[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const bool in = FULL || base + (int64_t)(u * TH + threadIdx.x) * 16 < total;
+        s[u] = in ? load<false>(cur.ptr()) : 0.0f;
+        cur.next();
+    }
+    // the code vectors in step order (an empty asm that clobbers memory after each
+    // load keeps the compiler from regrouping them), so that step u waits for its
+    // own vector only
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const bool in = FULL || base + (int64_t)(u * TH + threadIdx.x) * 16 < total;
+        c[u] = in ? load<kNTL>(src + u * TH) : v4u{0u, 0u, 0u, 0u};
+        __asm__ volatile("" ::: "memory");
+    }
+    // every scale 2^k, -121 <= k <= 119 (fp8blk_values16<true> is exact there): sign
+    // and significand bits all clear, the smallest and largest bit patterns in range
+    uint32_t frac = 0u, lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const uint32_t b = __float_as_uint(s[u]);
+        frac |= b & 0x807fffffu;
+        lo = umin(lo, b);
+        hi = umax(hi, b);
+    }
+    const bool pow2 = frac == 0u && lo >= (6u << 23) && hi <= (246u << 23);
+    if (!any_lane(!pow2)) rq_nvfp4_steps<U, FULL, LARGE, true, TH>(d, base, total, G, c, s);
+    else rq_nvfp4_steps<U, FULL, LARGE, false, TH>(d, base, total, G, c, s);
 }
 
 template <int U, int TH, bool GROUPED>

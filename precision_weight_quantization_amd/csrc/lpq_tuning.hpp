@@ -103,9 +103,6 @@
 #ifndef LPQ_RQM_AHEAD
 #define LPQ_RQM_AHEAD 1
 #endif
-#ifndef LPQ_RQN_AHEAD
-#define LPQ_RQN_AHEAD 0
-#endif
 #ifndef LPQ_I4Q_AHEAD
 #define LPQ_I4Q_AHEAD 0
 #endif

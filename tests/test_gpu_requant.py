@@ -73,6 +73,17 @@ def random_case(M, N, seed, lo=-20, hi=10, signed=False, zero_tile=True):
     return q, s
 
 
+def pow2_scales(shape, seed, ks, signs=(1.0,)):
+    """Tile scales +-2^k, k drawn from ``ks`` and the sign from ``signs`` by seeded bytes
+    (the block scales a trainer without FP32 block scales writes)."""
+    n = int(np.prod(shape))
+    kb = synth.random_bytes(seed, 3, n).astype(np.int64)
+    sb = synth.random_bytes(seed, 4, n).astype(np.int64)
+    k = np.asarray(ks, np.int64)[kb % len(ks)]
+    sg = np.asarray(signs, np.float64)[sb % len(signs)]
+    return (sg * np.ldexp(1.0, k)).astype(np.float32).reshape(shape)
+
+
 SHAPES = [(1, 32), (3, 64), (200, 320), (130, 2080), (257, 96), (40, 4128), (2, 16416), (1000, 7168)]
 
 
@@ -232,4 +243,49 @@ def test_requant_grouped(lpq):
     lpq.lpq_fp8blk_amax_grouped(t, amax2, accumulate=True)
     a2 = amax2.cpu().numpy()
     bad += int(a2[0] != np.float32(3.0e38)) + int(not np.array_equal(a2[1:], amax_h[1:]))
+    assert bad == 0
+
+
+# Power-of-two tile scales: every wave whose lanes all hold a scale 2^k with
+# -121 <= k <= 119 forms the dequantized values with the scaled convert (exact
+# there), the rest through multiply and BF16 rounding.  Both must give the same
+# bits, at the range's edges too.
+
+@pytest.mark.parametrize("M,N", [(1, 32), (200, 320), (130, 2080), (40, 4128), (1000, 7168)])
+def test_requant_pow2_scales(lpq, M, N):
+    q = synth.e4m3_codes(900 + M, 1, M, N)
+    s = pow2_scales(O.fp8blk_scale_shape(M, N), 900 + N, list(range(-121, 120)))
+    bad = check_mx(lpq, q, s, f"pow2 {M}x{N}") + check_nv(lpq, q, s, f"pow2 {M}x{N}")
+    bad += check_fp8(lpq, q, s, f"pow2 {M}x{N}")
+    assert bad == 0
+
+
+@pytest.mark.parametrize("ks,signs", [
+    ([-123, -122, -121, -120], (1.0,)),          # the bottom edge: 2^-122 and below take the general path
+    ([118, 119, 120, 121, 126], (1.0,)),         # the top edge: 2^120 and above take it
+    ([-121, -60, 0, 60, 119], (1.0, -1.0)),      # negative powers of two take it as well
+])
+def test_requant_pow2_scale_edges(lpq, ks, signs):
+    M, N = 384, 2048
+    q = synth.e4m3_codes(950, 1, M, N)
+    if max(ks) > 119:   # codes below 2 in magnitude keep every dequantized value finite (the contract)
+        q = q & np.uint8(0xB7)
+    s = pow2_scales(O.fp8blk_scale_shape(M, N), 951 + ks[0], ks, signs)
+    name = f"pow2 k in {ks} signs {signs}"
+    bad = check_mx(lpq, q, s, name) + check_nv(lpq, q, s, name) + check_fp8(lpq, q, s, name)
+    assert bad == 0
+
+
+def test_requant_pow2_mixed_waves(lpq):
+    """Half the tiles with power-of-two scales and half without, so that waves
+    straddle the two (they take the general path), on a trainer's real block-FP8
+    weight whose scales were rounded to powers of two in alternate tiles."""
+    M, N = 512, 2048
+    w = synth.generate(960, 1, M, N, *synth.DIST_MOE)
+    q, s = O.fp8blk_quantize(w)
+    s2 = s.copy()
+    s2[:, ::2] = np.ldexp(1.0, np.round(np.log2(s[:, ::2])).astype(np.int64)).astype(np.float32)
+    bad = check_mx(lpq, q, s2, "mixed pow2") + check_nv(lpq, q, s2, "mixed pow2") + check_fp8(lpq, q, s2, "mixed pow2")
+    s3 = np.ldexp(1.0, np.round(np.log2(s)).astype(np.int64)).astype(np.float32)
+    bad += check_mx(lpq, q, s3, "all pow2") + check_nv(lpq, q, s3, "all pow2") + check_fp8(lpq, q, s3, "all pow2")
     assert bad == 0

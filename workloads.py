@@ -23,7 +23,10 @@ distributions named for each workload.
           fused re-quantization into block-wise FP8 (all tensors), MXFP8
           (experts) and NVFP4 (experts and q/k/v, sibling groups as above),
           each next to the unfused dequantize-then-quantize sequence on the
-          same data.  Timed apart from the step.
+          same data; and the same fused re-quantizations with every tile scale
+          rounded to a power of two (the block scales a trainer writes unless
+          FP32 block scales are asked for, "Low Precision RL" 2).  Timed apart
+          from the step.
   int4    the moe workload's experts -> group-wise INT4 (group 128, the size
           "INT4 QAT 训练" gives for Qwen3-30B-A3B) quantize, dequantize and
           fake-quant.  Timed apart from the step.
@@ -292,9 +295,21 @@ def fp8_source(ws: WeightSet, device):
     return q, sc, (qslab, sslab)
 
 
-def requant_ops(ws: WeightSet, q8, s8, codes: Slab, out: Slab, bucket: str, device="cuda"):
+POW2_MASK = 0x7F800000   # the exponent field (the scales here are non-negative)
+
+
+def pow2_tile_scales(s8):
+    """Each tile scale cut to the power of two at or below it (its significand bits
+    cleared): the same codes then stand for a block-FP8 tensor with power-of-two
+    block scales."""
+    return [(s.view(torch.int32) & POW2_MASK).view(torch.float32) for s in s8]
+
+
+def requant_ops(ws: WeightSet, q8, s8, codes: Slab, out: Slab, bucket: str, device="cuda", tag="fp8train",
+                fused_only=False):
     """Fused FP8 -> MXFP8 (experts) and FP8 -> NVFP4 (all tensors) re-quantization,
-    and the unfused sequences they replace, writing into the shared slabs."""
+    and (unless fused_only) the unfused sequences they replace, writing into the
+    shared slabs."""
     specs = ws.specs
     ex = [i for i, s in enumerate(specs) if s.expert != 0xFFFF]
     n_ex, t_ex = sum(specs[i].numel for i in ex), sum(tiles_of(specs[i]) for i in ex)
@@ -350,25 +365,28 @@ def requant_ops(ws: WeightSet, q8, s8, codes: Slab, out: Slab, bucket: str, devi
     mx_bytes = 2 * n_ex + n_ex // 32 + 4 * t_ex
     amax_bytes = n + 4 * t
     nv_bytes = n + 4 * t + n // 2 + n // 16 + 4 * n_groups
-    ops = [
-        Op("requant.fp8blk[fp8train]", "fp8train", f8_bytes,
+    fused = [
+        Op(f"requant.fp8blk[{tag}]", tag, f8_bytes,
            [lambda r=r: lpq.lpq_requantize_fp8blk_grouped(r) for r in rf8]),
-        Op("requant.fp8blk.unfused[fp8train]", "fp8train", f8_bytes,
+        Op(f"requant.mxfp8[{tag}]", tag, mx_bytes,
+           [lambda r=r: lpq.lpq_requantize_fp8blk_mxfp8_grouped(r) for r in rmx]),
+        Op(f"requant.amax[{tag}]", tag, amax_bytes,
+           [lambda: lpq.lpq_fp8blk_amax_grouped(tamax, amax, accumulate=False)]),
+        Op(f"requant.nvfp4[{tag}]", tag, nv_bytes,
+           [lambda r=r: lpq.lpq_requantize_fp8blk_nvfp4_grouped(r, amax, g) for r in rnv]),
+    ]
+    unfused = [
+        Op(f"requant.fp8blk.unfused[{tag}]", tag, f8_bytes,
            [f for k in range(len(rf8)) for f in (lambda k=k: lpq.lpq_dequantize_fp8blk_grouped(dq_nv[k]),
                                                   lambda k=k: lpq.lpq_quantize_fp8blk_grouped(q_f8[k]))]),
-        Op("requant.mxfp8[fp8train]", "fp8train", mx_bytes,
-           [lambda r=r: lpq.lpq_requantize_fp8blk_mxfp8_grouped(r) for r in rmx]),
-        Op("requant.mxfp8.unfused[fp8train]", "fp8train", mx_bytes,
+        Op(f"requant.mxfp8.unfused[{tag}]", tag, mx_bytes,
            [lambda k=k: unfused_mx(k) for k in range(len(rmx))]),
-        Op("requant.amax[fp8train]", "fp8train", amax_bytes,
-           [lambda: lpq.lpq_fp8blk_amax_grouped(tamax, amax, accumulate=False)]),
-        Op("requant.nvfp4[fp8train]", "fp8train", nv_bytes,
-           [lambda r=r: lpq.lpq_requantize_fp8blk_nvfp4_grouped(r, amax, g) for r in rnv]),
-        Op("requant.nvfp4.unfused[fp8train]", "fp8train", amax_bytes + nv_bytes,
+        Op(f"requant.nvfp4.unfused[{tag}]", tag, amax_bytes + nv_bytes,
            [lambda t=t: lpq.lpq_dequantize_fp8blk_grouped(t) for t in dq_nv]
            + [lambda: lpq.lpq_nvfp4_amax_grouped(a_nv, amax, accumulate=False)]
            + [lambda t=t: lpq.lpq_quantize_nvfp4_grouped(t, amax, g) for t in q_nv]),
     ]
+    ops = fused if fused_only else [fused[0], unfused[0], fused[1], unfused[1], fused[2], fused[3], unfused[2]]
     return ops, dict(ex=ex, fq=fq, fs=fs, mq=mq, me=me, p=p, sb=sb, amax=amax, g=g, n_groups=n_groups, q8=q8, s8=s8)
 
 
@@ -476,6 +494,12 @@ class Bench:
             o["keep"] = keep
             self.next_ops += ops
             self.outputs["fp8train"] = o
+            s8p = pow2_tile_scales(s8)
+            ops, o2 = requant_ops(ws, q8, s8p, self.codes, self.out, bucket, device, tag="fp8train-pow2",
+                                  fused_only=True)
+            o2["keep"] = s8p
+            self.next_ops += ops
+            self.outputs["fp8train-pow2"] = o2
         if "int4" in which:
             ws = self.sets.get("moe_experts") or self._experts_only(self.sets["moe"])
             self.sets["moe_experts"] = ws
