@@ -345,8 +345,9 @@ lpq_status lpq_nvfp4_qdq_grouped_ex(const lpq_tensor* host, const lpq_tensor* de
  *
  * state: LPQ_OBSERVER_STATE_FLOATS words of caller-owned device memory, 4-byte
  * aligned, one per observed tensor: [0] min, [1] max, [2] batches seen (FP32),
- * the rest scratch of the calls below (on cache lines of their own: 512
- * bytes in all).  Reset it once before first use; calls
+ * the rest lpq_nvfp4_observe's control words (on cache lines of their own: 512
+ * bytes in all; lpq_nvfp4_observe_noalloc keeps them in the library and needs
+ * the first 3 words only).  Reset it once before first use; calls
  * on one state must not overlap.  The amax feeds lpq_nvfp4_qdq (the W4A4
  * activation fake-quant) or lpq_nvfp4_global_scale[_reciprocal] (the exported
  * input_scale / input_global_scale). */
@@ -362,6 +363,27 @@ lpq_status lpq_observer_reset(float* state, void* stream);
  * the three kinds: LPQ_ERR_ARG. */
 lpq_status lpq_nvfp4_observe(const uint16_t* x, int64_t M, int64_t N, int observer, float averaging_constant,
                              float* state, float* amax, void* stream);
+
+/* For callers that cannot allocate device memory per observed tensor beyond
+ * its statistics (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): lpq_nvfp4_observe with the call's control words (the
+ * batch keys and the arrival counter) in a 512-byte block the library holds on
+ * each device, instead of in the state.
+ *   state: 3 FP32 words of caller-owned device memory, 4-byte aligned --
+ *          [0] min, [1] max, [2] batches seen, as in lpq_nvfp4_observe's state
+ *          (zero them, or lpq_observer_reset a full state, before first use);
+ *          words past [2] are neither read nor written.
+ *   Everything else (x, observer, averaging_constant, amax, the checks and
+ *   their statuses) is as in lpq_nvfp4_observe; the control block is fixed
+ *   in size, so the only size limit is that call's (LPQ_ERR_SHAPE beyond it).
+ * The block is re-armed by a one-workgroup kernel at the start of every call,
+ * on the call's stream.  It is shared by every call of this function on one
+ * device, and lives until the process ends: calls that overlap on one device
+ * (two streams, two threads) race and give wrong statistics.  The first call
+ * on a device looks up the block's address there (LPQ_ERR_HIP if that fails);
+ * no call allocates memory. */
+lpq_status lpq_nvfp4_observe_noalloc(const uint16_t* x, int64_t M, int64_t N, int observer,
+                                     float averaging_constant, float* state, float* amax, void* stream);
 
 /* The multiplier form of a global scale, out[i] = fl(amax[i] / 2688), for n
  * device FP32 values (the input_scale / weight_scale_2 export of "verl NVFP4

@@ -79,6 +79,7 @@ _SIG = {
     "lpq_nvfp4_qdq_grouped_ex": (_int, [_tp, _vp, _i32, _vp, _i32, _int, _int, _vp]),
     "lpq_observer_reset": (_int, [_vp, _vp]),
     "lpq_nvfp4_observe": (_int, [_vp, _i64, _i64, _int, ctypes.c_float, _vp, _vp, _vp]),
+    "lpq_nvfp4_observe_noalloc": (_int, [_vp, _i64, _i64, _int, ctypes.c_float, _vp, _vp, _vp]),
     "lpq_nvfp4_amax": (_int, [_vp, _i64, _i64, _vp, _int, _vp]),
     "lpq_quantize_nvfp4": (_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "lpq_dequantize_nvfp4": (_int, [_vp, _vp, _vp, _i64, _i64, _vp, _vp]),
@@ -353,6 +354,20 @@ def lpq_nvfp4_observe(x, state, observer="static_minmax", averaging_constant=0.0
     kind = OBSERVERS[observer] if isinstance(observer, str) else int(observer)
     _check(_L.lpq_nvfp4_observe(x.data_ptr(), M, N, kind, float(averaging_constant), state.data_ptr(),
                                 amax.data_ptr(), _stream(stream)), "lpq_nvfp4_observe")
+    return amax
+
+
+def lpq_nvfp4_observe_noalloc(x, state, observer="static_minmax", averaging_constant=0.01, amax=None, stream=None):
+    """lpq_nvfp4_observe with the call's control words in a block the library holds on
+    the device: ``state`` needs only 3 FP32 words (min, max, batches seen).  Calls
+    that overlap on one device race."""
+    x = _bf16_in(x, "x")
+    M, N = x.shape
+    _f32_words(state, "state", x, 3)
+    amax = _empty((1,), torch.float32, x) if amax is None else _f32_words(amax, "amax", x)
+    kind = OBSERVERS[observer] if isinstance(observer, str) else int(observer)
+    _check(_L.lpq_nvfp4_observe_noalloc(x.data_ptr(), M, N, kind, float(averaging_constant), state.data_ptr(),
+                                        amax.data_ptr(), _stream(stream)), "lpq_nvfp4_observe_noalloc")
     return amax
 
 

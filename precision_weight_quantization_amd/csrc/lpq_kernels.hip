@@ -34,6 +34,8 @@
 #include <hip/hip_bf16.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "lpq.h"
 #include "lpq_device.hpp"
 
@@ -503,6 +505,69 @@ lpq_status nvfp4_grouped(Kind k, const lpq_tensor* host, const lpq_tensor* dev, 
     return launch<lpq_tensor>(k, host, dev, n, lpq_tensor{}, group_amax, k == NV_Q ? group_g : nullptr, s, gdiv);
 }
 
+// Host-side checks of an observer call; the workgroup count on success.
+lpq_status observe_args(const uint16_t* x, int64_t M, int64_t N, int observer, const float* state, const float* amax,
+                        lpq_tensor* one, int64_t* units) {
+    if (!state || !amax) return LPQ_ERR_NULL;
+    if (!aligned(state, 4) || !aligned(amax, 4)) return LPQ_ERR_ALIGN;
+    if (observer < LPQ_OBSERVER_MEMORYLESS_MINMAX || observer > LPQ_OBSERVER_MINMAX) return LPQ_ERR_ARG;
+    *one = make_one(x, nullptr, nullptr, M, N);
+    lpq_status st = check_tensor(NV_AMAX, *one, 0);   // same shape and alignment rules as the amax pass
+    if (st != LPQ_OK) return st;
+    *units = (M * N + chunk_elems<LPQ_AMAX_U>() - 1) / chunk_elems<LPQ_AMAX_U>();
+    return *units > kMaxGridX ? LPQ_ERR_SHAPE : LPQ_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// The allocation-free observer call keeps the control words of a call (batch
+// keys and arrival counter) in a block the library holds, instead of in the
+// caller's state.  Every device the library runs on holds its own copy of the
+// block until the process ends.  All such calls on one device share it: each
+// call re-arms it first, and calls that overlap on one device race.
+
+static __device__ __align__(256) uint32_t scratch[kObsCtlWords];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<uint32_t*> g_scratch_ptr[kMaxScratchDevices];
+
+inline lpq_status hip_failed(hipError_t e) {
+    g_last_hip_error = (int)e;
+    return LPQ_ERR_HIP;
+}
+
+// The device address of `scratch` on the device that `stream` runs on (the
+// current device for the null stream).  It is looked up once per device, with
+// that device current, and kept: on the host the name `scratch` is a stand-in,
+// not a device address, and each device holds the block at its own address.
+lpq_status scratch_on(hipStream_t stream, uint32_t** out) {
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_failed(e);
+    if (dev < 0 || dev >= kMaxScratchDevices) return hip_failed(hipErrorInvalidDevice);
+    uint32_t* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return hip_failed(e);
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_failed(e);
+        void* q = nullptr;
+        e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess) e = r;
+        }
+        if (e != hipSuccess) return hip_failed(e);
+        if (!q) return hip_failed(hipErrorInvalidSymbol);
+        p = static_cast<uint32_t*>(q);
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return LPQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -572,16 +637,27 @@ lpq_status lpq_observer_reset(float* state, void* stream) {
 
 lpq_status lpq_nvfp4_observe(const uint16_t* x, int64_t M, int64_t N, int observer, float averaging_constant,
                              float* state, float* amax, void* stream) {
-    if (!state || !amax) return LPQ_ERR_NULL;
-    if (!aligned(state, 4) || !aligned(amax, 4)) return LPQ_ERR_ALIGN;
-    if (observer < LPQ_OBSERVER_MEMORYLESS_MINMAX || observer > LPQ_OBSERVER_MINMAX) return LPQ_ERR_ARG;
-    const lpq_tensor one = make_one(x, nullptr, nullptr, M, N);
-    lpq_status st = check_tensor(NV_AMAX, one, 0);   // same shape and alignment rules as the amax pass
+    lpq_tensor one;
+    int64_t units = 0;
+    const lpq_status st = observe_args(x, M, N, observer, state, amax, &one, &units);
     if (st != LPQ_OK) return st;
-    const int64_t units = (M * N + chunk_elems<LPQ_AMAX_U>() - 1) / chunk_elems<LPQ_AMAX_U>();
-    if (units > kMaxGridX) return LPQ_ERR_SHAPE;
     hipLaunchKernelGGL((k_minmax<LPQ_AMAX_U>), dim3((unsigned)units), dim3(kThreads), 0, (hipStream_t)stream, one,
-                       observer, averaging_constant, reinterpret_cast<uint32_t*>(state), amax);
+                       observer, averaging_constant, state, reinterpret_cast<uint32_t*>(state), amax);
+    return launched();
+}
+
+lpq_status lpq_nvfp4_observe_noalloc(const uint16_t* x, int64_t M, int64_t N, int observer,
+                                     float averaging_constant, float* state, float* amax, void* stream) {
+    lpq_tensor one;
+    int64_t units = 0;
+    lpq_status st = observe_args(x, M, N, observer, state, amax, &one, &units);
+    if (st != LPQ_OK) return st;
+    uint32_t* ctl = nullptr;
+    if ((st = scratch_on((hipStream_t)stream, &ctl)) != LPQ_OK) return st;
+    hipLaunchKernelGGL(k_observer_arm, dim3(1), dim3(64), 0, (hipStream_t)stream, ctl);
+    if ((st = launched()) != LPQ_OK) return st;
+    hipLaunchKernelGGL((k_minmax<LPQ_AMAX_U>), dim3((unsigned)units), dim3(kThreads), 0, (hipStream_t)stream, one,
+                       observer, averaging_constant, state, ctl, amax);
     return launched();
 }
 

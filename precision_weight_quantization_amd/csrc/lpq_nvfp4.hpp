@@ -118,14 +118,18 @@ __device__ __forceinline__ v4u e2m1x8_to_bf16(uint32_t p, float S) {
 // ---------------------------------------------------------------------------
 //
 // Observer state (caller-owned device memory, LPQ_OBSERVER_STATE_FLOATS
-// words): [0] min, [1] max, [2] batches seen (FP32); then, each on a cache
-// line of its own so that the workgroups' atomics on them do not queue behind
-// one another, [32] / [64] the current batch's min / max as order-preserving
-// keys and [96] the number of workgroups of the current call that have folded
-// in their keys.  Keys map binary32 bits to unsigned integers whose order is
-// the values' order with -0 below +0: non-negative values get the sign bit
-// set, negative values have every bit flipped.
+// words): [0] min, [1] max, [2] batches seen (FP32); then the call's control
+// words, each on a cache line of its own so that the workgroups' atomics on
+// them do not queue behind one another: [32] / [64] the current batch's min /
+// max as order-preserving keys and [96] the number of workgroups of the
+// current call that have folded in their keys.  The kernels take the control
+// words through a pointer of their own (`ctl`, at the same offsets): the
+// state itself, or a block the library holds.  Keys map binary32 bits to
+// unsigned integers whose order is the values' order with -0 below +0:
+// non-negative values get the sign bit set, negative values have every bit
+// flipped.
 constexpr int kObsKeyMin = 32, kObsKeyMax = 64, kObsArrived = 96;
+constexpr int kObsCtlWords = 128;   // a control block: 512 bytes
 
 __device__ __forceinline__ uint32_t order_key(uint32_t u) { return (u >> 31) ? ~u : (u | 0x80000000u); }
 __device__ __forceinline__ uint32_t key_bits(uint32_t k) { return (k >> 31) ? (k & 0x7fffffffu) : ~k; }
@@ -134,14 +138,21 @@ __device__ __forceinline__ uint32_t umin(uint32_t a, uint32_t b) { return a < b 
 constexpr uint32_t kKeyMinIdentity = 0xffffffffu;
 constexpr uint32_t kKeyMaxIdentity = 0u;
 
+__device__ __forceinline__ void observer_arm(uint32_t* ctl) {
+    ctl[kObsKeyMin] = kKeyMinIdentity;
+    ctl[kObsKeyMax] = kKeyMaxIdentity;
+    ctl[kObsArrived] = 0u;
+}
+
 __global__ void k_observer_reset(uint32_t* state) {
     const int i = threadIdx.x;
     if (i < 3) state[i] = 0u;
-    if (i == 0) {
-        state[kObsKeyMin] = kKeyMinIdentity;
-        state[kObsKeyMax] = kKeyMaxIdentity;
-        state[kObsArrived] = 0u;
-    }
+    if (i == 0) observer_arm(state);
+}
+
+// Keys at their identities and no arrivals: a control block ready for a call.
+__global__ void k_observer_arm(uint32_t* ctl) {
+    if (threadIdx.x == 0) observer_arm(ctl);
 }
 
 __device__ __forceinline__ uint32_t dev_atomic_xchg(uint32_t* p, uint32_t v) {
@@ -153,10 +164,9 @@ __device__ __forceinline__ uint32_t dev_atomic_xchg(uint32_t* p, uint32_t v) {
 // order, as the definition: m += c * (b - m) for the moving average.  The keys
 // are taken (and reset to their identities) with device-scope atomic
 // exchanges, performed where the other workgroups' key atomics were.
-__device__ void observer_apply(int kind, float c, uint32_t* state, float* amax) {
-    float* f = reinterpret_cast<float*>(state);
-    const uint32_t kmin = dev_atomic_xchg(state + kObsKeyMin, kKeyMinIdentity);
-    const uint32_t kmax = dev_atomic_xchg(state + kObsKeyMax, kKeyMaxIdentity);
+__device__ void observer_apply(int kind, float c, float* f, uint32_t* ctl, float* amax) {
+    const uint32_t kmin = dev_atomic_xchg(ctl + kObsKeyMin, kKeyMinIdentity);
+    const uint32_t kmax = dev_atomic_xchg(ctl + kObsKeyMax, kKeyMaxIdentity);
     const float bmin = __uint_as_float(key_bits(kmin)), bmax = __uint_as_float(key_bits(kmax));
     float mn = f[0], mx = f[1];
     if (kind == LPQ_OBSERVER_MEMORYLESS_MINMAX || f[2] == 0.0f) {
@@ -180,7 +190,7 @@ __device__ void observer_apply(int kind, float c, uint32_t* state, float* amax) 
 // for another: each counts its arrival after its keys are in, and the one
 // that arrives last finds every key there).
 template <int U>
-__global__ __launch_bounds__(kThreads) void k_minmax(lpq_tensor one, int kind, float c, uint32_t* state,
+__global__ __launch_bounds__(kThreads) void k_minmax(lpq_tensor one, int kind, float c, float* state, uint32_t* ctl,
                                                      float* amax) {
     const int64_t total = one.rows * one.cols;
     const int64_t base = (int64_t)blockIdx.x * chunk_elems<U>();
@@ -218,13 +228,13 @@ __global__ __launch_bounds__(kThreads) void k_minmax(lpq_tensor one, int kind, f
             l = umin(l, plo[k]);
             h = umax(h, phi[k]);
         }
-        atomicMin(state + kObsKeyMin, l);
-        atomicMax(state + kObsKeyMax, h);
+        atomicMin(ctl + kObsKeyMin, l);
+        atomicMax(ctl + kObsKeyMax, h);
         // this workgroup's keys before its arrival; the last arriver's reads after every arrival
-        if (__hip_atomic_fetch_add(state + kObsArrived, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+        if (__hip_atomic_fetch_add(ctl + kObsArrived, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
             gridDim.x - 1) {
-            observer_apply(kind, c, state, amax);
-            __hip_atomic_store(state + kObsArrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // re-armed
+            observer_apply(kind, c, state, ctl, amax);
+            __hip_atomic_store(ctl + kObsArrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // re-armed
         }
     }
 }

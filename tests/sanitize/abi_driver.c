@@ -41,6 +41,8 @@ int main(void) {
     EXPECT(lpq_nvfp4_qdq(W, 4, 32, NULL, H, NULL), LPQ_ERR_ARG);   /* amax computed into y: x, y overlap */
     EXPECT(lpq_quantize_nvfp4_ex(W, 4, 32, F, 300, B, B, F, NULL), LPQ_ERR_ARG);
     EXPECT(lpq_nvfp4_observe(W, 4, 32, 7, 0.5f, F, F, NULL), LPQ_ERR_ARG);
+    EXPECT(lpq_nvfp4_observe_noalloc(W, 4, 32, 7, 0.5f, F, F, NULL), LPQ_ERR_ARG);
+    EXPECT(lpq_nvfp4_observe_noalloc(W, 4, 32, 1, 0.5f, NULL, F, NULL), LPQ_ERR_NULL);
     EXPECT(lpq_quantize_int4(W, 4, 128, 64, B, F, NULL), LPQ_ERR_ARG);
     EXPECT(lpq_requantize_fp8blk_mxfp8(B, F, (int64_t)1 << 31, 32, B, B, NULL), LPQ_ERR_SHAPE);
     EXPECT(lpq_nvfp4_global_scale_reciprocal(F, -5, F, NULL), LPQ_ERR_SHAPE);

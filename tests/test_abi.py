@@ -68,6 +68,15 @@ def test_single_call_validation(lib):
     assert L.lpq_nvfp4_observe(P, 4, 32, 3, 0.01, P, P, None) == 6            # unknown observer
     assert L.lpq_nvfp4_observe(P, 4, 24, 1, 0.01, P, P, None) == 2            # N % 16
     assert L.lpq_nvfp4_observe(P + 8, 4, 32, 1, 0.01, P, P, None) == 3
+    # the allocation-free observer refuses the same arguments before touching its device block
+    assert L.lpq_nvfp4_observe_noalloc(P, 4, 32, 1, 0.01, None, P, None) == 1
+    assert L.lpq_nvfp4_observe_noalloc(P, 4, 32, 1, 0.01, P, None, None) == 1
+    assert L.lpq_nvfp4_observe_noalloc(P, 4, 32, -1, 0.01, P, P, None) == 6
+    assert L.lpq_nvfp4_observe_noalloc(P, 4, 24, 1, 0.01, P, P, None) == 2
+    assert L.lpq_nvfp4_observe_noalloc(P, 0, 32, 1, 0.01, P, P, None) == 2
+    assert L.lpq_nvfp4_observe_noalloc(P, 4, 32, 1, 0.01, P + 2, P, None) == 3
+    assert L.lpq_nvfp4_observe_noalloc(P + 8, 4, 32, 1, 0.01, P, P, None) == 3
+    assert L.lpq_nvfp4_observe_noalloc(P, 1 << 40, 1 << 20, 1, 0.01, P, P, None) == 2   # beyond the grid limit
     assert L.lpq_dequantize_mxfp8(P, P, 4, 33, P, None) == 2
     assert L.lpq_dequantize_mxfp8(P + 4, P, 4, 32, P, None) == 3
     assert L.lpq_quantize_nvfp4(P, 4, 24, P, P, P, P, None) == 2
@@ -299,6 +308,8 @@ def test_binding_refuses_bad_tensors_before_any_call(lib, recorder):
         (ValueError, lambda: lib.lpq_dequantize_int4(u8(4, 32), f32(4, 1), 32)),
         (ValueError, lambda: lib.lpq_requantize_fp8blk_nvfp4(u8(4, 64), f32(1, 1), f32(1), sb=u8(4, 3))),
         (ValueError, lambda: lib.lpq_nvfp4_observe(w, f32(lib.OBSERVER_STATE_FLOATS - 1))),         # state too short
+        (ValueError, lambda: lib.lpq_nvfp4_observe_noalloc(w, f32(2))),                            # 3 words needed
+        (ValueError, lambda: lib.lpq_nvfp4_observe_noalloc(w, torch.zeros(3))),                    # host state
         (ValueError, lambda: lib.lpq_nvfp4_global_scale(f32(4), out=f32(3))),
     ]
     for exc, call in cases:

@@ -1,0 +1,84 @@
+"""The allocation-free observer call, lpq_nvfp4_observe_noalloc (its control
+words in a block the library holds on the device), against lpq_nvfp4_observe on
+the same batches, bit for bit: the activation amax and the min / max / batch
+count after each of two calls in a row, the second on a smaller, ragged batch.
+Both also match the oracle's observer update.  Batches are seeded synthetic
+activations (N(0, sigma) with 0.01% outliers x 100, the W4A4 workload's
+distribution)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from synth import synth
+from tests.gpu_util import to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lpq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import precision_weight_quantization_amd as m
+    return m
+
+
+def bits(t):
+    return t.detach().cpu().numpy().view(np.uint32)
+
+
+def f32_bits(v):
+    return np.asarray(v, np.float32).view(np.uint32)
+
+
+SHAPES = [(2048, 4096), (37, 2080)]   # the second call smaller, with a ragged last workgroup
+
+
+@pytest.mark.parametrize("kind", ["memoryless_minmax", "static_minmax", "minmax"])
+def test_noalloc_observer_matches_observe(lpq, kind):
+    c = 0.25 if kind == "minmax" else 0.0
+    ref_state = lpq.lpq_observer_reset(device="cuda")
+    # 8 words: the call uses [0, 3) and must leave the rest as they are
+    state = torch.full((8,), 7.0, dtype=torch.float32, device="cuda")
+    state[:3] = 0.0
+    ost = np.zeros(3, np.float32)
+    bad = 0
+    for t, (M, N) in enumerate(SHAPES):
+        print(f"  {kind} call {t}: {M}x{N}", flush=True)
+        x_np = synth.generate(4200 + M, t, M, N, 0.5 + t, 0.0, 1e-4, 100.0)
+        x = to_dev_bf16(x_np)
+        a_ref = lpq.lpq_nvfp4_observe(x, ref_state, kind, averaging_constant=c)
+        a = lpq.lpq_nvfp4_observe_noalloc(x, state, kind, averaging_constant=c)
+        a_or = O.observer_update(kind, ost, x_np, c=c)
+        bad += int((bits(a) != bits(a_ref)).sum()) + int((bits(state[:3]) != bits(ref_state[:3])).sum())
+        bad += int(bits(a)[0] != f32_bits(a_or)) + int((bits(state[:3]) != f32_bits(ost)).sum())
+    bad += int((state[3:].cpu() != 7.0).sum())
+    print(f"  {kind}: state {ost}", flush=True)
+    assert bad == 0
+
+
+def test_noalloc_observer_side_stream_and_interleaved(lpq):
+    """The block's address on the device of a non-default stream, and calls of the
+    two entry points interleaved on one stream (each with its own control words)."""
+    s = torch.cuda.Stream()
+    ref_state = lpq.lpq_observer_reset(device="cuda")
+    state = torch.zeros(3, dtype=torch.float32, device="cuda")
+    ost = np.zeros(3, np.float32)
+    bad = 0
+    for t, (M, N) in enumerate([(1024, 2048), (3, 48), (512, 1040)]):
+        print(f"  side stream call {t}: {M}x{N}", flush=True)
+        x_np = synth.generate(4300, t, M, N, 2.0 - 0.5 * t, 0.0, 1e-4, 100.0)
+        x = to_dev_bf16(x_np)
+        a = torch.empty(1, dtype=torch.float32, device="cuda")
+        a_ref = torch.empty(1, dtype=torch.float32, device="cuda")
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            lpq.lpq_nvfp4_observe(x, ref_state, "static_minmax", amax=a_ref, stream=s)
+            lpq.lpq_nvfp4_observe_noalloc(x, state, "static_minmax", amax=a, stream=s)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        a_or = O.observer_update("static_minmax", ost, x_np)
+        bad += int(bits(a)[0] != bits(a_ref)[0]) + int(bits(a)[0] != f32_bits(a_or))
+        bad += int((bits(state) != bits(ref_state[:3])).sum()) + int((bits(state) != f32_bits(ost)).sum())
+    assert bad == 0
