@@ -452,8 +452,9 @@ def time_next_rows(bench, steps: int):
                        "the Qwen3-30B-A3B weights held in block-wise FP8 (128x128 tiles, FP32 scales): the experts + "
                        "48 q/k/v (18,576 tensors) -> block-wise FP8; the 18,432 expert tensors -> MXFP8; the experts "
                        "+ q/k/v (12,336 sibling groups) -> NVFP4 with the model-wide amax pass; unfused = dequantize "
-                       "to BF16 in HBM, then quantize; the Qwen3-30B-A3B experts (18,432 tensors) -> group-wise INT4 "
-                       "(group 128) quantize, dequantize and QDQ")
+                       "to BF16 in HBM, then quantize; [fp8train-pow2] = the same fused re-quantizations with every tile "
+                       "scale cut to the power of two at or below it; the Qwen3-30B-A3B experts (18,432 tensors) -> "
+                       "group-wise INT4 (group 128) quantize, dequantize and QDQ")
     log(f"  fused speedup vs unfused: {sp}")
     return out
 

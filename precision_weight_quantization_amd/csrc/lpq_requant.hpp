@@ -407,10 +407,14 @@ __global__ __launch_bounds__(TH) void k_fp8blk_dequant_flat(const lpq_tensor* ta
 }
 
 // Block-wise FP8 -> block-wise FP8, TW adjacent 128x128 tiles per workgroup:
-// each tile's dequantized values y = BF16(fl(code * s)) stay in registers (16
-// codes per lane per pass), their amax gives the new scale s' = fl(amax/448),
-// and each y is encoded as E4M3(fl(y / s')).  Lane t covers codes
-// 16*(t % (8 TW)) .. +16 of rows (TW*256/(8 TW))*pass + t / (8 TW).
+// each tile's codes stay in registers (16 per lane per pass); the amax of the
+// dequantized values y = BF16(fl(code * s)) gives the new scale
+// s' = fl(amax/448), and each y is encoded as E4M3(fl(y / s')).  Lane t covers
+// codes 16*(t % (8 TW)) .. +16 of rows (TW*256/(8 TW))*pass + t / (8 TW).
+// The new code depends on the old code alone once s and s' are fixed, so each
+// tile's 256 possible codes are encoded once (one per lane of the tile, the
+// same operations as per element) into a table in LDS, and every element then
+// takes its new code from the table.
 template <int TW>
 struct RqWideShape {
     static constexpr int threads = 256 * TW;
@@ -440,6 +444,7 @@ __global__ __launch_bounds__(256 * TW) void k_requant_fp8blk(const lpq_requant_t
     const bool present = sub * kTile < cols;
     const float s = present ? d.src_scale[tr * tn + tcw * TW + sub] : 0.0f;
     const int64_t origin = r0 * N + c0;             // offset of the strip in the tensor
+    __shared__ uint32_t recode[TW * 64];            // new code of each old code, 256 bytes per tile
 
     // FAST: 16-byte aligned rows (N % 16 == 0, so a lane's 16 columns are all inside
     // the tensor or all outside) whose buffer offsets (< 128 * N) fit 32 bits; edge
@@ -497,27 +502,27 @@ __global__ __launch_bounds__(256 * TW) void k_requant_fp8blk(const lpq_requant_t
         const bool tiny = s2 > 0.0f && s2 < kTinyScale;
         const float sd = tiny ? s2 * kPreScale : s2;
         const float r = s2 > 0.0f ? rcp_rn(sd) : 0.0f;
-        const bool any_tiny = any_lane(tiny);
+        {
+            // this lane's entry of its tile's table: old code `cd` (the tile's 256
+            // lanes take the 256 codes), y = BF16(fl(code * s)), then E4M3(fl(y / s'))
+            // (y and s' pre-scaled alike when s' is tiny)
+            const uint32_t cd = ((uint32_t)lr << 3) | ((uint32_t)tid & 7u);
+            const float2_t v = __builtin_amdgcn_cvt_pk_f32_fp8((int)cd, false);
+            float x = __uint_as_float(bf16_in_f32(v[0] * s));
+            if (tiny) x *= kPreScale;
+            const float qv = quot_rn(x, sd, r);
+            reinterpret_cast<uint8_t*>(recode)[sub * 256 + cd] = (uint8_t)e4m3x2<false>(qv, qv, 0u);
+        }
+        __syncthreads();
+        const uint8_t* lut = reinterpret_cast<const uint8_t*>(recode) + sub * 256;
 
         auto encode = [&](int p, const v4u& cp) {
-            const Y16 y = fp8blk_values16(cp, s);
-            float x[16];
-#pragma unroll
-            for (int k = 0; k < 8; k++) {
-                x[k] = y.lo.x[k];
-                x[8 + k] = y.hi.x[k];
-            }
-            if (any_tiny) {
-#pragma unroll
-                for (int k = 0; k < 16; k++) x[k] *= tiny ? kPreScale : 1.0f;
-            }
+            const uint32_t w[4] = {cp.x, cp.y, cp.z, cp.w};
             uint32_t o[4];
 #pragma unroll
-            for (int k = 0; k < 4; k++) {
-                const float q0 = quot_rn(x[4 * k + 0], sd, r), q1 = quot_rn(x[4 * k + 1], sd, r);
-                const float q2 = quot_rn(x[4 * k + 2], sd, r), q3 = quot_rn(x[4 * k + 3], sd, r);
-                o[k] = e4m3x2<true>(q2, q3, e4m3x2<false>(q0, q1, 0u));
-            }
+            for (int k = 0; k < 4; k++)
+                o[k] = (uint32_t)lut[w[k] & 0xffu] | ((uint32_t)lut[(w[k] >> 8) & 0xffu] << 8) |
+                       ((uint32_t)lut[(w[k] >> 16) & 0xffu] << 16) | ((uint32_t)lut[w[k] >> 24] << 24);
             const int64_t row = S::rows_per_pass * p + lr;
             if constexpr (FAST) {
                 if (in_c && row < rows)
