@@ -66,7 +66,9 @@ typedef enum lpq_status {
     LPQ_OK = 0,
     LPQ_ERR_NULL = 1,   /* a required pointer is NULL                                   */
     LPQ_ERR_SHAPE = 2,  /* M or N <= 0, N not a multiple of the block (32 MXFP8, 16
-                           NVFP4), or a tensor count <= 0                               */
+                           NVFP4), a tensor count <= 0, or a tensor beyond the size
+                           limits (M * N above 2^40 for every call; tighter limits are
+                           stated where a call has one)                                 */
     LPQ_ERR_ALIGN = 3,  /* a pointer is not aligned as required (see above)             */
     LPQ_ERR_GROUP = 4,  /* an NVFP4 sibling-group index is outside [0, n_groups)        */
     LPQ_ERR_HIP = 5,    /* a HIP launch failed; lpq_last_hip_error() holds the code     */
@@ -375,7 +377,8 @@ lpq_status lpq_nvfp4_observe(const uint16_t* x, int64_t M, int64_t N, int observ
  *          words past [2] are neither read nor written.
  *   Everything else (x, observer, averaging_constant, amax, the checks and
  *   their statuses) is as in lpq_nvfp4_observe; the control block is fixed
- *   in size, so the only size limit is that call's (LPQ_ERR_SHAPE beyond it).
+ *   in size, so the only size limit is that call's: M * N up to 2^40
+ *   elements, LPQ_ERR_SHAPE beyond.
  * The block is re-armed by a one-workgroup kernel at the start of every call,
  * on the call's stream.  It is shared by every call of this function on one
  * device, and lives until the process ends: calls that overlap on one device
