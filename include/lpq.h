@@ -25,8 +25,10 @@
  * Conventions (all entry points):
  *  - Pointers are DEVICE pointers unless stated otherwise.  The caller owns
  *    every buffer; the library never allocates, frees or synchronizes, keeps
- *    no state between calls (apart from the thread-local last HIP error) and
- *    is safe to call from several host threads.
+ *    no state between calls (apart from the thread-local last HIP error, and
+ *    the per-device control block of lpq_nvfp4_observe_noalloc, whose calls
+ *    must not overlap on one device) and is safe to call from several host
+ *    threads.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Work is enqueued asynchronously; a kernel fault surfaces at the caller's
  *    next synchronization.  A call enqueues kernels only (no memset, copy or
