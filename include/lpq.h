@@ -385,8 +385,9 @@ lpq_status lpq_nvfp4_observe(const uint16_t* x, int64_t M, int64_t N, int observ
  * on the call's stream.  It is shared by every call of this function on one
  * device, and lives until the process ends: calls that overlap on one device
  * (two streams, two threads) race and give wrong statistics.  The first call
- * on a device looks up the block's address there (LPQ_ERR_HIP if that fails);
- * no call allocates memory. */
+ * on a device looks up the block's address there (LPQ_ERR_HIP if that fails):
+ * make one before capturing a graph that holds the call.  No call allocates
+ * memory. */
 lpq_status lpq_nvfp4_observe_noalloc(const uint16_t* x, int64_t M, int64_t N, int observer,
                                      float averaging_constant, float* state, float* amax, void* stream);
 

@@ -11,7 +11,7 @@ import torch
 
 from oracle import oracle as O
 from synth import synth
-from tests.gpu_util import to_dev_bf16
+from tests.gpu_util import host_u16, report, same_bits, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -81,4 +81,41 @@ def test_noalloc_observer_side_stream_and_interleaved(lpq):
         a_or = O.observer_update("static_minmax", ost, x_np)
         bad += int(bits(a)[0] != bits(a_ref)[0]) + int(bits(a)[0] != f32_bits(a_or))
         bad += int((bits(state) != bits(ref_state[:3])).sum()) + int((bits(state) != f32_bits(ost)).sum())
+    assert bad == 0
+
+
+def test_noalloc_observer_in_a_graph(lpq):
+    """The allocation-free observer and the QDQ under its amax, captured once in a
+    HIP graph and replayed over a sequence of batches (the callers it is for run
+    under graph capture). One call before the capture makes the library look up
+    its device block. Between replays a new batch is copied into the captured
+    input, with eager work and a synchronisation. After every replay the 3-word
+    statistics, the amax and the QDQ output must equal the oracle's sequence, bit
+    for bit: the block is re-armed inside every replay."""
+    M, N = 2048, 2048
+    x = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    amax = torch.empty(1, dtype=torch.float32, device="cuda")
+    stats = torch.zeros(3, dtype=torch.float32, device="cuda")
+    lpq.lpq_nvfp4_observe_noalloc(x, stats, "minmax", averaging_constant=0.125, amax=amax)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        lpq.lpq_nvfp4_observe_noalloc(x, stats, "minmax", averaging_constant=0.125, amax=amax)
+        lpq.lpq_nvfp4_qdq(x, amax, y)
+    stats.zero_()   # start the sequence from fresh statistics
+    ost = np.zeros(3, np.float32)
+    bad = 0
+    for t in range(4):
+        print(f"  graph replay {t}", flush=True)
+        sigma = float(np.ldexp(1.0, 1 - t)) * (1.0 + 0.3 * t)
+        x_np = synth.generate(778, t, M, N, sigma, 0.0, 1e-4, 100.0)
+        x.copy_(to_dev_bf16(x_np))
+        torch.zeros(1024, device="cuda").sum().item()   # other eager work and a synchronisation
+        graph.replay()
+        torch.cuda.synchronize()
+        a = O.observer_update("minmax", ost, x_np, c=0.125)
+        bad += int(not same_bits(stats, ost))
+        bad += int(not same_bits(amax, np.float32(a)))
+        bad += report(f"graph no-alloc W4A4 replay {t}", host_u16(y), O.nvfp4_qdq(x_np, O.nvfp4_global_scale(a)))
     assert bad == 0
