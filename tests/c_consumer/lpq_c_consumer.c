@@ -30,6 +30,7 @@ void oc_nvfp4_qdq(const uint16_t* x, int64_t M, int64_t N, float g, uint16_t* y)
 void oc_int4_quantize(const uint16_t* w, int64_t M, int64_t N, int64_t G, uint8_t* p, float* s);
 void oc_int4_dequantize(const uint8_t* p, const float* s, int64_t M, int64_t N, int64_t G, uint16_t* y);
 void oc_int4_qdq(const uint16_t* x, int64_t M, int64_t N, int64_t G, uint16_t* y);
+float oc_observer_update(int kind, float c, float* state, const uint16_t* x, int64_t n);
 
 static int failures = 0;
 
@@ -156,6 +157,28 @@ int main(void) {
         printf("lpq_nvfp4_qdq with amax NULL and overlapping x, y was not refused with LPQ_ERR_ARG\n");
         failures++;
     }
+
+    /* W4A4 observer (moving average), twice in a row on the same batch: with the
+     * caller's full state, and with the library's own control block and a
+     * 3-word state (lpq_nvfp4_observe_noalloc) */
+    float* dstate = (float*)dev_alloc(LPQ_OBSERVER_STATE_FLOATS * 4);
+    float* dstats = (float*)dev_alloc(3 * 4);
+    float* damax2 = (float*)dev_alloc(4);
+    float ostate[3] = {0.0f, 0.0f, 0.0f}, oamax[2];
+    lpq_ok(lpq_observer_reset(dstate, NULL), "lpq_observer_reset");
+    HIP_OK(hipMemset(dstats, 0, 3 * 4));
+    for (int t = 0; t < 2; t++) {
+        const int64_t rows = t == 0 ? M : M / 3;   /* the second batch smaller */
+        lpq_ok(lpq_nvfp4_observe(dw, rows, N, LPQ_OBSERVER_MINMAX, 0.25f, dstate, damax, NULL), "lpq_nvfp4_observe");
+        lpq_ok(lpq_nvfp4_observe_noalloc(dw, rows, N, LPQ_OBSERVER_MINMAX, 0.25f, dstats, damax2, NULL),
+               "lpq_nvfp4_observe_noalloc");
+        HIP_OK(hipDeviceSynchronize());
+        oamax[t] = oc_observer_update(LPQ_OBSERVER_MINMAX, 0.25f, ostate, w, rows * N);
+        check(t == 0 ? "observer amax 1" : "observer amax 2", damax, &oamax[t], 4);
+        check(t == 0 ? "no-alloc amax 1" : "no-alloc amax 2", damax2, &oamax[t], 4);
+    }
+    check("observer state", dstate, ostate, 3 * 4);
+    check("no-alloc statistics", dstats, ostate, 3 * 4);
 
     /* group-wise INT4, group 128 */
     lpq_ok(lpq_quantize_int4(dw, M, N, 128, dq, ds4, NULL), "lpq_quantize_int4");

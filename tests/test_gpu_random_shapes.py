@@ -1,7 +1,8 @@
 """Seeded random shapes and magnitudes through every format, bit for bit against
 the oracle: block-wise FP8, MXFP8, NVFP4 (quantize, dequantize, QDQ) and INT4
 with groups of 32 and, where N allows, 128; and 12 more shapes through the fused
-FP8 re-quantizers (tile scales 2^lo .. 2^hi of both signs, lo from -60 to 19).
+FP8 re-quantizers (tile scales 2^lo .. 2^hi of both signs, lo from -60 to 19),
+and 12 with power-of-two tile scales from 2^-121 to 2^119.
 
 24 shapes are drawn once from a fixed seed: M from 1 to 1500, N a multiple of
 32 from 32 to 8192, so that most shapes end in a ragged chunk, tile or row band.
@@ -78,4 +79,33 @@ def test_random_shape_requant(lpq, i, M, N, lo, hi):
     q, s = random_case(M, N, 400 + i, lo, hi, signed=True)
     name = f"{M}x{N} scales 2^[{lo},{hi}]"
     print(f"  requant case {i}: {name}", flush=True)
+    assert check_fp8(lpq, q, s, name) + check_mx(lpq, q, s, name) + check_nv(lpq, q, s, name) == 0
+
+
+def _pow2_cases():
+    rng = np.random.default_rng(20261205)
+    out = []
+    for i in range(12):
+        M = int(rng.integers(1, 1501))
+        N = 32 * int(rng.integers(1, 257))
+        lo = int(rng.integers(-121, 100))
+        out.append((i, M, N, lo, min(119, lo + int(rng.integers(0, 60)))))
+    return out
+
+
+POW2_CASES = _pow2_cases()
+
+
+@pytest.mark.parametrize("i,M,N,lo,hi", POW2_CASES, ids=[f"{M}x{N}" for _, M, N, _, _ in POW2_CASES])
+def test_random_shape_requant_pow2(lpq, i, M, N, lo, hi):
+    """Seeded E4M3 codes under power-of-two tile scales 2^lo .. 2^hi (inside the
+    range where FP8 -> NVFP4 takes its scaled decode, up to both of its edges),
+    through the three fused FP8 re-quantizers."""
+    from oracle import oracle as O
+    from synth import synth
+    from tests.test_gpu_requant import check_fp8, check_mx, check_nv, pow2_scales
+    q = synth.e4m3_codes(500 + i, 1, M, N)
+    s = pow2_scales(O.fp8blk_scale_shape(M, N), 600 + i, list(range(lo, hi + 1)))
+    name = f"{M}x{N} scales 2^[{lo},{hi}]"
+    print(f"  requant pow2 case {i}: {name}", flush=True)
     assert check_fp8(lpq, q, s, name) + check_mx(lpq, q, s, name) + check_nv(lpq, q, s, name) == 0
