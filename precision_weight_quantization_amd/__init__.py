@@ -360,7 +360,8 @@ def lpq_nvfp4_observe(x, state, observer="static_minmax", averaging_constant=0.0
 def lpq_nvfp4_observe_noalloc(x, state, observer="static_minmax", averaging_constant=0.01, amax=None, stream=None):
     """lpq_nvfp4_observe with the call's control words in a block the library holds on
     the device: ``state`` needs only 3 FP32 words (min, max, batches seen).  Calls
-    that overlap on one device race."""
+    that overlap on one device race.  Pass ``amax`` (1 FP32 on the device) for a call
+    that allocates nothing; without it this wrapper allocates the output."""
     x = _bf16_in(x, "x")
     M, N = x.shape
     _f32_words(state, "state", x, 3)
