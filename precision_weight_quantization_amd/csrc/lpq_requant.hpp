@@ -299,7 +299,8 @@ __device__ __forceinline__ void rq_nvfp4_steps(const lpq_requant_tensor& d, int6
 // learns from the scales alone (without waiting for its codes) whether all its
 // tiles have power-of-two scales, and runs the steps with the exact
 // scaled-convert dequantization if so (the block scales a trainer writes
-// unless FP32 block scales are asked for), else with multiply and rounding.
+// unless FP32 block scales are asked for: "Low Precision RL", "2. Unified
+// block-wise FP8"), else with multiply and rounding.
 template <int U, bool FULL, bool LARGE, int TH>
 __device__ __forceinline__ void rq_nvfp4_body(const lpq_requant_tensor& d, int64_t base, int64_t total,
                                               const GlobalScale& G) {
