@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak, GB/s
 GB = 1e9
+NEXT_CPU_STRIDE = 48   # the widening rows' oracle sample: every 48th tensor or sibling group
 
 
 def log(*a):
@@ -227,8 +228,14 @@ def linear_single_thread(min_seconds: float = 1.0):
 
 def next_rows_parity(bench, stride: int, threads: int):
     """Run each widening-row op and compare every `stride`-th tensor (NVFP4: sibling
-    group) of its outputs with the oracle.  The oracle starts from the BF16 weights:
-    it forms its own block-wise FP8 copy, then re-quantizes that."""
+    group) of its outputs with the oracle, timing the oracle per op.
+
+    The oracle starts from the BF16 weights: for the re-quantization rows it forms
+    its own block-wise FP8 copy (untimed, before the op's timed jobs), then
+    re-quantizes that.  Each op's sample is credited with the op's algorithmic
+    bytes in proportion to its share of the op's elements.  Returns the totals and,
+    per op, the oracle's rate on its sample (the unfused rows are checked, not timed:
+    their oracle is the fused rows')."""
     import numpy as np
     import torch
 
@@ -241,26 +248,30 @@ def next_rows_parity(bench, stride: int, threads: int):
     def h16(t):
         return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
-    jobs = []
+    per_op = []   # (op, [(prep, job, elements)], elements of the op)
     for op in bench.next_ops:
         op.run()
         torch.cuda.synchronize()
+        jobs = []
         if op.name.startswith("mxfp8.quantize.floor"):
             ws = bench.sets["moe_experts"]
             out = bench.outputs["moe"]
             for i in range(0, len(ws.specs), stride):
                 x, q, e = h16(ws.w[i]), h8(out["q"][i]), h8(out["e"][i])
 
-                def job(x=x, q=q, e=e):
+                def job(_, x=x, q=q, e=e):
                     oq, oe = O.mxfp8_floor_quantize(x)
                     return int((oq != q).sum() + (oe != e).sum())
-                jobs.append(job)
+                jobs.append((None, job, ws.specs[i].numel))
+            per_op.append((op, jobs, sum(sp.numel for sp in ws.specs)))
             continue
         if op.name.startswith("nvfp4.observe+qdq"):
             # the same batch every time: the static observer's extremes are that batch's
             a = bench.outputs["act"]
             x, y = h16(a["x"]), h16(a["y"])
-            jobs.append(lambda x=x, y=y: int((O.nvfp4_qdq(x, O.nvfp4_group_scale([x])[1]) != y).sum()))
+            jobs.append((None, lambda _, x=x, y=y: int((O.nvfp4_qdq(x, O.nvfp4_group_scale([x])[1]) != y).sum()),
+                         x.size))
+            per_op.append((op, jobs, x.size))
             continue
         if op.workload == "int4":
             ws = bench.sets["moe_experts"]
@@ -271,15 +282,18 @@ def next_rows_parity(bench, stride: int, threads: int):
                 if op.name.startswith("int4.quantize"):
                     p, s = h8(out["p"][i]), out["s"][i].cpu().numpy()
 
-                    def job(x=x, p=p, s=s):
+                    def job(_, x=x, p=p, s=s):
                         op_, os_ = O.int4_quantize(x, G)
                         return int((op_ != p).sum() + (os_.view(np.uint32) != s.view(np.uint32)).sum())
-                else:   # dequantize and QDQ both end in BF16(fl(code * s)) of the oracle's codes
+                    jobs.append((None, job, ws.specs[i].numel))
+                elif op.name.startswith("int4.dequantize"):   # from the oracle's own codes (untimed)
                     y = h16(out["y"][i])
-
-                    def job(x=x, y=y):
-                        return int((O.int4_dequantize(*O.int4_quantize(x, G), G) != y).sum())
-                jobs.append(job)
+                    jobs.append((lambda x=x: O.int4_quantize(x, G),
+                                 lambda c, y=y: int((O.int4_dequantize(*c, G) != y).sum()), ws.specs[i].numel))
+                else:   # QDQ: BF16(fl(code * s)) of the codes of the input, as the dequantized weight
+                    y = h16(out["y"][i])
+                    jobs.append((None, lambda _, x=x, y=y: int((O.int4_qdq(x, G) != y).sum()), ws.specs[i].numel))
+            per_op.append((op, jobs, sum(sp.numel for sp in ws.specs)))
             continue
         if op.workload not in ("fp8train", "fp8train-pow2") or op.name.startswith("requant.amax"):
             continue
@@ -295,18 +309,20 @@ def next_rows_parity(bench, stride: int, threads: int):
             for i in range(0, len(ws.specs), stride):
                 x, q, s8 = h16(ws.w[i]), h8(out["fq"][i]), out["fs"][i].cpu().numpy()
 
-                def job(x=x, q=q, s8=s8, fp8_of=fp8_of):
-                    oq, os_ = O.fp8blk_requantize_fp8blk(*fp8_of(x))
+                def job(src, q=q, s8=s8):
+                    oq, os_ = O.fp8blk_requantize_fp8blk(*src)
                     return int((oq != q).sum() + (os_.view(np.uint32) != s8.view(np.uint32)).sum())
-                jobs.append(job)
+                jobs.append((lambda x=x, f=fp8_of: f(x), job, ws.specs[i].numel))
+            per_op.append((op, jobs, sum(sp.numel for sp in ws.specs)))
         elif op.name.startswith("requant.mxfp8"):
             for i in out["ex"][::stride]:
                 x, q, e = h16(ws.w[i]), h8(out["mq"][i]), h8(out["me"][i])
 
-                def job(x=x, q=q, e=e, fp8_of=fp8_of):
-                    oq, oe = O.fp8blk_requantize_mxfp8(*fp8_of(x))
+                def job(src, q=q, e=e):
+                    oq, oe = O.fp8blk_requantize_mxfp8(*src)
                     return int((oq != q).sum() + (oe != e).sum())
-                jobs.append(job)
+                jobs.append((lambda x=x, f=fp8_of: f(x), job, ws.specs[i].numel))
+            per_op.append((op, jobs, sum(ws.specs[i].numel for i in out["ex"])))
         elif op.name.startswith("requant.nvfp4"):
             groups = {}
             for i, sp in enumerate(ws.specs):
@@ -318,17 +334,29 @@ def next_rows_parity(bench, stride: int, threads: int):
                 ps, ss = [h8(out["p"][i]) for i in idx], [h8(out["sb"][i]) for i in idx]
                 A_d, gg_d = np.float32(amax_d[gid]), np.float32(g_d[gid])
 
-                def job(xs=xs, ps=ps, ss=ss, A_d=A_d, gg_d=gg_d, fp8_of=fp8_of):
-                    A, g, res = O.fp8blk_requantize_nvfp4_group([fp8_of(x) for x in xs])
+                def job(srcs, ps=ps, ss=ss, A_d=A_d, gg_d=gg_d):
+                    A, g, res = O.fp8blk_requantize_nvfp4_group(srcs)
                     bad = int(np.float32(A) != A_d) + int(np.float32(g) != gg_d)
                     for (p, s), pp, sg in zip(res, ps, ss):
                         bad += int((p != pp).sum() + (s != sg).sum())
                     return bad
-                jobs.append(job)
+                jobs.append((lambda xs=xs, f=fp8_of: [f(x) for x in xs], job, sum(ws.specs[i].numel for i in idx)))
+            per_op.append((op, jobs, sum(sp.numel for sp in ws.specs)))
     O.default()
-    t0 = time.perf_counter()
-    res = O.run_parallel(lambda j: j(), jobs, threads)
-    return {"checked": len(jobs), "parity_mismatches": int(sum(res)), "seconds": round(time.perf_counter() - t0, 2)}
+    t_all, bad_all, n_all, rows = 0.0, 0, 0, {}
+    for op, jobs, op_elems in per_op:
+        preps = O.run_parallel(lambda j: j[0]() if j[0] else None, jobs, threads)   # untimed inputs
+        t0 = time.perf_counter()
+        res = O.run_parallel(lambda jp: jp[0][1](jp[1]), list(zip(jobs, preps)), threads)
+        dt = time.perf_counter() - t0
+        elems = sum(j[2] for j in jobs)
+        bad = int(sum(res))
+        t_all, bad_all, n_all = t_all + dt, bad_all + bad, n_all + len(jobs)
+        if ".unfused" not in op.name:
+            sample = op.bytes * elems / op_elems
+            rows[op.name] = {"GB/s": round(sample / dt / GB, 3), "sample_GB": round(sample / GB, 3),
+                             "seconds": round(dt, 2), "calls": len(jobs), "mismatches": bad}
+    return {"checked": n_all, "parity_mismatches": bad_all, "seconds": round(t_all, 2), "ops": rows}
 
 
 # --------------------------------------------------------------------------- HBM copy reference
@@ -567,6 +595,16 @@ def main():
         log(f"cpu baseline: {cpu['value']} GB/s, {cpu['parity_mismatches']} mismatches vs GPU, {cpu['seconds']} s; "
             f"one thread: {cpu['single_thread']['value']} GB/s ({cpu['single_thread']['sample']}); "
             f"one thread on the single Linear: {cpu['single_thread_linear']['value']} GB/s")
+        if next_rows is not None:
+            nr = next_rows_parity(bench, NEXT_CPU_STRIDE, threads)
+            next_rows["cpu_baseline"] = {
+                "kind": "oracle", "cores": threads, "unit": "GB/s",
+                "sample": f"every {NEXT_CPU_STRIDE}th tensor (NVFP4: sibling group) of each widening-row op, "
+                          "the whole activation for the observer row; the oracle's own block-FP8 copy of the "
+                          "weights is formed first, untimed",
+                "parity_mismatches": nr["parity_mismatches"], "seconds": nr["seconds"], "ops": nr["ops"]}
+            log(f"next rows, oracle: {nr['checked']} calls, {nr['parity_mismatches']} mismatches vs GPU, "
+                f"{nr['seconds']} s; " + ", ".join(f"{k} {v['GB/s']} GB/s" for k, v in nr["ops"].items()))
 
     result = {
         "metric": "quantize+dequant GB/s (bytes in+out) and % of HBM peak, per format, 1 GPU",
