@@ -1,4 +1,4 @@
-"""Calls on two streams at once share nothing.
+"""Calls on two streams at once share nothing, from one host thread or two.
 
 The library keeps no state of its own between or during calls (the observer
 state and the NVFP4 amax slots are the caller's), so independent calls may run
@@ -98,3 +98,35 @@ def test_two_streams_interleaved(lpq):
         fb()
     torch.cuda.synchronize()
     assert a.check("stream A") + b.check("stream B") == 0
+
+
+def test_two_host_threads(lpq):
+    """The same calls driven from two host threads at once (the binding releases the
+    interpreter lock inside each C call), each thread on its own stream and buffers,
+    each repeating its weight calls five times before its observer + QDQ: both
+    threads' outputs must still equal the oracle's, bit for bit."""
+    import threading
+    a, b = Lane(lpq, 503), Lane(lpq, 504)
+    errors = []
+
+    def drive(lane):
+        try:
+            steps = lane.steps()
+            for _ in range(5):
+                for f in steps[:5]:   # the weight calls
+                    f()
+            for f in steps[5:]:       # observer, then QDQ under its amax
+                f()
+            lane.stream.synchronize()
+        except Exception as e:   # reported by the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=drive, args=(lane,)) for lane in (a, b)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads)
+    torch.cuda.synchronize()
+    assert not errors, errors
+    assert a.check("thread A") + b.check("thread B") == 0
