@@ -91,7 +91,9 @@ __device__ __forceinline__ uint32_t e2m1x8(const F8& f, const BlockScale& B) {
     float q[8];
 #pragma unroll
     for (int k = 0; k < 8; k++) q[k] = quot_rn(x[k], B.Sd, B.r);
-    uint32_t p = 0;
+    // the four converts write the word's four bytes, so it starts from any value
+    // (one already in a register)
+    uint32_t p = __float_as_uint(q[0]);
     p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, q[0], q[1], 1.0f, 0);
     p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, q[2], q[3], 1.0f, 1);
     p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, q[4], q[5], 1.0f, 2);

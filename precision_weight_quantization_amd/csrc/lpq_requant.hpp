@@ -295,10 +295,10 @@ __device__ __forceinline__ void rq_nvfp4_steps(const lpq_requant_tensor& d, int6
     }
 }
 
-// Every load of a lane issued up front, its U tile scales first: the wave then
-// learns from the scales alone (without waiting for its codes) whether all its
-// tiles have power-of-two scales, and runs the steps with the exact
-// scaled-convert dequantization if so (the block scales a trainer writes
+// Every load of a lane issued up front, its U tile scales first (one scale when
+// all its steps fall in one tile): the wave then learns from the scales alone
+// (without waiting for its codes) whether all its tiles have power-of-two
+// scales, and runs the steps with the exact scaled-convert dequantization if so (the block scales a trainer writes
 // unless FP32 block scales are asked for: "Low Precision RL", "2. Unified
 // block-wise FP8"), else with multiply and rounding.
 template <int U, bool FULL, bool LARGE, int TH>
@@ -307,6 +307,25 @@ __device__ __forceinline__ void rq_nvfp4_body(const lpq_requant_tensor& d, int64
     const v4u* src = reinterpret_cast<const v4u*>(d.src) + base / 16 + threadIdx.x;
     TileCursor<16, TH> cur(d.src_scale, d.cols, base);
     v4u c[U];
+    // A full chunk whose steps are whole rows apart (N divides the step) and whose
+    // rows stay inside every lane's tile row gives each lane one tile for all its
+    // steps: one scale load, no walk (uniform test).
+    if (FULL && cur.sc == 0u && !any_lane((cur.r >> 7) != ((cur.r + (U - 1) * cur.sr) >> 7))) {
+        const float s0 = load<false>(cur.ptr());
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            c[u] = load<kNTL>(src + u * TH);
+            __asm__ volatile("" ::: "memory");
+        }
+        const uint32_t b0 = __float_as_uint(s0);
+        const bool pow2 = (b0 & 0x807fffffu) == 0u && b0 >= (6u << 23) && b0 <= (246u << 23);
+        float s[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) s[u] = s0;
+        if (!any_lane(!pow2)) rq_nvfp4_steps<U, FULL, LARGE, true, TH>(d, base, total, G, c, s);
+        else rq_nvfp4_steps<U, FULL, LARGE, false, TH>(d, base, total, G, c, s);
+        return;
+    }
     float s[U];
 #pragma unroll
     for (int u = 0; u < U; u++) {
