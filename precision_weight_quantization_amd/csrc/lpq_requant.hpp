@@ -298,9 +298,10 @@ __device__ __forceinline__ void rq_nvfp4_steps(const lpq_requant_tensor& d, int6
 // Every load of a lane issued up front, its U tile scales first (one scale when
 // all its steps fall in one tile): the wave then learns from the scales alone
 // (without waiting for its codes) whether all its tiles have power-of-two
-// scales, and runs the steps with the exact scaled-convert dequantization if so (the block scales a trainer writes
-// unless FP32 block scales are asked for: "Low Precision RL", "2. Unified
-// block-wise FP8"), else with multiply and rounding.
+// scales, and runs the steps with the exact scaled-convert dequantization if so
+// (the block scales a trainer writes unless FP32 block scales are asked for:
+// "Low Precision RL", "2. Unified block-wise FP8"), else with multiply and
+// rounding.  Both paths test the same range, 2^k with -121 <= k <= 119.
 template <int U, bool FULL, bool LARGE, int TH>
 __device__ __forceinline__ void rq_nvfp4_body(const lpq_requant_tensor& d, int64_t base, int64_t total,
                                               const GlobalScale& G) {
